@@ -1,0 +1,541 @@
+"""Pins of the CPU oracle against what the pages and mathematics fix (no GPU).
+
+Each test checks the oracle against something other than itself: a closed
+form, a textbook or library routine, an invariant, brute force on tiny inputs,
+or a value the pages print.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+from scipy import special, stats
+
+import oracle
+from oracle import drafter as od
+from synth import TINY, inputs, rng
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------- rounding
+
+def test_bf16_rounding_ties_and_ranges():
+    r = oracle.round_bf16
+    assert r(1.0) == 1.0
+    assert r(1 + 2.0 ** -8) == 1.0                      # tie -> even mantissa
+    assert r(1 + 3 * 2.0 ** -8) == 1 + 2.0 ** -6         # tie -> even (upward)
+    assert r(1 + 2.0 ** -8 + 2.0 ** -30) == 1 + 2.0 ** -7
+    assert r(-2.5) == -2.5
+    assert r(float.fromhex("0x1.fep127")) == float.fromhex("0x1.fep127")
+    assert np.isinf(r(float.fromhex("0x1.ffp127")))       # rounds past the largest finite
+    assert r(2.0 ** -133) == 2.0 ** -133                 # smallest subnormal
+    assert r(2.0 ** -134) == 0.0                         # tie with zero -> even (zero)
+    assert np.isnan(r(np.nan))
+
+
+def test_bf16_rounding_matches_bit_trick_on_fp32():
+    # textbook route for fp32 inputs: add 0x7FFF + lsb to the bits, truncate
+    x = np.random.default_rng(0).standard_normal(200_000).astype(np.float32) * 10
+    b = x.view(np.uint32).astype(np.uint64)
+    bits = ((b + 0x7FFF + ((b >> 16) & 1)) >> 16).astype(np.uint16)
+    np.testing.assert_array_equal(oracle.f64_to_bf16_bits(x.astype(np.float64)), bits)
+    back = oracle.bf16_bits_to_f64(bits)
+    np.testing.assert_array_equal(back, oracle.round_bf16(x.astype(np.float64)))
+    assert oracle.bf16_bits_to_f64(np.uint16(0x3F80)) == 1.0
+    assert oracle.bf16_bits_to_f64(np.uint16(0xC000)) == -2.0
+
+
+# ---------------------------------------------------------------- RMSNorm
+
+def test_rmsnorm_closed_forms():
+    y = od.rmsnorm(np.array([3.0, 4.0]), np.ones(2), 0.0)
+    np.testing.assert_allclose(y, np.array([3.0, 4.0]) / np.sqrt(12.5), rtol=1e-15)
+    x = np.random.default_rng(1).standard_normal((7, 64)) * 5
+    y = od.rmsnorm(x, np.ones(64), 0.0)
+    np.testing.assert_allclose(np.sqrt(np.mean(y * y, axis=1)), 1.0, rtol=1e-12)   # unit RMS
+    np.testing.assert_allclose(od.rmsnorm(3.7 * x, np.ones(64), 0.0), y, rtol=1e-12)  # scale free
+    g = np.linspace(0.5, 2.0, 64)
+    np.testing.assert_allclose(od.rmsnorm(x, g, 0.0), y * g, rtol=1e-12)
+    # eps: a zero row stays zero instead of dividing by zero
+    assert np.all(od.rmsnorm(np.zeros(8), np.ones(8), 1e-6) == 0)
+
+
+# ---------------------------------------------------------------- RoPE
+
+def _rope_complex(x, pos, theta):
+    """Rotary embedding as complex multiplication: (x_i + i x_{i+d/2}) * exp(i pos w_i)."""
+    d = x.shape[-1]
+    half = d // 2
+    w = theta ** (-np.arange(half) * 2.0 / d)
+    z = (x[..., :half] + 1j * x[..., half:]) * np.exp(1j * np.asarray(pos)[..., None, None] * w)
+    return np.concatenate([z.real, z.imag], axis=-1)
+
+
+def test_rope_is_complex_rotation():
+    g = np.random.default_rng(2)
+    x = g.standard_normal((5, 3, 16))
+    pos = np.array([0, 1, 7, 300, 32767])
+    out = od.rope_rotate(x, pos, 1e6)
+    np.testing.assert_allclose(out, _rope_complex(x, pos, 1e6), atol=1e-12)
+    np.testing.assert_allclose(out[0], x[0], atol=0)                           # position 0
+    np.testing.assert_allclose(np.linalg.norm(out, axis=-1), np.linalg.norm(x, axis=-1),
+                               rtol=1e-12)
+    # d = 2: a plain 2-D rotation by pos radians
+    v = np.array([[[1.0, 0.0]]])
+    np.testing.assert_allclose(od.rope_rotate(v, np.array([np.pi / 2]), 10.0), [[[0.0, 1.0]]],
+                               atol=1e-15)
+    assert np.array_equal(od.rope_rotate(x, pos, 0.0), x)                      # disabled
+
+
+def test_rope_scores_depend_on_relative_position():
+    g = np.random.default_rng(3)
+    q = g.standard_normal((1, 1, 32))
+    k = g.standard_normal((1, 1, 32))
+    s = [float(np.sum(od.rope_rotate(q, np.array([m + t]), 1e4) *
+                      od.rope_rotate(k, np.array([n + t]), 1e4)))
+         for (m, n, t) in [(10, 3, 0), (10, 3, 1000), (10, 3, 77)]]
+    np.testing.assert_allclose(s, s[0], rtol=1e-10)
+
+
+# ---------------------------------------------------------------- attention
+
+def _bruteforce_block_attention(q, k_ctx, v_ctx, k_blk, v_blk):
+    """Whole sequence [context ; block] with an explicit 0/-inf mask matrix built
+    from the rule: full attention inside the block, causal toward the context."""
+    C = k_ctx.shape[0]
+    S, nq, d = q.shape
+    nkv = k_ctx.shape[1]
+    n = C + S
+    keys = np.concatenate([k_ctx, k_blk])
+    vals = np.concatenate([v_ctx, v_blk])
+    rep = nq // nkv
+    keys = np.repeat(keys, rep, axis=1)          # [n, nq, d]
+    vals = np.repeat(vals, rep, axis=1)
+    mask = np.full((n, n), -np.inf)
+    for i in range(n):
+        for j in range(n):
+            in_block_i, in_block_j = i >= C, j >= C
+            if in_block_i and in_block_j:
+                mask[i, j] = 0.0                 # full attention inside the block
+            elif j <= i and not in_block_j:
+                mask[i, j] = 0.0                 # causal toward the (earlier) context
+    qfull = np.zeros((n, nq, d))
+    qfull[C:] = q
+    out = np.zeros((S, nq, d))
+    for h in range(nq):
+        s = qfull[:, h] @ keys[:, h].T / np.sqrt(d) + mask
+        p = special.softmax(s[C:], axis=1)
+        out[:, h] = p @ vals[:, h]
+    return out
+
+
+@pytest.mark.parametrize("C,S,nq,nkv", [(37, 5, 6, 2), (0, 4, 4, 4), (9, 1, 8, 2), (64, 16, 4, 1)])
+def test_block_attention_matches_bruteforce_mask(C, S, nq, nkv):
+    g = np.random.default_rng(C * 100 + S)
+    d = 16
+    q = g.standard_normal((S, nq, d))
+    kc, vc = g.standard_normal((C, nkv, d)), g.standard_normal((C, nkv, d))
+    kb, vb = g.standard_normal((S, nkv, d)), g.standard_normal((S, nkv, d))
+    np.testing.assert_allclose(od.block_attention(q, kc, vc, kb, vb),
+                               _bruteforce_block_attention(q, kc, vc, kb, vb), atol=1e-12)
+
+
+def test_block_attention_special_cases():
+    g = np.random.default_rng(5)
+    C, S, nq, nkv, d = 20, 3, 4, 2, 8
+    q = g.standard_normal((S, nq, d))
+    kc, vc = g.standard_normal((C, nkv, d)), g.standard_normal((C, nkv, d))
+    kb, vb = g.standard_normal((S, nkv, d)), g.standard_normal((S, nkv, d))
+    o = od.block_attention(q, kc, vc, kb, vb)
+    # GQA == MHA with each key/value head repeated for its query group
+    o_mha = od.block_attention(q, np.repeat(kc, 2, 1), np.repeat(vc, 2, 1),
+                               np.repeat(kb, 2, 1), np.repeat(vb, 2, 1))
+    np.testing.assert_allclose(o, o_mha, atol=1e-12)
+    # permuting the context rows (no positions involved here) changes nothing
+    perm = g.permutation(C)
+    np.testing.assert_allclose(od.block_attention(q, kc[perm], vc[perm], kb, vb), o, atol=1e-12)
+    # zero queries: uniform weights over all C + S visible keys
+    o0 = od.block_attention(np.zeros_like(q), kc, vc, kb, vb)
+    mean_v = np.concatenate([vc, vb]).mean(0)                       # [nkv, d]
+    np.testing.assert_allclose(o0, np.broadcast_to(np.repeat(mean_v, 2, 0), o0.shape), atol=1e-12)
+    # S = 1: plain decode attention of one query over C + 1 keys
+    o1 = od.block_attention(q[:1], kc, vc, kb[:1], vb[:1])
+    keys = np.concatenate([kc, kb[:1]])[:, 0]
+    vals = np.concatenate([vc, vb[:1]])[:, 0]
+    w = special.softmax(keys @ q[0, 0] / np.sqrt(d))
+    np.testing.assert_allclose(o1[0, 0], w @ vals, atol=1e-12)
+
+
+# ---------------------------------------------------------------- drafter
+
+def _tiny(**kw):
+    base = dict(batch=2, block=4, ctx=24, n_layers=1, hidden=32, n_q_heads=4, n_kv_heads=2,
+                head_dim=8, mlp_dim=48, vocab=50, n_target_layers=3, markov_rank=4)
+    base.update(kw)
+    return TINY.with_(name="pin", **base)
+
+
+def _shape(w):
+    return od.DrafterShape.of(w)
+
+
+def _run(w, weights, step, kc, vc):
+    kc, vc = kc.copy(), vc.copy()
+    logits, new_len = od.draft_step(_shape(w), weights, step["hidden_new"], step["n_new"], kc, vc,
+                                    step["ctx_len"], step["last_token"])
+    return logits, new_len, kc, vc
+
+
+def test_kv_injection_context_kv_independent_of_block_and_shared_across_layers():
+    w = _tiny(n_layers=3)
+    weights = inputs.drafter_weights(w, 0, gain_std=0.1)
+    for l in (1, 2):                                      # same Wk, Wv in every layer
+        weights[f"layers.{l}.wk"] = weights["layers.0.wk"]
+        weights[f"layers.{l}.wv"] = weights["layers.0.wv"]
+    step = inputs.step_inputs(w, 0)
+    kc, vc = inputs.cache_prefix(w, 0, step["ctx_len"])
+    _, _, k1, v1 = _run(w, weights, step, kc, vc)
+    step2 = dict(step, last_token=(step["last_token"] + 7) % (w.vocab - 1))
+    _, _, k2, v2 = _run(w, weights, step2, kc, vc)
+    assert np.array_equal(k1, k2) and np.array_equal(v1, v2)    # block tokens do not matter
+    for b in range(w.batch):                                    # same features in every layer
+        c = step["ctx_len"][b]
+        new = slice(c, c + w.block)
+        for l in (1, 2):
+            assert np.array_equal(k1[l, b, new], k1[0, b, new])
+            assert np.array_equal(v1[l, b, new], v1[0, b, new])
+    # the appended slots are exactly ctx_len .. ctx_len + n_new - 1
+    for b in range(w.batch):
+        c = step["ctx_len"][b]
+        assert np.array_equal(k1[:, b, :c], kc[:, b, :c])
+        assert not np.array_equal(k1[:, b, c:c + w.block], kc[:, b, c:c + w.block])
+        assert np.array_equal(k1[:, b, c + w.block:], kc[:, b, c + w.block:])
+
+
+def test_drafter_closed_form_without_attention_and_mlp_output():
+    # Wo = 0 and W_down = 0: the residual stream stays at the embeddings, so every
+    # mask row's logits are RMSNorm(E[MASK]) . W_lm^T whatever the context
+    w = _tiny()
+    weights = inputs.drafter_weights(w, 1, gain_std=0.1)
+    weights["layers.0.wo"] = np.zeros_like(weights["layers.0.wo"])
+    weights["layers.0.w_down"] = np.zeros_like(weights["layers.0.w_down"])
+    step = inputs.step_inputs(w, 1)
+    kc, vc = inputs.cache_prefix(w, 1, step["ctx_len"])
+    logits, _, _, _ = _run(w, weights, step, kc, vc)
+    e = weights["embed"][w.mask_token_id].astype(np.float64)
+    g = weights["final_norm"].astype(np.float64)
+    z = e / np.sqrt(np.mean(e * e) + w.rms_eps) * g
+    z = z.astype(np.float32).astype(np.float64)
+    want = (weights["lm_head"].astype(np.float64) @ z).astype(np.float32)
+    for b in range(w.batch):
+        for j in range(w.gamma):
+            np.testing.assert_array_equal(logits[b, j], want)
+
+
+def _rms(x, g, eps):
+    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps) * g
+
+
+def _bruteforce_one_layer_drafter(w, weights, hidden_all, last_token):
+    """Sequence-level formulation of a 1-layer drafter with its MLP switched off:
+    every context row j (features at position j) and every block row (position
+    C + j) projects its own keys and values; only block rows query; an explicit
+    mask implements full-in-block / causal-to-context.  fp32 storage throughout."""
+    f32 = lambda a: np.asarray(a, np.float64).astype(np.float32).astype(np.float64)
+    W = {k: np.asarray(v, np.float64) for k, v in weights.items()}
+    C = hidden_all.shape[0]
+    S, H, nq, nkv, d = w.block, w.hidden, w.n_q_heads, w.n_kv_heads, w.head_dim
+    feats = f32(_rms(hidden_all @ W["fc"].T, W["fc_norm"], w.rms_eps))
+    toks = [last_token] + [w.mask_token_id] * (S - 1)
+    x = f32(W["embed"][toks])
+    a = f32(_rms(x, W["layers.0.attn_norm"], w.rms_eps))
+    rows = np.concatenate([feats, a])                           # [C + S, H]
+    pos = np.arange(C + S)
+    k = f32(_rope_complex((rows @ W["layers.0.wk"].T).reshape(-1, nkv, d), pos, w.rope_theta))
+    v = f32((rows @ W["layers.0.wv"].T).reshape(-1, nkv, d))
+    q = f32(_rope_complex((a @ W["layers.0.wq"].T).reshape(-1, nq, d), pos[C:], w.rope_theta))
+    o = _bruteforce_block_attention(q, k[:C], v[:C], k[C:], v[C:])
+    x = f32(x + f32(o).reshape(S, nq * d) @ W["layers.0.wo"].T)
+    z = f32(_rms(x[1:], W["final_norm"], w.rms_eps))
+    return (z @ W["lm_head"].T).astype(np.float32)
+
+
+@pytest.mark.parametrize("split", [None, 9])
+def test_drafter_matches_sequence_level_bruteforce(split):
+    # one layer, MLP output off, fp32; the context is appended in one call
+    # (prefill) or in two calls; positions come out of the cache bookkeeping
+    w = _tiny(batch=1, ctx=21, dtype="f32", rope_theta=100.0)
+    weights = inputs.drafter_weights(w, 2, gain_std=0.1)
+    weights["layers.0.w_down"] = np.zeros_like(weights["layers.0.w_down"])
+    C = 17
+    hid = rng.normal(2, "pin_hidden", (1, C, w.n_target_layers * w.hidden), 1.0)
+    last = np.array([5], np.int32)
+    sh = _shape(w)
+    kc = np.zeros((1, 1, w.max_ctx, w.n_kv_heads, w.head_dim), np.float32)
+    vc = np.zeros_like(kc)
+    ctx = np.zeros(1, np.int32)
+    for lo, hi in ([(0, C)] if split is None else [(0, split), (split, C)]):
+        logits, ctx = od.draft_step(sh, weights, hid[:, lo:hi], np.array([hi - lo]), kc, vc,
+                                    ctx, last)
+    assert ctx[0] == C
+    want = _bruteforce_one_layer_drafter(w, weights, hid[0].astype(np.float64), 5)
+    np.testing.assert_allclose(logits[0], want, atol=2e-6, rtol=0)
+
+
+def test_drafter_batch_rows_independent_and_garbage_slots_ignored():
+    w = _tiny(n_layers=2, ctx=40)
+    weights = inputs.drafter_weights(w, 3, gain_std=0.1)
+    step = inputs.step_inputs(w, 3, ctx_len=[20, 30], n_new=[4, 2], n_new_max=4)
+    kc, vc = inputs.cache_prefix(w, 3, step["ctx_len"])
+    kg, vg = inputs.cache_prefix(w, 3, step["ctx_len"], garbage="big")
+    l1, n1, _, _ = _run(w, weights, step, kc, vc)
+    l2, n2, _, _ = _run(w, weights, step, kg, vg)
+    np.testing.assert_array_equal(l1, l2)
+    np.testing.assert_array_equal(n1, [24, 32])
+    # changing batch row 1's inputs leaves row 0 alone
+    step3 = dict(step, last_token=np.array([step["last_token"][0], 3], np.int32))
+    l3, _, _, _ = _run(w, weights, step3, kc, vc)
+    np.testing.assert_array_equal(l3[0], l1[0])
+    assert not np.array_equal(l3[1], l1[1])
+
+
+def test_mask_rows_identical_without_positions():
+    # with rotary embedding off nothing distinguishes the mask rows: full
+    # attention inside the block gives them identical outputs
+    w = _tiny(rope_theta=0.0)
+    weights = inputs.drafter_weights(w, 4, gain_std=0.1)
+    step = inputs.step_inputs(w, 4)
+    kc, vc = inputs.cache_prefix(w, 4, step["ctx_len"])
+    logits, _, _, _ = _run(w, weights, step, kc, vc)
+    for j in range(1, w.gamma):
+        np.testing.assert_array_equal(logits[:, j], logits[:, 0])
+
+
+# ---------------------------------------------------------------- sampling
+
+def test_inverse_cdf_hand_examples():
+    assert oracle.inverse_cdf([1, 2, 3, 4], 0.25) == (1, pytest.approx(0.05))
+    assert oracle.inverse_cdf([0, 0, 5, 1], 0.0)[0] == 2                 # u = 0: first positive
+    assert oracle.inverse_cdf([0, 0, 0, 1, 0], 0.7)[0] == 3              # one-hot
+    assert oracle.inverse_cdf([1, 1, 1, 0], 1 - 2 ** -24)[0] == 2        # top end
+    assert oracle.argmax_with_gap([1.0, 3.0, 3.0, 2.0]) == (1, 0.0)      # lowest index on ties
+
+
+def test_inverse_cdf_equals_searchsorted():
+    g = np.random.default_rng(6)
+    for _ in range(200):
+        w = g.exponential(size=int(g.integers(1, 40)))
+        u = g.random()
+        k, _ = oracle.inverse_cdf(w, u)
+        assert k == int(np.searchsorted(np.cumsum(w), u * w.sum(), side="right"))
+
+
+def test_softmax_weights_normalise_to_scipy_softmax():
+    g = np.random.default_rng(7)
+    x = g.standard_normal((3, 100)) * 3
+    for T in (1.0, 0.5, 2.0):
+        w = oracle.softmax_weights(x, T)
+        np.testing.assert_allclose(w / w.sum(1, keepdims=True), special.softmax(x / T, axis=1),
+                                   rtol=1e-12)
+
+
+def _chi2_pvalue(counts, probs):
+    exp = probs * counts.sum()
+    keep = exp >= 5
+    obs = np.append(counts[keep], counts[~keep].sum())
+    ex = np.append(exp[keep], exp[~keep].sum())
+    if ex[-1] == 0:
+        obs, ex = obs[:-1], ex[:-1]
+    return stats.chisquare(obs, ex).pvalue
+
+
+def test_sampler_chi_square():
+    g = np.random.default_rng(8)
+    x = g.standard_normal(8)
+    q = special.softmax(x)
+    us = rng.uniform01(8, "chi_u", (40_000,))
+    counts = np.bincount([oracle.sample_row(x, u, 1.0)[0] for u in us], minlength=8)
+    assert _chi2_pvalue(counts, q) > 1e-4
+
+
+# ---------------------------------------------------------------- Markov head
+
+def test_markov_bias_is_row_of_low_rank_bigram_table():
+    V, r, G = 12, 3, 4
+    g = np.random.default_rng(9)
+    U = g.standard_normal((V, r)).astype(np.float32)
+    Wt = g.standard_normal((V, r)).astype(np.float32)
+    table = U.astype(np.float64) @ Wt.astype(np.float64).T       # dense V x V bigram bias
+    assert np.linalg.matrix_rank(table) == r
+    base = g.standard_normal((2, G, V)).astype(np.float32)
+    last = np.array([3, 11])
+    u = rng.uniform01(9, "mk", (2, G))
+    final, tok, _ = oracle.markov_sample(base, U, Wt, "f32", last, u, 1.0)
+    for b in range(2):
+        prev = last[b]
+        for i in range(G):
+            np.testing.assert_allclose(final[b, i].astype(np.float64) - base[b, i],
+                                       table[prev], atol=2e-6)
+            prev = tok[b, i]
+    # rank 0: no head, positions are sampled independently from the base logits
+    f0, t0, _ = oracle.markov_sample(base, None, None, "f32", last, u, 1.0)
+    assert np.array_equal(f0, base)
+    for b in range(2):
+        for i in range(G):
+            assert t0[b, i] == oracle.sample_row(base[b, i], u[b, i], 1.0)[0]
+
+
+def test_markov_sequence_distribution_chi_square():
+    # V = 8, gamma = 3: the empirical distribution of drafted sequences equals
+    # prod_i softmax(base_i + table[d_{i-1}])(d_i), enumerated over all 8^3 sequences
+    V, G, r, N = 8, 3, 4, 30_000
+    g = np.random.default_rng(10)
+    U = (g.standard_normal((V, r)) * r ** -0.25).astype(np.float32)
+    Wt = (g.standard_normal((V, r)) * r ** -0.25).astype(np.float32)
+    base1 = g.standard_normal((G, V)).astype(np.float32)
+    table = U.astype(np.float64) @ Wt.astype(np.float64).T
+    last = 2
+    probs = np.zeros(V ** G)
+    for idx in range(V ** G):
+        seq = np.unravel_index(idx, (V,) * G)
+        pr, prev = 1.0, last
+        for i in range(G):
+            pr *= special.softmax(base1[i] + table[prev])[seq[i]]
+            prev = seq[i]
+        probs[idx] = pr
+    base = np.broadcast_to(base1, (N, G, V))
+    u = rng.uniform01(10, "mk_seq", (N, G))
+    _, tok, _ = oracle.markov_sample(base, U, Wt, "f32", np.full(N, last), u, 1.0)
+    idx = np.ravel_multi_index(tuple(tok.T), (V,) * G)
+    assert _chi2_pvalue(np.bincount(idx, minlength=V ** G), probs) > 1e-4
+
+
+# ---------------------------------------------------------------- verify
+
+def _verify_trials(p_logits, q_logits, N, seed, temperature=1.0):
+    """Drafts sampled from q by the oracle sampler, then verified against p."""
+    G = q_logits.shape[0]
+    ud = rng.uniform01(seed, "vt_draft", (N, G))
+    ua = rng.uniform01(seed, "vt_acc", (N, G))
+    uf = rng.uniform01(seed, "vt_fin", (N,))
+    qw = special.softmax(q_logits.astype(np.float64) / temperature, axis=1)
+    cum = np.cumsum(qw, axis=1)
+    drafts = np.array([[int(np.searchsorted(cum[i], ud[n, i] * cum[i, -1], side="right"))
+                        for i in range(G)] for n in range(N)], np.int32)
+    ql = np.broadcast_to(q_logits, (N,) + q_logits.shape)
+    pl = np.broadcast_to(p_logits, (N,) + p_logits.shape)
+    out, nacc, _ = oracle.verify(ql, pl, drafts, ua, uf, temperature)
+    return out, nacc, drafts
+
+
+def test_verify_is_lossless_chi_square_and_acceptance_matches_tv():
+    V, G, N = 8, 3, 20_000
+    g = np.random.default_rng(11)
+    p_logits = g.standard_normal((G + 1, V)).astype(np.float32)
+    q_logits = g.standard_normal((G, V)).astype(np.float32)
+    out, nacc, _ = _verify_trials(p_logits, q_logits, N, 11)
+    p = special.softmax(p_logits.astype(np.float64), axis=1)
+    q = special.softmax(q_logits.astype(np.float64), axis=1)
+    for i in range(G + 1):
+        reached = nacc >= i
+        assert _chi2_pvalue(np.bincount(out[reached, i], minlength=V), p[i]) > 1e-4
+    alphas = [oracle.acceptance_rate(p[i], q[i]) for i in range(G)]
+    assert np.isclose(alphas[0], 1 - 0.5 * np.abs(p[0] - q[0]).sum())        # 1 - TV
+    acc1 = np.mean(nacc >= 1)
+    assert abs(acc1 - alphas[0]) < 4 * np.sqrt(alphas[0] * (1 - alphas[0]) / N)
+    tau = oracle.tau_from_accepted(nacc)
+    et = oracle.expected_tau_independent(alphas)
+    assert abs(tau.mean() - et) < 4 * tau.std() / np.sqrt(N)
+    assert np.all((tau >= 1) & (tau <= G + 1))
+    for n in range(N):                                   # -1 padding after the last token
+        assert np.all(out[n, nacc[n] + 1:] == -1) and np.all(out[n, :nacc[n] + 1] >= 0)
+
+
+def test_verify_identical_and_disjoint_distributions():
+    V, G, N = 8, 3, 2000
+    g = np.random.default_rng(12)
+    lg = g.standard_normal((G + 1, V)).astype(np.float32)
+    out, nacc, drafts = _verify_trials(lg, lg[:G], N, 12)
+    assert np.all(nacc == G)                             # q == p: everything accepted
+    assert np.array_equal(out[:, :G], drafts)
+    # disjoint supports: q only on 0..3, p only on 4..7 -> reject at once, draw from p
+    q = np.full((G, V), -np.inf, np.float32); q[:, :4] = g.standard_normal((G, 4))
+    p = np.full((G + 1, V), -np.inf, np.float32); p[:, 4:] = g.standard_normal((G + 1, 4))
+    out, nacc, _ = _verify_trials(p, q, 20_000, 13)
+    assert np.all(nacc == 0)
+    assert _chi2_pvalue(np.bincount(out[:, 0], minlength=V),
+                        special.softmax(p[0].astype(np.float64))) > 1e-4
+
+
+def test_verify_greedy_and_out_of_range():
+    V, G = 10, 4
+    g = np.random.default_rng(14)
+    pl = g.standard_normal((1, G + 1, V)).astype(np.float32)
+    ql = g.standard_normal((1, G, V)).astype(np.float32)
+    arg = pl[0].argmax(1)
+    drafts = arg[:G].copy()[None].astype(np.int32)
+    drafts[0, 2] = (arg[2] + 1) % V                         # first mismatch at position 3
+    out, nacc, _ = oracle.verify(ql, pl, drafts, np.zeros((1, G)), np.zeros(1), 0.0)
+    assert nacc[0] == 2 and list(out[0]) == [arg[0], arg[1], arg[2], -1, -1]
+    drafts = arg[:G][None].astype(np.int32)
+    out, nacc, _ = oracle.verify(ql, pl, drafts, np.zeros((1, G)), np.zeros(1), 0.0)
+    assert nacc[0] == G and out[0, G] == arg[G]             # bonus = argmax of the last row
+    bad = np.array([[V + 3, 0, 0, 0]], np.int32)            # out-of-range draft: rejected
+    out, nacc, _ = oracle.verify(ql, pl, bad, np.zeros((1, G)), np.full(1, 0.5), 1.0)
+    assert nacc[0] == 0 and 0 <= out[0, 0] < V
+
+
+def test_verify_with_markov_drafts_matches_enumerated_expected_tau():
+    V, G, r, N = 6, 3, 3, 20_000
+    g = np.random.default_rng(15)
+    U = (g.standard_normal((V, r)) * r ** -0.25).astype(np.float32)
+    Wt = (g.standard_normal((V, r)) * r ** -0.25).astype(np.float32)
+    base1 = g.standard_normal((G, V)).astype(np.float32)
+    p_logits = g.standard_normal((G + 1, V)).astype(np.float32)
+    last = 1
+    ud = rng.uniform01(15, "mv_d", (N, G))
+    ua = rng.uniform01(15, "mv_a", (N, G))
+    uf = rng.uniform01(15, "mv_f", (N,))
+    final, tok, _ = oracle.markov_sample(np.broadcast_to(base1, (N, G, V)), U, Wt, "f32",
+                                         np.full(N, last), ud, 1.0)
+    out, nacc, _ = oracle.verify(final, np.broadcast_to(p_logits, (N, G + 1, V)), tok, ua, uf, 1.0)
+    table = U.astype(np.float64) @ Wt.astype(np.float64).T
+    p = special.softmax(p_logits[:G].astype(np.float64), axis=1)
+    q_first = special.softmax(base1[0] + table[last])
+    q_next = np.stack([special.softmax(base1[i][None, :] + table, axis=1) for i in range(1, G)])
+    et = oracle.expected_tau_markov(p, q_first, q_next)
+    tau = oracle.tau_from_accepted(nacc)
+    assert abs(tau.mean() - et) < 4 * tau.std() / np.sqrt(N)
+    pf = special.softmax(p_logits.astype(np.float64), axis=1)
+    for i in range(G + 1):                               # lossless with a Markov draft too
+        reached = nacc >= i
+        assert _chi2_pvalue(np.bincount(out[reached, i], minlength=V), pf[i]) > 1e-4
+
+
+# ---------------------------------------------------------------- bookkeeping
+
+def test_latency_bookkeeping_closed_forms_and_page_figures():
+    assert oracle.latency_per_token(3.0, 5.0, 4.0) == 2.0
+    assert oracle.expected_tau_independent([1, 1, 1]) == 4.0
+    assert oracle.expected_tau_independent([0, 1, 1]) == 1.0
+    a, G = 0.7, 5
+    assert np.isclose(oracle.expected_tau_independent([a] * G), (1 - a ** (G + 1)) / (1 - a))
+    # prefix-independent draft distributions: the Markov enumeration reduces to the product form
+    g = np.random.default_rng(16)
+    p = special.softmax(g.standard_normal((3, 4)), axis=1)
+    q = special.softmax(g.standard_normal((3, 4)), axis=1)
+    q_next = np.stack([np.broadcast_to(q[i], (4, 4)) for i in (1, 2)])
+    alphas = [oracle.acceptance_rate(p[i], q[i]) for i in range(3)]
+    assert np.isclose(oracle.expected_tau_markov(p, q[0], q_next),
+                      oracle.expected_tau_independent(alphas))
+    # the DSpark page's figures: +0.2-1.3 % per round for +30 % accepted length
+    fx = json.load(open(os.path.join(GOLDEN, "dspark_head_latency.json")))
+    lo, hi = fx["round_latency_overhead"]
+    gain = fx["accepted_length_gain"]
+    t_round, tau0 = 1.0, 2.0
+    base_L = oracle.latency_per_token(0.3 * t_round, 0.7 * t_round, tau0)
+    for ov in (lo, hi):
+        L = oracle.latency_per_token(0.3 * (1 + ov), 0.7 * (1 + ov), tau0 * (1 + gain))
+        assert np.isclose(L / base_L, (1 + ov) / (1 + gain))
+    assert 0.770 < (1 + lo) / (1 + gain) < (1 + hi) / (1 + gain) < 0.780
