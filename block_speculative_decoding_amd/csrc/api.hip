@@ -1,0 +1,579 @@
+// C ABI of the dfspec library: host-side validation, workspace carving and the
+// launch sequence of each entry point.  See include/dfspec.h for the contract.
+#include "../../include/dfspec.h"
+#include "kernels.h"
+
+using namespace dfs;
+
+namespace {
+
+#define DFS_TRY(expr)                          \
+  do {                                         \
+    if ((expr) != hipSuccess) return DFS_EHIP; \
+  } while (0)
+
+size_t dtype_size(int dt) { return dt == DFS_BF16 ? 2 : 4; }
+
+struct DraftDims {
+  int L, H, nq, nkv, d, F, V, nT, S, G, max_ctx, group, R, Rpad;
+  int B, nmax, Mc, Mb, Mx, Nqkv;
+  size_t es;
+};
+
+int check_cfg(const dfs_drafter_cfg* c) {
+  if (!c) return DFS_EINVAL;
+  if (c->n_layers < 1 || c->hidden < 1 || c->n_q_heads < 1 || c->n_kv_heads < 1 || c->head_dim < 2 ||
+      c->mlp_dim < 1 || c->vocab < 1 || c->n_target_layers < 1 || c->block < 2 || c->max_ctx < 1)
+    return DFS_EINVAL;
+  if (c->n_q_heads % c->n_kv_heads != 0 || c->head_dim % 2 != 0) return DFS_EINVAL;
+  if (c->mask_token_id < 0 || c->mask_token_id >= c->vocab) return DFS_EINVAL;
+  if (c->dtype != DFS_F32 && c->dtype != DFS_BF16) return DFS_EINVAL;
+  if (!(c->rms_eps >= 0.f)) return DFS_EINVAL;
+  if (c->max_ctx % 64 != 0 || c->block > 64 || c->hidden > 8192) return DFS_EUNSUPPORTED;
+  const long R = (long)(c->n_q_heads / c->n_kv_heads) * c->block;
+  if (c->dtype == DFS_BF16) {
+    if (c->head_dim != 128 || c->hidden % 64 || (c->n_q_heads * c->head_dim) % 64 || c->mlp_dim % 64 ||
+        ((long)c->n_target_layers * c->hidden) % 64 || R > 64)
+      return DFS_EUNSUPPORTED;
+  } else {
+    if (c->head_dim > 256 || R > 256) return DFS_EUNSUPPORTED;
+  }
+  return DFS_OK;
+}
+
+DraftDims dims_of(const dfs_drafter_cfg* c, int B, int nmax) {
+  DraftDims d;
+  d.L = c->n_layers;
+  d.H = c->hidden;
+  d.nq = c->n_q_heads;
+  d.nkv = c->n_kv_heads;
+  d.d = c->head_dim;
+  d.F = c->mlp_dim;
+  d.V = c->vocab;
+  d.nT = c->n_target_layers;
+  d.S = c->block;
+  d.G = c->block - 1;
+  d.max_ctx = c->max_ctx;
+  d.group = d.nq / d.nkv;
+  d.R = d.group * d.S;
+  d.Rpad = (d.R + 15) / 16 * 16;
+  d.B = B;
+  d.nmax = nmax;
+  d.Mc = B * nmax;
+  d.Mb = B * d.S;
+  d.Mx = d.Mc + d.Mb;
+  d.Nqkv = (d.nq + 2 * d.nkv) * d.d;
+  d.es = dtype_size(c->dtype);
+  return d;
+}
+
+struct DraftWs {
+  int32_t* meta;
+  float2* rope;
+  char* xs;
+  float* resid;
+  char* mlp_in;
+  char* attn_o;
+  char* hmid;
+  char* z;
+  char* q_att;
+  char* k_blk;
+  char* v_blk;
+  float* part;
+  float* apart_o;
+  float* apart_ml;
+  size_t bytes;
+};
+
+DraftWs carve_draft(void* base, const DraftDims& d, int dtype) {
+  Carver cv(base);
+  DraftWs w;
+  w.meta = cv.take<int32_t>(3 * (size_t)d.B);
+  w.rope = cv.take<float2>((size_t)d.Mx * (d.d / 2));
+  w.xs = cv.take<char>((size_t)d.Mx * d.H * d.es);
+  w.resid = cv.take<float>((size_t)d.Mb * d.H);
+  w.mlp_in = cv.take<char>((size_t)d.Mb * d.H * d.es);
+  w.attn_o = cv.take<char>((size_t)d.Mb * d.nq * d.d * d.es);
+  w.hmid = cv.take<char>((size_t)d.Mb * d.F * d.es);
+  w.z = cv.take<char>((size_t)d.B * d.G * d.H * d.es);
+  w.q_att = cv.take<char>((size_t)d.B * d.nkv * d.Rpad * d.d * d.es);
+  w.k_blk = cv.take<char>((size_t)d.B * d.nkv * 64 * d.d * d.es);
+  w.v_blk = cv.take<char>((size_t)d.B * d.nkv * d.d * 64 * d.es);
+  size_t part = 0;
+  auto upd = [&](int M, int N, int K) {
+    if (M <= 0) return;
+    const GemmPlan p = gemm_plan(M, N, K, dtype);
+    const size_t e = gemm_partial_elems(p, M, N);
+    if (e > part) part = e;
+  };
+  upd(d.Mc, d.H, d.nT * d.H);
+  upd(d.Mx, d.Nqkv, d.H);
+  upd(d.Mb, d.H, d.nq * d.d);
+  upd(d.Mb, 2 * d.F, d.H);
+  upd(d.Mb, d.H, d.F);
+  w.part = cv.take<float>(part);
+  const int units = attn_max_units(d.B, d.nkv, d.max_ctx, dtype);
+  w.apart_o = cv.take<float>(attn_partial_elems(units, d.B, d.nkv, d.Rpad, d.d));
+  w.apart_ml = cv.take<float>((size_t)d.B * d.nkv * units * d.Rpad * 2);
+  w.bytes = cv.off + 256;
+  return w;
+}
+
+hipError_t run_gemm(const void* X, int ldx, int M, int N, int K, const void* w0, const void* w1, int n1,
+                    const void* w2, int n2, float* Y, int dtype, hipStream_t s, int* splits_out,
+                    size_t* stride_out, int force_splits = 0, long ldy = 0) {
+  GemmArgs a;
+  a.X = X;
+  a.ldx = ldx;
+  a.x_rows = M;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.seg[0].w = w0;
+  a.seg[0].n0 = 0;
+  a.nseg = 1;
+  if (w1) {
+    a.seg[1].w = w1;
+    a.seg[1].n0 = n1;
+    a.nseg = 2;
+  }
+  if (w2) {
+    a.seg[2].w = w2;
+    a.seg[2].n0 = n2;
+    a.nseg = 3;
+  }
+  const GemmPlan p = gemm_plan(M, N, K, dtype, force_splits);
+  a.Y = Y;
+  a.ldy = ldy ? ldy : N;
+  a.y_split_stride = (size_t)M * N;
+  if (splits_out) *splits_out = p.splits;
+  if (stride_out) *stride_out = (size_t)M * N;
+  return launch_gemm(a, p, dtype, s);
+}
+
+template <typename P>
+const char* at(const P* base, size_t off) {
+  return (const char*)base + off;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dfs_status_string(int st) {
+  switch (st) {
+    case DFS_OK: return "ok";
+    case DFS_EINVAL: return "invalid argument";
+    case DFS_EUNSUPPORTED: return "unsupported shape or dtype";
+    case DFS_EHIP: return "HIP launch failed";
+    case DFS_EWORKSPACE: return "workspace too small";
+    default: return "unknown status";
+  }
+}
+
+size_t dflash_draft_workspace_size(const dfs_drafter_cfg* cfg, int32_t batch, int32_t n_new_max) {
+  if (check_cfg(cfg) != DFS_OK || batch < 1 || n_new_max < 0) return 0;
+  const DraftDims d = dims_of(cfg, batch, n_new_max);
+  return carve_draft(nullptr, d, cfg->dtype).bytes;
+}
+
+int dflash_draft_step(const dfs_drafter_cfg* cfg, const dfs_drafter_weights* wt, int32_t batch,
+                      const void* hidden_new, const int32_t* n_new, int32_t n_new_max, int32_t ctx_bound,
+                      void* k_cache, void* v_cache, int32_t* ctx_len, const int32_t* last_token,
+                      float* base_logits, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_cfg(cfg);
+  if (st != DFS_OK) return st;
+  if (!wt || batch < 1 || n_new_max < 0 || !n_new || !k_cache || !v_cache || !ctx_len || !last_token ||
+      !base_logits || !workspace)
+    return DFS_EINVAL;
+  if (n_new_max > 0 && !hidden_new) return DFS_EINVAL;
+  if (ctx_bound < 1 || ctx_bound > cfg->max_ctx) return DFS_EINVAL;
+  if (batch > 65535) return DFS_EUNSUPPORTED;   // batch is a grid dimension of the attention kernels
+  if (!wt->embed || !wt->fc || !wt->fc_norm || !wt->final_norm || !wt->lm_head || !wt->attn_norm || !wt->wq ||
+      !wt->wk || !wt->wv || !wt->wo || !wt->mlp_norm || !wt->w_gate || !wt->w_up || !wt->w_down)
+    return DFS_EINVAL;
+  for (int l = 0; l < cfg->n_layers; ++l)
+    if (!wt->attn_norm[l] || !wt->wq[l] || !wt->wk[l] || !wt->wv[l] || !wt->wo[l] || !wt->mlp_norm[l] ||
+        !wt->w_gate[l] || !wt->w_up[l] || !wt->w_down[l])
+      return DFS_EINVAL;
+  const DraftDims d = dims_of(cfg, batch, n_new_max);
+  const int dt = cfg->dtype;
+  const DraftWs w = carve_draft(workspace, d, dt);
+  if (workspace_bytes < w.bytes) return DFS_EWORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  const size_t es = d.es;
+
+  // positions, rotary table, bookkeeping
+  MetaArgs ma;
+  ma.ctx_len = ctx_len;
+  ma.n_new = n_new;
+  ma.meta = w.meta;
+  ma.rope = cfg->rope_theta > 0.f ? w.rope : nullptr;
+  ma.B = d.B;
+  ma.S = d.S;
+  ma.n_new_max = d.nmax;
+  ma.d = d.d;
+  ma.ctx_bound = ctx_bound;
+  ma.theta = cfg->rope_theta;
+  DFS_TRY(launch_prep(ma, s));
+  DFS_TRY(launch_embed(dt, wt->embed, last_token, cfg->mask_token_id, d.V, d.H, d.B, d.S, w.resid, s));
+
+  int sp;
+  size_t pst;
+  // 1. context features f = RMSNorm(concat(h) . fc^T) -> xs rows [0, Mc)
+  if (d.Mc > 0) {
+    DFS_TRY(run_gemm(hidden_new, d.nT * d.H, d.Mc, d.H, d.nT * d.H, wt->fc, nullptr, 0, nullptr, 0, w.part, dt, s,
+                     &sp, &pst));
+    NormArgs na;
+    na.part = w.part;
+    na.sp = sp;
+    na.part_stride = pst;
+    na.gain = wt->fc_norm;
+    na.out = w.xs;
+    na.rows = d.Mc;
+    na.H = d.H;
+    na.eps = cfg->rms_eps;
+    DFS_TRY(launch_norm(na, dt, s));
+  }
+  char* xs_blk = w.xs + (size_t)d.Mc * d.H * es;
+  {  // layer 0 attention pre-norm of the block rows
+    NormArgs na;
+    na.resid = w.resid;
+    na.gain = wt->attn_norm[0];
+    na.out = xs_blk;
+    na.rows = d.Mb;
+    na.H = d.H;
+    na.eps = cfg->rms_eps;
+    DFS_TRY(launch_norm(na, dt, s));
+  }
+  const AttnPlan ap = attn_plan(d.B, d.nkv, ctx_bound, dt);
+  const size_t layer_cache = (size_t)d.B * d.nkv * d.max_ctx * d.d * es;
+  for (int l = 0; l < d.L; ++l) {
+    // 2. Q|K|V of [features ; block rows] in one pass over wq|wk|wv
+    DFS_TRY(run_gemm(w.xs, d.H, d.Mx, d.Nqkv, d.H, wt->wq[l], wt->wk[l], d.nq * d.d, wt->wv[l],
+                     (d.nq + d.nkv) * d.d, w.part, dt, s, &sp, &pst));
+    QkvArgs qa;
+    qa.part = w.part;
+    qa.sp = sp;
+    qa.part_stride = pst;
+    qa.meta = w.meta;
+    qa.rope = w.rope;
+    qa.use_rope = cfg->rope_theta > 0.f;
+    qa.k_cache = (char*)k_cache + l * layer_cache;
+    qa.v_cache = (char*)v_cache + l * layer_cache;
+    qa.q_att = w.q_att;
+    qa.k_blk = w.k_blk;
+    qa.v_blk = w.v_blk;
+    qa.B = d.B;
+    qa.S = d.S;
+    qa.n_new_max = d.nmax;
+    qa.nq = d.nq;
+    qa.nkv = d.nkv;
+    qa.d = d.d;
+    qa.max_ctx = d.max_ctx;
+    qa.Rpad = d.Rpad;
+    DFS_TRY(launch_qkv_epilogue(qa, dt, s));
+    // 3. block attention over [context keys ; block keys]
+    AttnArgs aa;
+    aa.q = w.q_att;
+    aa.k_blk = w.k_blk;
+    aa.v_blk = w.v_blk;
+    aa.k_cache = qa.k_cache;
+    aa.v_cache = qa.v_cache;
+    aa.ctx_len = w.meta + 2 * d.B;
+    aa.out = w.attn_o;
+    aa.part_o = w.apart_o;
+    aa.part_ml = w.apart_ml;
+    aa.B = d.B;
+    aa.S = d.S;
+    aa.nq = d.nq;
+    aa.nkv = d.nkv;
+    aa.d = d.d;
+    aa.max_ctx = d.max_ctx;
+    aa.ctx_bound = ctx_bound;
+    aa.R = d.R;
+    aa.Rpad = d.Rpad;
+    aa.keys_per_split = ap.keys_per_split;
+    aa.n_ctx_splits = ap.n_ctx_splits;
+    DFS_TRY(launch_attention(aa, dt, s));
+    // 4. O projection, residual add, MLP pre-norm
+    DFS_TRY(run_gemm(w.attn_o, d.nq * d.d, d.Mb, d.H, d.nq * d.d, wt->wo[l], nullptr, 0, nullptr, 0, w.part, dt,
+                     s, &sp, &pst));
+    {
+      NormArgs na;
+      na.resid = w.resid;
+      na.part = w.part;
+      na.sp = sp;
+      na.part_stride = pst;
+      na.update_resid = 1;
+      na.gain = wt->mlp_norm[l];
+      na.out = w.mlp_in;
+      na.rows = d.Mb;
+      na.H = d.H;
+      na.eps = cfg->rms_eps;
+      DFS_TRY(launch_norm(na, dt, s));
+    }
+    // 5. SwiGLU MLP: [gate | up] in one pass, then down, residual add, next pre-norm
+    DFS_TRY(run_gemm(w.mlp_in, d.H, d.Mb, 2 * d.F, d.H, wt->w_gate[l], wt->w_up[l], d.F, nullptr, 0, w.part, dt,
+                     s, &sp, &pst));
+    DFS_TRY(launch_swiglu(w.part, sp, pst, d.Mb, d.F, w.hmid, dt, s));
+    DFS_TRY(run_gemm(w.hmid, d.F, d.Mb, d.H, d.F, wt->w_down[l], nullptr, 0, nullptr, 0, w.part, dt, s, &sp,
+                     &pst));
+    {
+      NormArgs na;
+      na.resid = w.resid;
+      na.part = w.part;
+      na.sp = sp;
+      na.part_stride = pst;
+      na.update_resid = 1;
+      na.rows = d.Mb;
+      na.H = d.H;
+      na.eps = cfg->rms_eps;
+      if (l + 1 < d.L) {
+        na.gain = wt->attn_norm[l + 1];
+        na.out = xs_blk;
+      } else {   // final norm of the mask rows only -> z [B*(S-1), H]
+        na.gain = wt->final_norm;
+        na.out = w.z;
+        na.out_mode = 1;
+        na.S = d.S;
+      }
+      DFS_TRY(launch_norm(na, dt, s));
+    }
+  }
+  // 6. LM head on the mask rows -> base logits [B, S-1, V]
+  DFS_TRY(run_gemm(w.z, d.H, d.B * d.G, d.V, d.H, wt->lm_head, nullptr, 0, nullptr, 0, base_logits, dt, s, &sp,
+                   &pst, 1));
+  DFS_TRY(launch_finish(w.meta, ctx_len, d.B, s));
+  return DFS_OK;
+}
+
+// ------------------------------------------------------------------ Markov head + sampling
+
+size_t markov_bias_sample_workspace_size(int32_t batch, int32_t n_draft, int32_t vocab) {
+  if (batch < 1 || n_draft < 1 || vocab < 1) return 0;
+  const size_t nch = (size_t)ceil_div(vocab, kChunk);
+  return align_up((size_t)batch * n_draft * nch * sizeof(double2), 256) + 256;
+}
+
+int markov_bias_sample(int32_t batch, int32_t n_draft, int32_t vocab, int32_t rank, float* logits, const void* U,
+                       const void* Wt, int32_t uw_dtype, const int32_t* last_token, const float* u_draft,
+                       float temperature, int32_t* draft_tokens, double* row_stats, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  if (batch < 1 || n_draft < 1 || vocab < 1 || rank < 0 || !logits || !last_token || !u_draft || !draft_tokens ||
+      !workspace)
+    return DFS_EINVAL;
+  if (!(temperature >= 0.f)) return DFS_EINVAL;
+  if (rank > 0 && (!U || !Wt)) return DFS_EINVAL;
+  if (rank > 0 && uw_dtype != DFS_F32 && uw_dtype != DFS_BF16) return DFS_EINVAL;
+  if (rank > 0 && uw_dtype == DFS_BF16 && rank % 64 != 0) return DFS_EUNSUPPORTED;
+  if (workspace_bytes < markov_bias_sample_workspace_size(batch, n_draft, vocab)) return DFS_EWORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  Carver cv(workspace);
+  const int nch = ceil_div(vocab, kChunk);
+  double2* stats = cv.take<double2>((size_t)batch * n_draft * nch);
+  const long rowV = (long)n_draft * vocab;
+  if (rank == 0) {
+    ProfScope ps("sample", s);
+    DFS_TRY(launch_chunk_stats(logits, vocab, batch * n_draft, vocab, temperature, stats, s));
+    PickArgs pa;
+    pa.x = logits;
+    pa.row_stride = vocab;
+    pa.rows = batch * n_draft;
+    pa.V = vocab;
+    pa.temperature = temperature;
+    pa.stats = stats;
+    pa.u = u_draft;
+    pa.u_stride = 1;
+    pa.tokens = draft_tokens;
+    pa.tok_stride = 1;
+    pa.row_stats = row_stats;
+    pa.rs_stride = 2;
+    DFS_TRY(launch_pick(pa, s));
+    return DFS_OK;
+  }
+  ProfScope ps("markov", s);
+  const GemmPlan plan = gemm_plan(batch, vocab, rank, uw_dtype, 1);
+  for (int i = 0; i < n_draft; ++i) {
+    // final_i = base_i + U[prev] . W   (rows gathered by the previous token)
+    GemmArgs ga;
+    ga.X = U;
+    ga.ldx = rank;
+    ga.row_idx = i == 0 ? last_token : draft_tokens + (i - 1);
+    ga.row_idx_stride = i == 0 ? 1 : n_draft;
+    ga.x_rows = vocab;
+    ga.M = batch;
+    ga.N = vocab;
+    ga.K = rank;
+    ga.seg[0].w = Wt;
+    ga.nseg = 1;
+    ga.Y = logits + (size_t)i * vocab;
+    ga.ldy = rowV;
+    ga.y_split_stride = 0;
+    ga.accumulate = 1;
+    DFS_TRY(launch_gemm(ga, plan, uw_dtype, s));
+    DFS_TRY(launch_chunk_stats(logits + (size_t)i * vocab, rowV, batch, vocab, temperature, stats, s));
+    PickArgs pa;
+    pa.x = logits + (size_t)i * vocab;
+    pa.row_stride = rowV;
+    pa.rows = batch;
+    pa.V = vocab;
+    pa.temperature = temperature;
+    pa.stats = stats;
+    pa.u = u_draft + i;
+    pa.u_stride = n_draft;
+    pa.tokens = draft_tokens + i;
+    pa.tok_stride = n_draft;
+    pa.row_stats = row_stats ? row_stats + 2 * i : nullptr;
+    pa.rs_stride = 2 * (long)n_draft;
+    DFS_TRY(launch_pick(pa, s));
+  }
+  return DFS_OK;
+}
+
+// ------------------------------------------------------------------ verify
+
+static size_t verify_carve(int B, int G, int V, void* base, VerifyArgs* a) {
+  Carver cv(base);
+  const size_t nch = (size_t)ceil_div(V, kChunk);
+  double2* p_chunk = cv.take<double2>((size_t)B * (G + 1) * nch);
+  double2* q_chunk = cv.take<double2>((size_t)B * G * nch);
+  double* rowinfo = cv.take<double>((size_t)B * 4);
+  double2* sums = cv.take<double2>((size_t)B * nch);
+  double* r_chunk = cv.take<double>((size_t)B * nch);
+  int32_t* state = cv.take<int32_t>(B);
+  if (a) {
+    a->p_chunk = p_chunk;
+    a->q_chunk = q_chunk;
+    a->rowinfo = rowinfo;
+    a->sums = sums;
+    a->r_chunk = r_chunk;
+    a->state = state;
+  }
+  return cv.off + 256;
+}
+
+size_t spec_verify_workspace_size(int32_t batch, int32_t n_draft, int32_t vocab) {
+  if (batch < 1 || n_draft < 1 || vocab < 1) return 0;
+  return verify_carve(batch, n_draft, vocab, nullptr, nullptr);
+}
+
+int spec_verify(int32_t batch, int32_t n_draft, int32_t vocab, const float* draft_logits,
+                const float* target_logits, const int32_t* draft_tokens, const float* u_accept,
+                const float* u_final, float temperature, const double* draft_row_stats, int32_t* out_tokens,
+                int32_t* n_accepted, void* workspace, size_t workspace_bytes, void* stream) {
+  if (batch < 1 || n_draft < 1 || vocab < 1 || !draft_logits || !target_logits || !draft_tokens || !u_accept ||
+      !u_final || !out_tokens || !n_accepted || !workspace)
+    return DFS_EINVAL;
+  if (!(temperature >= 0.f)) return DFS_EINVAL;
+  if (workspace_bytes < spec_verify_workspace_size(batch, n_draft, vocab)) return DFS_EWORKSPACE;
+  VerifyArgs a;
+  verify_carve(batch, n_draft, vocab, workspace, &a);
+  a.q = draft_logits;
+  a.p = target_logits;
+  a.drafts = draft_tokens;
+  a.u_accept = u_accept;
+  a.u_final = u_final;
+  a.temperature = temperature;
+  a.q_stats = draft_row_stats;
+  a.out_tokens = out_tokens;
+  a.n_accepted = n_accepted;
+  a.B = batch;
+  a.G = n_draft;
+  a.V = vocab;
+  DFS_TRY(launch_verify(a, (hipStream_t)stream));
+  return DFS_OK;
+}
+
+// ------------------------------------------------------------------ kernel-level hooks
+
+size_t dfs_block_attention_workspace_size(int32_t batch, int32_t block, int32_t n_q_heads, int32_t n_kv_heads,
+                                          int32_t head_dim, int32_t ctx_bound, int32_t dtype) {
+  if (batch < 1 || block < 1 || block > 64 || n_q_heads < 1 || n_kv_heads < 1 || head_dim < 2 || ctx_bound < 1)
+    return 0;
+  const int R = n_q_heads / n_kv_heads * block, Rpad = (R + 15) / 16 * 16;
+  const size_t es = dtype_size(dtype);
+  Carver cv(nullptr);
+  cv.take<char>((size_t)batch * n_kv_heads * Rpad * head_dim * es);
+  cv.take<char>((size_t)batch * n_kv_heads * 64 * head_dim * es);
+  cv.take<char>((size_t)batch * n_kv_heads * head_dim * 64 * es);
+  const AttnPlan ap = attn_plan(batch, n_kv_heads, ctx_bound, dtype);
+  cv.take<float>(attn_partial_elems(ap.n_ctx_splits + 1, batch, n_kv_heads, Rpad, head_dim));
+  cv.take<float>((size_t)batch * n_kv_heads * (ap.n_ctx_splits + 1) * Rpad * 2);
+  return cv.off + 256;
+}
+
+int dfs_block_attention(int32_t batch, int32_t block, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                        int32_t max_ctx, int32_t ctx_bound, int32_t dtype, const void* q, const void* k_blk,
+                        const void* v_blk, const void* k_cache, const void* v_cache, const int32_t* ctx_len,
+                        void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k_blk || !v_blk || !k_cache || !v_cache || !ctx_len || !out || !workspace) return DFS_EINVAL;
+  if (batch < 1 || block < 1 || n_q_heads < 1 || n_kv_heads < 1 || n_q_heads % n_kv_heads || max_ctx < 1 ||
+      ctx_bound < 1 || ctx_bound > max_ctx || (dtype != DFS_F32 && dtype != DFS_BF16))
+    return DFS_EINVAL;
+  const int R = n_q_heads / n_kv_heads * block, Rpad = (R + 15) / 16 * 16;
+  if (block > 64 || max_ctx % 64 || batch > 65535) return DFS_EUNSUPPORTED;
+  if (dtype == DFS_BF16 && (head_dim != 128 || R > 64)) return DFS_EUNSUPPORTED;
+  if (dtype == DFS_F32 && (head_dim > 256 || R > 256)) return DFS_EUNSUPPORTED;
+  if (workspace_bytes <
+      dfs_block_attention_workspace_size(batch, block, n_q_heads, n_kv_heads, head_dim, ctx_bound, dtype))
+    return DFS_EWORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  const size_t es = dtype_size(dtype);
+  Carver cv(workspace);
+  char* q_att = cv.take<char>((size_t)batch * n_kv_heads * Rpad * head_dim * es);
+  char* kb = cv.take<char>((size_t)batch * n_kv_heads * 64 * head_dim * es);
+  char* vb = cv.take<char>((size_t)batch * n_kv_heads * head_dim * 64 * es);
+  const AttnPlan ap = attn_plan(batch, n_kv_heads, ctx_bound, dtype);
+  float* po = cv.take<float>(attn_partial_elems(ap.n_ctx_splits + 1, batch, n_kv_heads, Rpad, head_dim));
+  float* pml = cv.take<float>((size_t)batch * n_kv_heads * (ap.n_ctx_splits + 1) * Rpad * 2);
+  DFS_TRY(launch_attn_stage(q, k_blk, v_blk, q_att, kb, vb, batch, block, n_q_heads, n_kv_heads, head_dim, Rpad,
+                            dtype, s));
+  AttnArgs aa;
+  aa.q = q_att;
+  aa.k_blk = kb;
+  aa.v_blk = vb;
+  aa.k_cache = k_cache;
+  aa.v_cache = v_cache;
+  aa.ctx_len = ctx_len;
+  aa.out = out;
+  aa.part_o = po;
+  aa.part_ml = pml;
+  aa.B = batch;
+  aa.S = block;
+  aa.nq = n_q_heads;
+  aa.nkv = n_kv_heads;
+  aa.d = head_dim;
+  aa.max_ctx = max_ctx;
+  aa.ctx_bound = ctx_bound;
+  aa.R = R;
+  aa.Rpad = Rpad;
+  aa.keys_per_split = ap.keys_per_split;
+  aa.n_ctx_splits = ap.n_ctx_splits;
+  DFS_TRY(launch_attention(aa, dtype, s));
+  return DFS_OK;
+}
+
+size_t dfs_gemm_workspace_size(int32_t M, int32_t N, int32_t K, int32_t dtype, int32_t splits) {
+  if (M < 1 || N < 1 || K < 1) return 0;
+  const GemmPlan p = gemm_plan(M, N, K, dtype, splits);
+  return p.splits > 1 ? align_up(gemm_partial_elems(p, M, N) * sizeof(float), 256) + 256 : 256;
+}
+
+int dfs_gemm(int32_t M, int32_t N, int32_t K, int32_t dtype, const void* X, const void* W, float* Y,
+             int32_t splits, void* workspace, size_t workspace_bytes, void* stream) {
+  if (M < 1 || N < 1 || K < 1 || !X || !W || !Y || splits < 0 || (dtype != DFS_F32 && dtype != DFS_BF16))
+    return DFS_EINVAL;
+  if (dtype == DFS_BF16 && K % 64) return DFS_EUNSUPPORTED;
+  if (workspace_bytes < dfs_gemm_workspace_size(M, N, K, dtype, splits) || !workspace) return DFS_EWORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  const GemmPlan p = gemm_plan(M, N, K, dtype, splits);
+  float* target = p.splits > 1 ? (float*)workspace : Y;
+  int sp;
+  size_t pst;
+  DFS_TRY(run_gemm(X, K, M, N, K, W, nullptr, 0, nullptr, 0, target, dtype, s, &sp, &pst, splits));
+  if (sp > 1) DFS_TRY(launch_reduce(target, sp, pst, (size_t)M * N, Y, s));
+  return DFS_OK;
+}
+
+}  // extern "C"

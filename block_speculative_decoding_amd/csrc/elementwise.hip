@@ -1,0 +1,257 @@
+// Row-wise and element-wise kernels of the drafter: positions and rotary
+// tables, embedding gather, RMSNorm (fused with the reduction of split-K GEMM
+// partials and with the fp32 residual update), the Q/K/V epilogue (rotary
+// embedding + KV injection into the caches + block K/V staging) and SwiGLU.
+// All of them are HBM/latency bound and touch each byte once.
+#include "kernels.h"
+
+#include <math.h>
+
+namespace dfs {
+namespace {
+
+// Rotary table of every row the call touches:
+//   context row (b, j), j < n_new_max  -> position ctx_len[b] + j
+//   block row (b, s), s < S            -> position C_b + s,  C_b = ctx_len[b] + n_new[b]
+// Angles pos * theta^(-2i/d) are formed and evaluated in fp64 (positions reach
+// 32K, where an fp32 angle would already be off by ~1e-3 rad), then stored fp32.
+// Block 0 also publishes per-row bookkeeping (clamped): base, appended rows, C_b.
+__global__ void prep_kernel(MetaArgs a) {
+  const int half = a.d / 2;
+  const int Mc = a.B * a.n_new_max, Mx = Mc + a.B * a.S;
+  const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (blockIdx.x == 0 && threadIdx.x < a.B) {
+    const int b = threadIdx.x;
+    const int base = min(max(a.ctx_len[b], 0), a.ctx_bound);
+    const int nn = min(max(a.n_new[b], 0), a.n_new_max);
+    const int cb = min(base + nn, a.ctx_bound);
+    a.meta[b] = base;
+    a.meta[a.B + b] = cb - base;
+    a.meta[2 * a.B + b] = cb;
+  }
+  if (!a.rope || idx >= (long)Mx * half) return;
+  const int row = (int)(idx / half), i = (int)(idx % half);
+  int b, pos;
+  if (row < Mc) {
+    b = row / a.n_new_max;
+    pos = min(max(a.ctx_len[b], 0), a.ctx_bound) + row % a.n_new_max;
+  } else {
+    b = (row - Mc) / a.S;
+    const int base = min(max(a.ctx_len[b], 0), a.ctx_bound);
+    const int cb = min(base + min(max(a.n_new[b], 0), a.n_new_max), a.ctx_bound);
+    pos = cb + (row - Mc) % a.S;
+  }
+  const double inv_freq = pow((double)a.theta, -2.0 * i / (double)a.d);
+  const double ang = (double)pos * inv_freq;
+  double sn, cs;
+  sincos(ang, &sn, &cs);
+  a.rope[idx] = make_float2((float)cs, (float)sn);
+}
+
+__global__ void finish_kernel(const int32_t* meta, int32_t* ctx_len, int B) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b < B) ctx_len[b] = meta[2 * B + b];
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void embed_kernel(const T* E, const int32_t* last_token, int mask_id,
+                                                    int V, int H, int S, float* resid) {
+  const int r = blockIdx.x, b = r / S, s = r % S;
+  int tok = s == 0 ? last_token[b] : mask_id;
+  tok = tok < 0 ? 0 : (tok >= V ? V - 1 : tok);
+  for (int h = threadIdx.x; h < H; h += 256) resid[(size_t)r * H + h] = Elem<T>::load(E, (size_t)tok * H + h);
+}
+
+// One workgroup per row.  v = resid (+ sum of partials) or sum of partials;
+// optionally stored back as the new residual; out = T(v * rsqrt(mean(v^2)+eps) * g).
+constexpr int kNormPer = 32;   // elements per thread: H <= 8192
+template <typename T>
+__global__ __launch_bounds__(256) void norm_kernel(NormArgs a) {
+  __shared__ float red[4];
+  const int r = blockIdx.x, tid = threadIdx.x;
+  float v[kNormPer];
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < kNormPer; ++i) {
+    const int h = tid + i * 256;
+    v[i] = 0.f;
+    if (h < a.H) {
+      float x = 0.f;
+      const size_t off = (size_t)r * a.H + h;
+      if (a.part) {
+        for (int z = 0; z < a.sp; ++z) x += a.part[z * a.part_stride + off];
+        if (a.update_resid) {
+          x = a.resid[off] + x;
+          a.resid[off] = x;
+        }
+      } else {
+        x = a.resid[off];
+      }
+      v[i] = x;
+      ss += x * x;
+    }
+  }
+  ss = block_sum<256>(ss, red);
+  const float rs = rsqrtf(ss / (float)a.H + a.eps);
+  int orow = r;
+  if (a.out_mode == 1) {
+    const int s = r % a.S;
+    if (s == 0) return;
+    orow = (r / a.S) * (a.S - 1) + s - 1;
+  }
+#pragma unroll
+  for (int i = 0; i < kNormPer; ++i) {
+    const int h = tid + i * 256;
+    if (h < a.H) {
+      const float g = Elem<T>::load((const T*)a.gain, h);
+      Elem<T>::store((T*)a.out, (size_t)orow * a.H + h, v[i] * rs * g);
+    }
+  }
+}
+
+// Q/K/V epilogue: one workgroup per (row, head).  Sums the GEMM's split-K
+// partials, applies the rotary embedding to queries and keys, and scatters:
+//   context row -> K cache slot base+j (KV injection, layout [b][g][slot][d]),
+//                  V cache [b][g][d][slot] (values transposed)
+//   block row   -> queries [b][g][hh*S + s][d], block keys [b][g][s][d],
+//                  block values [b][g][d][s]
+template <typename T>
+__global__ __launch_bounds__(64) void qkv_kernel(QkvArgs a) {
+  const int row = blockIdx.x, hd = blockIdx.y;
+  const int d = a.d, half = d / 2;
+  const int Mc = a.B * a.n_new_max;
+  const int Nqkv = (a.nq + 2 * a.nkv) * d;
+  const bool ctx = row < Mc;
+  int b, j, pos_slot;
+  if (ctx) {
+    b = row / a.n_new_max;
+    j = row % a.n_new_max;
+    if (j >= a.meta[a.B + b] || hd < a.nq) return;     // not appended, or no query for context rows
+    pos_slot = a.meta[b] + j;
+  } else {
+    b = (row - Mc) / a.S;
+    j = (row - Mc) % a.S;
+    pos_slot = j;
+  }
+  const int col0 = hd * d;
+  const bool is_q = hd < a.nq, is_k = !is_q && hd < a.nq + a.nkv;
+  const int g = is_q ? hd / (a.nq / a.nkv) : (is_k ? hd - a.nq : hd - a.nq - a.nkv);
+  const size_t bg = (size_t)b * a.nkv + g;
+  auto val = [&](int col) {
+    float x = 0.f;
+    const size_t off = (size_t)row * Nqkv + col0 + col;
+    for (int z = 0; z < a.sp; ++z) x += a.part[z * a.part_stride + off];
+    return x;
+  };
+  for (int i = threadIdx.x; i < half; i += 64) {
+    float x1 = val(i), x2 = val(i + half);
+    if ((is_q || is_k) && a.use_rope) {
+      const float2 cs = a.rope[(size_t)row * half + i];
+      const float y1 = x1 * cs.x - x2 * cs.y;
+      const float y2 = x2 * cs.x + x1 * cs.y;
+      x1 = y1;
+      x2 = y2;
+    }
+    if (is_q) {
+      const int hh = hd % (a.nq / a.nkv);
+      T* dst = (T*)a.q_att + (bg * a.Rpad + hh * a.S + j) * d;
+      Elem<T>::store(dst, i, x1);
+      Elem<T>::store(dst, i + half, x2);
+    } else if (is_k) {
+      T* dst = ctx ? (T*)a.k_cache + (bg * a.max_ctx + pos_slot) * d : (T*)a.k_blk + (bg * 64 + j) * d;
+      Elem<T>::store(dst, i, x1);
+      Elem<T>::store(dst, i + half, x2);
+    } else {
+      const size_t ld = ctx ? (size_t)a.max_ctx : 64;
+      T* dst = ctx ? (T*)a.v_cache + bg * d * ld : (T*)a.v_blk + bg * d * ld;
+      Elem<T>::store(dst, (size_t)i * ld + pos_slot, x1);
+      Elem<T>::store(dst, (size_t)(i + half) * ld + pos_slot, x2);
+    }
+  }
+}
+
+// h = T(silu(gate) * up) with gate = sum_z part[z][m][f], up = sum_z part[z][m][F + f]
+template <typename T>
+__global__ __launch_bounds__(256) void swiglu_kernel(const float* part, int sp, size_t ps, int M, int F,
+                                                     T* out) {
+  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (size_t)M * F) return;
+  const size_t m = idx / F, f = idx % F;
+  float gte = 0.f, up = 0.f;
+  for (int z = 0; z < sp; ++z) {
+    gte += part[z * ps + m * 2 * F + f];
+    up += part[z * ps + m * 2 * F + F + f];
+  }
+  const float silu = gte / (1.f + expf(-gte));
+  Elem<T>::store(out, idx, silu * up);
+}
+
+__global__ __launch_bounds__(256) void reduce_kernel(const float* part, int sp, size_t ps, size_t n, float* out) {
+  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= n) return;
+  float x = 0.f;
+  for (int z = 0; z < sp; ++z) x += part[z * ps + idx];
+  out[idx] = x;
+}
+
+}  // namespace
+
+hipError_t launch_reduce(const float* part, int sp, size_t ps, size_t n, float* out, hipStream_t s) {
+  ProfScope pr("elementwise", s);
+  hipLaunchKernelGGL(reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, part, sp, ps, n, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_prep(const MetaArgs& a, hipStream_t s) {
+  ProfScope ps("elementwise", s);
+  const long n = (long)(a.B * a.n_new_max + a.B * a.S) * (a.d / 2);
+  const int grid = n > 0 ? (int)((n + 255) / 256) : 1;
+  hipLaunchKernelGGL(prep_kernel, dim3(grid), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_finish(const int32_t* meta, int32_t* ctx_len, int B, hipStream_t s) {
+  ProfScope ps("elementwise", s);
+  hipLaunchKernelGGL(finish_kernel, dim3(ceil_div(B, 256)), dim3(256), 0, s, meta, ctx_len, B);
+  return hipGetLastError();
+}
+
+hipError_t launch_embed(int dtype, const void* embed, const int32_t* last_token, int mask_id, int V,
+                        int H, int B, int S, float* resid, hipStream_t s) {
+  ProfScope ps("elementwise", s);
+  if (dtype == 1)
+    hipLaunchKernelGGL(embed_kernel<bf16_t>, dim3(B * S), dim3(256), 0, s, (const bf16_t*)embed, last_token,
+                       mask_id, V, H, S, resid);
+  else
+    hipLaunchKernelGGL(embed_kernel<float>, dim3(B * S), dim3(256), 0, s, (const float*)embed, last_token,
+                       mask_id, V, H, S, resid);
+  return hipGetLastError();
+}
+
+hipError_t launch_norm(const NormArgs& a, int dtype, hipStream_t s) {
+  ProfScope ps("elementwise", s);
+  if (dtype == 1) hipLaunchKernelGGL(norm_kernel<bf16_t>, dim3(a.rows), dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(norm_kernel<float>, dim3(a.rows), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_qkv_epilogue(const QkvArgs& a, int dtype, hipStream_t s) {
+  ProfScope ps("elementwise", s);
+  dim3 grid(a.B * a.n_new_max + a.B * a.S, a.nq + 2 * a.nkv);
+  if (dtype == 1) hipLaunchKernelGGL(qkv_kernel<bf16_t>, grid, dim3(64), 0, s, a);
+  else hipLaunchKernelGGL(qkv_kernel<float>, grid, dim3(64), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_swiglu(const float* part, int sp, size_t ps_, int M, int F, void* out, int dtype,
+                         hipStream_t s) {
+  ProfScope ps("elementwise", s);
+  const int grid = ceil_div(M * F, 256);
+  if (dtype == 1)
+    hipLaunchKernelGGL(swiglu_kernel<bf16_t>, dim3(grid), dim3(256), 0, s, part, sp, ps_, M, F, (bf16_t*)out);
+  else
+    hipLaunchKernelGGL(swiglu_kernel<float>, dim3(grid), dim3(256), 0, s, part, sp, ps_, M, F, (float*)out);
+  return hipGetLastError();
+}
+
+}  // namespace dfs

@@ -1,0 +1,162 @@
+// Internal host-side launchers shared between the translation units of the
+// dfspec library.  Not part of the C ABI.
+#pragma once
+
+#include "common.h"
+
+namespace dfs {
+
+// ------------------------------------------------------------------ GEMM
+// Y[z][m][n] (+)= sum_{k in split z} X[row(m)][k] * W[n][k]
+// W is the row-concatenation of up to three [n_i, K] segments (e.g. wq|wk|wv).
+struct GemmSeg {
+  const void* w = nullptr;
+  int n0 = 0;   // first logical row of W held by this segment
+};
+
+struct GemmArgs {
+  const void* X = nullptr;
+  int ldx = 0;                        // elements between X rows
+  const int32_t* row_idx = nullptr;   // optional row gather: X row of m = row_idx[m * row_idx_stride]
+  int row_idx_stride = 1;
+  int x_rows = 0;                     // rows of X (gathered indices are clamped to it)
+  int M = 0, N = 0, K = 0;
+  GemmSeg seg[3];
+  int nseg = 1;
+  float* Y = nullptr;
+  long ldy = 0;
+  size_t y_split_stride = 0;          // elements between split slices of Y
+  int accumulate = 0;                 // 1: Y += acc (single split only)
+};
+
+struct GemmPlan {
+  int bm = 128, bn = 128, splits = 1, k_per_split = 0;
+};
+
+GemmPlan gemm_plan(int M, int N, int K, int dtype, int force_splits = 0);
+size_t gemm_partial_elems(const GemmPlan& p, int M, int N);   // sp * M * N
+hipError_t launch_gemm(const GemmArgs& a, const GemmPlan& p, int dtype, hipStream_t s);
+
+// ------------------------------------------------------------------ attention
+struct AttnArgs {
+  const void* q;        // [B][nkv][Rpad][d]  rows r = hh * S + s
+  const void* k_blk;    // [B][nkv][64][d]
+  const void* v_blk;    // [B][nkv][d][64]   (transposed)
+  const void* k_cache;  // [B][nkv][max_ctx][d]   (one layer)
+  const void* v_cache;  // [B][nkv][d][max_ctx]   (one layer, transposed)
+  const int32_t* ctx_len;   // [B] context keys per row (already clamped)
+  void* out;            // [B][S][nq][d]
+  float* part_o;        // [B][nkv][nunits][Rpad][d]
+  float* part_ml;       // [B][nkv][nunits][Rpad][2]
+  int B, S, nq, nkv, d, max_ctx, ctx_bound;
+  int R, Rpad;          // rows per kv head = (nq/nkv)*S, padded to 16
+  int keys_per_split, n_ctx_splits;   // units = n_ctx_splits + 1 (last = block keys)
+};
+struct AttnPlan {
+  int keys_per_split, n_ctx_splits;
+};
+AttnPlan attn_plan(int B, int nkv, int ctx_bound, int dtype);
+int attn_max_units(int B, int nkv, int max_ctx, int dtype);
+size_t attn_partial_elems(int units, int B, int nkv, int Rpad, int d);
+hipError_t launch_attention(const AttnArgs& a, int dtype, hipStream_t s);
+// Re-layout of plain [B, S, nq, d] queries and [B, S, nkv, d] keys/values into
+// the attention kernel's operand layouts (used by the stand-alone attention entry).
+hipError_t launch_attn_stage(const void* q, const void* k, const void* v, void* q_att, void* k_blk,
+                             void* v_blk, int B, int S, int nq, int nkv, int d, int Rpad, int dtype,
+                             hipStream_t s);
+
+// ------------------------------------------------------------------ drafter elementwise
+struct MetaArgs {
+  const int32_t* ctx_len;   // [B] in
+  const int32_t* n_new;     // [B] in
+  int32_t* meta;            // [3][B]: base, nn, C_b
+  float2* rope;             // [(B*n_new_max + B*S)][d/2] (cos, sin)
+  int B, S, n_new_max, d, ctx_bound;
+  float theta;
+};
+hipError_t launch_prep(const MetaArgs& a, hipStream_t s);
+hipError_t launch_finish(const int32_t* meta, int32_t* ctx_len, int B, hipStream_t s);
+
+hipError_t launch_embed(int dtype, const void* embed, const int32_t* last_token, int mask_id,
+                        int V, int H, int B, int S, float* resid, hipStream_t s);
+
+// out[row_map(r)] = T( RMSNorm( in[r] (+= sum_z part[z][r]) ; gain ) )
+struct NormArgs {
+  float* resid = nullptr;         // [rows][H] fp32 residual (updated when part != null and update_resid)
+  const float* part = nullptr;    // [sp][rows][H] partials to reduce (nullable)
+  int sp = 0;
+  size_t part_stride = 0;
+  int update_resid = 0;           // 1: resid += sum(part), then normalise resid
+  const void* gain = nullptr;     // [H] dtype
+  void* out = nullptr;            // dtype
+  int rows = 0, H = 0;
+  float eps = 0.f;
+  int out_mode = 0;               // 0: out row = r; 1: only rows with r % S != 0 -> b*(S-1) + s-1
+  int S = 1;
+};
+hipError_t launch_norm(const NormArgs& a, int dtype, hipStream_t s);
+
+struct QkvArgs {
+  const float* part;     // [sp][Mx][Nqkv]
+  int sp;
+  size_t part_stride;
+  const int32_t* meta;   // [3][B]
+  const float2* rope;    // [Mx][d/2]
+  int use_rope;
+  void* k_cache;         // layer base [B][nkv][max_ctx][d]
+  void* v_cache;         // layer base [B][nkv][d][max_ctx]
+  void* q_att;           // [B][nkv][Rpad][d]
+  void* k_blk;           // [B][nkv][64][d]
+  void* v_blk;           // [B][nkv][d][64]
+  int B, S, n_new_max, nq, nkv, d, max_ctx, Rpad;
+};
+hipError_t launch_qkv_epilogue(const QkvArgs& a, int dtype, hipStream_t s);
+
+hipError_t launch_reduce(const float* part, int sp, size_t part_stride, size_t n, float* out, hipStream_t s);
+
+hipError_t launch_swiglu(const float* part, int sp, size_t part_stride, int M, int F, void* out,
+                         int dtype, hipStream_t s);
+
+// ------------------------------------------------------------------ sampling / verify
+// Chunked row statistics: per (row, chunk): (max, sum exp((x-max)/T)) in fp64, or for
+// T == 0 (max, index of the first maximum).
+constexpr int kChunk = 4096;
+hipError_t launch_chunk_stats(const float* x, long row_stride, int rows, int V, float temperature,
+                              double2* stats, hipStream_t s);
+
+struct PickArgs {
+  const float* x;          // logits rows
+  long row_stride;
+  int rows, V;
+  float temperature;
+  const double2* stats;    // [rows][nchunks]
+  const float* u;          // [rows] (stride u_stride)
+  long u_stride;
+  int32_t* tokens;         // [rows] (stride tok_stride)
+  long tok_stride;
+  double* row_stats;       // [rows][2] (stride rs_stride doubles), nullable
+  long rs_stride;
+};
+hipError_t launch_pick(const PickArgs& a, hipStream_t s);
+
+struct VerifyArgs {
+  const float* q;          // draft logits [B][G][V]
+  const float* p;          // target logits [B][G+1][V]
+  const int32_t* drafts;   // [B][G]
+  const float* u_accept;   // [B][G]
+  const float* u_final;    // [B]
+  float temperature;
+  const double* q_stats;   // [B][G][2] (max, sum) of the draft rows, or null -> q_chunk
+  const double2* q_chunk;  // [B*G][nch]
+  const double2* p_chunk;  // [B*(G+1)][nch]
+  double* rowinfo;         // [B][4]: target (max, sum), draft (max, sum) at the decided position
+  double2* sums;           // [B][nch]: fp64 sums of exp for target / draft row at the rejection
+  double* r_chunk;         // [B][nch]: residual mass max(0, p - q) per chunk
+  int32_t* state;          // [B]: first rejected position (G = all accepted)
+  int32_t* out_tokens;     // [B][G+1]
+  int32_t* n_accepted;     // [B]
+  int B, G, V;
+};
+hipError_t launch_verify(const VerifyArgs& a, hipStream_t s);
+
+}  // namespace dfs

@@ -1,0 +1,253 @@
+/*
+ * dfspec.h — C ABI of one block-parallel speculative draft-and-verify step on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Three entry points, called in this order for one cycle:
+ *
+ *   dflash_draft_step   DFlash-style drafter forward pass.  Page "DFlash —
+ *                       диффузионный метод спекулятивного декодинга"
+ *                       (telemetr.me), architecture paragraph: hidden states of
+ *                       several target layers are concatenated, linearly
+ *                       projected and normalised into context features; the same
+ *                       features enter every drafter layer as keys/values ("KV
+ *                       injection"); the block is the last decoded token plus
+ *                       mask tokens, predicted in one pass; attention is full
+ *                       inside the block and causal toward the context.
+ *   markov_bias_sample  DSpark sequential head + sampling.  Page "DeepSeek
+ *                       prezentuje DSpark: przyspieszenie generowania
+ *                       DeepSeek-V4 o 60-85%" (aigest.pl), section "Innowacje w
+ *                       tworzeniu tokenów": a light sequential head adds a bias
+ *                       that depends on the previous token (Markov head,
+ *                       low-rank factorisation, rank 256) to each position's base
+ *                       logits before that position is sampled.
+ *   spec_verify         Rejection-sampling verification.  Same DSpark page,
+ *                       section "Jak działa spekulatywne dekodowanie DSpark?":
+ *                       the target keeps the longest valid prefix and adds one
+ *                       token, exactly preserving the target distribution.  The
+ *                       rule is the standard speculative-sampling one: accept
+ *                       draft d_i while u_i < p_i(d_i)/q_i(d_i); at the first
+ *                       rejection draw from normalise(max(0, p - q)); after a
+ *                       fully accepted block draw one bonus token from p.
+ *
+ * Conventions for every function below
+ *  - Tensor pointers are DEVICE pointers unless marked "host".  All tensors are
+ *    dense, row-major, in the layouts stated.  The caller owns every buffer,
+ *    including the workspace; the library allocates no device memory, keeps no
+ *    mutable global state, never synchronises, and enqueues all work on
+ *    `stream` (a hipStream_t; NULL = the null stream).  Results are valid once
+ *    the caller has synchronised with that stream.
+ *  - Return value: DFS_OK (0) or a negative dfs_status.  Every shape, pointer
+ *    and size check is done on the host before anything is enqueued; on error
+ *    nothing is enqueued and no output is touched.  DFS_EHIP reports a failed
+ *    launch (hipGetLastError), in which case outputs are unspecified.
+ *  - Device-resident integers (token ids, lengths) are not visible to the host
+ *    checks.  Kernels clamp them so that no access leaves its buffer: an
+ *    out-of-range last token is clamped to [0, V-1]; an out-of-range draft token
+ *    is treated as rejected by spec_verify.
+ *  - Calls on one stream are ordered; concurrent calls on different streams
+ *    must not share a workspace or any output buffer.
+ */
+#ifndef DFSPEC_H
+#define DFSPEC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DFS_OK = 0,
+  DFS_EINVAL = -1,        /* null pointer, negative or inconsistent size */
+  DFS_EUNSUPPORTED = -2,  /* valid but outside what the kernels implement (see each call) */
+  DFS_EHIP = -3,          /* a HIP launch failed */
+  DFS_EWORKSPACE = -4     /* workspace smaller than the matching *_workspace_size() */
+} dfs_status;
+
+typedef enum { DFS_F32 = 0, DFS_BF16 = 1 } dfs_dtype;
+
+/* Drafter shape.  B (batch) and the per-call row counts are arguments of the
+ * calls, not part of the configuration. */
+typedef struct {
+  int32_t n_layers;        /* L >= 1 */
+  int32_t hidden;          /* H */
+  int32_t n_q_heads;       /* nq, a multiple of n_kv_heads */
+  int32_t n_kv_heads;      /* nkv */
+  int32_t head_dim;        /* d, even */
+  int32_t mlp_dim;         /* F (SwiGLU width) */
+  int32_t vocab;           /* V */
+  int32_t n_target_layers; /* nT: target layers whose hidden states are concatenated */
+  int32_t block;           /* S = 1 last decoded token + (S-1) mask tokens, S >= 2 */
+  int32_t max_ctx;         /* cache slots per sequence, a multiple of 64 */
+  int32_t mask_token_id;   /* embedding row used for every mask slot, in [0, V) */
+  float rms_eps;           /* RMSNorm: y = x / sqrt(mean(x^2) + eps) * g */
+  float rope_theta;        /* rotate-half rotary base; <= 0 disables rotary embedding */
+  int32_t dtype;           /* dfs_dtype of weights, hidden states, caches and activations */
+} dfs_drafter_cfg;
+
+/* Drafter weights, all in cfg.dtype, matrices stored [out, in] (row = output
+ * feature, inputs contiguous).  The per-layer members point to HOST arrays of
+ * L device pointers.  The embedding and LM head are the target's, reused
+ * (DSpark page, section "Optymalizacja weryfikacji i wydajności"). */
+typedef struct {
+  const void* embed;       /* [V, H] */
+  const void* fc;          /* [H, nT*H]; input = target hiddens concatenated in ascending layer order */
+  const void* fc_norm;     /* [H] RMSNorm gain of the context features */
+  const void* final_norm;  /* [H] */
+  const void* lm_head;     /* [V, H] */
+  const void* const* attn_norm; /* L x [H] */
+  const void* const* wq;        /* L x [nq*d, H] */
+  const void* const* wk;        /* L x [nkv*d, H] */
+  const void* const* wv;        /* L x [nkv*d, H] */
+  const void* const* wo;        /* L x [H, nq*d] */
+  const void* const* mlp_norm;  /* L x [H] */
+  const void* const* w_gate;    /* L x [F, H] */
+  const void* const* w_up;      /* L x [F, H] */
+  const void* const* w_down;    /* L x [H, F] */
+} dfs_drafter_weights;
+
+/* ------------------------------------------------------------------ draft */
+
+/* Bytes of workspace dflash_draft_step needs for this batch and n_new_max.
+ * Returns 0 for an invalid configuration. */
+size_t dflash_draft_workspace_size(const dfs_drafter_cfg* cfg, int32_t batch, int32_t n_new_max);
+
+/* One drafter call.
+ *
+ * 1. Context features of the rows the target committed since the previous
+ *    call: f = RMSNorm(hidden_new[b, j] . fc^T; fc_norm) for j < n_new[b].
+ * 2. KV injection: for every layer l, K = RoPE(f . wk[l]^T), V = f . wv[l]^T are
+ *    written to cache slots ctx_len[b] + j (positions ctx_len[b] + j).
+ * 3. The block [last_token[b], mask x (S-1)] at positions C_b .. C_b+S-1, where
+ *    C_b = ctx_len[b] + n_new[b], runs through the L pre-norm layers
+ *    (attention over the C_b cached keys and the S block keys, full inside the
+ *    block; then a SwiGLU MLP; fp32 residual stream).
+ * 4. base_logits[b, j-1] = RMSNorm(x_j; final_norm) . lm_head^T for mask slot
+ *    j = 1..S-1 (slot j predicts the token at slot j).
+ * 5. ctx_len[b] is advanced to C_b.
+ *
+ * hidden_new  [B, n_new_max, nT*H] cfg.dtype; rows j >= n_new[b] are ignored.
+ * n_new       [B] int32 (device), values clamped to [0, n_new_max].  A prefill
+ *             is a call (or several) with large n_new_max.
+ * n_new_max   host, >= 0.
+ * ctx_bound   host, 1 <= ctx_bound <= max_ctx, and ctx_bound >= ctx_len[b] +
+ *             n_new[b] for every b (used to size the attention grid).  A row
+ *             that breaks it is computed with C_b clamped to ctx_bound (memory
+ *             safe, result unspecified).
+ * k_cache     [L, B, nkv, max_ctx, d] cfg.dtype, in/out, keys after RoPE.
+ * v_cache     [L, B, nkv, d, max_ctx] cfg.dtype, in/out — values stored
+ *             transposed (slots contiguous) so the attention kernel reads them
+ *             as matrix-core operands straight from memory.
+ *             Slots >= C_b are never read (they may hold anything).
+ * ctx_len     [B] int32 (device), in/out.
+ * last_token  [B] int32 (device).
+ * base_logits [B, S-1, V] fp32, out.
+ *
+ * DFS_EUNSUPPORTED for cfg.dtype == DFS_BF16 unless head_dim == 128,
+ * hidden, nq*d, mlp_dim, nT*H are multiples of 64 and (nq/nkv)*S <= 64;
+ * for DFS_F32 unless head_dim <= 256 and (nq/nkv)*S <= 256.
+ */
+int dflash_draft_step(const dfs_drafter_cfg* cfg, const dfs_drafter_weights* weights,
+                      int32_t batch, const void* hidden_new, const int32_t* n_new,
+                      int32_t n_new_max, int32_t ctx_bound, void* k_cache, void* v_cache,
+                      int32_t* ctx_len, const int32_t* last_token, float* base_logits,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------ Markov + sample */
+
+size_t markov_bias_sample_workspace_size(int32_t batch, int32_t n_draft, int32_t vocab);
+
+/* Sequential head and sampling of the gamma = n_draft draft positions.
+ *
+ * For i = 1..gamma (prev_1 = last_token[b], prev_i = d_{i-1}):
+ *   final_i = base_i + U[prev_i] . W      (rank > 0; W stored transposed as Wt)
+ *   d_i     = inverse-CDF draw from softmax(final_i / T) with u_draft[b, i]
+ *             (token ids scanned in increasing order; first k whose running
+ *             sum exceeds u * total), or the lowest-index argmax when T == 0.
+ * With rank == 0 there is no head and all positions are drawn independently.
+ *
+ * logits      [B, gamma, V] fp32, in: base logits, out: final logits (in place).
+ * U, Wt       [V, rank] in uw_dtype (NULL when rank == 0).
+ * last_token  [B] int32; out-of-range previous tokens are clamped to [0, V-1].
+ * u_draft     [B, gamma] fp32 in [0, 1).
+ * temperature host, >= 0.
+ * draft_tokens[B, gamma] int32 out.
+ * row_stats   [B, gamma, 2] fp64 out, may be NULL: (max, sum exp((x - max)/T))
+ *             of each final row (T == 0: (max, 1)); spec_verify can reuse them.
+ *
+ * DFS_EUNSUPPORTED for a bf16 head unless rank is a multiple of 64.
+ */
+int markov_bias_sample(int32_t batch, int32_t n_draft, int32_t vocab, int32_t rank,
+                       float* logits, const void* U, const void* Wt, int32_t uw_dtype,
+                       const int32_t* last_token, const float* u_draft, float temperature,
+                       int32_t* draft_tokens, double* row_stats, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+/* ----------------------------------------------------------------- verify */
+
+size_t spec_verify_workspace_size(int32_t batch, int32_t n_draft, int32_t vocab);
+
+/* Rejection-sampling verification of gamma = n_draft draft tokens per row.
+ *
+ * p_i = softmax(target_logits[b, i] / T), q_i = softmax(draft_logits[b, i] / T).
+ * For i = 1..gamma: accept d_i iff u_accept[b, i] < p_i(d_i) / q_i(d_i)
+ * (q = 0 counts as +inf when p > 0, else 0; an out-of-range d_i is rejected).
+ * At the first rejection a: out token = inverse-CDF draw with u_final[b] from
+ * max(0, p_a - q_a) (from p_a if that has no mass).  If all are accepted: bonus
+ * token = draw from p_{gamma+1} with u_final[b].  T == 0: greedy (accept while
+ * d_i equals the target argmax, emit the argmax).
+ *
+ * draft_logits   [B, gamma, V] fp32 (the final logits the drafts were drawn from).
+ * target_logits  [B, gamma+1, V] fp32.
+ * draft_tokens   [B, gamma] int32.
+ * u_accept       [B, gamma] fp32; u_final [B] fp32.
+ * draft_row_stats[B, gamma, 2] fp64 from markov_bias_sample, or NULL to recompute.
+ * out_tokens     [B, gamma+1] int32 out: accepted drafts, the correction or bonus
+ *                token, then -1.
+ * n_accepted     [B] int32 out, in [0, gamma]; the cycle yields n_accepted + 1 tokens.
+ */
+int spec_verify(int32_t batch, int32_t n_draft, int32_t vocab, const float* draft_logits,
+                const float* target_logits, const int32_t* draft_tokens, const float* u_accept,
+                const float* u_final, float temperature, const double* draft_row_stats,
+                int32_t* out_tokens, int32_t* n_accepted, void* workspace,
+                size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------ misc */
+
+const char* dfs_status_string(int status);
+
+/* Kernel-level hooks used by tests and the benchmark. */
+
+/* Block attention alone, same math and layouts as inside dflash_draft_step:
+ * q [B, S, nq, d], k_blk [B, S, nkv, d], v_blk [B, S, nkv, d] (all cfg dtype),
+ * caches as above for ONE layer ([B, nkv, max_ctx, d] and [B, nkv, d, max_ctx]),
+ * ctx_len [B] int32 = context keys of each row, out [B, S, nq, d] cfg dtype. */
+size_t dfs_block_attention_workspace_size(int32_t batch, int32_t block, int32_t n_q_heads,
+                                          int32_t n_kv_heads, int32_t head_dim, int32_t ctx_bound,
+                                          int32_t dtype);
+int dfs_block_attention(int32_t batch, int32_t block, int32_t n_q_heads, int32_t n_kv_heads,
+                        int32_t head_dim, int32_t max_ctx, int32_t ctx_bound, int32_t dtype,
+                        const void* q, const void* k_blk, const void* v_blk, const void* k_cache,
+                        const void* v_cache, const int32_t* ctx_len, void* out, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+/* Y[M, N] fp32 = X[M, K] . W[N, K]^T, both in `dtype`; the matrix-core kernel of
+ * the drafter (split over K when `splits` > 1; splits = 0 picks automatically). */
+size_t dfs_gemm_workspace_size(int32_t M, int32_t N, int32_t K, int32_t dtype, int32_t splits);
+int dfs_gemm(int32_t M, int32_t N, int32_t K, int32_t dtype, const void* X, const void* W,
+             float* Y, int32_t splits, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Per-kernel timing with HIP events recorded around every launch of the named
+ * kernel group on the launching stream ("gemm", "attention", "sample", "verify",
+ * "markov", "elementwise").  dfs_profile_begin arms recording for at most
+ * max_launches launches (host allocates the events once, outside any timed
+ * region); dfs_profile_end synchronises the events and returns the number of
+ * launches recorded and their summed duration in milliseconds. */
+int dfs_profile_begin(const char* group, int32_t max_launches);
+int dfs_profile_end(int32_t* launches, double* total_ms);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DFSPEC_H */

@@ -1,0 +1,68 @@
+"""Helpers of the GPU parity tests: device upload/download and flag-aware
+comparison of draws.  Imported only by tests marked ``gpu``."""
+import sys
+
+import numpy as np
+import torch
+
+DEV = "cuda"
+FLAG = 1e-6          # draws whose oracle margin is below this may legitimately differ
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def up(arr, kind):
+    a = np.ascontiguousarray(arr)
+    if kind == "bf16":
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(DEV)
+    if kind == "f32":
+        return torch.from_numpy(a.astype(np.float32, copy=False)).to(DEV)
+    if kind == "i32":
+        return torch.from_numpy(a.astype(np.int32, copy=False)).to(DEV)
+    if kind == "f64":
+        return torch.from_numpy(a.astype(np.float64, copy=False)).to(DEV)
+    raise ValueError(kind)
+
+
+def down(t):
+    t = t.detach().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def as_f64(arr, kind):
+    if kind == "bf16":
+        b = np.asarray(arr, np.uint16).astype(np.uint32) << 16
+        return b.view(np.float32).astype(np.float64)
+    return np.asarray(arr, np.float64)
+
+
+def workspace(nbytes):
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=DEV)
+
+
+def compare_sequential_draws(gpu, ora, margins, what):
+    """Rows of sequential draws: equal until the first flagged draw of a row
+    (that draw and everything after it in the row are excluded)."""
+    gpu = np.asarray(gpu)
+    ora = np.asarray(ora)
+    n_cmp = n_flag = 0
+    for b in range(ora.shape[0]):
+        for i in range(ora.shape[1]):
+            if margins[b, i] < FLAG:
+                n_flag += 1
+                break
+            assert gpu[b, i] == ora[b, i], f"{what}: row {b} position {i}: gpu {gpu[b, i]} oracle {ora[b, i]}"
+            n_cmp += 1
+    return n_cmp, n_flag
+
+
+def upload_weights(w, np_weights):
+    from block_speculative_decoding_amd import dfspec as D
+    cfg = D.DrafterConfig.of(w)
+    t = {k: up(v, w.dtype) for k, v in np_weights.items()}
+    return cfg, D.DrafterWeights(cfg, t)
