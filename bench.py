@@ -1,0 +1,249 @@
+"""Benchmark of one block-parallel speculative draft-and-verify step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload C1] [--no-cpu-baseline]
+
+A step = dflash_draft_step (n_new = S freshly committed rows appended onto
+C - S cached rows, block of S) + markov_bias_sample (parallel sampling when the
+workload has no Markov head) + spec_verify against synthetic target logits,
+with every input already resident in HBM.  The context length is reset to
+C - S before each step so each step does identical work.  Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from synth import WORKLOADS, inputs  # noqa: E402
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "draft-verify steps/sec + HBM GB/s, B=8 block=16 ctx=4K vocab=152K (1 GPU)"
+
+
+def algorithmic_bytes(w):
+    """Bytes the step must move at minimum, per kernel group (see the design notes)."""
+    es = 2 if w.dtype == "bf16" else 4
+    B, S, G, C, L, H = w.batch, w.block, w.gamma, w.ctx, w.n_layers, w.hidden
+    nq, nkv, d, F, V, nT, r = (w.n_q_heads, w.n_kv_heads, w.head_dim, w.mlp_dim, w.vocab,
+                               w.n_target_layers, w.markov_rank)
+    Mb, Mc = B * S, B * S
+    per_layer_w = (nq * d * H + 2 * nkv * d * H + H * nq * d + 3 * F * H) * es
+    gemm_w = L * per_layer_w + (H * nT * H + V * H) * es
+    # activations in/out of every GEMM (X read once per launch, fp32 result written once)
+    gemm_act = (Mc * nT * H * es + Mc * H * 4
+                + L * ((Mc + Mb) * H * es + (Mc + Mb) * (nq + 2 * nkv) * d * 4
+                       + Mb * nq * d * es + Mb * H * 4 + Mb * H * es + Mb * 2 * F * 4
+                       + Mb * F * es + Mb * H * 4)
+                + B * G * H * es + B * G * V * 4)
+    attn = L * (B * nkv * (C + S) * d * 2 * es + Mb * nq * d * es * 2)
+    sample = B * G * V * 4                               # read final logits once
+    markov = (V * r * es + B * G * V * 4 * 2) if r > 0 else 0
+    verify = B * (G + 1) * V * 4 + 2 * B * V * 4        # target rows + the two rows at the rejection
+    return {"gemm": gemm_w + gemm_act, "gemm_weights": gemm_w, "attention": attn, "sample": sample,
+            "markov": markov, "verify": verify}
+
+
+class Step:
+    def __init__(self, w, seed=0):
+        import torch
+        from block_speculative_decoding_amd import dfspec as D
+        self.D, self.torch, self.w = D, torch, w
+        dev = "cuda"
+        t0 = time.time()
+
+        def up(a, kind):
+            a = np.ascontiguousarray(a)
+            if kind == "bf16":
+                return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+            return torch.from_numpy(a).to(dev)
+
+        self.np_weights = inputs.drafter_weights(w, seed)
+        self.cfg = D.DrafterConfig.of(w)
+        self.wdev = D.DrafterWeights(self.cfg, {k: up(v, w.dtype) for k, v in self.np_weights.items()})
+        step = inputs.step_inputs(w, seed)
+        self.np_step = step
+        kc, vc = inputs.cache_prefix(w, seed, step["ctx_len"])
+        self.np_cache = (kc, vc)
+        self.k, self.v = D.cache_from_logical(up(kc, w.dtype), up(vc, w.dtype))
+        self.hidden = up(step["hidden_new"], w.dtype)
+        self.n_new = up(step["n_new"], "i32")
+        self.ctx0 = up(step["ctx_len"], "i32")
+        self.ctx = self.ctx0.clone()
+        self.last = up(step["last_token"], "i32")
+        B, G, V = w.batch, w.gamma, w.vocab
+        self.logits = torch.empty((B, G, V), dtype=torch.float32, device=dev)
+        self.tokens = torch.empty((B, G), dtype=torch.int32, device=dev)
+        self.row_stats = torch.empty((B, G, 2), dtype=torch.float64, device=dev)
+        self.out = torch.empty((B, G + 1), dtype=torch.int32, device=dev)
+        self.nacc = torch.empty((B,), dtype=torch.int32, device=dev)
+        ud, ua, uf = inputs.uniforms(w, seed)
+        self.ud, self.ua, self.uf = up(ud, "f32"), up(ua, "f32"), up(uf, "f32")
+        if w.markov_rank > 0:
+            U, Wt = inputs.markov_factors(w, seed)
+            self.U, self.Wt = up(U, w.dtype), up(Wt, w.dtype)
+        else:
+            self.U = self.Wt = None
+        self.ws_d = torch.empty(D.dflash_draft_workspace_size(self.cfg, B, step["n_new_max"]),
+                                dtype=torch.uint8, device=dev)
+        self.ws_m = torch.empty(D.markov_bias_sample_workspace_size(B, G, V), dtype=torch.uint8, device=dev)
+        self.ws_v = torch.empty(D.spec_verify_workspace_size(B, G, V), dtype=torch.uint8, device=dev)
+        if w.target_noise_std > 0:       # target = draft logits + noise: needs one draft pass first
+            self.draft()
+            self.sample()
+            torch.cuda.synchronize()
+            self.target = up(inputs.target_logits(w, seed, draft_logits=self.logits.cpu().numpy()), "f32")
+        else:
+            self.target = up(inputs.target_logits(w, seed), "f32")
+        torch.cuda.synchronize()
+        self.setup_s = time.time() - t0
+
+    def draft(self):
+        self.ctx.copy_(self.ctx0)
+        self.D.dflash_draft_step(self.cfg, self.wdev, self.hidden, self.n_new, self.w.block, self.w.ctx,
+                                 self.k, self.v, self.ctx, self.last, self.logits, self.ws_d)
+
+    def sample(self):
+        self.D.markov_bias_sample(self.logits, self.U, self.Wt, self.last, self.ud, self.w.temperature,
+                                  self.tokens, self.row_stats, self.ws_m)
+
+    def verify(self):
+        self.D.spec_verify(self.logits, self.target, self.tokens, self.ua, self.uf, self.w.temperature,
+                           self.row_stats, self.out, self.nacc, self.ws_v)
+
+    def __call__(self):
+        self.draft()
+        self.sample()
+        self.verify()
+
+
+def time_steps(step, K):
+    torch = step.torch
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    s.record()
+    for _ in range(K):
+        step()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / K
+
+
+def profile_group(step, group, K, launches_per_step):
+    D = step.D
+    D.dfs_profile_begin(group, K * launches_per_step + 8)
+    ms = time_steps(step, K)
+    n, tot = D.dfs_profile_end()
+    return n, tot, ms
+
+
+def cpu_baseline(w, step, budget_s=20.0):
+    """The oracle, as it stands, on batch row 0 of the same workload: one drafter
+    call (its append + block), that row's sampling and its verification.  Scaled
+    to a whole step by the batch size."""
+    import oracle
+    from oracle import drafter as od
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = None
+    cores = len(os.sched_getaffinity(0))
+    kc, vc = step.np_cache
+    st = step.np_step
+    times = []
+    t_end = time.time() + budget_s
+    while not times or (time.time() < t_end and len(times) < 3):
+        ko = kc[:, :1].copy()
+        vo = vc[:, :1].copy()
+        t0 = time.perf_counter()
+        base, _ = od.draft_step(od.DrafterShape.of(w.with_(batch=1)), step.np_weights, st["hidden_new"][:1],
+                                st["n_new"][:1], ko, vo, st["ctx_len"][:1], st["last_token"][:1])
+        ud, ua, uf = (x[:1] for x in inputs.uniforms(w, 0))
+        if w.markov_rank > 0:
+            U, Wt = inputs.markov_factors(w, 0)
+            final, tok, _ = oracle.markov_sample(base, U, Wt, w.dtype, st["last_token"][:1], ud, w.temperature)
+        else:
+            final, tok, _ = oracle.markov_sample(base, None, None, w.dtype, st["last_token"][:1], ud,
+                                                 w.temperature)
+        tgt = step.target[:1].cpu().numpy()
+        oracle.verify(final, tgt, tok, ua, uf, w.temperature)
+        times.append(time.perf_counter() - t0)
+    per_row = float(np.median(times))
+    return {"value": 1.0 / (per_row * w.batch), "unit": "steps/s", "cores": blas_threads or cores,
+            "kind": "oracle",
+            "sample": f"batch row 0 of {w.batch} (drafter call incl. its {w.block}-row append, sampling, "
+                      f"verify), median of {len(times)} run(s) of {per_row:.2f} s, scaled x{w.batch}; "
+                      f"{cores} host cores visible"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="C1", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-roofline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+    w = WORKLOADS[args.workload]
+    print(f"[bench] setting up {w.name}", file=sys.stderr, flush=True)
+    step = Step(w)
+    print(f"[bench] setup {step.setup_s:.1f}s; warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    ms = time_steps(step, args.steps)
+    print(f"[bench] {ms:.3f} ms/step", file=sys.stderr, flush=True)
+    ab = algorithmic_bytes(w)
+    step_bytes = sum(v for k, v in ab.items() if k != "gemm_weights")
+    res = {
+        "metric": METRIC, "value": 1000.0 / ms, "unit": "steps/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic (seeded; weights N(0,0.02^2))",
+        "config": {"workload": w.name, "batch": w.batch, "block": w.block, "ctx": w.ctx, "vocab": w.vocab,
+                   "drafter_layers": w.n_layers, "hidden": w.hidden, "markov_rank": w.markov_rank},
+        "hbm_gbps": step_bytes / (ms * 1e-3) / 1e9,
+        "hbm_frac": step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+    }
+    if not args.no_roofline:
+        L = w.n_layers
+        n, tot, ms_p = profile_group(step, "gemm", args.steps, 4 * L + 2)
+        per_launch_ms = tot / max(n, 1)
+        launches_per_step = n / args.steps
+        gemm_bytes_per_launch = ab["gemm"] / launches_per_step
+        achieved = gemm_bytes_per_launch / (per_launch_ms * 1e-3) / 1e9
+        res["roofline"] = {"kernel": "gemm_bf16_nt (all drafter GEMM launches)", "bound": "hbm",
+                           "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                           "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                           "launches_per_step": launches_per_step, "avg_launch_us": per_launch_ms * 1e3,
+                           "ms_per_step_profiled": ms_p}
+        groups = {}
+        for g, per_step in (("attention", L), ("verify", 1), ("sample", 1), ("markov", 1), ("elementwise", 0)):
+            if g == "markov" and w.markov_rank == 0:
+                continue
+            if g == "sample" and w.markov_rank > 0:
+                continue
+            n, tot, _ = profile_group(step, g, args.steps, max(per_step, 1) * 64)
+            t = tot / args.steps
+            groups[g] = {"ms_per_step": t}
+            if g in ab and ab[g] and t > 0:
+                groups[g]["gbps"] = ab[g] / (t * 1e-3) / 1e9
+                groups[g]["frac"] = groups[g]["gbps"] / HBM_PEAK_GBPS
+        res["groups"] = groups
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(w, step)
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

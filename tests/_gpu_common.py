@@ -9,6 +9,12 @@ DEV = "cuda"
 FLAG = 1e-6          # draws whose oracle margin is below this may legitimately differ
 
 
+def flag_budget(V, n_draws):
+    """Upper bound on flagged draws: a threshold u*S lands within FLAG*S of one of
+    the (up to V) interval ends with probability sum_k min(2*FLAG, p_k) <= 2*FLAG*V."""
+    return 3 + int(3 * 2 * FLAG * V * n_draws)
+
+
 def say(msg):
     print(msg, flush=True)
     sys.stdout.flush()
