@@ -31,7 +31,7 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ bf16x8 load8(const bf16_t* p) {
-  return __builtin_bit_cast(bf16x8, *(const uint4*)p);
+  return __builtin_bit_cast(bf16x8, ldg16(p));
 }
 
 __device__ __forceinline__ bf16x8 zero8() { return __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0)); }

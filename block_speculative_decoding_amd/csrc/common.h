@@ -14,6 +14,17 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 
+// ----------------------------------------------------------------- global loads
+// 16-byte load through an explicit global (address space 1) pointer.  A load
+// through a generic pointer may compile to a flat load, which also counts in
+// the LDS/scalar counter: every wait for an LDS read would then drain all
+// outstanding HBM loads.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) const u32x4 global_u32x4;
+__device__ __forceinline__ uint4 ldg16(const void* p) { return __builtin_bit_cast(uint4, *(global_u32x4*)p); }
+typedef __attribute__((address_space(1))) const bf16x8 global_bf16x8;
+__device__ __forceinline__ bf16x8 ldg_bf16x8(const void* p) { return *(global_bf16x8*)p; }
+
 // ----------------------------------------------------------------- scalar conversions
 
 __device__ __forceinline__ float bf2f(bf16_t v) { return __uint_as_float(((uint32_t)v) << 16); }

@@ -62,36 +62,35 @@ __global__ __launch_bounds__(256) void embed_kernel(const T* E, const int32_t* l
   for (int h = threadIdx.x; h < H; h += 256) resid[(size_t)r * H + h] = Elem<T>::load(E, (size_t)tok * H + h);
 }
 
-// One workgroup per row.  v = resid (+ sum of partials) or sum of partials;
-// optionally stored back as the new residual; out = T(v * rsqrt(mean(v^2)+eps) * g).
-constexpr int kNormPer = 32;   // elements per thread: H <= 8192
+// RMSNorm of one row per workgroup (1024 threads): out = T(x * rsqrt(mean(x^2)+eps) * g)
+// with x = the fp32 row `resid`.  Each thread holds up to two 4-element groups
+// (H <= 8192); vector loads when H is a multiple of 4.
+constexpr int kNormThreads = 1024;
 template <typename T>
-__global__ __launch_bounds__(256) void norm_kernel(NormArgs a) {
-  __shared__ float red[4];
+__global__ __launch_bounds__(1024) void norm_kernel(NormArgs a) {
+  __shared__ float red[kNormThreads / 64];
   const int r = blockIdx.x, tid = threadIdx.x;
-  float v[kNormPer];
+  const bool vec = (a.H & 3) == 0;
+  const float* row = a.resid + (size_t)r * a.H;
+  float v[2][4];
   float ss = 0.f;
 #pragma unroll
-  for (int i = 0; i < kNormPer; ++i) {
-    const int h = tid + i * 256;
-    v[i] = 0.f;
-    if (h < a.H) {
-      float x = 0.f;
-      const size_t off = (size_t)r * a.H + h;
-      if (a.part) {
-        for (int z = 0; z < a.sp; ++z) x += a.part[z * a.part_stride + off];
-        if (a.update_resid) {
-          x = a.resid[off] + x;
-          a.resid[off] = x;
-        }
-      } else {
-        x = a.resid[off];
-      }
-      v[i] = x;
-      ss += x * x;
+  for (int i = 0; i < 2; ++i) {
+    const int h = 4 * (tid + i * kNormThreads);
+    if (vec && h < a.H) {
+      const float4 t = *(const float4*)(row + h);
+      v[i][0] = t.x;
+      v[i][1] = t.y;
+      v[i][2] = t.z;
+      v[i][3] = t.w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[i][e] = h + e < a.H ? row[h + e] : 0.f;
     }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ss += v[i][e] * v[i][e];
   }
-  ss = block_sum<256>(ss, red);
+  ss = block_sum<kNormThreads>(ss, red);
   const float rs = rsqrtf(ss / (float)a.H + a.eps);
   int orow = r;
   if (a.out_mode == 1) {
@@ -99,13 +98,13 @@ __global__ __launch_bounds__(256) void norm_kernel(NormArgs a) {
     if (s == 0) return;
     orow = (r / a.S) * (a.S - 1) + s - 1;
   }
+  T* out = (T*)a.out + (size_t)orow * a.H;
 #pragma unroll
-  for (int i = 0; i < kNormPer; ++i) {
-    const int h = tid + i * 256;
-    if (h < a.H) {
-      const float g = Elem<T>::load((const T*)a.gain, h);
-      Elem<T>::store((T*)a.out, (size_t)orow * a.H + h, v[i] * rs * g);
-    }
+  for (int i = 0; i < 2; ++i) {
+    const int h = 4 * (tid + i * kNormThreads);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (h + e < a.H) Elem<T>::store(out, h + e, v[i][e] * rs * Elem<T>::load((const T*)a.gain, h + e));
   }
 }
 
@@ -186,19 +185,52 @@ __global__ __launch_bounds__(256) void swiglu_kernel(const float* part, int sp, 
   Elem<T>::store(out, idx, silu * up);
 }
 
-__global__ __launch_bounds__(256) void reduce_kernel(const float* part, int sp, size_t ps, size_t n, float* out) {
+// out = (accumulate ? out : 0) + sum_z part[z]; split slices summed in z order.
+__global__ __launch_bounds__(256) void reduce_kernel(const float* part, int sp, size_t ps, size_t n, float* out,
+                                                     int accumulate) {
   const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
   if (idx >= n) return;
-  float x = 0.f;
-  for (int z = 0; z < sp; ++z) x += part[z * ps + idx];
-  out[idx] = x;
+  float x = accumulate ? out[idx] : 0.f;
+  float y = 0.f;
+  for (int z = 0; z < sp; ++z) y += part[z * ps + idx];
+  out[idx] = x + y;
+}
+
+// float4 variant (n, ps multiples of 4 and 16-byte aligned buffers)
+__global__ __launch_bounds__(256) void reduce4_kernel(const float4* part, int sp, size_t ps4, size_t n4, float4* out,
+                                                      int accumulate) {
+  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= n4) return;
+  float4 y = part[idx];
+  for (int z = 1; z < sp; ++z) {
+    const float4 t = part[z * ps4 + idx];
+    y.x += t.x;
+    y.y += t.y;
+    y.z += t.z;
+    y.w += t.w;
+  }
+  if (accumulate) {
+    const float4 x = out[idx];
+    y.x += x.x;
+    y.y += x.y;
+    y.z += x.z;
+    y.w += x.w;
+  }
+  out[idx] = y;
 }
 
 }  // namespace
 
-hipError_t launch_reduce(const float* part, int sp, size_t ps, size_t n, float* out, hipStream_t s) {
+hipError_t launch_reduce(const float* part, int sp, size_t ps, size_t n, float* out, hipStream_t s,
+                         int accumulate) {
   ProfScope pr("elementwise", s);
-  hipLaunchKernelGGL(reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, part, sp, ps, n, out);
+  const bool vec = n % 4 == 0 && ps % 4 == 0 && ((uintptr_t)part & 15) == 0 && ((uintptr_t)out & 15) == 0;
+  if (vec && sp >= 1)
+    hipLaunchKernelGGL(reduce4_kernel, dim3((unsigned)((n / 4 + 255) / 256)), dim3(256), 0, s, (const float4*)part,
+                       sp, ps / 4, n / 4, (float4*)out, accumulate);
+  else
+    hipLaunchKernelGGL(reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, part, sp, ps, n, out,
+                       accumulate);
   return hipGetLastError();
 }
 
@@ -228,10 +260,21 @@ hipError_t launch_embed(int dtype, const void* embed, const int32_t* last_token,
   return hipGetLastError();
 }
 
-hipError_t launch_norm(const NormArgs& a, int dtype, hipStream_t s) {
+// With split-K partials: first a fully parallel reduction (into the residual, or
+// in place into partial slice 0), then the row-wise normalisation of that buffer.
+hipError_t launch_norm(const NormArgs& in, int dtype, hipStream_t s) {
+  NormArgs a = in;
+  if (a.part) {
+    float* dst = a.update_resid ? a.resid : const_cast<float*>(a.part);
+    hipError_t e = launch_reduce(a.part, a.sp, a.part_stride, (size_t)a.rows * a.H, dst, s, a.update_resid);
+    if (e != hipSuccess) return e;
+    a.resid = dst;
+    a.part = nullptr;
+    a.update_resid = 0;
+  }
   ProfScope ps("elementwise", s);
-  if (dtype == 1) hipLaunchKernelGGL(norm_kernel<bf16_t>, dim3(a.rows), dim3(256), 0, s, a);
-  else hipLaunchKernelGGL(norm_kernel<float>, dim3(a.rows), dim3(256), 0, s, a);
+  if (dtype == 1) hipLaunchKernelGGL(norm_kernel<bf16_t>, dim3(a.rows), dim3(kNormThreads), 0, s, a);
+  else hipLaunchKernelGGL(norm_kernel<float>, dim3(a.rows), dim3(kNormThreads), 0, s, a);
   return hipGetLastError();
 }
 

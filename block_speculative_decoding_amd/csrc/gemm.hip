@@ -14,6 +14,11 @@
 // fp32: a plain LDS-tiled VALU kernel (the fp32 configuration is tiny).
 #include "kernels.h"
 
+#ifdef DFS_TUNING
+#include <stdio.h>
+#include <stdlib.h>
+#endif
+
 namespace dfs {
 
 namespace {
@@ -74,10 +79,10 @@ __global__ __launch_bounds__(256) void gemm_bf16_nt(GemmArgs a, int k_per_split)
   auto gload = [&](int kt) {
 #pragma unroll
     for (int i = 0; i < A_CH; ++i)
-      ra[i] = a_ok[i] ? *(const uint4*)(a_src[i] + kt * BK) : make_uint4(0, 0, 0, 0);
+      ra[i] = a_ok[i] ? ldg16(a_src[i] + kt * BK) : make_uint4(0, 0, 0, 0);
 #pragma unroll
     for (int i = 0; i < B_CH; ++i)
-      rb[i] = b_ok[i] ? *(const uint4*)(b_src[i] + kt * BK) : make_uint4(0, 0, 0, 0);
+      rb[i] = b_ok[i] ? ldg16(b_src[i] + kt * BK) : make_uint4(0, 0, 0, 0);
   };
   auto sstore = [&](int buf) {
 #pragma unroll
@@ -139,6 +144,163 @@ __global__ __launch_bounds__(256) void gemm_bf16_nt(GemmArgs a, int k_per_split)
     }
 }
 
+// Weight-streaming kernel for the drafter's small M (<= 256 rows), with
+// producer/consumer waves.  A workgroup has 8 waves:
+//   waves 4..7 (producers) stream the X tile (all BM rows x 64 k per step)
+//     global -> registers -> LDS, XPD steps ahead;
+//   waves 0..3 (consumers) stream their own 16*NW rows of W straight into MFMA
+//     B-operand registers, PD steps ahead, and run the matrix-core math.
+// Vector-memory counters are per wave and retire in order, so a wave that
+// issued both operands would have to drain its deep W prefetch every time it
+// waited for the (younger) X step; splitting the roles keeps every wave's
+// waits on its own oldest loads only.  One barrier per k step; X is double
+// buffered in LDS.
+//
+// Every load is unconditional (a predicated load becomes a branch, after which
+// the compiler waits for everything): rows past M of X and past N of W read a
+// valid row instead — output row m depends only on X row m and output column n
+// only on W row n, and neither is stored — and steps past the end re-read the
+// last step (cache hits) with the math skipped.
+//
+// Grid: 1-D over (m tile, n tile, k split), m tile fastest, remapped so that
+// consecutive logical ids run on the same XCD (the hardware sends workgroup i
+// to XCD i % 8): M tiles sharing one W slab then hit the same L2.
+__device__ __forceinline__ int xcd_logical_id(int id, int total) {
+  const int full = total & ~7;
+  if (id >= full) return id;
+  return (id & 7) * (full >> 3) + (id >> 3);
+}
+
+template <int MT, int NW>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void gemm_stream_bf16(GemmArgs a, int k_per_split, int mtiles, int ntiles) {
+  constexpr int BM = 16 * MT, BN = 64 * NW;
+  constexpr int XCH = BM * BK / 8 / 256;                // 16-byte X chunks per producer lane per step
+  static_assert(XCH >= 1, "tile too small");
+  __shared__ __attribute__((aligned(16))) bf16_t Xs[2][BM * LDK];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const bool producer = wave >= 4;
+  const int lid = xcd_logical_id(blockIdx.x, gridDim.x);
+  const int mtile = lid % mtiles, rest = lid / mtiles;
+  const int n0 = (rest % ntiles) * BN, m0 = mtile * BM, z = rest / ntiles;
+  const int kbeg = z * k_per_split;
+  const int kend = min(a.K, kbeg + k_per_split);
+  const int nk = kend > kbeg ? (kend - kbeg) / BK : 0;
+  if (nk == 0) return;                                   // uniform over the workgroup
+  const int c = lane & 15, g4 = lane >> 4;
+
+  // producer state: X rows of this tile
+  const bf16_t* x_src[XCH];
+  int x_dst[XCH];
+  // consumer state: W rows of this wave
+  const bf16_t* w_src[NW];
+  if (producer) {
+    const int ptid = tid - 256;
+#pragma unroll
+    for (int i = 0; i < XCH; ++i) {
+      const int ch = ptid + i * 256, row = ch >> 3, col = (ch & 7) * 8, m = min(m0 + row, a.M - 1);
+      x_src[i] = (const bf16_t*)a.X + (size_t)x_row(a, m) * a.ldx + kbeg + col;
+      x_dst[i] = row * LDK + col;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < NW; ++j) {
+      const int n = min(n0 + wave * 16 * NW + j * 16 + c, a.N - 1);
+      w_src[j] = (const bf16_t*)seg_row(a, n, 2) + kbeg + g4 * 8;
+    }
+  }
+
+  // The two roles run separate loops with the same barrier sequence (one per k
+  // step).  Steps are expanded by macro so every ring index is a constant.
+  if (producer) {
+    // X comes from L2: a 2-deep ring (two named stages) is enough.
+    uint4 xr0[XCH], xr1[XCH];
+#pragma unroll
+    for (int i = 0; i < XCH; ++i) {
+      xr0[i] = ldg16(x_src[i]);
+      xr1[i] = ldg16(x_src[i] + min(1, nk - 1) * BK);
+    }
+#define DFS_PRODUCER_STEP(ST, XR)                                              \
+  {                                                                            \
+    const int kt = kb + ST;                                                    \
+    if (kt < nk) {                                                             \
+      bf16_t* xs = Xs[ST & 1];                                                 \
+      _Pragma("unroll") for (int i = 0; i < XCH; ++i) *(uint4*)&xs[x_dst[i]] = XR[i]; \
+      __syncthreads();                                                         \
+    }                                                                          \
+    const int kk = min(kt + 2, nk - 1) * BK;                                   \
+    _Pragma("unroll") for (int i = 0; i < XCH; ++i) XR[i] = ldg16(x_src[i] + kk);          \
+  }
+    for (int kb = 0; kb < nk; kb += 4) {
+      DFS_PRODUCER_STEP(0, xr0)
+      DFS_PRODUCER_STEP(1, xr1)
+      DFS_PRODUCER_STEP(2, xr0)
+      DFS_PRODUCER_STEP(3, xr1)
+    }
+#undef DFS_PRODUCER_STEP
+    return;
+  }
+
+  f32x4 acc[MT][NW];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < NW; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  bf16x8 wr[4][NW][2];
+#pragma unroll
+  for (int st = 0; st < 4; ++st)
+#pragma unroll
+    for (int j = 0; j < NW; ++j)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+        wr[st][j][ks] = ldg_bf16x8(w_src[j] + min(st, nk - 1) * BK + ks * 32);
+#define DFS_CONSUMER_STEP(ST)                                                                  \
+  {                                                                                            \
+    const int kt = kb + ST;                                                                    \
+    if (kt < nk) {                                                                             \
+      __syncthreads();                                                                         \
+      const bf16_t* xs = Xs[ST & 1];                                                           \
+      _Pragma("unroll") for (int ks = 0; ks < 2; ++ks) {                                       \
+        bf16x8 bfg[NW];                                                                        \
+        _Pragma("unroll") for (int j = 0; j < NW; ++j) bfg[j] = wr[ST][j][ks];                \
+        _Pragma("unroll") for (int i = 0; i < MT; ++i) {                                       \
+          const bf16x8 af = *(const bf16x8*)&xs[(i * 16 + c) * LDK + ks * 32 + g4 * 8];          \
+          _Pragma("unroll") for (int j = 0; j < NW; ++j)                                       \
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bfg[j], acc[i][j], 0, 0, 0);   \
+        }                                                                                      \
+      }                                                                                        \
+    }                                                                                          \
+    const int kk = min(kt + 4, nk - 1) * BK;                                                   \
+    _Pragma("unroll") for (int j = 0; j < NW; ++j)                                             \
+      _Pragma("unroll") for (int ks = 0; ks < 2; ++ks) wr[ST][j][ks] = ldg_bf16x8(w_src[j] + kk + ks * 32); \
+  }
+  for (int kb = 0; kb < nk; kb += 4) {
+    DFS_CONSUMER_STEP(0)
+    DFS_CONSUMER_STEP(1)
+    DFS_CONSUMER_STEP(2)
+    DFS_CONSUMER_STEP(3)
+  }
+#undef DFS_CONSUMER_STEP
+
+  float* Y = a.Y + (size_t)z * a.y_split_stride;
+#pragma unroll
+  for (int j = 0; j < NW; ++j) {
+    const int n = n0 + wave * 16 * NW + j * 16 + c;
+    if (n >= a.N) continue;
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = m0 + i * 16 + g4 * 4 + r;
+        if (m >= a.M) continue;
+        float* y = Y + (size_t)m * a.ldy + n;
+        if (a.accumulate) *y = *y + acc[i][j][r];
+        else *y = acc[i][j][r];
+      }
+  }
+}
+
 // fp32: 64x64 output tile, 256 threads each computing a 4x4 block, BK = 16.
 __global__ __launch_bounds__(256) void gemm_f32_nt(GemmArgs a, int k_per_split) {
   constexpr int T = 64, KT = 16;
@@ -190,49 +352,84 @@ __global__ __launch_bounds__(256) void gemm_f32_nt(GemmArgs a, int k_per_split) 
 
 }  // namespace
 
-// Pick tile shape and K split.  Cost model (bytes-equivalent): weights once from
-// HBM, X once per column tile (mostly from L2, weighted 1/4), fp32 partial
-// slices written and read back (when split), scaled up when the grid is too
-// small to keep ~2 workgroups on each of the 256 CUs.
+// Kernel configurations the planner chooses from.
+//   kind 0: LDS-tiled (both operands staged), BM x BN in {128,64}^2 — large M.
+//   kind 1: weight streaming, BM = 16*MT rows, BN = 64*NW columns — M <= 256.
+struct Cand {
+  int kind, bm, bn, mt, nw;
+};
+static const Cand kCands[] = {
+    {1, 128, 128, 8, 2}, {1, 128, 64, 8, 1}, {1, 64, 128, 4, 2}, {1, 64, 64, 4, 1},
+    {1, 32, 128, 2, 2},  {1, 32, 64, 2, 1},  {1, 256, 64, 16, 1},
+    {0, 128, 128, 0, 0}, {0, 128, 64, 0, 0}, {0, 64, 128, 0, 0}, {0, 64, 64, 0, 0},
+};
+
+// Cost model (seconds at the HBM roofline): weights once per M tile, X staged
+// once per column tile (mostly L2 hits, weighted 1/4), fp32 split partials
+// written and read back (mostly MALL-resident, weighted 1/2), the dense product
+// at ~half the bf16 peak, all divided by how well the grid fills 256 CUs.
 GemmPlan gemm_plan(int M, int N, int K, int dtype, int force_splits) {
   GemmPlan best;
   if (dtype != 1) {   // fp32 VALU kernel
+    best.kind = 2;
     best.bm = best.bn = 64;
     best.splits = 1;
     best.k_per_split = K;
     return best;
   }
   const int kb = K / BK;
-  const int cand[4][2] = {{128, 128}, {128, 64}, {64, 128}, {64, 64}};
+#ifdef DFS_TUNING
+  // tuning builds only: DFS_GEMM_FORCE="kind,bm,bn,mt,nw,splits" selects a configuration
+  if (const char* f = getenv("DFS_GEMM_FORCE")) {
+    GemmPlan p;
+    int sp = 1;
+    if (sscanf(f, "%d,%d,%d,%d,%d,%d", &p.kind, &p.bm, &p.bn, &p.mt, &p.nw, &sp) == 6) {
+      const int kps_blocks = ceil_div(kb, sp);
+      p.splits = ceil_div(kb, kps_blocks);
+      p.k_per_split = kps_blocks * BK;
+      return p;
+    }
+  }
+#endif
   double best_cost = 1e300;
-  for (auto& c : cand) {
-    const int bm = c[0], bn = c[1];
-    const int mt = ceil_div(M, bm), nt = ceil_div(N, bn);
+  for (const Cand& c : kCands) {
+    if (c.kind == 1 && M > 256) continue;
+    const int mt = ceil_div(M, c.bm), nt = ceil_div(N, c.bn);
     for (int sp = 1; sp <= 32; ++sp) {
       if (force_splits && sp != force_splits) continue;
       const int kps_blocks = ceil_div(kb, sp);
       const int real_sp = ceil_div(kb, kps_blocks);
       if (real_sp != sp) continue;
       if (sp > 1 && kps_blocks < 4 && !force_splits) continue;
-      const double w = 2.0 * N * K;
-      const double x = 2.0 * (double)mt * bm * K * nt;                 // staged X bytes
-      const double flops = 2.0 * (double)mt * bm * nt * bn * K;
-      const double part = sp > 1 ? 8.0 * M * N * sp : 4.0 * M * N;
+      // the streaming kernel runs the M tiles of one W slab on the same XCD
+      // (partial L2 reuse); staged X is mostly L2 hits
+      const double w = 2.0 * N * K * (c.kind == 1 ? 1.0 + 0.5 * (mt - 1) : mt);
+      const double x = 2.0 * (double)mt * c.bm * K * nt;
+      const double flops = 2.0 * (double)mt * c.bm * nt * c.bn * K;
+      // fp32 output: one slice, or sp slices written and read back by the consumer
+      const double part = sp > 1 ? 1.5 * 4.0 * M * N * sp : 4.0 * M * N;
       const double wgs = (double)mt * nt * sp;
-      const double fill = wgs >= 512 ? 1.0 : wgs / 512.0;
-      const double mem = (w + 0.25 * x + part) / 8.0e12;
-      const double cmp = flops / 1.2e15;                                  // ~half of dense peak
+      // one 512-thread streaming workgroup per CU already saturates its share;
+      // the LDS-tiled kernel runs two 256-thread workgroups per CU
+      const double full = c.kind == 1 ? 192.0 : 512.0;
+      const double fill = wgs >= full ? 1.0 : wgs / full;
+      const double mem = (w + 0.5 * x + part) / 8.0e12;
+      const double cmp = flops / 1.2e15;
       const double cost = (mem > cmp ? mem : cmp) / fill;
       if (cost < best_cost * 0.999) {
         best_cost = cost;
-        best.bm = bm;
-        best.bn = bn;
+        best.kind = c.kind;
+        best.bm = c.bm;
+        best.bn = c.bn;
+        best.mt = c.mt;
+        best.nw = c.nw;
         best.splits = sp;
         best.k_per_split = kps_blocks * BK;
       }
     }
   }
-  if (best_cost == 1e300) {   // forced split count not representable: closest valid
+  if (best_cost == 1e300) {   // forced split count not representable
+    best.kind = 0;
     best.bm = 128;
     best.bn = 128;
     best.splits = 1;
@@ -251,14 +448,33 @@ hipError_t launch_gemm(const GemmArgs& a, const GemmPlan& p, int dtype, hipStrea
     return hipGetLastError();
   }
   dim3 grid(ceil_div(a.N, p.bn), ceil_div(a.M, p.bm), p.splits);
+  const int kps = p.k_per_split;
+  if (p.kind == 1) {
+    const int mtl = ceil_div(a.M, p.bm), ntl = ceil_div(a.N, p.bn);
+    const dim3 g1(mtl * ntl * p.splits);
+#define DFS_STREAM(MT_, NW_, PD_)                                                                        \
+  if (p.mt == MT_ && p.nw == NW_) {                                                                       \
+    hipLaunchKernelGGL((gemm_stream_bf16<MT_, NW_>), g1, dim3(512), 0, s, a, kps, mtl, ntl);          \
+    return hipGetLastError();                                                                             \
+  }
+    DFS_STREAM(2, 2, 4)
+    DFS_STREAM(2, 1, 4)
+    DFS_STREAM(4, 2, 4)
+    DFS_STREAM(4, 1, 4)
+    DFS_STREAM(8, 2, 4)
+    DFS_STREAM(8, 1, 4)
+    DFS_STREAM(16, 1, 4)
+#undef DFS_STREAM
+    return hipErrorInvalidValue;
+  }
   if (p.bm == 128 && p.bn == 128)
-    hipLaunchKernelGGL((gemm_bf16_nt<128, 128>), grid, dim3(256), 0, s, a, p.k_per_split);
+    hipLaunchKernelGGL((gemm_bf16_nt<128, 128>), grid, dim3(256), 0, s, a, kps);
   else if (p.bm == 128 && p.bn == 64)
-    hipLaunchKernelGGL((gemm_bf16_nt<128, 64>), grid, dim3(256), 0, s, a, p.k_per_split);
+    hipLaunchKernelGGL((gemm_bf16_nt<128, 64>), grid, dim3(256), 0, s, a, kps);
   else if (p.bm == 64 && p.bn == 128)
-    hipLaunchKernelGGL((gemm_bf16_nt<64, 128>), grid, dim3(256), 0, s, a, p.k_per_split);
+    hipLaunchKernelGGL((gemm_bf16_nt<64, 128>), grid, dim3(256), 0, s, a, kps);
   else
-    hipLaunchKernelGGL((gemm_bf16_nt<64, 64>), grid, dim3(256), 0, s, a, p.k_per_split);
+    hipLaunchKernelGGL((gemm_bf16_nt<64, 64>), grid, dim3(256), 0, s, a, kps);
   return hipGetLastError();
 }
 

@@ -30,7 +30,8 @@ struct GemmArgs {
 };
 
 struct GemmPlan {
-  int bm = 128, bn = 128, splits = 1, k_per_split = 0;
+  int kind = 0;            // 0: LDS-tiled, 1: weight streaming, 2: fp32 VALU
+  int bm = 128, bn = 128, mt = 0, nw = 0, splits = 1, k_per_split = 0;
 };
 
 GemmPlan gemm_plan(int M, int N, int K, int dtype, int force_splits = 0);
@@ -112,7 +113,8 @@ struct QkvArgs {
 };
 hipError_t launch_qkv_epilogue(const QkvArgs& a, int dtype, hipStream_t s);
 
-hipError_t launch_reduce(const float* part, int sp, size_t part_stride, size_t n, float* out, hipStream_t s);
+hipError_t launch_reduce(const float* part, int sp, size_t part_stride, size_t n, float* out, hipStream_t s,
+                         int accumulate = 0);
 
 hipError_t launch_swiglu(const float* part, int sp, size_t part_stride, int M, int F, void* out,
                          int dtype, hipStream_t s);
