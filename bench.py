@@ -191,10 +191,21 @@ def main():
     ap.add_argument("--workload", default="C1", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-roofline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy 5 times (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build measures one GPU only; --gpus must be 1"}))
         sys.exit(2)
+    if args.calibrate_copy:
+        import torch
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_per_launch": src.numel() * 4, "launches": 5}))
+        return
     w = WORKLOADS[args.workload]
     print(f"[bench] setting up {w.name}", file=sys.stderr, flush=True)
     step = Step(w)

@@ -3,22 +3,13 @@
 // context key precedes the block, so each block row sees all C_b context keys
 // and all S block keys).
 //
-// bf16 path.  One wave owns one work unit (batch row b, key/value head g, key
-// range).  Its queries are the R = (nq/nkv)*S rows of the GQA group (<= 64),
-// held in registers for the whole unit.  Keys are walked 32 at a time:
-//   S^T = K . Q^T    (v_mfma_f32_16x16x32_bf16; A = 16 keys x 32 dims read
-//                     straight from the [slot][d] key cache)
-//   online softmax in the exp2 domain, per query row (a row's 32 scores live in
-//                     4 lanes: two cross-lane xor-shuffles reduce them)
-//   O^T += V^T . P^T (A = 16 dims x 32 keys read straight from the transposed
-//                     [d][slot] value cache; B = the probabilities exactly as the
-//                     S^T step left them in registers)
-// Key order inside a 32-key step is permuted for the S^T operand (A row c holds
-// key 8*(c/4) + 4*t + c%4 of tile t) so that each lane ends up holding 8
-// consecutive keys of one query row — the B-operand layout of the next MFMA —
-// with no LDS round trip.  Context keys are split over units; one extra unit
-// per (b, g) takes the S block keys; a combine kernel merges the units'
-// (max, sum, O) partials.
+// bf16 path (matrix cores, v_mfma_f32_16x16x32_bf16).  The work unit is
+// (batch row b, key/value head g, key range); its queries are the
+// R = (nq/nkv)*S rows of the GQA group (<= 64).  A 4-wave workgroup streams the
+// unit's K and V^T tiles through LDS once and each wave multiplies them against
+// its own 16 query rows (details at the kernel).  Context keys are split over
+// units so that the grid fills the GPU; one extra unit per (b, g) takes the S
+// block keys; a combine kernel merges the units' (max, sum, O) partials.
 //
 // fp32 path: one workgroup per query row, two-pass chunked softmax on VALU.
 #include "kernels.h"
@@ -36,10 +27,29 @@ __device__ __forceinline__ bf16x8 load8(const bf16_t* p) {
 
 __device__ __forceinline__ bf16x8 zero8() { return __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0)); }
 
-template <int RT>
-__global__ __launch_bounds__(64) void attn_bf16_d128(AttnArgs a) {
-  constexpr int D = 128;
-  const int lane = threadIdx.x, c = lane & 15, g4 = lane >> 4;
+// One workgroup (4 waves) per unit: batch row b, key/value head g, key range.
+// Wave w owns query rows [16w, 16w+16) of the GQA group (rows >= R idle).
+// Keys are walked 64 at a time.  All 256 threads load the step's K tile
+// (64 slots x 128 dims, contiguous in the [slot][d] cache) and V^T tile
+// (128 dims x 64 slots of the transposed [d][slot] cache) into registers two
+// steps ahead, then into double-buffered LDS; the 4 waves share both tiles.
+//   S^T = K . Q^T    A = 16 keys x 32 dims from LDS; B = the wave's queries (registers)
+//   online softmax in the exp2 domain (a row's 64 scores live in 4 lanes)
+//   O^T += V^T . P^T A = 16 dims x 32 keys from LDS; B = the probabilities as the
+//                    S^T step left them (key order permuted inside a step: A row c
+//                    of key tile t is key 32*(t/2) + 8*(c/4) + 4*(t%2) + c%4, so
+//                    each lane holds 8 consecutive keys of one query row)
+// Value slots past the end of the range are zeroed on their way into LDS (slots
+// past C_b may hold anything, including NaN); their scores are masked to -inf.
+constexpr int kAttnKeys = 64;
+constexpr int kKLd = 128 + 8;              // LDS row of the K tile (bf16 elements)
+constexpr int kVLd = kAttnKeys + 8;        // LDS row of the V^T tile
+
+__global__ __launch_bounds__(256) void attn_bf16_d128(AttnArgs a) {
+  constexpr int D = 128, KS = kAttnKeys;
+  __shared__ __attribute__((aligned(16))) bf16_t Ks[2][KS * kKLd];
+  __shared__ __attribute__((aligned(16))) bf16_t Vs[2][D * kVLd];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, c = lane & 15, g4 = lane >> 4;
   const int unit = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int units = a.n_ctx_splits + 1;
   const size_t bg = (size_t)b * a.nkv + g;
@@ -60,138 +70,158 @@ __global__ __launch_bounds__(64) void attn_bf16_d128(AttnArgs a) {
     k_begin = unit * a.keys_per_split;
     k_end = min(min(a.ctx_len[b], a.ctx_bound), k_begin + a.keys_per_split);
   }
+  const int nsteps = k_end > k_begin ? (k_end - k_begin + KS - 1) / KS : 0;
 
-  // queries as the B operand of S^T: lane supplies row rt*16 + c, dims ds*32 + g4*8 .. +8
-  const bf16_t* Q = (const bf16_t*)a.q + bg * a.Rpad * D;
-  bf16x8 qf[RT][4];
+  // staging: 16-byte chunks, 4 of K and 4 of V^T per thread per step
+  //   K chunk q: slot q/16, dims (q%16)*8..+8      V chunk q: dim q/8, slots (q%8)*8..+8
+  int kq_slot[4], kq_col[4], vq_row[4], vq_col[4];
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-    for (int ds = 0; ds < 4; ++ds) {
-      const int row = rt * 16 + c;
-      qf[rt][ds] = row < a.R ? load8(Q + (size_t)row * D + ds * 32 + g4 * 8) : zero8();
-    }
-
-  f32x4 o[8][RT];
-#pragma unroll
-  for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) o[dt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run[RT], l_run[RT];
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    m_run[rt] = -INFINITY;
-    l_run[rt] = 0.f;
+  for (int i = 0; i < 4; ++i) {
+    const int q = tid + 256 * i;
+    kq_slot[i] = q >> 4;
+    kq_col[i] = (q & 15) * 8;
+    vq_row[i] = q >> 3;
+    vq_col[i] = (q & 7) * 8;
   }
-  const float sc = kLog2e * rsqrtf((float)D);
-
-  // operand loads of one 32-key step starting at key k0
-  bf16x8 kf[2][4], vf[8];
-  auto load_step = [&](int k0) {
+  uint4 kr0[4], vr0[4], kr1[4], vr1[4];
+  auto issue = [&](int st, uint4* kr, uint4* vr) {
+    const int k0 = k_begin + min(st, nsteps - 1) * KS;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int key = k0 + 8 * (c >> 2) + 4 * t + (c & 3);
-#pragma unroll
-      for (int ds = 0; ds < 4; ++ds) kf[t][ds] = load8(K + (size_t)key * D + ds * 32 + g4 * 8);
+    for (int i = 0; i < 4; ++i) {
+      kr[i] = ldg16(K + (size_t)(k0 + kq_slot[i]) * D + kq_col[i]);
+      vr[i] = ldg16(Vt + (size_t)vq_row[i] * ldv + k0 + vq_col[i]);
     }
+  };
+  // branch-free: no divergent control flow between loads and their waits
+  auto keep = [](int nvalid, int w) -> unsigned {   // mask of the two bf16 in 32-bit word w
+    return (2 * w < nvalid ? 0x0000FFFFu : 0u) | (2 * w + 1 < nvalid ? 0xFFFF0000u : 0u);
+  };
+  auto stage = [&](int st, const uint4* kr, const uint4* vr, int buf) {
+    const int k0 = k_begin + st * KS;
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) vf[dt] = load8(Vt + (size_t)(dt * 16 + c) * ldv + k0 + g4 * 8);
+    for (int i = 0; i < 4; ++i) {
+      *(uint4*)&Ks[buf][kq_slot[i] * kKLd + kq_col[i]] = kr[i];
+      const int nvalid = k_end - (k0 + vq_col[i]);   // value slots j < nvalid are real
+      uint4 v = vr[i];
+      v.x &= keep(nvalid, 0);
+      v.y &= keep(nvalid, 1);
+      v.z &= keep(nvalid, 2);
+      v.w &= keep(nvalid, 3);
+      *(uint4*)&Vs[buf][vq_row[i] * kVLd + vq_col[i]] = v;
+    }
   };
 
-  if (k_begin < k_end) load_step(k_begin);
-  for (int k0 = k_begin; k0 < k_end; k0 += 32) {
-    bf16x8 kc[2][4], vc[8];
+  // this wave's queries as the B operand of S^T: row 16*wave + c, dims ds*32 + g4*8 .. +8
+  const int row = wave * 16 + c;
+  const bool active = wave * 16 < a.R;
+  bf16x8 qf[4];
+  const bf16_t* Q = (const bf16_t*)a.q + (bg * a.Rpad + min(row, a.Rpad - 1)) * D;
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+  for (int ds = 0; ds < 4; ++ds) {
+    qf[ds] = __builtin_bit_cast(bf16x8, ldg16(Q + ds * 32 + g4 * 8));
+    if (row >= a.R) qf[ds] = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
+  }
+  f32x4 o[8];
 #pragma unroll
-      for (int ds = 0; ds < 4; ++ds) kc[t][ds] = kf[t][ds];
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) vc[dt] = vf[dt];
-    if (k0 + 32 < k_end) load_step(k0 + 32);          // next step's loads in flight
+  for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+  const float sc = kLog2e * rsqrtf((float)D);
 
-    f32x4 s[2][RT];
+  auto compute = [&](int st, int buf) {
+    const int k0 = k_begin + st * KS;
+    const bf16_t* ks = Ks[buf];
+    const bf16_t* vs = Vs[buf];
+    f32x4 s[4];
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < 4; ++t) {
+      const int key = 32 * (t >> 1) + 8 * (c >> 2) + 4 * (t & 1) + (c & 3);
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ds = 0; ds < 4; ++ds)
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kc[t][ds], qf[rt][ds], acc, 0, 0, 0);
-        s[t][rt] = acc;
-      }
-
-    // this lane's scores are keys k0 + 8*g4 + 4*t + i of query row rt*16 + c
-    const int kbase = k0 + 8 * g4;
-    const int nvalid = k_end - kbase;                 // keys j < nvalid are real
-    if (nvalid < 8) {
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        bf16_t e[8];
-        *(uint4*)e = __builtin_bit_cast(uint4, vc[dt]);
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-          if (j >= nvalid) e[j] = 0;
-        vc[dt] = __builtin_bit_cast(bf16x8, *(uint4*)e);
-      }
+      for (int ds = 0; ds < 4; ++ds)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)&ks[key * kKLd + ds * 32 + g4 * 8], qf[ds],
+                                                      acc, 0, 0, 0);
+      s[t] = acc;
     }
-
-    bf16x8 pf[RT];
+    // lane's scores: tile t, reg i -> key k0 + 32*(t/2) + 8*g4 + 4*(t%2) + i of query row `row`
+    float v[16];
+    float mx = -INFINITY;
+    if (k0 + KS <= k_end) {                              // full step (uniform): no masking
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      float v[8];
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
+      for (int t = 0; t < 4; ++t)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int j = 4 * t + i;
-          v[j] = j < nvalid ? s[t][rt][i] * sc : -INFINITY;
+          v[4 * t + i] = s[t][i] * sc;
+          mx = fmaxf(mx, v[4 * t + i]);
         }
-      float mx = v[0];
+    } else {
 #pragma unroll
-      for (int j = 1; j < 8; ++j) mx = fmaxf(mx, v[j]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_new = fmaxf(m_run[rt], mx);
-      const bool none = m_new == -INFINITY;
-      const float alpha = none ? 1.f : exp2f(m_run[rt] - m_new);
-      bf16_t pb[8];
-      float rs = 0.f;
+      for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float p = none ? 0.f : exp2f(v[j] - m_new);
-        pb[j] = f2bf(p);
-        rs += bf2f(pb[j]);                            // normalise with the rounded weights
-      }
-      rs += __shfl_xor(rs, 16, 64);
-      rs += __shfl_xor(rs, 32, 64);
-      l_run[rt] = l_run[rt] * alpha + rs;
-      m_run[rt] = m_new;
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) o[dt][rt] *= alpha;
-      pf[rt] = __builtin_bit_cast(bf16x8, *(uint4*)pb);
+        for (int i = 0; i < 4; ++i) {
+          const int key = k0 + 32 * (t >> 1) + 8 * g4 + 4 * (t & 1) + i;
+          v[4 * t + i] = key < k_end ? s[t][i] * sc : -INFINITY;
+          mx = fmaxf(mx, v[4 * t + i]);
+        }
     }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    // Lazy rescaling: the reference m_run only moves when a row's maximum grows
+    // by more than 2^8 (weights stay <= 256, exact in the fp32/bf16 range), so
+    // the O rescale below is skipped by the whole wave on most steps.
+    const bool grow = mx > m_run + 8.f;
+    const float alpha = grow ? exp2f(m_run - mx) : 1.f;   // m_run = -inf -> 0
+    if (grow) m_run = mx;
+    float rs = 0.f;
+    bf16x8 pf[2];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const __bf16 p = (__bf16)(v[j] > -INFINITY ? exp2f(v[j] - m_run) : 0.f);
+      pf[j >> 3][j & 7] = p;
+      rs += (float)p;                                     // normalise with the rounded weights
+    }
+    rs += __shfl_xor(rs, 16, 64);
+    rs += __shfl_xor(rs, 32, 64);
+    l_run = l_run * alpha + rs;
+    if (__any(grow)) {
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) o[dt] *= alpha;
+    }
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {                     // keys 32*kh .. 32*kh+31
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            *(const bf16x8*)&vs[(dt * 16 + c) * kVLd + 32 * kh + g4 * 8], pf[kh], o[dt], 0, 0, 0);
+    }
+  };
 
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
-        o[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vc[dt], pf[rt], o[dt][rt], 0, 0, 0);
+  // Two steps per iteration, both always staged (a step past the end stages
+  // clamped, fully masked tiles) so loads and waits sit in straight-line code;
+  // only the math is skipped.
+  if (nsteps > 0) {
+    issue(0, kr0, vr0);
+    issue(1, kr1, vr1);
+    for (int it = 0; it < nsteps; it += 2) {
+      stage(it, kr0, vr0, 0);
+      __syncthreads();
+      issue(it + 2, kr0, vr0);
+      if (active) compute(it, 0);
+      stage(it + 1, kr1, vr1, 1);
+      __syncthreads();
+      issue(it + 3, kr1, vr1);
+      if (active && it + 1 < nsteps) compute(it + 1, 1);
+    }
   }
+  if (!active || row >= a.R) return;
 
-  // partial O^T tile (dt, rt): lane holds dims dt*16 + 4*g4 + i of row rt*16 + c
+  // partial O^T tile dt: lane holds dims dt*16 + 4*g4 + i of row `row`
   const size_t ubase = (bg * units + unit) * a.Rpad;
-  float* po = a.part_o + ubase * D;
+  float* po = a.part_o + (ubase + row) * D;
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    const int row = rt * 16 + c;
-    if (row >= a.R) continue;
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) *(f32x4*)(po + (size_t)row * D + dt * 16 + 4 * g4) = o[dt][rt];
-    if (g4 == 0) {
-      a.part_ml[(ubase + row) * 2 + 0] = m_run[rt];
-      a.part_ml[(ubase + row) * 2 + 1] = l_run[rt];
-    }
+  for (int dt = 0; dt < 8; ++dt) *(f32x4*)(po + dt * 16 + 4 * g4) = o[dt];
+  if (g4 == 0) {
+    a.part_ml[(ubase + row) * 2 + 0] = m_run;
+    a.part_ml[(ubase + row) * 2 + 1] = l_run;
   }
 }
 
@@ -314,8 +344,8 @@ AttnPlan attn_plan(int B, int nkv, int ctx_bound, int dtype) {
     return p;
   }
   const int pairs = B * nkv;
-  int splits = ceil_div(512, pairs);
-  const int max_splits = ceil_div(ctx_bound, 256);   // at least 256 keys per unit
+  int splits = ceil_div(256, pairs);                 // ~256 four-wave workgroups
+  const int max_splits = ceil_div(ctx_bound, 256);   // at least 256 keys (4 steps) per unit
   if (splits > max_splits) splits = max_splits;
   if (splits < 1) splits = 1;
   int kps = ceil_div(ceil_div(ctx_bound, splits), 64) * 64;
@@ -329,7 +359,7 @@ AttnPlan attn_plan(int B, int nkv, int ctx_bound, int dtype) {
 // count actually used never exceeds the target split count).
 int attn_max_units(int B, int nkv, int max_ctx, int dtype) {
   if (dtype != 1) return 1;
-  int splits = ceil_div(512, B * nkv);
+  int splits = ceil_div(256, B * nkv);
   const int max_splits = ceil_div(max_ctx, 256);
   if (splits > max_splits) splits = max_splits;
   if (splits < 1) splits = 1;
@@ -347,11 +377,7 @@ hipError_t launch_attention(const AttnArgs& a, int dtype, hipStream_t s) {
     return hipGetLastError();
   }
   dim3 grid(a.n_ctx_splits + 1, a.nkv, a.B);
-  const int rt = a.Rpad / 16;
-  if (rt == 1) hipLaunchKernelGGL(attn_bf16_d128<1>, grid, dim3(64), 0, s, a);
-  else if (rt == 2) hipLaunchKernelGGL(attn_bf16_d128<2>, grid, dim3(64), 0, s, a);
-  else if (rt == 3) hipLaunchKernelGGL(attn_bf16_d128<3>, grid, dim3(64), 0, s, a);
-  else hipLaunchKernelGGL(attn_bf16_d128<4>, grid, dim3(64), 0, s, a);
+  hipLaunchKernelGGL(attn_bf16_d128, grid, dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(attn_combine<bf16_t>, dim3(a.R, a.nkv, a.B), dim3(128), 0, s, a);

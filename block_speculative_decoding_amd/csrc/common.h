@@ -29,13 +29,9 @@ __device__ __forceinline__ bf16x8 ldg_bf16x8(const void* p) { return *(global_bf
 
 __device__ __forceinline__ float bf2f(bf16_t v) { return __uint_as_float(((uint32_t)v) << 16); }
 
-// round to nearest, ties to even; NaN stays NaN
-__device__ __forceinline__ bf16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (bf16_t)(u >> 16);
-}
+// round to nearest, ties to even (gfx950 converts in hardware: v_cvt_pk_bf16_f32);
+// NaN stays NaN
+__device__ __forceinline__ bf16_t f2bf(float f) { return __builtin_bit_cast(bf16_t, (__bf16)f); }
 
 template <typename T> struct Elem;
 template <> struct Elem<float> {

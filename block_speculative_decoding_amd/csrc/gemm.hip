@@ -224,7 +224,7 @@ void gemm_stream_bf16(GemmArgs a, int k_per_split, int mtiles, int ntiles) {
 #define DFS_PRODUCER_STEP(ST, XR)                                              \
   {                                                                            \
     const int kt = kb + ST;                                                    \
-    if (kt < nk) {                                                             \
+    {                                                                          \
       bf16_t* xs = Xs[ST & 1];                                                 \
       _Pragma("unroll") for (int i = 0; i < XCH; ++i) *(uint4*)&xs[x_dst[i]] = XR[i]; \
       __syncthreads();                                                         \
@@ -232,11 +232,15 @@ void gemm_stream_bf16(GemmArgs a, int k_per_split, int mtiles, int ntiles) {
     const int kk = min(kt + 2, nk - 1) * BK;                                   \
     _Pragma("unroll") for (int i = 0; i < XCH; ++i) XR[i] = ldg16(x_src[i] + kk);          \
   }
-    for (int kb = 0; kb < nk; kb += 4) {
+    for (int kb = 0; kb < nk; kb += 8) {
       DFS_PRODUCER_STEP(0, xr0)
       DFS_PRODUCER_STEP(1, xr1)
       DFS_PRODUCER_STEP(2, xr0)
       DFS_PRODUCER_STEP(3, xr1)
+      DFS_PRODUCER_STEP(4, xr0)
+      DFS_PRODUCER_STEP(5, xr1)
+      DFS_PRODUCER_STEP(6, xr0)
+      DFS_PRODUCER_STEP(7, xr1)
     }
 #undef DFS_PRODUCER_STEP
     return;
@@ -255,15 +259,15 @@ void gemm_stream_bf16(GemmArgs a, int k_per_split, int mtiles, int ntiles) {
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
         wr[st][j][ks] = ldg_bf16x8(w_src[j] + min(st, nk - 1) * BK + ks * 32);
-#define DFS_CONSUMER_STEP(ST)                                                                  \
+#define DFS_CONSUMER_STEP(ST, R)                                                               \
   {                                                                                            \
     const int kt = kb + ST;                                                                    \
+    __syncthreads();                                                                           \
     if (kt < nk) {                                                                             \
-      __syncthreads();                                                                         \
       const bf16_t* xs = Xs[ST & 1];                                                           \
       _Pragma("unroll") for (int ks = 0; ks < 2; ++ks) {                                       \
         bf16x8 bfg[NW];                                                                        \
-        _Pragma("unroll") for (int j = 0; j < NW; ++j) bfg[j] = wr[ST][j][ks];                \
+        _Pragma("unroll") for (int j = 0; j < NW; ++j) bfg[j] = wr[R][j][ks];                 \
         _Pragma("unroll") for (int i = 0; i < MT; ++i) {                                       \
           const bf16x8 af = *(const bf16x8*)&xs[(i * 16 + c) * LDK + ks * 32 + g4 * 8];          \
           _Pragma("unroll") for (int j = 0; j < NW; ++j)                                       \
@@ -271,15 +275,22 @@ void gemm_stream_bf16(GemmArgs a, int k_per_split, int mtiles, int ntiles) {
         }                                                                                      \
       }                                                                                        \
     }                                                                                          \
+    __builtin_amdgcn_sched_barrier(0); /* keep the refill after this step's math */            \
     const int kk = min(kt + 4, nk - 1) * BK;                                                   \
     _Pragma("unroll") for (int j = 0; j < NW; ++j)                                             \
-      _Pragma("unroll") for (int ks = 0; ks < 2; ++ks) wr[ST][j][ks] = ldg_bf16x8(w_src[j] + kk + ks * 32); \
+      _Pragma("unroll") for (int ks = 0; ks < 2; ++ks) wr[R][j][ks] = ldg_bf16x8(w_src[j] + kk + ks * 32); \
   }
-  for (int kb = 0; kb < nk; kb += 4) {
-    DFS_CONSUMER_STEP(0)
-    DFS_CONSUMER_STEP(1)
-    DFS_CONSUMER_STEP(2)
-    DFS_CONSUMER_STEP(3)
+  // 8 steps (two turns of the 4-deep ring) per loop iteration: the wait-count
+  // analysis is conservative across the loop back edge, so cross it less often
+  for (int kb = 0; kb < nk; kb += 8) {
+    DFS_CONSUMER_STEP(0, 0)
+    DFS_CONSUMER_STEP(1, 1)
+    DFS_CONSUMER_STEP(2, 2)
+    DFS_CONSUMER_STEP(3, 3)
+    DFS_CONSUMER_STEP(4, 0)
+    DFS_CONSUMER_STEP(5, 1)
+    DFS_CONSUMER_STEP(6, 2)
+    DFS_CONSUMER_STEP(7, 3)
   }
 #undef DFS_CONSUMER_STEP
 
