@@ -171,13 +171,17 @@ __global__ __launch_bounds__(256) void attn_bf16_d128(AttnArgs a) {
     const bool grow = mx > m_run + 8.f;
     const float alpha = grow ? exp2f(m_run - mx) : 1.f;   // m_run = -inf -> 0
     if (grow) m_run = mx;
+    // P enters the P.V product as two bf16 parts, hi = bf16(p) and lo = bf16(p - hi):
+    // a single bf16 P (8 significant bits) costs ~1 bf16 ulp on every output element
     float rs = 0.f;
-    bf16x8 pf[2];
+    bf16x8 pf[2], pl[2];
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      const __bf16 p = (__bf16)(v[j] > -INFINITY ? exp2f(v[j] - m_run) : 0.f);
-      pf[j >> 3][j & 7] = p;
-      rs += (float)p;                                     // normalise with the rounded weights
+      const float p = v[j] > -INFINITY ? exp2f(v[j] - m_run) : 0.f;
+      const __bf16 hi = (__bf16)p;
+      pf[j >> 3][j & 7] = hi;
+      pl[j >> 3][j & 7] = (__bf16)(p - (float)hi);
+      rs += p;
     }
     rs += __shfl_xor(rs, 16, 64);
     rs += __shfl_xor(rs, 32, 64);
@@ -189,9 +193,11 @@ __global__ __launch_bounds__(256) void attn_bf16_d128(AttnArgs a) {
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh) {                     // keys 32*kh .. 32*kh+31
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt)
-        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            *(const bf16x8*)&vs[(dt * 16 + c) * kVLd + 32 * kh + g4 * 8], pf[kh], o[dt], 0, 0, 0);
+      for (int dt = 0; dt < 8; ++dt) {
+        const bf16x8 vf = *(const bf16x8*)&vs[(dt * 16 + c) * kVLd + 32 * kh + g4 * 8];
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[kh], o[dt], 0, 0, 0);
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pl[kh], o[dt], 0, 0, 0);
+      }
     }
   };
 
