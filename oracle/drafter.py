@@ -32,6 +32,12 @@ the design notes of the repository):
 Storage boundaries (rounded exactly where the GPU path stores a tensor):
 features, K/V, attention inputs/outputs, MLP input and SwiGLU product in the
 weight dtype; residual stream and logits in fp32.
+
+Arithmetic is float64 throughout.  ``arith=np.float32`` evaluates the same
+steps with every operation in fp32 instead (storage roundings unchanged); the
+gap between the two evaluations measures how far any correct fp32 evaluation
+of this network can drift from the float64 one, and is used only as a
+yardstick of conditioning.
 """
 from __future__ import annotations
 
@@ -65,51 +71,51 @@ class DrafterShape:
         return cls(**{f: getattr(w, f) for f in cls.__dataclass_fields__})
 
 
-def rmsnorm(x, gain, eps):
-    """y = x / sqrt(mean(x^2) + eps) * gain along the last axis (float64)."""
-    x = np.asarray(x, dtype=np.float64)
+def rmsnorm(x, gain, eps, arith=np.float64):
+    """y = x / sqrt(mean(x^2) + eps) * gain along the last axis."""
+    x = np.asarray(x, dtype=arith)
     ms = np.mean(x * x, axis=-1, keepdims=True)
-    return x / np.sqrt(ms + eps) * np.asarray(gain, dtype=np.float64)
+    return x / np.sqrt(ms + arith(eps)) * np.asarray(gain, dtype=arith)
 
 
-def rope_rotate(x, positions, theta):
+def rope_rotate(x, positions, theta, arith=np.float64):
     """Rotate-half rotary embedding.
 
     x: [..., n_heads, d]; ``positions`` has shape x.shape[:-2] (one position
     per row, shared by its heads).  Pair (i, i + d/2) of every head is rotated
-    by the angle pos * theta**(-2i/d).
+    by the angle pos * theta**(-2i/d) (angles and their sines in float64).
     """
-    x = np.asarray(x, dtype=np.float64)
+    x = np.asarray(x, dtype=arith)
     if theta <= 0:
         return x.copy()
     d = x.shape[-1]
     half = d // 2
     inv_freq = theta ** (-np.arange(half, dtype=np.float64) * 2.0 / d)
     ang = np.asarray(positions, dtype=np.float64)[..., None] * inv_freq      # [..., half]
-    cos = np.cos(ang)[..., None, :]
-    sin = np.sin(ang)[..., None, :]
+    cos = np.cos(ang).astype(arith)[..., None, :]
+    sin = np.sin(ang).astype(arith)[..., None, :]
     x1, x2 = x[..., :half], x[..., half:]
     return np.concatenate([x1 * cos - x2 * sin, x2 * cos + x1 * sin], axis=-1)
 
 
-def block_attention(q, k_ctx, v_ctx, k_blk, v_blk):
+def block_attention(q, k_ctx, v_ctx, k_blk, v_blk, arith=np.float64):
     """Attention of the block rows, by definition.
 
     q [S, nq, d]; k_ctx, v_ctx [C_b, nkv, d]; k_blk, v_blk [S, nkv, d].
     Every context key precedes every block row, so "causal toward the context"
     lets each block row see all C_b context keys, and "full inside the block"
-    lets it see all S block keys.  Returns o [S, nq, d] in float64.
+    lets it see all S block keys.  Returns o [S, nq, d].
     """
-    q = np.asarray(q, np.float64)
-    keys = np.concatenate([np.asarray(k_ctx, np.float64), np.asarray(k_blk, np.float64)], 0)
-    vals = np.concatenate([np.asarray(v_ctx, np.float64), np.asarray(v_blk, np.float64)], 0)
+    q = np.asarray(q, arith)
+    keys = np.concatenate([np.asarray(k_ctx, arith), np.asarray(k_blk, arith)], 0)
+    vals = np.concatenate([np.asarray(v_ctx, arith), np.asarray(v_blk, arith)], 0)
     S, nq, d = q.shape
     nkv = keys.shape[1]
     group = nq // nkv
     o = np.empty_like(q)
     for h in range(nq):
         g = h // group
-        s = q[:, h, :] @ keys[:, g, :].T / np.sqrt(d)          # [S, C_b + S]
+        s = q[:, h, :] @ keys[:, g, :].T / arith(np.sqrt(d))   # [S, C_b + S]
         s = s - s.max(axis=1, keepdims=True)
         p = np.exp(s)
         p /= p.sum(axis=1, keepdims=True)
@@ -117,23 +123,23 @@ def block_attention(q, k_ctx, v_ctx, k_blk, v_blk):
     return o
 
 
-def _w(weights, name, dtype):
-    return as_f64(weights[name], dtype)
+def _w(weights, name, dtype, arith=np.float64):
+    return as_f64(weights[name], dtype).astype(arith, copy=False)
 
 
-def context_features(shape: DrafterShape, weights, hidden_rows):
+def context_features(shape: DrafterShape, weights, hidden_rows, arith=np.float64):
     """f = RMSNorm(concat_t(h_t) . W_fc^T; g_fc), rounded to the weight dtype.
 
     hidden_rows [n, nT*H] already concatenated in ascending target-layer order.
     """
     dt = shape.dtype
-    h = as_f64(hidden_rows, dt)
-    y = h @ _w(weights, "fc", dt).T
-    return round_to(rmsnorm(y, _w(weights, "fc_norm", dt), shape.rms_eps), dt)
+    h = as_f64(hidden_rows, dt).astype(arith, copy=False)
+    y = h @ _w(weights, "fc", dt, arith).T
+    return round_to(rmsnorm(y, _w(weights, "fc_norm", dt, arith), shape.rms_eps, arith), dt).astype(arith)
 
 
 def draft_step(shape: DrafterShape, weights, hidden_new, n_new, k_cache, v_cache,
-               ctx_len, last_token, batch_rows=None):
+               ctx_len, last_token, batch_rows=None, arith=np.float64):
     """One drafter call: append the newly committed context rows, then draft a block.
 
     Arguments mirror the library entry point, in logical layouts:
@@ -142,7 +148,8 @@ def draft_step(shape: DrafterShape, weights, hidden_new, n_new, k_cache, v_cache
       in place at slots ctx_len[b] .. ctx_len[b]+n_new[b]-1), ctx_len [B]
       (not modified; the new lengths are returned), last_token [B].
     ``batch_rows`` restricts the work to some batch rows (others are skipped
-    and their logits left as NaN).
+    and their logits left as NaN).  ``arith``: float64, or float32 for the
+    conditioning yardstick described in the module notes.
     Returns (base_logits [B, S-1, V] float32, new_ctx_len [B]).
     """
     sh = shape
@@ -151,6 +158,14 @@ def draft_step(shape: DrafterShape, weights, hidden_new, n_new, k_cache, v_cache
     S = sh.block
     nq, nkv, d, H = sh.n_q_heads, sh.n_kv_heads, sh.head_dim, sh.hidden
     rows = range(B) if batch_rows is None else list(batch_rows)
+    F = arith
+
+    def rnd(v):                     # storage rounding, back in the arithmetic type
+        return round_to(v, dt).astype(F)
+
+    def wt(name):
+        return _w(weights, name, dt, F)
+
     new_len = np.asarray(ctx_len, np.int64) + np.asarray(n_new, np.int64)
     if np.any(new_len > sh.max_ctx):
         raise ValueError("context overflow")
@@ -167,13 +182,13 @@ def draft_step(shape: DrafterShape, weights, hidden_new, n_new, k_cache, v_cache
     for b in rows:
         nb = int(n_new[b])
         if nb > 0:
-            feats[b] = context_features(sh, weights, hidden_new[b, :nb])
+            feats[b] = context_features(sh, weights, hidden_new[b, :nb], F)
     for l in range(sh.n_layers):
-        wk = _w(weights, f"layers.{l}.wk", dt)
-        wv = _w(weights, f"layers.{l}.wv", dt)
+        wk = wt(f"layers.{l}.wk")
+        wv = wt(f"layers.{l}.wv")
         for b, f in feats.items():
             pos = int(ctx_len[b]) + np.arange(f.shape[0])
-            k = rope_rotate((f @ wk.T).reshape(-1, nkv, d), pos, sh.rope_theta)
+            k = rope_rotate((f @ wk.T).reshape(-1, nkv, d), pos, sh.rope_theta, F)
             v = (f @ wv.T).reshape(-1, nkv, d)
             store(k_cache, l, b, pos, round_to(k, dt))
             store(v_cache, l, b, pos, round_to(v, dt))
@@ -182,38 +197,36 @@ def draft_step(shape: DrafterShape, weights, hidden_new, n_new, k_cache, v_cache
     rows = list(rows)
     tok = np.full((len(rows), S), sh.mask_token_id, np.int64)
     tok[:, 0] = np.clip(np.asarray(last_token)[rows], 0, sh.vocab - 1)
-    emb = _w(weights, "embed", dt)
-    x = round_f32(emb[tok])                                   # [R, S, H] residual stream
+    emb = wt("embed")
+    x = round_f32(emb[tok]).astype(F)                         # [R, S, H] residual stream
     pos = new_len[rows][:, None] + np.arange(S)[None, :]      # [R, S]
 
     for l in range(sh.n_layers):
         p = f"layers.{l}."
-        a = round_to(rmsnorm(x, _w(weights, p + "attn_norm", dt), sh.rms_eps), dt)
-        q = round_to(rope_rotate((a @ _w(weights, p + "wq", dt).T).reshape(-1, S, nq, d), pos,
-                                 sh.rope_theta), dt)
-        k = round_to(rope_rotate((a @ _w(weights, p + "wk", dt).T).reshape(-1, S, nkv, d), pos,
-                                 sh.rope_theta), dt)
-        v = round_to((a @ _w(weights, p + "wv", dt).T).reshape(-1, S, nkv, d), dt)
+        a = rnd(rmsnorm(x, wt(p + "attn_norm"), sh.rms_eps, F))
+        q = rnd(rope_rotate((a @ wt(p + "wq").T).reshape(-1, S, nq, d), pos, sh.rope_theta, F))
+        k = rnd(rope_rotate((a @ wt(p + "wk").T).reshape(-1, S, nkv, d), pos, sh.rope_theta, F))
+        v = rnd((a @ wt(p + "wv").T).reshape(-1, S, nkv, d))
         o = np.empty_like(q)
         for i, b in enumerate(rows):
             cb = int(new_len[b])
             kc = as_f64(k_cache[l, b, :cb], dt)
             vc = as_f64(v_cache[l, b, :cb], dt)
-            o[i] = block_attention(q[i], kc, vc, k[i], v[i])
-        o = round_to(o, dt).reshape(-1, S, nq * d)
-        x = round_f32(x + o @ _w(weights, p + "wo", dt).T)
-        m = round_to(rmsnorm(x, _w(weights, p + "mlp_norm", dt), sh.rms_eps), dt)
-        g = m @ _w(weights, p + "w_gate", dt).T
-        u = m @ _w(weights, p + "w_up", dt).T
+            o[i] = block_attention(q[i], kc, vc, k[i], v[i], F)
+        o = rnd(o).reshape(-1, S, nq * d)
+        x = round_f32(x + o @ wt(p + "wo").T).astype(F)
+        m = rnd(rmsnorm(x, wt(p + "mlp_norm"), sh.rms_eps, F))
+        g = m @ wt(p + "w_gate").T
+        u = m @ wt(p + "w_up").T
         with np.errstate(over="ignore"):
-            hmid = round_to(g / (1.0 + np.exp(-g)) * u, dt)       # silu(g) * u
-        x = round_f32(x + hmid @ _w(weights, p + "w_down", dt).T)
+            hmid = rnd(g / (F(1) + np.exp(-g)) * u)                # silu(g) * u
+        x = round_f32(x + hmid @ wt(p + "w_down").T).astype(F)
 
-    z = round_to(rmsnorm(x[:, 1:, :], _w(weights, "final_norm", dt), sh.rms_eps), dt)
+    z = rnd(rmsnorm(x[:, 1:, :], wt("final_norm"), sh.rms_eps, F))
     out = np.full((B, S - 1, sh.vocab), np.nan, np.float32)
     lm = weights["lm_head"]
     chunk = 16384
     for v0 in range(0, sh.vocab, chunk):
-        wl = as_f64(lm[v0:v0 + chunk], dt)
+        wl = as_f64(lm[v0:v0 + chunk], dt).astype(F, copy=False)
         out[rows, :, v0:v0 + chunk] = (z @ wl.T).astype(np.float32)
     return out, new_len.astype(np.int32)

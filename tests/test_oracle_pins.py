@@ -261,10 +261,11 @@ def _bruteforce_one_layer_drafter(w, weights, hidden_all, last_token):
     return (z @ W["lm_head"].T).astype(np.float32)
 
 
-@pytest.mark.parametrize("split", [None, 9])
-def test_drafter_matches_sequence_level_bruteforce(split):
-    # one layer, MLP output off, fp32; the context is appended in one call
-    # (prefill) or in two calls; positions come out of the cache bookkeeping
+@pytest.mark.parametrize("split,arith", [(None, np.float64), (9, np.float64), (None, np.float32)])
+def test_drafter_matches_sequence_level_bruteforce(split, arith):
+    # one layer, MLP output off, fp32 storage; the context is appended in one
+    # call (prefill) or in two calls; positions come out of the cache
+    # bookkeeping.  The fp32-arithmetic evaluation computes the same function.
     w = _tiny(batch=1, ctx=21, dtype="f32", rope_theta=100.0)
     weights = inputs.drafter_weights(w, 2, gain_std=0.1)
     weights["layers.0.w_down"] = np.zeros_like(weights["layers.0.w_down"])
@@ -277,10 +278,10 @@ def test_drafter_matches_sequence_level_bruteforce(split):
     ctx = np.zeros(1, np.int32)
     for lo, hi in ([(0, C)] if split is None else [(0, split), (split, C)]):
         logits, ctx = od.draft_step(sh, weights, hid[:, lo:hi], np.array([hi - lo]), kc, vc,
-                                    ctx, last)
+                                    ctx, last, arith=arith)
     assert ctx[0] == C
     want = _bruteforce_one_layer_drafter(w, weights, hid[0].astype(np.float64), 5)
-    np.testing.assert_allclose(logits[0], want, atol=2e-6, rtol=0)
+    np.testing.assert_allclose(logits[0], want, atol=2e-6 if arith is np.float64 else 1e-4, rtol=0)
 
 
 def test_drafter_batch_rows_independent_and_garbage_slots_ignored():
