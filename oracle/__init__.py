@@ -10,7 +10,9 @@ arithmetic).
 Everything is plain NumPy in float64.  Values are rounded to the declared
 storage precision (bf16 or fp32) at the same tensor boundaries as the storage
 the GPU path uses, so that both sides compute the same function; inside one
-boundary the oracle keeps full float64.
+boundary the oracle keeps full float64.  (``draft_step`` can also evaluate the
+same steps in fp32 arithmetic; tests use that only to measure how far any
+fp32 evaluation drifts from the float64 one.)
 
 Citation key (the pages, by title; sections are named as they appear):
 
