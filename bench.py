@@ -66,7 +66,9 @@ class Step:
 
         self.np_weights = inputs.drafter_weights(w, seed)
         self.cfg = D.DrafterConfig.of(w)
-        self.wdev = D.DrafterWeights(self.cfg, {k: up(v, w.dtype) for k, v in self.np_weights.items()})
+        # bf16 matrices in the tile-packed layout the matrix-core kernels stream (packed once here)
+        self.wdev = D.DrafterWeights(self.cfg, {k: up(v, w.dtype) for k, v in self.np_weights.items()},
+                                     packed=w.dtype == "bf16")
         step = inputs.step_inputs(w, seed)
         self.np_step = step
         kc, vc = inputs.cache_prefix(w, seed, step["ctx_len"])
@@ -88,8 +90,12 @@ class Step:
         if w.markov_rank > 0:
             U, Wt = inputs.markov_factors(w, seed)
             self.U, self.Wt = up(U, w.dtype), up(Wt, w.dtype)
+            self.wt_packed = w.dtype == "bf16"
+            if self.wt_packed:
+                self.Wt = D.pack_matrix(self.Wt.view(w.vocab, w.markov_rank))
         else:
             self.U = self.Wt = None
+            self.wt_packed = False
         self.ws_d = torch.empty(D.dflash_draft_workspace_size(self.cfg, B, step["n_new_max"]),
                                 dtype=torch.uint8, device=dev)
         self.ws_m = torch.empty(D.markov_bias_sample_workspace_size(B, G, V), dtype=torch.uint8, device=dev)
@@ -111,7 +117,7 @@ class Step:
 
     def sample(self):
         self.D.markov_bias_sample(self.logits, self.U, self.Wt, self.last, self.ud, self.w.temperature,
-                                  self.tokens, self.row_stats, self.ws_m)
+                                  self.tokens, self.row_stats, self.ws_m, wt_packed=self.wt_packed)
 
     def verify(self):
         self.D.spec_verify(self.logits, self.target, self.tokens, self.ua, self.uf, self.w.temperature,

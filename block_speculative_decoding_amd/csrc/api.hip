@@ -120,9 +120,10 @@ DraftWs carve_draft(void* base, const DraftDims& d, int dtype) {
 }
 
 hipError_t run_gemm(const void* X, int ldx, int M, int N, int K, const void* w0, const void* w1, int n1,
-                    const void* w2, int n2, float* Y, int dtype, hipStream_t s, int* splits_out,
+                    const void* w2, int n2, float* Y, int dtype, int packed, hipStream_t s, int* splits_out,
                     size_t* stride_out, int force_splits = 0, long ldy = 0) {
   GemmArgs a;
+  a.packed = packed;
   a.X = X;
   a.ldx = ldx;
   a.x_rows = M;
@@ -198,6 +199,9 @@ int dflash_draft_step(const dfs_drafter_cfg* cfg, const dfs_drafter_weights* wt,
       return DFS_EINVAL;
   const DraftDims d = dims_of(cfg, batch, n_new_max);
   const int dt = cfg->dtype;
+  const int pk = wt->packed;
+  if (pk != 0 && pk != 1) return DFS_EINVAL;
+  if (pk && dt != DFS_BF16) return DFS_EUNSUPPORTED;
   const DraftWs w = carve_draft(workspace, d, dt);
   if (workspace_bytes < w.bytes) return DFS_EWORKSPACE;
   hipStream_t s = (hipStream_t)stream;
@@ -222,7 +226,7 @@ int dflash_draft_step(const dfs_drafter_cfg* cfg, const dfs_drafter_weights* wt,
   size_t pst;
   // 1. context features f = RMSNorm(concat(h) . fc^T) -> xs rows [0, Mc)
   if (d.Mc > 0) {
-    DFS_TRY(run_gemm(hidden_new, d.nT * d.H, d.Mc, d.H, d.nT * d.H, wt->fc, nullptr, 0, nullptr, 0, w.part, dt, s,
+    DFS_TRY(run_gemm(hidden_new, d.nT * d.H, d.Mc, d.H, d.nT * d.H, wt->fc, nullptr, 0, nullptr, 0, w.part, dt, pk, s,
                      &sp, &pst));
     NormArgs na;
     na.part = w.part;
@@ -251,7 +255,7 @@ int dflash_draft_step(const dfs_drafter_cfg* cfg, const dfs_drafter_weights* wt,
   for (int l = 0; l < d.L; ++l) {
     // 2. Q|K|V of [features ; block rows] in one pass over wq|wk|wv
     DFS_TRY(run_gemm(w.xs, d.H, d.Mx, d.Nqkv, d.H, wt->wq[l], wt->wk[l], d.nq * d.d, wt->wv[l],
-                     (d.nq + d.nkv) * d.d, w.part, dt, s, &sp, &pst));
+                     (d.nq + d.nkv) * d.d, w.part, dt, pk, s, &sp, &pst));
     QkvArgs qa;
     qa.part = w.part;
     qa.sp = sp;
@@ -298,7 +302,7 @@ int dflash_draft_step(const dfs_drafter_cfg* cfg, const dfs_drafter_weights* wt,
     DFS_TRY(launch_attention(aa, dt, s));
     // 4. O projection, residual add, MLP pre-norm
     DFS_TRY(run_gemm(w.attn_o, d.nq * d.d, d.Mb, d.H, d.nq * d.d, wt->wo[l], nullptr, 0, nullptr, 0, w.part, dt,
-                     s, &sp, &pst));
+                     pk, s, &sp, &pst));
     {
       NormArgs na;
       na.resid = w.resid;
@@ -315,10 +319,10 @@ int dflash_draft_step(const dfs_drafter_cfg* cfg, const dfs_drafter_weights* wt,
     }
     // 5. SwiGLU MLP: [gate | up] in one pass, then down, residual add, next pre-norm
     DFS_TRY(run_gemm(w.mlp_in, d.H, d.Mb, 2 * d.F, d.H, wt->w_gate[l], wt->w_up[l], d.F, nullptr, 0, w.part, dt,
-                     s, &sp, &pst));
+                     pk, s, &sp, &pst));
     DFS_TRY(launch_swiglu(w.part, sp, pst, d.Mb, d.F, w.hmid, dt, s));
-    DFS_TRY(run_gemm(w.hmid, d.F, d.Mb, d.H, d.F, wt->w_down[l], nullptr, 0, nullptr, 0, w.part, dt, s, &sp,
-                     &pst));
+    DFS_TRY(run_gemm(w.hmid, d.F, d.Mb, d.H, d.F, wt->w_down[l], nullptr, 0, nullptr, 0, w.part, dt, pk, s,
+                     &sp, &pst));
     {
       NormArgs na;
       na.resid = w.resid;
@@ -342,8 +346,8 @@ int dflash_draft_step(const dfs_drafter_cfg* cfg, const dfs_drafter_weights* wt,
     }
   }
   // 6. LM head on the mask rows -> base logits [B, S-1, V]
-  DFS_TRY(run_gemm(w.z, d.H, d.B * d.G, d.V, d.H, wt->lm_head, nullptr, 0, nullptr, 0, base_logits, dt, s, &sp,
-                   &pst, 1));
+  DFS_TRY(run_gemm(w.z, d.H, d.B * d.G, d.V, d.H, wt->lm_head, nullptr, 0, nullptr, 0, base_logits, dt, pk, s,
+                   &sp, &pst, 1));
   DFS_TRY(launch_finish(w.meta, ctx_len, d.B, s));
   return DFS_OK;
 }
@@ -365,8 +369,10 @@ int markov_bias_sample(int32_t batch, int32_t n_draft, int32_t vocab, int32_t ra
     return DFS_EINVAL;
   if (!(temperature >= 0.f)) return DFS_EINVAL;
   if (rank > 0 && (!U || !Wt)) return DFS_EINVAL;
-  if (rank > 0 && uw_dtype != DFS_F32 && uw_dtype != DFS_BF16) return DFS_EINVAL;
-  if (rank > 0 && uw_dtype == DFS_BF16 && rank % 64 != 0) return DFS_EUNSUPPORTED;
+  if (rank > 0 && uw_dtype != DFS_F32 && uw_dtype != DFS_BF16 && uw_dtype != DFS_BF16_PACKED) return DFS_EINVAL;
+  if (rank > 0 && uw_dtype != DFS_F32 && rank % 64 != 0) return DFS_EUNSUPPORTED;
+  const int uw_packed = uw_dtype == DFS_BF16_PACKED;
+  if (uw_packed) uw_dtype = DFS_BF16;
   if (workspace_bytes < markov_bias_sample_workspace_size(batch, n_draft, vocab)) return DFS_EWORKSPACE;
   hipStream_t s = (hipStream_t)stream;
   Carver cv(workspace);
@@ -411,6 +417,7 @@ int markov_bias_sample(int32_t batch, int32_t n_draft, int32_t vocab, int32_t ra
     ga.ldy = rowV;
     ga.y_split_stride = 0;
     ga.accumulate = 1;
+    ga.packed = uw_packed;
     DFS_TRY(launch_gemm(ga, plan, uw_dtype, s));
     DFS_TRY(launch_chunk_stats(logits + (size_t)i * vocab, rowV, batch, vocab, temperature, stats, s));
     PickArgs pa;
@@ -561,18 +568,32 @@ size_t dfs_gemm_workspace_size(int32_t M, int32_t N, int32_t K, int32_t dtype, i
 }
 
 int dfs_gemm(int32_t M, int32_t N, int32_t K, int32_t dtype, const void* X, const void* W, float* Y,
-             int32_t splits, void* workspace, size_t workspace_bytes, void* stream) {
-  if (M < 1 || N < 1 || K < 1 || !X || !W || !Y || splits < 0 || (dtype != DFS_F32 && dtype != DFS_BF16))
+             int32_t splits, int32_t w_packed, void* workspace, size_t workspace_bytes, void* stream) {
+  if (M < 1 || N < 1 || K < 1 || !X || !W || !Y || splits < 0 || (dtype != DFS_F32 && dtype != DFS_BF16) ||
+      (w_packed != 0 && w_packed != 1))
     return DFS_EINVAL;
   if (dtype == DFS_BF16 && K % 64) return DFS_EUNSUPPORTED;
+  if (w_packed && dtype != DFS_BF16) return DFS_EUNSUPPORTED;
   if (workspace_bytes < dfs_gemm_workspace_size(M, N, K, dtype, splits) || !workspace) return DFS_EWORKSPACE;
   hipStream_t s = (hipStream_t)stream;
   const GemmPlan p = gemm_plan(M, N, K, dtype, splits);
   float* target = p.splits > 1 ? (float*)workspace : Y;
   int sp;
   size_t pst;
-  DFS_TRY(run_gemm(X, K, M, N, K, W, nullptr, 0, nullptr, 0, target, dtype, s, &sp, &pst, splits));
+  DFS_TRY(run_gemm(X, K, M, N, K, W, nullptr, 0, nullptr, 0, target, dtype, w_packed, s, &sp, &pst, splits));
   if (sp > 1) DFS_TRY(launch_reduce(target, sp, pst, (size_t)M * N, Y, s));
+  return DFS_OK;
+}
+
+size_t dfs_packed_matrix_bytes(int32_t rows, int32_t cols) {
+  if (rows < 1 || cols < 64 || cols % 64) return 0;
+  return packed_matrix_elems(rows, cols) * sizeof(bf16_t);
+}
+
+int dfs_pack_matrix(int32_t rows, int32_t cols, const void* src, void* dst, void* stream) {
+  if (rows < 1 || cols < 1 || !src || !dst || src == dst) return DFS_EINVAL;
+  if (cols % 64) return DFS_EUNSUPPORTED;
+  DFS_TRY(launch_pack(src, dst, rows, cols, (hipStream_t)stream));
   return DFS_OK;
 }
 

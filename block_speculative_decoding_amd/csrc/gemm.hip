@@ -33,14 +33,24 @@ __device__ __forceinline__ const void* seg_row(const GemmArgs& a, int n, int es)
   return (const char*)a.seg[s].w + (size_t)(n - a.seg[s].n0) * a.K * es;
 }
 
+// first element of the packed 16-row tile group that holds logical W row n
+constexpr int kTileElems = 16 * BK;   // one 16 x 64 tile (2 KB)
+__device__ __forceinline__ const bf16_t* seg_tile(const GemmArgs& a, int n) {
+  int s = 0;
+  if (a.nseg > 1 && n >= a.seg[1].n0) s = 1;
+  if (a.nseg > 2 && n >= a.seg[2].n0) s = 2;
+  return (const bf16_t*)a.seg[s].w + (size_t)((n - a.seg[s].n0) >> 4) * (a.K / BK) * kTileElems;
+}
+
 __device__ __forceinline__ int x_row(const GemmArgs& a, int m) {
   if (!a.row_idx) return m;
   int r = a.row_idx[(size_t)m * a.row_idx_stride];
   return r < 0 ? 0 : (r >= a.x_rows ? a.x_rows - 1 : r);
 }
 
-template <int BM, int BN>
+template <int BM, int BN, bool PACKED>
 __global__ __launch_bounds__(256) void gemm_bf16_nt(GemmArgs a, int k_per_split) {
+  constexpr int WSTEP = PACKED ? kTileElems : BK;     // W elements per k step
   constexpr int TM = BM / 32, TN = BN / 32;            // 16x16 tiles per wave (2x2 waves)
   constexpr int A_CH = BM * BK / 8 / 256;               // 16-byte chunks per thread
   constexpr int B_CH = BN * BK / 8 / 256;
@@ -69,10 +79,20 @@ __global__ __launch_bounds__(256) void gemm_bf16_nt(GemmArgs a, int k_per_split)
   int b_dst[B_CH];
 #pragma unroll
   for (int i = 0; i < B_CH; ++i) {
-    const int c = tid + i * 256, row = c >> 3, col = (c & 7) * 8, n = n0 + row;
-    b_ok[i] = n < a.N;
-    b_src[i] = (const bf16_t*)seg_row(a, b_ok[i] ? n : 0, 2) + kbeg + col;
-    b_dst[i] = row * LDK + col;
+    const int c = tid + i * 256;
+    if constexpr (PACKED) {
+      // chunk c of the step: tile c / 128, operand slot (ks, lane) = c % 128
+      const int t = c >> 7, q = c & 127, l = q & 63;
+      const int row = t * 16 + (l & 15), n = n0 + row;
+      b_ok[i] = n < a.N;
+      b_src[i] = seg_tile(a, b_ok[i] ? n : 0) + (size_t)(kbeg / BK) * kTileElems + q * 8;
+      b_dst[i] = row * LDK + (q >> 6) * 32 + (l >> 4) * 8;
+    } else {
+      const int row = c >> 3, col = (c & 7) * 8, n = n0 + row;
+      b_ok[i] = n < a.N;
+      b_src[i] = (const bf16_t*)seg_row(a, b_ok[i] ? n : 0, 2) + kbeg + col;
+      b_dst[i] = row * LDK + col;
+    }
   }
 
   uint4 ra[A_CH], rb[B_CH];
@@ -82,7 +102,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_nt(GemmArgs a, int k_per_split)
       ra[i] = a_ok[i] ? ldg16(a_src[i] + kt * BK) : make_uint4(0, 0, 0, 0);
 #pragma unroll
     for (int i = 0; i < B_CH; ++i)
-      rb[i] = b_ok[i] ? ldg16(b_src[i] + kt * BK) : make_uint4(0, 0, 0, 0);
+      rb[i] = b_ok[i] ? ldg16(b_src[i] + (size_t)kt * WSTEP) : make_uint4(0, 0, 0, 0);
   };
   auto sstore = [&](int buf) {
 #pragma unroll
@@ -171,9 +191,13 @@ __device__ __forceinline__ int xcd_logical_id(int id, int total) {
   return (id & 7) * (full >> 3) + (id >> 3);
 }
 
-template <int MT, int NW>
+template <int MT, int NW, int PD, int XD, bool PACKED>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_stream_bf16(GemmArgs a, int k_per_split, int mtiles, int ntiles) {
+  // W elements per k step and between the two 32-wide k halves of a step
+  constexpr int WSTEP = PACKED ? kTileElems : BK, WKS = PACKED ? kTileElems / 2 : 32;
+  static_assert(PD == 4 || PD == 6 || PD == 8, "ring depth");
+  static_assert(XD == 2 || XD == PD, "X ring depth");
   constexpr int BM = 16 * MT, BN = 64 * NW;
   constexpr int XCH = BM * BK / 8 / 256;                // 16-byte X chunks per producer lane per step
   static_assert(XCH >= 1, "tile too small");
@@ -207,40 +231,48 @@ void gemm_stream_bf16(GemmArgs a, int k_per_split, int mtiles, int ntiles) {
 #pragma unroll
     for (int j = 0; j < NW; ++j) {
       const int n = min(n0 + wave * 16 * NW + j * 16 + c, a.N - 1);
-      w_src[j] = (const bf16_t*)seg_row(a, n, 2) + kbeg + g4 * 8;
+      if constexpr (PACKED)   // the wave's 16 rows: one contiguous run of tiles
+        w_src[j] = seg_tile(a, n) + (size_t)(kbeg / BK) * kTileElems + lane * 8;
+      else
+        w_src[j] = (const bf16_t*)seg_row(a, n, 2) + kbeg + g4 * 8;
     }
   }
 
   // The two roles run separate loops with the same barrier sequence (one per k
   // step).  Steps are expanded by macro so every ring index is a constant.
   if (producer) {
-    // X comes from L2: a 2-deep ring (two named stages) is enough.
-    uint4 xr0[XCH], xr1[XCH];
+    // X comes from L2, but behind the consumers' HBM misses in the same memory
+    // pipeline, so it is prefetched XD steps ahead (XD = 2 or the W depth).
+    uint4 xr[XD][XCH];
 #pragma unroll
-    for (int i = 0; i < XCH; ++i) {
-      xr0[i] = ldg16(x_src[i]);
-      xr1[i] = ldg16(x_src[i] + min(1, nk - 1) * BK);
+    for (int st = 0; st < XD; ++st) {
+#pragma unroll
+      for (int i = 0; i < XCH; ++i) xr[st][i] = ldg16(x_src[i] + min(st, nk - 1) * BK);
+      __builtin_amdgcn_sched_barrier(0);   // oldest-first, as in the consumers
     }
-#define DFS_PRODUCER_STEP(ST, XR)                                              \
+#define DFS_PRODUCER_STEP(ST)                                                  \
   {                                                                            \
     const int kt = kb + ST;                                                    \
     {                                                                          \
       bf16_t* xs = Xs[ST & 1];                                                 \
-      _Pragma("unroll") for (int i = 0; i < XCH; ++i) *(uint4*)&xs[x_dst[i]] = XR[i]; \
+      _Pragma("unroll") for (int i = 0; i < XCH; ++i) *(uint4*)&xs[x_dst[i]] = xr[ST % XD][i]; \
       __syncthreads();                                                         \
     }                                                                          \
-    const int kk = min(kt + 2, nk - 1) * BK;                                   \
-    _Pragma("unroll") for (int i = 0; i < XCH; ++i) XR[i] = ldg16(x_src[i] + kk);          \
+    const int kk = min(kt + XD, nk - 1) * BK;                                  \
+    _Pragma("unroll") for (int i = 0; i < XCH; ++i) xr[ST % XD][i] = ldg16(x_src[i] + kk);    \
   }
-    for (int kb = 0; kb < nk; kb += 8) {
-      DFS_PRODUCER_STEP(0, xr0)
-      DFS_PRODUCER_STEP(1, xr1)
-      DFS_PRODUCER_STEP(2, xr0)
-      DFS_PRODUCER_STEP(3, xr1)
-      DFS_PRODUCER_STEP(4, xr0)
-      DFS_PRODUCER_STEP(5, xr1)
-      DFS_PRODUCER_STEP(6, xr0)
-      DFS_PRODUCER_STEP(7, xr1)
+    // as many steps per iteration as the consumers run (same barrier sequence)
+    for (int kb = 0; kb < nk; kb += (PD == 6 ? 6 : 8)) {
+      DFS_PRODUCER_STEP(0)
+      DFS_PRODUCER_STEP(1)
+      DFS_PRODUCER_STEP(2)
+      DFS_PRODUCER_STEP(3)
+      DFS_PRODUCER_STEP(4)
+      DFS_PRODUCER_STEP(5)
+      if constexpr (PD != 6) {
+        DFS_PRODUCER_STEP(6)
+        DFS_PRODUCER_STEP(7)
+      }
     }
 #undef DFS_PRODUCER_STEP
     return;
@@ -251,14 +283,18 @@ void gemm_stream_bf16(GemmArgs a, int k_per_split, int mtiles, int ntiles) {
   for (int i = 0; i < MT; ++i)
 #pragma unroll
     for (int j = 0; j < NW; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  bf16x8 wr[4][NW][2];
+  bf16x8 wr[PD][NW][2];
 #pragma unroll
-  for (int st = 0; st < 4; ++st)
+  for (int st = 0; st < PD; ++st) {
 #pragma unroll
     for (int j = 0; j < NW; ++j)
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
-        wr[st][j][ks] = ldg_bf16x8(w_src[j] + min(st, nk - 1) * BK + ks * 32);
+        wr[st][j][ks] = ldg_bf16x8(w_src[j] + (size_t)min(st, nk - 1) * WSTEP + ks * WKS);
+    // keep the ring filled oldest-first: the loop's wait counts assume step 0
+    // holds the oldest loads, also on entry
+    __builtin_amdgcn_sched_barrier(0);
+  }
 #define DFS_CONSUMER_STEP(ST, R)                                                               \
   {                                                                                            \
     const int kt = kb + ST;                                                                    \
@@ -271,44 +307,58 @@ void gemm_stream_bf16(GemmArgs a, int k_per_split, int mtiles, int ntiles) {
         _Pragma("unroll") for (int i = 0; i < MT; ++i) {                                       \
           const bf16x8 af = *(const bf16x8*)&xs[(i * 16 + c) * LDK + ks * 32 + g4 * 8];          \
           _Pragma("unroll") for (int j = 0; j < NW; ++j)                                       \
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bfg[j], acc[i][j], 0, 0, 0);   \
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfg[j], af, acc[i][j], 0, 0, 0);   \
         }                                                                                      \
       }                                                                                        \
     }                                                                                          \
     __builtin_amdgcn_sched_barrier(0); /* keep the refill after this step's math */            \
-    const int kk = min(kt + 4, nk - 1) * BK;                                                   \
+    const size_t kk = (size_t)min(kt + PD, nk - 1) * WSTEP;                                    \
     _Pragma("unroll") for (int j = 0; j < NW; ++j)                                             \
-      _Pragma("unroll") for (int ks = 0; ks < 2; ++ks) wr[R][j][ks] = ldg_bf16x8(w_src[j] + kk + ks * 32); \
+      _Pragma("unroll") for (int ks = 0; ks < 2; ++ks) wr[R][j][ks] = ldg_bf16x8(w_src[j] + kk + ks * WKS); \
   }
-  // 8 steps (two turns of the 4-deep ring) per loop iteration: the wait-count
-  // analysis is conservative across the loop back edge, so cross it less often
-  for (int kb = 0; kb < nk; kb += 8) {
+  // 8 steps (two turns of a 4-deep ring, one turn of an 8-deep one) or 6 per
+  // loop iteration: the wait-count analysis is conservative across the loop
+  // back edge, so cross it less often
+  for (int kb = 0; kb < nk; kb += (PD == 6 ? 6 : 8)) {
     DFS_CONSUMER_STEP(0, 0)
     DFS_CONSUMER_STEP(1, 1)
     DFS_CONSUMER_STEP(2, 2)
     DFS_CONSUMER_STEP(3, 3)
-    DFS_CONSUMER_STEP(4, 0)
-    DFS_CONSUMER_STEP(5, 1)
-    DFS_CONSUMER_STEP(6, 2)
-    DFS_CONSUMER_STEP(7, 3)
+    DFS_CONSUMER_STEP(4, 4 % PD)
+    DFS_CONSUMER_STEP(5, 5 % PD)
+    if constexpr (PD != 6) {
+      DFS_CONSUMER_STEP(6, 6 % PD)
+      DFS_CONSUMER_STEP(7, 7 % PD)
+    }
   }
 #undef DFS_CONSUMER_STEP
 
+  // W is the A operand and X the B operand, so each 16x16 tile comes out
+  // transposed: lane (c, g4) holds output row m = c and the four consecutive
+  // columns n = 4*g4 .. 4*g4+3 — one 16-byte store per tile and lane.
   float* Y = a.Y + (size_t)z * a.y_split_stride;
+  const bool vec = (a.ldy & 3) == 0 && ((uintptr_t)Y & 15) == 0;
 #pragma unroll
-  for (int j = 0; j < NW; ++j) {
-    const int n = n0 + wave * 16 * NW + j * 16 + c;
-    if (n >= a.N) continue;
+  for (int i = 0; i < MT; ++i) {
+    const int m = m0 + i * 16 + c;
+    if (m >= a.M) continue;
+    float* yrow = Y + (size_t)m * a.ldy;
 #pragma unroll
-    for (int i = 0; i < MT; ++i)
+    for (int j = 0; j < NW; ++j) {
+      const int n = n0 + wave * 16 * NW + j * 16 + g4 * 4;
+      if (vec && n + 3 < a.N) {
+        f32x4 v = acc[i][j];
+        if (a.accumulate) v += *(const f32x4*)(yrow + n);
+        *(f32x4*)(yrow + n) = v;
+      } else {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = m0 + i * 16 + g4 * 4 + r;
-        if (m >= a.M) continue;
-        float* y = Y + (size_t)m * a.ldy + n;
-        if (a.accumulate) *y = *y + acc[i][j][r];
-        else *y = acc[i][j][r];
+        for (int r = 0; r < 4; ++r) {
+          if (n + r >= a.N) break;
+          if (a.accumulate) yrow[n + r] += acc[i][j][r];
+          else yrow[n + r] = acc[i][j][r];
+        }
       }
+    }
   }
 }
 
@@ -361,6 +411,25 @@ __global__ __launch_bounds__(256) void gemm_f32_nt(GemmArgs a, int k_per_split) 
     }
 }
 
+// Reorders a row-major bf16 [N, K] matrix into the tile-packed layout; one
+// thread per 16-byte chunk of the output (grid-stride), rows past N zero.
+__global__ __launch_bounds__(256) void pack_kernel(const bf16_t* __restrict__ src, bf16_t* __restrict__ dst, int N,
+                                                   int K) {
+  const int kb = K / BK;
+  const size_t chunks = (size_t)ceil_div(N, 16) * 16 * K / 8;
+  for (size_t c = (size_t)blockIdx.x * 256 + threadIdx.x; c < chunks; c += (size_t)gridDim.x * 256) {
+    const size_t tile = c >> 7;
+    const int q = (int)(c & 127), l = q & 63;
+    const size_t nt = tile / kb;
+    const int kt = (int)(tile % kb);
+    const size_t row = nt * 16 + (l & 15);
+    const int col = kt * BK + (q >> 6) * 32 + (l >> 4) * 8;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (row < (size_t)N) v = ldg16(src + row * K + col);
+    *(uint4*)(dst + c * 8) = v;
+  }
+}
+
 }  // namespace
 
 // Kernel configurations the planner chooses from.
@@ -394,7 +463,7 @@ GemmPlan gemm_plan(int M, int N, int K, int dtype, int force_splits) {
   if (const char* f = getenv("DFS_GEMM_FORCE")) {
     GemmPlan p;
     int sp = 1;
-    if (sscanf(f, "%d,%d,%d,%d,%d,%d", &p.kind, &p.bm, &p.bn, &p.mt, &p.nw, &sp) == 6) {
+    if (sscanf(f, "%d,%d,%d,%d,%d,%d,%d,%d", &p.kind, &p.bm, &p.bn, &p.mt, &p.nw, &sp, &p.pd, &p.xd) >= 6) {
       const int kps_blocks = ceil_div(kb, sp);
       p.splits = ceil_div(kb, kps_blocks);
       p.k_per_split = kps_blocks * BK;
@@ -436,6 +505,8 @@ GemmPlan gemm_plan(int M, int N, int K, int dtype, int force_splits) {
         best.nw = c.nw;
         best.splits = sp;
         best.k_per_split = kps_blocks * BK;
+        // X prefetched as deep as W where that variant is built (measured a little faster)
+        best.xd = (c.kind == 1 && ((c.mt == 8 && c.nw == 2) || (c.mt == 16 && c.nw == 1))) ? 4 : 2;
       }
     }
   }
@@ -463,29 +534,53 @@ hipError_t launch_gemm(const GemmArgs& a, const GemmPlan& p, int dtype, hipStrea
   if (p.kind == 1) {
     const int mtl = ceil_div(a.M, p.bm), ntl = ceil_div(a.N, p.bn);
     const dim3 g1(mtl * ntl * p.splits);
-#define DFS_STREAM(MT_, NW_, PD_)                                                                        \
-  if (p.mt == MT_ && p.nw == NW_) {                                                                       \
-    hipLaunchKernelGGL((gemm_stream_bf16<MT_, NW_>), g1, dim3(512), 0, s, a, kps, mtl, ntl);          \
+#define DFS_STREAM(MT_, NW_, PD_, XD_)                                                                   \
+  if (p.mt == MT_ && p.nw == NW_ && p.pd == PD_ && p.xd == XD_) {                                         \
+    if (a.packed)                                                                                         \
+      hipLaunchKernelGGL((gemm_stream_bf16<MT_, NW_, PD_, XD_, true>), g1, dim3(512), 0, s, a, kps, mtl, ntl); \
+    else                                                                                                  \
+      hipLaunchKernelGGL((gemm_stream_bf16<MT_, NW_, PD_, XD_, false>), g1, dim3(512), 0, s, a, kps, mtl, ntl); \
     return hipGetLastError();                                                                             \
   }
-    DFS_STREAM(2, 2, 4)
-    DFS_STREAM(2, 1, 4)
-    DFS_STREAM(4, 2, 4)
-    DFS_STREAM(4, 1, 4)
-    DFS_STREAM(8, 2, 4)
-    DFS_STREAM(8, 1, 4)
-    DFS_STREAM(16, 1, 4)
+    DFS_STREAM(2, 2, 4, 2)
+    DFS_STREAM(2, 1, 4, 2)
+    DFS_STREAM(4, 2, 4, 2)
+    DFS_STREAM(4, 1, 4, 2)
+    DFS_STREAM(8, 2, 4, 2)
+    DFS_STREAM(8, 1, 4, 2)
+    DFS_STREAM(16, 1, 4, 2)
+    DFS_STREAM(8, 2, 4, 4)
+    DFS_STREAM(8, 2, 8, 8)
+    DFS_STREAM(8, 1, 8, 8)
+    DFS_STREAM(8, 2, 6, 6)
+    DFS_STREAM(16, 1, 4, 4)
 #undef DFS_STREAM
     return hipErrorInvalidValue;
   }
-  if (p.bm == 128 && p.bn == 128)
-    hipLaunchKernelGGL((gemm_bf16_nt<128, 128>), grid, dim3(256), 0, s, a, kps);
-  else if (p.bm == 128 && p.bn == 64)
-    hipLaunchKernelGGL((gemm_bf16_nt<128, 64>), grid, dim3(256), 0, s, a, kps);
-  else if (p.bm == 64 && p.bn == 128)
-    hipLaunchKernelGGL((gemm_bf16_nt<64, 128>), grid, dim3(256), 0, s, a, kps);
-  else
-    hipLaunchKernelGGL((gemm_bf16_nt<64, 64>), grid, dim3(256), 0, s, a, kps);
+#define DFS_TILED(BM_, BN_)                                                                              \
+  if (p.bm == BM_ && p.bn == BN_) {                                                                       \
+    if (a.packed)                                                                                         \
+      hipLaunchKernelGGL((gemm_bf16_nt<BM_, BN_, true>), grid, dim3(256), 0, s, a, kps);                  \
+    else                                                                                                  \
+      hipLaunchKernelGGL((gemm_bf16_nt<BM_, BN_, false>), grid, dim3(256), 0, s, a, kps);                 \
+    return hipGetLastError();                                                                             \
+  }
+  DFS_TILED(128, 128)
+  DFS_TILED(128, 64)
+  DFS_TILED(64, 128)
+  DFS_TILED(64, 64)
+#undef DFS_TILED
+  return hipErrorInvalidValue;
+}
+
+size_t packed_matrix_elems(int N, int K) { return (size_t)ceil_div(N, 16) * 16 * K; }
+
+hipError_t launch_pack(const void* src, void* dst, int N, int K, hipStream_t s) {
+  const size_t chunks = packed_matrix_elems(N, K) / 8;
+  const size_t need = (chunks + 255) / 256;
+  const unsigned blocks = (unsigned)(need < 16384 ? need : 16384);
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(pack_kernel, dim3(blocks), dim3(256), 0, s, (const bf16_t*)src, (bf16_t*)dst, N, K);
   return hipGetLastError();
 }
 

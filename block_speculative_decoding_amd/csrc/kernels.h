@@ -27,14 +27,22 @@ struct GemmArgs {
   long ldy = 0;
   size_t y_split_stride = 0;          // elements between split slices of Y
   int accumulate = 0;                 // 1: Y += acc (single split only)
+  int packed = 0;                     // 1: W segments tile-packed (bf16; see pack_tile_offset)
 };
 
 struct GemmPlan {
   int kind = 0;            // 0: LDS-tiled, 1: weight streaming, 2: fp32 VALU
   int bm = 128, bn = 128, mt = 0, nw = 0, splits = 1, k_per_split = 0;
+  int pd = 4, xd = 2;      // weight-streaming kernel: k steps of W / X in flight per wave
 };
 
 GemmPlan gemm_plan(int M, int N, int K, int dtype, int force_splits = 0);
+// Tile-packed bf16 weights: [ceil(N/16)][K/64] tiles of 16 rows x 64 columns,
+// each 2 KB tile stored in matrix-core operand order [ks 0..1][lane 0..63][8]:
+// lane l holds row 16*nt + (l % 16), columns 64*kt + 32*ks + 8*(l / 16) .. +7.
+// Rows past N are zero.  A wave loads one k step of 16 rows as 2 contiguous KB.
+size_t packed_matrix_elems(int N, int K);
+hipError_t launch_pack(const void* src, void* dst, int N, int K, hipStream_t s);
 size_t gemm_partial_elems(const GemmPlan& p, int M, int N);   // sp * M * N
 hipError_t launch_gemm(const GemmArgs& a, const GemmPlan& p, int dtype, hipStream_t s);
 

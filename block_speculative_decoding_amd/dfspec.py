@@ -17,7 +17,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdfspec.so")
 
 DFS_OK, DFS_EINVAL, DFS_EUNSUPPORTED, DFS_EHIP, DFS_EWORKSPACE = 0, -1, -2, -3, -4
-DFS_F32, DFS_BF16 = 0, 1
+DFS_F32, DFS_BF16, DFS_BF16_PACKED = 0, 1, 2
 
 EXPORTS = [
     "dflash_draft_workspace_size", "dflash_draft_step",
@@ -25,6 +25,7 @@ EXPORTS = [
     "spec_verify_workspace_size", "spec_verify", "dfs_status_string",
     "dfs_block_attention_workspace_size", "dfs_block_attention",
     "dfs_gemm_workspace_size", "dfs_gemm", "dfs_profile_begin", "dfs_profile_end",
+    "dfs_packed_matrix_bytes", "dfs_pack_matrix",
 ]
 
 
@@ -48,7 +49,7 @@ class CDrafterWeights(ctypes.Structure):
     _fields_ = [("embed", ctypes.c_void_p), ("fc", ctypes.c_void_p), ("fc_norm", ctypes.c_void_p),
                 ("final_norm", ctypes.c_void_p), ("lm_head", ctypes.c_void_p)] + [
         (n, _PP) for n in ("attn_norm", "wq", "wk", "wv", "wo", "mlp_norm", "w_gate", "w_up",
-                           "w_down")]
+                           "w_down")] + [("packed", ctypes.c_int32)]
 
 
 def _load():
@@ -69,7 +70,9 @@ def _load():
         "dfs_block_attention": (ctypes.c_int, [i32, i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp,
                                                vp, vp, vp, vp, sz, vp]),
         "dfs_gemm_workspace_size": (sz, [i32, i32, i32, i32, i32]),
-        "dfs_gemm": (ctypes.c_int, [i32, i32, i32, i32, vp, vp, vp, i32, vp, sz, vp]),
+        "dfs_gemm": (ctypes.c_int, [i32, i32, i32, i32, vp, vp, vp, i32, i32, vp, sz, vp]),
+        "dfs_packed_matrix_bytes": (sz, [i32, i32]),
+        "dfs_pack_matrix": (ctypes.c_int, [i32, i32, vp, vp, vp]),
         "dfs_profile_begin": (ctypes.c_int, [ctypes.c_char_p, i32]),
         "dfs_profile_end": (ctypes.c_int, [ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_double)]),
     }
@@ -151,17 +154,25 @@ class DrafterConfig:
 
 class DrafterWeights:
     """Device tensors of the drafter keyed like the synthetic generator
-    ("embed", "fc", ..., "layers.{l}.wq", ...), plus the C struct pointing at them."""
+    ("embed", "fc", ..., "layers.{l}.wq", ...), plus the C struct pointing at them.
+    packed=True (bf16) packs every matrix but the embedding with dfs_pack_matrix
+    (new device tensors; the row-major ones are not kept)."""
 
     PER_LAYER = ("attn_norm", "wq", "wk", "wv", "wo", "mlp_norm", "w_gate", "w_up", "w_down")
+    PACKED = ("fc", "lm_head", "wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down")
 
-    def __init__(self, cfg: DrafterConfig, tensors: dict):
+    def __init__(self, cfg: DrafterConfig, tensors: dict, packed: bool = False):
         self.cfg = cfg
-        self.t = tensors
         dt = torch_dtype(cfg.dtype)
         for k, v in tensors.items():
             if v.dtype != dt or not v.is_cuda or not v.is_contiguous():
                 raise TypeError(f"weight {k} must be a contiguous {dt} CUDA tensor")
+        if packed:
+            if cfg.dtype != DFS_BF16:
+                raise ValueError("packed weights need bf16")
+            tensors = {k: (pack_matrix(v) if k.split(".")[-1] in self.PACKED else v) for k, v in tensors.items()}
+        self.t = tensors
+        self.packed = bool(packed)
         L = cfg.n_layers
         self._arrays = {}
         for n in self.PER_LAYER:
@@ -170,7 +181,7 @@ class DrafterWeights:
         self.c = CDrafterWeights(
             tensors["embed"].data_ptr(), tensors["fc"].data_ptr(), tensors["fc_norm"].data_ptr(),
             tensors["final_norm"].data_ptr(), tensors["lm_head"].data_ptr(),
-            *[ctypes.cast(self._arrays[n], _PP) for n in self.PER_LAYER])
+            *[ctypes.cast(self._arrays[n], _PP) for n in self.PER_LAYER], int(self.packed))
 
 
 # ------------------------------------------------------------------ entry points
@@ -203,14 +214,21 @@ def markov_bias_sample_workspace_size(batch: int, n_draft: int, vocab: int) -> i
 
 
 def markov_bias_sample(logits, U, Wt, last_token, u_draft, temperature: float, draft_tokens,
-                       row_stats, workspace, stream=None):
+                       row_stats, workspace, stream=None, wt_packed: bool = False):
+    """wt_packed: Wt was packed by pack_matrix (bf16)."""
     B, G, V = logits.shape
     rank = 0 if U is None else U.shape[1]
     uw_dtype = DFS_F32
     if U is not None:
         uw_dtype = DFS_BF16 if U.dtype == torch.bfloat16 else DFS_F32
         _ptr(U, torch_dtype(uw_dtype), V * rank, "U")
-        _ptr(Wt, torch_dtype(uw_dtype), V * rank, "Wt")
+        if wt_packed:
+            if uw_dtype != DFS_BF16:
+                raise ValueError("a packed Wt must be bf16")
+            _ptr(Wt, torch.bfloat16, packed_matrix_bytes(V, rank) // 2, "Wt")
+            uw_dtype = DFS_BF16_PACKED
+        else:
+            _ptr(Wt, torch_dtype(uw_dtype), V * rank, "Wt")
     st = LIB.markov_bias_sample(
         B, G, V, rank, _ptr(logits, torch.float32, B * G * V, "logits"),
         _ptr(U, name="U"), _ptr(Wt, name="Wt"), uw_dtype,
@@ -262,14 +280,34 @@ def dfs_gemm_workspace_size(M, N, K, dtype, splits=0) -> int:
     return int(LIB.dfs_gemm_workspace_size(M, N, K, dtype, splits))
 
 
-def dfs_gemm(X, W, Y, splits: int, workspace, stream=None):
+def dfs_gemm(X, W, Y, splits: int, workspace, stream=None, w_packed: bool = False):
+    """Y = X . W^T; with w_packed, W is pack_matrix(W') of a [N, K] matrix and N = Y.shape[1]."""
     M, K = X.shape
-    N = W.shape[0]
+    N = Y.shape[1] if w_packed else W.shape[0]
     dtype = DFS_BF16 if X.dtype == torch.bfloat16 else DFS_F32
-    st = LIB.dfs_gemm(M, N, K, dtype, _ptr(X, X.dtype, name="X"), _ptr(W, X.dtype, N * K, "W"),
-                      _ptr(Y, torch.float32, M * N, "Y"), splits, _ptr(workspace, torch.uint8, None, "workspace"),
-                      workspace.numel(), _stream(stream))
+    wn = packed_matrix_bytes(N, K) // 2 if w_packed else N * K
+    st = LIB.dfs_gemm(M, N, K, dtype, _ptr(X, X.dtype, name="X"), _ptr(W, X.dtype, wn, "W"),
+                      _ptr(Y, torch.float32, M * N, "Y"), splits, int(w_packed),
+                      _ptr(workspace, torch.uint8, None, "workspace"), workspace.numel(), _stream(stream))
     _check(st, "dfs_gemm")
+
+
+def packed_matrix_bytes(rows: int, cols: int) -> int:
+    return int(LIB.dfs_packed_matrix_bytes(rows, cols))
+
+
+def pack_matrix(w, stream=None):
+    """Tile-packed copy of a row-major bf16 [rows, cols] device matrix (flat bf16 tensor)."""
+    if w.dim() != 2 or w.dtype != torch.bfloat16:
+        raise TypeError("pack_matrix takes a 2-D bf16 tensor")
+    rows, cols = w.shape
+    n = packed_matrix_bytes(rows, cols)
+    if n == 0:
+        raise ValueError(f"cannot pack a [{rows}, {cols}] matrix (cols must be a multiple of 64)")
+    out = torch.empty(n // 2, dtype=torch.bfloat16, device=w.device)
+    _check(LIB.dfs_pack_matrix(rows, cols, _ptr(w, torch.bfloat16, rows * cols, "w"),
+                               _ptr(out, torch.bfloat16, n // 2, "out"), _stream(stream)), "dfs_pack_matrix")
+    return out
 
 
 def dfs_profile_begin(group: str, max_launches: int):

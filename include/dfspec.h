@@ -65,7 +65,11 @@ typedef enum {
   DFS_EWORKSPACE = -4     /* workspace smaller than the matching *_workspace_size() */
 } dfs_status;
 
-typedef enum { DFS_F32 = 0, DFS_BF16 = 1 } dfs_dtype;
+typedef enum {
+  DFS_F32 = 0,
+  DFS_BF16 = 1,
+  DFS_BF16_PACKED = 2   /* a bf16 weight matrix in the tile-packed layout of dfs_pack_matrix */
+} dfs_dtype;
 
 /* Drafter shape.  B (batch) and the per-call row counts are arguments of the
  * calls, not part of the configuration. */
@@ -87,9 +91,12 @@ typedef struct {
 } dfs_drafter_cfg;
 
 /* Drafter weights, all in cfg.dtype, matrices stored [out, in] (row = output
- * feature, inputs contiguous).  The per-layer members point to HOST arrays of
- * L device pointers.  The embedding and LM head are the target's, reused
- * (DSpark page, section "Optymalizacja weryfikacji i wydajności"). */
+ * feature, inputs contiguous), or — with packed = 1, bf16 only — every matrix
+ * except the embedding in the tile-packed layout written by dfs_pack_matrix
+ * (the layout the matrix-core kernels stream at full HBM bandwidth; pack once
+ * at load time).  The per-layer members point to HOST arrays of L device
+ * pointers.  The embedding and LM head are the target's, reused (DSpark page,
+ * section "Optymalizacja weryfikacji i wydajności"). */
 typedef struct {
   const void* embed;       /* [V, H] */
   const void* fc;          /* [H, nT*H]; input = target hiddens concatenated in ascending layer order */
@@ -105,6 +112,8 @@ typedef struct {
   const void* const* w_gate;    /* L x [F, H] */
   const void* const* w_up;      /* L x [F, H] */
   const void* const* w_down;    /* L x [H, F] */
+  int32_t packed;               /* 0: row-major matrices; 1: tile-packed (fc, wq, wk, wv, wo, w_gate,
+                                   w_up, w_down, lm_head), DFS_EUNSUPPORTED for fp32 */
 } dfs_drafter_weights;
 
 /* ------------------------------------------------------------------ draft */
@@ -168,7 +177,8 @@ size_t markov_bias_sample_workspace_size(int32_t batch, int32_t n_draft, int32_t
  * With rank == 0 there is no head and all positions are drawn independently.
  *
  * logits      [B, gamma, V] fp32, in: base logits, out: final logits (in place).
- * U, Wt       [V, rank] in uw_dtype (NULL when rank == 0).
+ * U, Wt       [V, rank] in uw_dtype (NULL when rank == 0).  uw_dtype =
+ *             DFS_BF16_PACKED: U row-major bf16, Wt tile-packed by dfs_pack_matrix.
  * last_token  [B] int32; out-of-range previous tokens are clamped to [0, V-1].
  * u_draft     [B, gamma] fp32 in [0, 1).
  * temperature host, >= 0.
@@ -233,10 +243,25 @@ int dfs_block_attention(int32_t batch, int32_t block, int32_t n_q_heads, int32_t
                         size_t workspace_bytes, void* stream);
 
 /* Y[M, N] fp32 = X[M, K] . W[N, K]^T, both in `dtype`; the matrix-core kernel of
- * the drafter (split over K when `splits` > 1; splits = 0 picks automatically). */
+ * the drafter (split over K when `splits` > 1; splits = 0 picks automatically).
+ * w_packed = 1: W is tile-packed (bf16 only). */
 size_t dfs_gemm_workspace_size(int32_t M, int32_t N, int32_t K, int32_t dtype, int32_t splits);
 int dfs_gemm(int32_t M, int32_t N, int32_t K, int32_t dtype, const void* X, const void* W,
-             float* Y, int32_t splits, void* workspace, size_t workspace_bytes, void* stream);
+             float* Y, int32_t splits, int32_t w_packed, void* workspace, size_t workspace_bytes,
+             void* stream);
+
+/* Weight layout for the matrix-core kernels.  A bf16 matrix W [rows, cols]
+ * (cols a multiple of 64) becomes ceil(rows/16) x (cols/64) tiles of 16 rows x
+ * 64 columns, row-tile major; each 2 KB tile holds [half h = 0..1][lane l =
+ * 0..63][8 values]: row 16*t + (l % 16), columns 64*c + 32*h + 8*(l / 16) .. +7,
+ * i.e. exactly the operand fragment each lane of a wave feeds the 16x16x32
+ * matrix instruction; rows past `rows` are zero.  One k step of 16 rows is
+ * then two contiguous kilobytes, the access pattern HBM streams best.
+ * dfs_packed_matrix_bytes returns 0 for unsupported shapes.  dfs_pack_matrix
+ * reads src (row-major, device) and writes dst (device, that many bytes, not
+ * overlapping src) on `stream`. */
+size_t dfs_packed_matrix_bytes(int32_t rows, int32_t cols);
+int dfs_pack_matrix(int32_t rows, int32_t cols, const void* src, void* dst, void* stream);
 
 /* Per-kernel timing with HIP events recorded around every launch of the named
  * kernel group on the launching stream ("gemm", "attention", "sample", "verify",

@@ -67,8 +67,8 @@ def compare_sequential_draws(gpu, ora, margins, what):
     return n_cmp, n_flag
 
 
-def upload_weights(w, np_weights):
+def upload_weights(w, np_weights, packed=False):
     from block_speculative_decoding_amd import dfspec as D
     cfg = D.DrafterConfig.of(w)
     t = {k: up(v, w.dtype) for k, v in np_weights.items()}
-    return cfg, D.DrafterWeights(cfg, t)
+    return cfg, D.DrafterWeights(cfg, t, packed=packed)

@@ -97,3 +97,18 @@ def test_invalid_arguments_rejected_on_host(lib):
                            16, None) == -4
     lib.dfs_status_string.restype = ctypes.c_char_p
     assert lib.dfs_status_string(-4) == b"workspace too small"
+
+
+def test_packed_matrix_sizes_and_rejections(lib):
+    lib.dfs_packed_matrix_bytes.restype = ctypes.c_size_t
+    # rows rounded up to whole 16-row tiles, 2 bytes per value
+    assert lib.dfs_packed_matrix_bytes(100, 128) == 112 * 128 * 2
+    assert lib.dfs_packed_matrix_bytes(151936, 4096) == 151936 * 4096 * 2
+    assert lib.dfs_packed_matrix_bytes(16, 96) == 0          # columns must be whole 64-wide tiles
+    assert lib.dfs_packed_matrix_bytes(0, 64) == 0
+    lib.dfs_pack_matrix.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                                    ctypes.c_void_p]
+    fake = ctypes.c_void_p(0x1000)
+    assert lib.dfs_pack_matrix(16, 64, None, fake, None) == -1
+    assert lib.dfs_pack_matrix(16, 64, fake, fake, None) == -1     # in place is not allowed
+    assert lib.dfs_pack_matrix(16, 96, fake, ctypes.c_void_p(0x2000), None) == -2

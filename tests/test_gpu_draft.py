@@ -22,6 +22,9 @@ CASES = {
     "medium_ragged": (MEDIUM, 3, [284, 131, 7], [16, 5, 0], 16),
     "medium_prefill": (MEDIUM.with_(batch=2), 4, [0, 0], [284, 150], 284),
     "medium_b1_s8": (MEDIUM.with_(batch=1, block=8, ctx=1000), 5, None, None, None),
+    # weights in the tile-packed layout (V = 5000 leaves a partial last row tile)
+    "medium_packed": (MEDIUM, 2, None, None, None, True),
+    "medium_ragged_packed": (MEDIUM, 3, [284, 131, 7], [16, 5, 0], 16, True),
 }
 
 
@@ -33,13 +36,13 @@ def D():
     return dfspec
 
 
-def run_case(D, w, seed, ctx_len, n_new, nmax, gain_std=0.1):
+def run_case(D, w, seed, ctx_len, n_new, nmax, packed=False, gain_std=0.1):
     import torch
     weights = inputs.drafter_weights(w, seed, gain_std=gain_std)
     step = inputs.step_inputs(w, seed, n_new=n_new, ctx_len=ctx_len, n_new_max=nmax)
     kc, vc = inputs.cache_prefix(w, seed, step["ctx_len"], garbage="nan")
     B, G = w.batch, w.gamma
-    cfg, wdev = upload_weights(w, weights)
+    cfg, wdev = upload_weights(w, weights, packed=packed)
     kdev, vdev = D.cache_from_logical(up(kc, w.dtype), up(vc, w.dtype))
     ctx_dev = up(step["ctx_len"], "i32")
     logits = torch.full((B, G, w.vocab), float("nan"), dtype=torch.float32, device=DEV)
@@ -59,9 +62,9 @@ def run_case(D, w, seed, ctx_len, n_new, nmax, gain_std=0.1):
 
 @pytest.mark.parametrize("name", list(CASES))
 def test_draft_step_matches_oracle(D, name):
-    w, seed, ctx_len, n_new, nmax = CASES[name]
+    w, seed, ctx_len, n_new, nmax, *packed = CASES[name]
     say(f"draft step {name}: {w.name} B={w.batch} S={w.block}")
-    gpu, ora, step = run_case(D, w, seed, ctx_len, n_new, nmax)
+    gpu, ora, step = run_case(D, w, seed, ctx_len, n_new, nmax, packed=bool(packed and packed[0]))
     tol = 1e-4 if w.dtype == "f32" else 2e-2
     np.testing.assert_array_equal(gpu["ctx"], ora["ctx"])
     err = np.abs(gpu["logits"].astype(np.float64) - ora["logits"])
@@ -85,3 +88,12 @@ def test_draft_step_is_deterministic(D):
     a, _, _ = run_case(D, w, seed, ctx_len, n_new, nmax)
     b, _, _ = run_case(D, w, seed, ctx_len, n_new, nmax)
     assert np.array_equal(a["logits"].view(np.uint32), b["logits"].view(np.uint32))
+
+
+def test_draft_packed_weights_bit_identical_to_row_major(D):
+    w, seed, ctx_len, n_new, nmax = CASES["medium_ragged"]
+    a, _, _ = run_case(D, w, seed, ctx_len, n_new, nmax, packed=False)
+    b, _, _ = run_case(D, w, seed, ctx_len, n_new, nmax, packed=True)
+    assert np.array_equal(a["logits"].view(np.uint32), b["logits"].view(np.uint32))
+    for key in ("k", "v"):
+        assert np.array_equal(a[key].view(np.uint8), b[key].view(np.uint8))

@@ -37,6 +37,49 @@ def test_gemm_bf16_matches_fp64_product(D, M, N, K, splits):
     np.testing.assert_allclose(got, want, atol=2e-5 * np.sqrt(K), rtol=1e-5)
 
 
+def _packed_reference(W):
+    """The tile-packed layout written out from its definition: tiles of 16 rows x 64
+    columns, row-tile major; inside a tile [half h][lane l][8 values] = row
+    16t + l % 16, columns 64c + 32h + 8(l // 16) .. +7; rows past N zero."""
+    N, K = W.shape
+    nt = -(-N // 16)
+    Wp = np.zeros((nt * 16, K), W.dtype)
+    Wp[:N] = W
+    out = np.empty((nt, K // 64, 2, 64, 8), W.dtype)
+    for l in range(64):
+        for h in range(2):
+            cols = np.arange(8) + 32 * h + 8 * (l // 16)
+            # [nt, K//64, 8]: row 16t + l%16, column 64c + cols
+            out[:, :, h, l, :] = Wp[l % 16::16].reshape(nt, K // 64, 64)[:, :, cols]
+    return out.reshape(-1)
+
+
+@pytest.mark.parametrize("N,K", [(16, 64), (100, 192), (1000, 512)])
+def test_pack_matrix_layout(D, N, K):
+    W = rng.integers(9, "packw", (N, K), 0, 65535).astype(np.uint16)     # arbitrary bit patterns
+    got = down(D.pack_matrix(up(W, "bf16").view(N, K)))
+    np.testing.assert_array_equal(got.view(np.uint16), _packed_reference(W))
+
+
+@pytest.mark.parametrize("M,N,K,splits", [(1, 64, 64, 0), (120, 300, 256, 3), (128, 1000, 512, 0),
+                                          (256, 1000, 512, 7), (300, 200, 256, 0), (130, 4096, 1024, 0)])
+def test_gemm_packed_weights_bit_identical(D, M, N, K, splits):
+    # same operands in the same order: the packed and row-major kernels agree bit for bit
+    import torch
+    say(f"gemm packed M={M} N={N} K={K} splits={splits}")
+    X = rng.normal(1, "gx", (M, K), 1.0, dtype="bf16")
+    W = rng.normal(1, "gw", (N, K), 0.05, dtype="bf16")
+    Wd = up(W, "bf16").view(N, K)
+    Y0 = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    Y1 = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    ws = workspace(D.dfs_gemm_workspace_size(M, N, K, D.DFS_BF16, splits))
+    D.dfs_gemm(up(X, "bf16").view(M, K), Wd, Y0, splits, ws)
+    D.dfs_gemm(up(X, "bf16").view(M, K), D.pack_matrix(Wd), Y1, splits, ws, w_packed=True)
+    assert np.array_equal(down(Y0).view(np.uint32), down(Y1).view(np.uint32))
+    want = as_f64(X, "bf16") @ as_f64(W, "bf16").T
+    np.testing.assert_allclose(down(Y1).astype(np.float64), want, atol=2e-5 * np.sqrt(K), rtol=1e-5)
+
+
 def test_gemm_f32(D):
     import torch
     M, N, K = 5, 70, 48
@@ -146,6 +189,26 @@ def test_markov_head_matches_oracle(D, dtype, B, G, V, r):
             np.testing.assert_allclose(got_final[b, i], final[b, i], atol=1e-4, rtol=0)
     assert n_flag <= flag_budget(V, B * G)
     say(f"  compared {n_cmp} draws, {n_flag} flagged")
+
+
+def test_markov_head_packed_wt_bit_identical(D):
+    import torch
+    B, G, V, r = 5, 4, 3000, 64
+    base = rng.normal(6, "pmb", (B, G, V), 1.5)
+    U = rng.normal(6, "pmU", (V, r), r ** -0.25, dtype="bf16")
+    Wt = rng.normal(6, "pmW", (V, r), r ** -0.25, dtype="bf16")
+    last = up(rng.integers(6, "pml", (B,), 0, V - 1), "i32")
+    u = up(rng.uniform01(6, "pmu", (B, G)), "f32")
+    outs = []
+    for packed in (False, True):
+        lt = up(base, "f32")
+        tok = torch.empty((B, G), dtype=torch.int32, device=DEV)
+        wt = up(Wt, "bf16").view(V, r)
+        D.markov_bias_sample(lt, up(U, "bf16"), D.pack_matrix(wt) if packed else wt, last, u, 1.0, tok, None,
+                             workspace(D.markov_bias_sample_workspace_size(B, G, V)), wt_packed=packed)
+        outs.append((down(lt), down(tok)))
+    assert np.array_equal(outs[0][0].view(np.uint32), outs[1][0].view(np.uint32))
+    assert np.array_equal(outs[0][1], outs[1][1])
 
 
 # ---------------------------------------------------------------- verify
