@@ -152,6 +152,26 @@ hipError_t run_gemm(const void* X, int ldx, int M, int N, int K, const void* w0,
   return launch_gemm(a, p, dtype, s);
 }
 
+// SwiGLU MLP input: hout[m][f] = bf16(silu(X.Wg^T) * (X.Wu^T)) in one weight pass
+hipError_t run_gemm_gated(const void* X, int ldx, int M, int F, int K, const void* wg, const void* wu, void* hout,
+                          int packed, const GemmPlan& p, hipStream_t s) {
+  GemmArgs a;
+  a.X = X;
+  a.ldx = ldx;
+  a.x_rows = M;
+  a.M = M;
+  a.N = F;
+  a.K = K;
+  a.seg[0].w = wg;
+  a.seg[1].w = wu;
+  a.nseg = 2;
+  a.ldy = F;
+  a.packed = packed;
+  a.gated = 1;
+  a.hout = hout;
+  return launch_gemm(a, p, DFS_BF16, s);
+}
+
 template <typename P>
 const char* at(const P* base, size_t off) {
   return (const char*)base + off;
@@ -251,6 +271,7 @@ int dflash_draft_step(const dfs_drafter_cfg* cfg, const dfs_drafter_weights* wt,
     DFS_TRY(launch_norm(na, dt, s));
   }
   const AttnPlan ap = attn_plan(d.B, d.nkv, ctx_bound, dt);
+  const GemmPlan gated = gemm_plan_gated(d.Mb, d.F, d.H, dt);
   const size_t layer_cache = (size_t)d.B * d.nkv * d.max_ctx * d.d * es;
   for (int l = 0; l < d.L; ++l) {
     // 2. Q|K|V of [features ; block rows] in one pass over wq|wk|wv
@@ -317,10 +338,16 @@ int dflash_draft_step(const dfs_drafter_cfg* cfg, const dfs_drafter_weights* wt,
       na.eps = cfg->rms_eps;
       DFS_TRY(launch_norm(na, dt, s));
     }
-    // 5. SwiGLU MLP: [gate | up] in one pass, then down, residual add, next pre-norm
-    DFS_TRY(run_gemm(w.mlp_in, d.H, d.Mb, 2 * d.F, d.H, wt->w_gate[l], wt->w_up[l], d.F, nullptr, 0, w.part, dt,
-                     pk, s, &sp, &pst));
-    DFS_TRY(launch_swiglu(w.part, sp, pst, d.Mb, d.F, w.hmid, dt, s));
+    // 5. SwiGLU MLP: gate and up in one weight pass (the product formed in the
+    //    GEMM epilogue when a gated plan fits, else by a separate pass over the
+    //    fp32 results), then down, residual add, next pre-norm
+    if (gated.kind == 1) {
+      DFS_TRY(run_gemm_gated(w.mlp_in, d.H, d.Mb, d.F, d.H, wt->w_gate[l], wt->w_up[l], w.hmid, pk, gated, s));
+    } else {
+      DFS_TRY(run_gemm(w.mlp_in, d.H, d.Mb, 2 * d.F, d.H, wt->w_gate[l], wt->w_up[l], d.F, nullptr, 0, w.part, dt,
+                       pk, s, &sp, &pst));
+      DFS_TRY(launch_swiglu(w.part, sp, pst, d.Mb, d.F, w.hmid, dt, s));
+    }
     DFS_TRY(run_gemm(w.hmid, d.F, d.Mb, d.H, d.F, wt->w_down[l], nullptr, 0, nullptr, 0, w.part, dt, pk, s,
                      &sp, &pst));
     {

@@ -62,30 +62,48 @@ __global__ __launch_bounds__(256) void embed_kernel(const T* E, const int32_t* l
   for (int h = threadIdx.x; h < H; h += 256) resid[(size_t)r * H + h] = Elem<T>::load(E, (size_t)tok * H + h);
 }
 
-// RMSNorm of one row per workgroup (1024 threads): out = T(x * rsqrt(mean(x^2)+eps) * g)
-// with x = the fp32 row `resid`.  Each thread holds up to two 4-element groups
-// (H <= 8192); vector loads when H is a multiple of 4.
+// RMSNorm of one row per workgroup (1024 threads), fused with the reduction of
+// split-K GEMM partials and the fp32 residual update:
+//   x = (resid or 0) + sum_z part[z]   (partials summed in z order after resid)
+//   resid = x (when update_resid), out = T(x * rsqrt(mean(x^2)+eps) * g)
+// Each thread holds up to two 4-element groups (H <= 8192); vector accesses
+// when H is a multiple of 4.
 constexpr int kNormThreads = 1024;
 template <typename T>
 __global__ __launch_bounds__(1024) void norm_kernel(NormArgs a) {
   __shared__ float red[kNormThreads / 64];
   const int r = blockIdx.x, tid = threadIdx.x;
   const bool vec = (a.H & 3) == 0;
-  const float* row = a.resid + (size_t)r * a.H;
+  const size_t row0 = (size_t)r * a.H;
+  const bool use_resid = a.resid && (a.update_resid || !a.part);
   float v[2][4];
   float ss = 0.f;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int h = 4 * (tid + i * kNormThreads);
-    if (vec && h < a.H) {
-      const float4 t = *(const float4*)(row + h);
-      v[i][0] = t.x;
-      v[i][1] = t.y;
-      v[i][2] = t.z;
-      v[i][3] = t.w;
-    } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[i][e] = h + e < a.H ? row[h + e] : 0.f;
+    for (int e = 0; e < 4; ++e) v[i][e] = 0.f;
+    if (h < a.H) {
+      if (vec) {
+        if (use_resid) {
+          const float4 t = *(const float4*)(a.resid + row0 + h);
+          v[i][0] = t.x, v[i][1] = t.y, v[i][2] = t.z, v[i][3] = t.w;
+        }
+        for (int z = 0; z < (a.part ? a.sp : 0); ++z) {
+          const float4 t = *(const float4*)(a.part + z * a.part_stride + row0 + h);
+          v[i][0] += t.x, v[i][1] += t.y, v[i][2] += t.z, v[i][3] += t.w;
+        }
+        if (a.part && a.update_resid) *(float4*)(a.resid + row0 + h) = make_float4(v[i][0], v[i][1], v[i][2], v[i][3]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (h + e >= a.H) break;
+          float x = use_resid ? a.resid[row0 + h + e] : 0.f;
+          for (int z = 0; z < (a.part ? a.sp : 0); ++z) x += a.part[z * a.part_stride + row0 + h + e];
+          if (a.part && a.update_resid) a.resid[row0 + h + e] = x;
+          v[i][e] = x;
+        }
+      }
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) ss += v[i][e] * v[i][e];
@@ -260,18 +278,7 @@ hipError_t launch_embed(int dtype, const void* embed, const int32_t* last_token,
   return hipGetLastError();
 }
 
-// With split-K partials: first a fully parallel reduction (into the residual, or
-// in place into partial slice 0), then the row-wise normalisation of that buffer.
-hipError_t launch_norm(const NormArgs& in, int dtype, hipStream_t s) {
-  NormArgs a = in;
-  if (a.part) {
-    float* dst = a.update_resid ? a.resid : const_cast<float*>(a.part);
-    hipError_t e = launch_reduce(a.part, a.sp, a.part_stride, (size_t)a.rows * a.H, dst, s, a.update_resid);
-    if (e != hipSuccess) return e;
-    a.resid = dst;
-    a.part = nullptr;
-    a.update_resid = 0;
-  }
+hipError_t launch_norm(const NormArgs& a, int dtype, hipStream_t s) {
   ProfScope ps("elementwise", s);
   if (dtype == 1) hipLaunchKernelGGL(norm_kernel<bf16_t>, dim3(a.rows), dim3(kNormThreads), 0, s, a);
   else hipLaunchKernelGGL(norm_kernel<float>, dim3(a.rows), dim3(kNormThreads), 0, s, a);

@@ -191,14 +191,18 @@ __device__ __forceinline__ int xcd_logical_id(int id, int total) {
   return (id & 7) * (full >> 3) + (id >> 3);
 }
 
-template <int MT, int NW, int PD, int XD, bool PACKED>
+// GATED (NW = 2): the workgroup covers 64 output features; wave w streams the
+// rows of features n0+16w .. +15 from W_gate (j = 0) and W_up (j = 1), so its
+// epilogue holds gate and up of the same outputs and writes the SwiGLU product.
+template <int MT, int NW, int PD, int XD, bool PACKED, bool GATED>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_stream_bf16(GemmArgs a, int k_per_split, int mtiles, int ntiles) {
+  static_assert(!GATED || NW == 2, "gated tiles pair gate and up");
   // W elements per k step and between the two 32-wide k halves of a step
   constexpr int WSTEP = PACKED ? kTileElems : BK, WKS = PACKED ? kTileElems / 2 : 32;
-  static_assert(PD == 4 || PD == 6 || PD == 8, "ring depth");
+  static_assert(PD == 4 || PD == 8, "ring depth divides the 8-step loop body");
   static_assert(XD == 2 || XD == PD, "X ring depth");
-  constexpr int BM = 16 * MT, BN = 64 * NW;
+  constexpr int BM = 16 * MT, BN = GATED ? 64 : 64 * NW;
   constexpr int XCH = BM * BK / 8 / 256;                // 16-byte X chunks per producer lane per step
   static_assert(XCH >= 1, "tile too small");
   __shared__ __attribute__((aligned(16))) bf16_t Xs[2][BM * LDK];
@@ -230,11 +234,20 @@ void gemm_stream_bf16(GemmArgs a, int k_per_split, int mtiles, int ntiles) {
   } else {
 #pragma unroll
     for (int j = 0; j < NW; ++j) {
-      const int n = min(n0 + wave * 16 * NW + j * 16 + c, a.N - 1);
-      if constexpr (PACKED)   // the wave's 16 rows: one contiguous run of tiles
-        w_src[j] = seg_tile(a, n) + (size_t)(kbeg / BK) * kTileElems + lane * 8;
-      else
-        w_src[j] = (const bf16_t*)seg_row(a, n, 2) + kbeg + g4 * 8;
+      if constexpr (GATED) {
+        const int n = min(n0 + wave * 16 + c, a.N - 1);
+        const bf16_t* w = (const bf16_t*)a.seg[j].w;
+        if constexpr (PACKED)
+          w_src[j] = w + ((size_t)(n >> 4) * (a.K / BK) + kbeg / BK) * kTileElems + lane * 8;
+        else
+          w_src[j] = w + (size_t)n * a.K + kbeg + g4 * 8;
+      } else {
+        const int n = min(n0 + wave * 16 * NW + j * 16 + c, a.N - 1);
+        if constexpr (PACKED)   // the wave's 16 rows: one contiguous run of tiles
+          w_src[j] = seg_tile(a, n) + (size_t)(kbeg / BK) * kTileElems + lane * 8;
+        else
+          w_src[j] = (const bf16_t*)seg_row(a, n, 2) + kbeg + g4 * 8;
+      }
     }
   }
 
@@ -262,17 +275,15 @@ void gemm_stream_bf16(GemmArgs a, int k_per_split, int mtiles, int ntiles) {
     _Pragma("unroll") for (int i = 0; i < XCH; ++i) xr[ST % XD][i] = ldg16(x_src[i] + kk);    \
   }
     // as many steps per iteration as the consumers run (same barrier sequence)
-    for (int kb = 0; kb < nk; kb += (PD == 6 ? 6 : 8)) {
+    for (int kb = 0; kb < nk; kb += 8) {
       DFS_PRODUCER_STEP(0)
       DFS_PRODUCER_STEP(1)
       DFS_PRODUCER_STEP(2)
       DFS_PRODUCER_STEP(3)
       DFS_PRODUCER_STEP(4)
       DFS_PRODUCER_STEP(5)
-      if constexpr (PD != 6) {
-        DFS_PRODUCER_STEP(6)
-        DFS_PRODUCER_STEP(7)
-      }
+      DFS_PRODUCER_STEP(6)
+      DFS_PRODUCER_STEP(7)
     }
 #undef DFS_PRODUCER_STEP
     return;
@@ -316,26 +327,47 @@ void gemm_stream_bf16(GemmArgs a, int k_per_split, int mtiles, int ntiles) {
     _Pragma("unroll") for (int j = 0; j < NW; ++j)                                             \
       _Pragma("unroll") for (int ks = 0; ks < 2; ++ks) wr[R][j][ks] = ldg_bf16x8(w_src[j] + kk + ks * WKS); \
   }
-  // 8 steps (two turns of a 4-deep ring, one turn of an 8-deep one) or 6 per
-  // loop iteration: the wait-count analysis is conservative across the loop
-  // back edge, so cross it less often
-  for (int kb = 0; kb < nk; kb += (PD == 6 ? 6 : 8)) {
+  // 8 steps (two turns of a 4-deep ring, one turn of an 8-deep one) per loop
+  // iteration: the wait-count analysis is conservative across the loop back
+  // edge, so cross it less often
+  for (int kb = 0; kb < nk; kb += 8) {
     DFS_CONSUMER_STEP(0, 0)
     DFS_CONSUMER_STEP(1, 1)
     DFS_CONSUMER_STEP(2, 2)
     DFS_CONSUMER_STEP(3, 3)
     DFS_CONSUMER_STEP(4, 4 % PD)
     DFS_CONSUMER_STEP(5, 5 % PD)
-    if constexpr (PD != 6) {
-      DFS_CONSUMER_STEP(6, 6 % PD)
-      DFS_CONSUMER_STEP(7, 7 % PD)
-    }
+    DFS_CONSUMER_STEP(6, 6 % PD)
+    DFS_CONSUMER_STEP(7, 7 % PD)
   }
 #undef DFS_CONSUMER_STEP
 
   // W is the A operand and X the B operand, so each 16x16 tile comes out
   // transposed: lane (c, g4) holds output row m = c and the four consecutive
   // columns n = 4*g4 .. 4*g4+3 — one 16-byte store per tile and lane.
+  if constexpr (GATED) {
+    // h = bf16(silu(gate) * up) for features n .. n+3 of row m (one 8-byte store)
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      const int m = m0 + i * 16 + c, n = n0 + wave * 16 + g4 * 4;
+      if (m >= a.M) continue;
+      bf16_t* hrow = (bf16_t*)a.hout + (size_t)m * a.ldy;
+      bf16_t h[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float g = acc[i][0][e], u = acc[i][1][e];
+        h[e] = f2bf(g / (1.f + expf(-g)) * u);
+      }
+      if (n + 3 < a.N) {
+        *(uint2*)(hrow + n) = make_uint2((uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16));
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (n + e < a.N) hrow[n + e] = h[e];
+      }
+    }
+    return;
+  }
   float* Y = a.Y + (size_t)z * a.y_split_stride;
   const bool vec = (a.ldy & 3) == 0 && ((uintptr_t)Y & 15) == 0;
 #pragma unroll
@@ -520,7 +552,44 @@ GemmPlan gemm_plan(int M, int N, int K, int dtype, int force_splits) {
   return best;
 }
 
+// Gated gate|up GEMM: the weight-streaming kernel with paired tiles, no K split
+// (the SwiGLU needs complete sums); 64 features per workgroup.
+GemmPlan gemm_plan_gated(int M, int N, int K, int dtype) {
+  GemmPlan p;
+  p.kind = -1;
+  if (dtype != 1 || M > 128 || K % BK) return p;
+  p.kind = 1;
+  p.nw = 2;
+  p.mt = M <= 32 ? 2 : (M <= 64 ? 4 : 8);
+  p.bm = 16 * p.mt;
+  p.bn = 64;
+  p.splits = 1;
+  p.k_per_split = K;
+  p.pd = 4;
+  p.xd = p.mt == 8 ? 4 : 2;
+  return p;
+}
+
 size_t gemm_partial_elems(const GemmPlan& p, int M, int N) { return (size_t)p.splits * M * N; }
+
+template <int MT, int NW, int PD, int XD>
+hipError_t launch_stream(const GemmArgs& a, dim3 g1, int kps, int mtl, int ntl, hipStream_t s) {
+  if constexpr (NW == 2) {
+    if (a.gated) {
+      if (a.packed)
+        hipLaunchKernelGGL((gemm_stream_bf16<MT, NW, PD, XD, true, true>), g1, dim3(512), 0, s, a, kps, mtl, ntl);
+      else
+        hipLaunchKernelGGL((gemm_stream_bf16<MT, NW, PD, XD, false, true>), g1, dim3(512), 0, s, a, kps, mtl, ntl);
+      return hipGetLastError();
+    }
+  }
+  if (a.gated) return hipErrorInvalidValue;
+  if (a.packed)
+    hipLaunchKernelGGL((gemm_stream_bf16<MT, NW, PD, XD, true, false>), g1, dim3(512), 0, s, a, kps, mtl, ntl);
+  else
+    hipLaunchKernelGGL((gemm_stream_bf16<MT, NW, PD, XD, false, false>), g1, dim3(512), 0, s, a, kps, mtl, ntl);
+  return hipGetLastError();
+}
 
 hipError_t launch_gemm(const GemmArgs& a, const GemmPlan& p, int dtype, hipStream_t s) {
   ProfScope ps("gemm", s);
@@ -535,28 +604,19 @@ hipError_t launch_gemm(const GemmArgs& a, const GemmPlan& p, int dtype, hipStrea
     const int mtl = ceil_div(a.M, p.bm), ntl = ceil_div(a.N, p.bn);
     const dim3 g1(mtl * ntl * p.splits);
 #define DFS_STREAM(MT_, NW_, PD_, XD_)                                                                   \
-  if (p.mt == MT_ && p.nw == NW_ && p.pd == PD_ && p.xd == XD_) {                                         \
-    if (a.packed)                                                                                         \
-      hipLaunchKernelGGL((gemm_stream_bf16<MT_, NW_, PD_, XD_, true>), g1, dim3(512), 0, s, a, kps, mtl, ntl); \
-    else                                                                                                  \
-      hipLaunchKernelGGL((gemm_stream_bf16<MT_, NW_, PD_, XD_, false>), g1, dim3(512), 0, s, a, kps, mtl, ntl); \
-    return hipGetLastError();                                                                             \
-  }
+  if (p.mt == MT_ && p.nw == NW_ && p.pd == PD_ && p.xd == XD_)                                           \
+    return launch_stream<MT_, NW_, PD_, XD_>(a, g1, kps, mtl, ntl, s);
     DFS_STREAM(2, 2, 4, 2)
     DFS_STREAM(2, 1, 4, 2)
     DFS_STREAM(4, 2, 4, 2)
     DFS_STREAM(4, 1, 4, 2)
-    DFS_STREAM(8, 2, 4, 2)
     DFS_STREAM(8, 1, 4, 2)
-    DFS_STREAM(16, 1, 4, 2)
     DFS_STREAM(8, 2, 4, 4)
-    DFS_STREAM(8, 2, 8, 8)
-    DFS_STREAM(8, 1, 8, 8)
-    DFS_STREAM(8, 2, 6, 6)
     DFS_STREAM(16, 1, 4, 4)
 #undef DFS_STREAM
     return hipErrorInvalidValue;
   }
+  if (a.gated) return hipErrorInvalidValue;
 #define DFS_TILED(BM_, BN_)                                                                              \
   if (p.bm == BM_ && p.bn == BN_) {                                                                       \
     if (a.packed)                                                                                         \

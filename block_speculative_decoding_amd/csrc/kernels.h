@@ -27,7 +27,11 @@ struct GemmArgs {
   long ldy = 0;
   size_t y_split_stride = 0;          // elements between split slices of Y
   int accumulate = 0;                 // 1: Y += acc (single split only)
-  int packed = 0;                     // 1: W segments tile-packed (bf16; see pack_tile_offset)
+  int packed = 0;                     // 1: W segments tile-packed (bf16; see packed_matrix_elems)
+  // gated (SwiGLU) output: seg[0] = W_gate, seg[1] = W_up, both [N, K]; the kernel
+  // writes hout[m][n] = bf16(silu(gate) * up) (row stride ldy) instead of Y
+  int gated = 0;
+  void* hout = nullptr;
 };
 
 struct GemmPlan {
@@ -37,6 +41,8 @@ struct GemmPlan {
 };
 
 GemmPlan gemm_plan(int M, int N, int K, int dtype, int force_splits = 0);
+// plan of a gated gate|up GEMM (N = features), or kind < 0 when no gated kernel fits
+GemmPlan gemm_plan_gated(int M, int N, int K, int dtype);
 // Tile-packed bf16 weights: [ceil(N/16)][K/64] tiles of 16 rows x 64 columns,
 // each 2 KB tile stored in matrix-core operand order [ks 0..1][lane 0..63][8]:
 // lane l holds row 16*nt + (l % 16), columns 64*kt + 32*ks + 8*(l / 16) .. +7.
