@@ -15,11 +15,15 @@
 #include "kernels.h"
 
 #include <math.h>
+#ifdef DFS_TUNING
+#include <stdlib.h>
+#endif
 
 namespace dfs {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kAttnTargetUnits = 256;        // context units per launch: one per CU
 
 __device__ __forceinline__ bf16x8 load8(const bf16_t* p) {
   return __builtin_bit_cast(bf16x8, ldg16(p));
@@ -45,12 +49,19 @@ constexpr int kAttnKeys = 64;
 constexpr int kKLd = 128 + 8;              // LDS row of the K tile (bf16 elements)
 constexpr int kVLd = kAttnKeys + 8;        // LDS row of the V^T tile
 
+// Grid: 1-D, the B*nkv*n_ctx_splits context units first and the B*nkv block-key
+// units last, so that the (heavy) context units are dispatched one per CU ahead
+// of the (tiny) block units instead of doubling up on some CUs.
 __global__ __launch_bounds__(256) void attn_bf16_d128(AttnArgs a) {
   constexpr int D = 128, KS = kAttnKeys;
   __shared__ __attribute__((aligned(16))) bf16_t Ks[2][KS * kKLd];
   __shared__ __attribute__((aligned(16))) bf16_t Vs[2][D * kVLd];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, c = lane & 15, g4 = lane >> 4;
-  const int unit = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int pairs = a.B * a.nkv, nctx = pairs * a.n_ctx_splits;
+  const int id = blockIdx.x;
+  const int unit = id < nctx ? id % a.n_ctx_splits : a.n_ctx_splits;
+  const int pair = id < nctx ? id / a.n_ctx_splits : id - nctx;
+  const int g = pair % a.nkv, b = pair / a.nkv;
   const int units = a.n_ctx_splits + 1;
   const size_t bg = (size_t)b * a.nkv + g;
 
@@ -350,7 +361,10 @@ AttnPlan attn_plan(int B, int nkv, int ctx_bound, int dtype) {
     return p;
   }
   const int pairs = B * nkv;
-  int splits = ceil_div(256, pairs);                 // ~256 four-wave workgroups
+  int splits = ceil_div(kAttnTargetUnits, pairs);    // ~one four-wave context unit per CU
+#ifdef DFS_TUNING
+  if (const char* f = getenv("DFS_ATTN_SPLITS")) splits = atoi(f);
+#endif
   const int max_splits = ceil_div(ctx_bound, 256);   // at least 256 keys (4 steps) per unit
   if (splits > max_splits) splits = max_splits;
   if (splits < 1) splits = 1;
@@ -365,7 +379,10 @@ AttnPlan attn_plan(int B, int nkv, int ctx_bound, int dtype) {
 // count actually used never exceeds the target split count).
 int attn_max_units(int B, int nkv, int max_ctx, int dtype) {
   if (dtype != 1) return 1;
-  int splits = ceil_div(256, B * nkv);
+#ifdef DFS_TUNING
+  if (getenv("DFS_ATTN_SPLITS")) return 65;
+#endif
+  int splits = ceil_div(kAttnTargetUnits, B * nkv);
   const int max_splits = ceil_div(max_ctx, 256);
   if (splits > max_splits) splits = max_splits;
   if (splits < 1) splits = 1;
@@ -382,7 +399,7 @@ hipError_t launch_attention(const AttnArgs& a, int dtype, hipStream_t s) {
     hipLaunchKernelGGL(attn_f32, dim3(a.S, a.nq, a.B), dim3(256), 0, s, a);
     return hipGetLastError();
   }
-  dim3 grid(a.n_ctx_splits + 1, a.nkv, a.B);
+  const dim3 grid((unsigned)(a.B * a.nkv * (a.n_ctx_splits + 1)));
   hipLaunchKernelGGL(attn_bf16_d128, grid, dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
