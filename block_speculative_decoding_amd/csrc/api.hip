@@ -14,6 +14,9 @@ namespace {
 
 size_t dtype_size(int dt) { return dt == DFS_BF16 ? 2 : 4; }
 
+// the vocabulary-streaming kernels select among at most 1024 chunks of 4096 tokens
+constexpr int kMaxVocab = 1024 * kChunk;
+
 struct DraftDims {
   int L, H, nq, nkv, d, F, V, nT, S, G, max_ctx, group, R, Rpad;
   int B, nmax, Mc, Mb, Mx, Nqkv;
@@ -240,7 +243,8 @@ int dflash_draft_step(const dfs_drafter_cfg* cfg, const dfs_drafter_weights* wt,
   ma.ctx_bound = ctx_bound;
   ma.theta = cfg->rope_theta;
   DFS_TRY(launch_prep(ma, s));
-  DFS_TRY(launch_embed(dt, wt->embed, last_token, cfg->mask_token_id, d.V, d.H, d.B, d.S, w.resid, s));
+  DFS_TRY(launch_embed(dt, wt->embed, last_token, cfg->mask_token_id, d.V, d.H, d.B, d.S, w.resid, w.meta, ctx_len,
+                       s));
 
   int sp;
   size_t pst;
@@ -375,7 +379,6 @@ int dflash_draft_step(const dfs_drafter_cfg* cfg, const dfs_drafter_weights* wt,
   // 6. LM head on the mask rows -> base logits [B, S-1, V]
   DFS_TRY(run_gemm(w.z, d.H, d.B * d.G, d.V, d.H, wt->lm_head, nullptr, 0, nullptr, 0, base_logits, dt, pk, s,
                    &sp, &pst, 1));
-  DFS_TRY(launch_finish(w.meta, ctx_len, d.B, s));
   return DFS_OK;
 }
 
@@ -394,6 +397,7 @@ int markov_bias_sample(int32_t batch, int32_t n_draft, int32_t vocab, int32_t ra
   if (batch < 1 || n_draft < 1 || vocab < 1 || rank < 0 || !logits || !last_token || !u_draft || !draft_tokens ||
       !workspace)
     return DFS_EINVAL;
+  if (vocab > kMaxVocab) return DFS_EUNSUPPORTED;
   if (!(temperature >= 0.f)) return DFS_EINVAL;
   if (rank > 0 && (!U || !Wt)) return DFS_EINVAL;
   if (rank > 0 && uw_dtype != DFS_F32 && uw_dtype != DFS_BF16 && uw_dtype != DFS_BF16_PACKED) return DFS_EINVAL;
@@ -499,6 +503,7 @@ int spec_verify(int32_t batch, int32_t n_draft, int32_t vocab, const float* draf
   if (batch < 1 || n_draft < 1 || vocab < 1 || !draft_logits || !target_logits || !draft_tokens || !u_accept ||
       !u_final || !out_tokens || !n_accepted || !workspace)
     return DFS_EINVAL;
+  if (vocab > kMaxVocab) return DFS_EUNSUPPORTED;
   if (!(temperature >= 0.f)) return DFS_EINVAL;
   if (workspace_bytes < spec_verify_workspace_size(batch, n_draft, vocab)) return DFS_EWORKSPACE;
   VerifyArgs a;

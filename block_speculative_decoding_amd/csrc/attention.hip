@@ -242,32 +242,50 @@ __global__ __launch_bounds__(256) void attn_bf16_d128(AttnArgs a) {
   }
 }
 
-// Merge the units of one (b, g, row): out = sum_u 2^(m_u - M) O_u / sum_u 2^(m_u - M) l_u
+// Merge the units of one (b, g, row): out = sum_u 2^(m_u - M) O_u / sum_u 2^(m_u - M) l_u.
+// One thread per output element; with up to 8 units every load is issued at
+// once (one memory round trip), otherwise the units are walked in groups of 8.
 template <typename T>
 __global__ __launch_bounds__(128) void attn_combine(AttnArgs a) {
+  constexpr int U = 8;
   const int r = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int units = a.n_ctx_splits + 1;
   const size_t bg = (size_t)b * a.nkv + g;
   const float* ml = a.part_ml + (bg * units * a.Rpad + r) * 2;   // unit u at ml[u * Rpad * 2]
   const size_t ustride = (size_t)a.Rpad * 2;
-  float M = -INFINITY;
-  for (int u = 0; u < units; ++u) M = fmaxf(M, ml[u * ustride]);
-  float den = 0.f;
-  for (int u = 0; u < units; ++u) {
-    const float m = ml[u * ustride];
-    if (m != -INFINITY) den += exp2f(m - M) * ml[u * ustride + 1];
-  }
   const int group = a.nq / a.nkv;
   const int hh = r / a.S, s = r % a.S, h = g * group + hh;
-  const float inv = 1.f / den;
   for (int dd = threadIdx.x; dd < a.d; dd += blockDim.x) {
-    float num = 0.f;
-    for (int u = 0; u < units; ++u) {
-      const float m = ml[u * ustride];
-      if (m != -INFINITY)
-        num += exp2f(m - M) * a.part_o[((bg * units + u) * a.Rpad + r) * a.d + dd];
+    const float* po = a.part_o + (bg * units * a.Rpad + r) * a.d + dd;   // unit u at po[u * Rpad * d]
+    const size_t pstride = (size_t)a.Rpad * a.d;
+    float M = -INFINITY, den = 0.f, num = 0.f;         // running merge over groups of U units
+    for (int u0 = 0; u0 < units; u0 += U) {
+      float m[U], l[U], o[U];
+#pragma unroll
+      for (int i = 0; i < U; ++i) {
+        const int u = min(u0 + i, units - 1);
+        m[i] = ml[u * ustride];
+        l[i] = ml[u * ustride + 1];
+        o[i] = po[u * pstride];
+      }
+      float mg = M;
+#pragma unroll
+      for (int i = 0; i < U; ++i)
+        if (u0 + i < units) mg = fmaxf(mg, m[i]);
+      if (mg == -INFINITY) continue;
+      const float alpha = M == -INFINITY ? 0.f : exp2f(M - mg);
+      den *= alpha;
+      num *= alpha;
+#pragma unroll
+      for (int i = 0; i < U; ++i) {
+        if (u0 + i >= units || m[i] == -INFINITY) continue;
+        const float w = exp2f(m[i] - mg);
+        den += w * l[i];
+        num += w * o[i];
+      }
+      M = mg;
     }
-    Elem<T>::store((T*)a.out, (((size_t)b * a.S + s) * a.nq + h) * a.d + dd, num * inv);
+    Elem<T>::store((T*)a.out, (((size_t)b * a.S + s) * a.nq + h) * a.d + dd, num / den);
   }
 }
 

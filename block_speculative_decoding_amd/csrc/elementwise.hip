@@ -48,18 +48,33 @@ __global__ void prep_kernel(MetaArgs a) {
   a.rope[idx] = make_float2((float)cs, (float)sn);
 }
 
-__global__ void finish_kernel(const int32_t* meta, int32_t* ctx_len, int B) {
-  const int b = blockIdx.x * blockDim.x + threadIdx.x;
-  if (b < B) ctx_len[b] = meta[2 * B + b];
-}
-
 template <typename T>
 __global__ __launch_bounds__(256) void embed_kernel(const T* E, const int32_t* last_token, int mask_id,
-                                                    int V, int H, int S, float* resid) {
+                                                    int V, int H, int S, float* resid, const int32_t* meta,
+                                                    int32_t* ctx_len, int B) {
   const int r = blockIdx.x, b = r / S, s = r % S;
+  if (r == 0)
+    for (int i = threadIdx.x; i < B; i += 256) ctx_len[i] = meta[2 * B + i];
   int tok = s == 0 ? last_token[b] : mask_id;
   tok = tok < 0 ? 0 : (tok >= V ? V - 1 : tok);
-  for (int h = threadIdx.x; h < H; h += 256) resid[(size_t)r * H + h] = Elem<T>::load(E, (size_t)tok * H + h);
+  const T* e = E + (size_t)tok * H;
+  float* x = resid + (size_t)r * H;
+  if (sizeof(T) == 2 && H % 8 == 0) {
+    for (int h = threadIdx.x * 8; h < H; h += 256 * 8) {
+      const uint4 v = ldg16(e + h);
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+      float f[8];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        f[2 * k] = __uint_as_float(w[k] << 16);
+        f[2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
+      }
+      *(float4*)(x + h) = make_float4(f[0], f[1], f[2], f[3]);
+      *(float4*)(x + h + 4) = make_float4(f[4], f[5], f[6], f[7]);
+    }
+  } else {
+    for (int h = threadIdx.x; h < H; h += 256) x[h] = Elem<T>::load(e, h);
+  }
 }
 
 // RMSNorm of one row per workgroup (1024 threads), fused with the reduction of
@@ -260,21 +275,15 @@ hipError_t launch_prep(const MetaArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_finish(const int32_t* meta, int32_t* ctx_len, int B, hipStream_t s) {
-  ProfScope ps("elementwise", s);
-  hipLaunchKernelGGL(finish_kernel, dim3(ceil_div(B, 256)), dim3(256), 0, s, meta, ctx_len, B);
-  return hipGetLastError();
-}
-
 hipError_t launch_embed(int dtype, const void* embed, const int32_t* last_token, int mask_id, int V,
-                        int H, int B, int S, float* resid, hipStream_t s) {
+                        int H, int B, int S, float* resid, const int32_t* meta, int32_t* ctx_len, hipStream_t s) {
   ProfScope ps("elementwise", s);
   if (dtype == 1)
     hipLaunchKernelGGL(embed_kernel<bf16_t>, dim3(B * S), dim3(256), 0, s, (const bf16_t*)embed, last_token,
-                       mask_id, V, H, S, resid);
+                       mask_id, V, H, S, resid, meta, ctx_len, B);
   else
     hipLaunchKernelGGL(embed_kernel<float>, dim3(B * S), dim3(256), 0, s, (const float*)embed, last_token,
-                       mask_id, V, H, S, resid);
+                       mask_id, V, H, S, resid, meta, ctx_len, B);
   return hipGetLastError();
 }
 

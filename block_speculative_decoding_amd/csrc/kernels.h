@@ -90,10 +90,10 @@ struct MetaArgs {
   float theta;
 };
 hipError_t launch_prep(const MetaArgs& a, hipStream_t s);
-hipError_t launch_finish(const int32_t* meta, int32_t* ctx_len, int B, hipStream_t s);
-
+// also advances ctx_len to meta's C_b
 hipError_t launch_embed(int dtype, const void* embed, const int32_t* last_token, int mask_id,
-                        int V, int H, int B, int S, float* resid, hipStream_t s);
+                        int V, int H, int B, int S, float* resid, const int32_t* meta, int32_t* ctx_len,
+                        hipStream_t s);
 
 // out[row_map(r)] = T( RMSNorm( in[r] (+= sum_z part[z][r]) ; gain ) )
 struct NormArgs {

@@ -57,8 +57,6 @@ __global__ __launch_bounds__(256) void pick_kernel(PickArgs a, int nch, bool vec
   __shared__ double redd[4];
   __shared__ float redf[4];
   __shared__ int smi[2];
-  __shared__ double cs_sh[1];
-  __shared__ int cidx_sh[1];
   const int r = blockIdx.x, tid = threadIdx.x;
   const double2* st = a.stats + (size_t)r * nch;
   const float* row = a.x + (size_t)r * a.row_stride;
@@ -89,40 +87,25 @@ __global__ __launch_bounds__(256) void pick_kernel(PickArgs a, int nch, bool vec
   tot = block_sum<256>(tot, redd);
   const double u = a.u[(size_t)r * a.u_stride];
   const double t = u * tot;
-  if (tid == 0) {
-    double before = 0.0;
-    int cstar = -1, lastpos = -1;
-    double before_last = 0.0;
-    for (int c = 0; c < nch; ++c) {
-      const double m = st[c].x;
-      const double w = m == -INFINITY ? 0.0 : st[c].y * exp((m - (double)mx) / T);
-      if (w > 0) {
-        lastpos = c;
-        before_last = before;
-      }
-      if (before + w > t) {
-        cstar = c;
-        break;
-      }
-      before += w;
-    }
-    if (cstar < 0) {
-      cstar = lastpos < 0 ? 0 : lastpos;
-      before = before_last;
-    }
-    cidx_sh[0] = cstar;
-    cs_sh[0] = before;
-  }
-  __syncthreads();
-  const int cstar = cidx_sh[0];
-  const double before = cs_sh[0];
+  double before;
+  const int cstar = select_chunk(
+      nch, t,
+      [&](int c) -> double {
+        const double m = st[c].x;
+        return m == -INFINITY ? 0.0 : st[c].y * exp((m - (double)mx) / T);
+      },
+      &before, redd, smi);
   const float k = kLog2e / a.temperature;
   const float fmx = mx;
-  auto weight = [&](int e) -> double {
-    const float xv = row[e];
-    return xv == -INFINITY ? 0.0 : (double)exp2f((xv - fmx) * k);
-  };
-  int tok = chunk_search(cstar, a.V, before, t, weight, redd, smi);
+  const int tok = chunk_search(
+      cstar, a.V, before, t,
+      [&](int e0, double* w) {
+        float v[kPer];
+        load_run(row, a.V, e0, vec, v);
+#pragma unroll
+        for (int e = 0; e < kPer; ++e) w[e] = v[e] == -INFINITY ? 0.0 : (double)exp2f((v[e] - fmx) * k);
+      },
+      redd, smi);
   if (tid == 0) {
     a.tokens[(size_t)r * a.tok_stride] = tok < 0 ? 0 : tok;
     if (a.row_stats) {

@@ -44,22 +44,73 @@ __device__ __forceinline__ double block_exclusive_scan(double v, double* smem /*
   return off + inc - v;
 }
 
-// Shared by spec_verify: locate the token of an inverse-CDF draw inside one
-// chunk.  weight(e) gives the unnormalised weight of element e (>= 0); `before`
-// is the mass of all earlier chunks and `t` the threshold.  Returns the first
-// element whose running sum exceeds t, else the last element of the chunk with
-// positive weight (rounding), else -1.
-template <typename WeightFn>
-__device__ __forceinline__ int chunk_search(int c, int V, double before, double t, WeightFn weight, double* smem, int* smemi) {
+// Inverse-CDF over chunks, by the whole block: chunk c (c < nch) has mass
+// weight(c) >= 0; finds the first chunk whose running mass (chunks in order)
+// exceeds t, else the last chunk with positive mass (rounding), else chunk 0.
+// Returns the chunk and, in *before, the mass of the chunks ahead of it.  One
+// thread per chunk (a thread takes consecutive chunks when nch > 256) and an
+// fp64 block scan, instead of one thread walking every chunk.
+template <typename ChunkWeight>
+__device__ __forceinline__ int select_chunk(int nch, double t, ChunkWeight weight, double* before, double* smem,
+                                            int* smemi) {
+  const int tid = threadIdx.x;
+  const int per = (nch + 255) / 256, c0 = tid * per;
+  double w[4];                                   // per <= 4: nch <= 1024 chunks (V <= 4M)
+  double loc = 0.0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    w[k] = (k < per && c0 + k < nch) ? weight(c0 + k) : 0.0;
+    loc += w[k];
+  }
+  double total;
+  double run = block_exclusive_scan(loc, smem, &total);
+  int found = 0x7fffffff, last = -1;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    if (found == 0x7fffffff && w[k] > 0.0 && run + w[k] > t) found = c0 + k;
+    if (w[k] > 0.0) last = c0 + k;
+    run += w[k];
+  }
+  __syncthreads();
+  if (tid == 0) {
+    smemi[0] = 0x7fffffff;
+    smemi[1] = -1;
+  }
+  __syncthreads();
+  if (found != 0x7fffffff) atomicMin(&smemi[0], found);
+  if (last >= 0) atomicMax(&smemi[1], last);
+  __syncthreads();
+  const int pick = smemi[0] != 0x7fffffff ? smemi[0] : (smemi[1] >= 0 ? smemi[1] : 0);
+  // the owner of the picked chunk publishes its prefix mass
+  __syncthreads();
+  if (pick >= c0 && pick < c0 + per) {
+    double r = 0.0;
+    for (int k = 0; k < 4; ++k)
+      if (k < per && c0 + k < pick) r += w[k];
+    smem[0] = run - loc + r;   // exclusive prefix of this thread + its chunks before `pick`
+  }
+  __syncthreads();
+  *before = smem[0];
+  __syncthreads();
+  return pick;
+}
+
+// Locate the token of an inverse-CDF draw inside one chunk (pick and verify).
+// weights16(e0, w) fills the unnormalised weights (>= 0, 0 past V) of the 16
+// consecutive elements e0 .. e0+15 a thread owns; `before` is the mass of all
+// earlier chunks and `t` the threshold.  Returns the first element whose running
+// sum exceeds t, else the last element of the chunk with positive weight
+// (rounding), else -1.
+template <typename Weights16>
+__device__ __forceinline__ int chunk_search(int c, int V, double before, double t, Weights16 weights16, double* smem,
+                                            int* smemi) {
   const int tid = threadIdx.x;
   const int e0 = c * kChunk + tid * kPer;
   double w[kPer];
+  weights16(e0, w);
   double loc = 0.0;
 #pragma unroll
-  for (int e = 0; e < kPer; ++e) {
-    w[e] = e0 + e < V ? weight(e0 + e) : 0.0;
-    loc += w[e];
-  }
+  for (int e = 0; e < kPer; ++e) loc += w[e];
   double total;
   double run = before + block_exclusive_scan(loc, smem, &total);
   int found = 0x7fffffff, last_pos = -1;

@@ -110,7 +110,7 @@ __global__ __launch_bounds__(64) void decide_kernel(VerifyArgs a, int nch) {
 }
 
 // fp64 exp-sums over one chunk of the target and draft rows at the rejection
-__global__ __launch_bounds__(256) void reject_sums_kernel(VerifyArgs a, int nch) {
+__global__ __launch_bounds__(256) void reject_sums_kernel(VerifyArgs a, int nch, bool vec) {
   __shared__ double red[4];
   const int c = blockIdx.x % nch, b = blockIdx.x / nch, tid = threadIdx.x;
   const int i = a.state[b];
@@ -119,136 +119,120 @@ __global__ __launch_bounds__(256) void reject_sums_kernel(VerifyArgs a, int nch)
   const double Mp = a.rowinfo[b * 4], Mq = a.rowinfo[b * 4 + 2];
   const float* prow = a.p + ((size_t)b * (a.G + 1) + i) * a.V;
   const float* qrow = a.q + ((size_t)b * a.G + i) * a.V;
-  double sp = 0.0, sq = 0.0;
   const int e0 = c * kChunk + tid * kPer;
-  for (int e = e0; e < min(e0 + kPer, a.V); ++e) {
-    const float xp = prow[e], xq = qrow[e];
-    if (xp != -INFINITY) sp += exp(((double)xp - Mp) / T);
-    if (xq != -INFINITY) sq += exp(((double)xq - Mq) / T);
+  float vp[kPer], vq[kPer];
+  load_run(prow, a.V, e0, vec, vp);                  // -inf past V: no mass
+  load_run(qrow, a.V, e0, vec, vq);
+  double sp = 0.0, sq = 0.0;
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) {
+    if (vp[e] != -INFINITY) sp += exp(((double)vp[e] - Mp) / T);
+    if (vq[e] != -INFINITY) sq += exp(((double)vq[e] - Mq) / T);
   }
   sp = block_sum<256>(sp, red);
   sq = block_sum<256>(sq, red);
   if (tid == 0) a.sums[(size_t)b * nch + c] = make_double2(sp, sq);
 }
 
-struct ResidualWeight {
-  const float* prow;
-  const float* qrow;
-  double Mp, Mq, Sp, Sq, T;
-  __device__ double operator()(int e) const {
-    const float xp = prow[e], xq = qrow[e];
-    const double p = xp == -INFINITY ? 0.0 : exp(((double)xp - Mp) / T) / Sp;
-    const double q = xq == -INFINITY ? 0.0 : exp(((double)xq - Mq) / T) / Sq;
-    return p > q ? p - q : 0.0;
+// max(0, p - q) with p, q normalised in fp64, for the 16 elements e0 .. e0+15
+__device__ __forceinline__ void residual16(const float* prow, const float* qrow, int V, int e0, bool vec, double Mp,
+                                           double Mq, double Sp, double Sq, double T, double* w) {
+  float vp[kPer], vq[kPer];
+  load_run(prow, V, e0, vec, vp);
+  load_run(qrow, V, e0, vec, vq);
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) {
+    const double p = vp[e] == -INFINITY ? 0.0 : exp(((double)vp[e] - Mp) / T) / Sp;
+    const double q = vq[e] == -INFINITY ? 0.0 : exp(((double)vq[e] - Mq) / T) / Sq;
+    w[e] = p > q ? p - q : 0.0;
   }
-};
+}
 
-__device__ __forceinline__ void row_sums(const VerifyArgs& a, int b, int nch, double* Sp, double* Sq) {
+// row totals (Sp, Sq) of the rejected position: block sum of the chunk sums
+__device__ __forceinline__ void row_sums(const VerifyArgs& a, int b, int nch, double* Sp, double* Sq, double* red) {
   double sp = 0.0, sq = 0.0;
-  for (int c = 0; c < nch; ++c) {
+  for (int c = threadIdx.x; c < nch; c += 256) {
     sp += a.sums[(size_t)b * nch + c].x;
     sq += a.sums[(size_t)b * nch + c].y;
   }
-  *Sp = sp;
-  *Sq = sq;
+  *Sp = block_sum<256>(sp, red);
+  *Sq = block_sum<256>(sq, red);
 }
 
-__global__ __launch_bounds__(256) void residual_kernel(VerifyArgs a, int nch) {
+__global__ __launch_bounds__(256) void residual_kernel(VerifyArgs a, int nch, bool vec) {
   __shared__ double red[4];
   const int c = blockIdx.x % nch, b = blockIdx.x / nch, tid = threadIdx.x;
   const int i = a.state[b];
   if (i >= a.G) return;
-  ResidualWeight w;
-  w.prow = a.p + ((size_t)b * (a.G + 1) + i) * a.V;
-  w.qrow = a.q + ((size_t)b * a.G + i) * a.V;
-  w.Mp = a.rowinfo[b * 4];
-  w.Mq = a.rowinfo[b * 4 + 2];
-  w.T = a.temperature;
-  row_sums(a, b, nch, &w.Sp, &w.Sq);
+  double Sp, Sq;
+  row_sums(a, b, nch, &Sp, &Sq, red);
+  double w[kPer];
+  residual16(a.p + ((size_t)b * (a.G + 1) + i) * a.V, a.q + ((size_t)b * a.G + i) * a.V, a.V,
+             c * kChunk + tid * kPer, vec, a.rowinfo[b * 4], a.rowinfo[b * 4 + 2], Sp, Sq, a.temperature, w);
   double s = 0.0;
-  const int e0 = c * kChunk + tid * kPer;
-  for (int e = e0; e < min(e0 + kPer, a.V); ++e) s += w(e);
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) s += w[e];
   s = block_sum<256>(s, red);
   if (tid == 0) a.r_chunk[(size_t)b * nch + c] = s;
 }
 
-struct TargetWeight {
-  const float* row;
-  float M, k;
-  __device__ double operator()(int e) const {
-    const float x = row[e];
-    return x == -INFINITY ? 0.0 : (double)exp2f((x - M) * k);
-  }
-};
-
-__global__ __launch_bounds__(256) void final_kernel(VerifyArgs a, int nch) {
+// The one draw of a row: from the residual at the rejection (from p there when
+// the residual has no mass), or the bonus token from p_{G+1}.
+__global__ __launch_bounds__(256) void final_kernel(VerifyArgs a, int nch, bool vec) {
   __shared__ double red[4];
+  __shared__ float redf[4];
   __shared__ int smi[2];
-  __shared__ double before_sh;
-  __shared__ int c_sh, use_resid_sh;
-  __shared__ double t_sh;
   const int b = blockIdx.x, tid = threadIdx.x;
   const int G = a.G;
   const int i = a.state[b];
   const double T = a.temperature;
   const double u = a.u_final[b];
-  if (tid == 0) {
-    // residual mass per chunk, or target row i (bonus: row G) chunk masses
-    double W = 0.0;
-    if (i < G)
-      for (int c = 0; c < nch; ++c) W += a.r_chunk[(size_t)b * nch + c];
-    const bool use_resid = i < G && W > 0.0;
-    const double2* pst = a.p_chunk + ((size_t)b * (G + 1) + i) * nch;
-    double Mp = -INFINITY;
-    if (!use_resid) {
-      for (int c = 0; c < nch; ++c) Mp = fmax(Mp, pst[c].x);
-      W = 0.0;
-      for (int c = 0; c < nch; ++c)
-        if (pst[c].x != -INFINITY) W += pst[c].y * exp((pst[c].x - Mp) / T);
-    }
-    const double t = u * W;
-    double before = 0.0, before_last = 0.0;
-    int cstar = -1, lastpos = -1;
-    for (int c = 0; c < nch; ++c) {
-      const double w = use_resid ? a.r_chunk[(size_t)b * nch + c]
-                                 : (pst[c].x == -INFINITY ? 0.0 : pst[c].y * exp((pst[c].x - Mp) / T));
-      if (w > 0) {
-        lastpos = c;
-        before_last = before;
-      }
-      if (before + w > t) {
-        cstar = c;
-        break;
-      }
-      before += w;
-    }
-    if (cstar < 0) {
-      cstar = lastpos < 0 ? 0 : lastpos;
-      before = before_last;
-    }
-    c_sh = cstar;
-    before_sh = before;
-    use_resid_sh = use_resid;
-    t_sh = t;
-    if (!use_resid) a.rowinfo[b * 4] = Mp;    // exact row max for the target-row draw
+  const double2* pst = a.p_chunk + ((size_t)b * (G + 1) + i) * nch;
+  double W = 0.0;
+  if (i < G) {
+    for (int c = tid; c < nch; c += 256) W += a.r_chunk[(size_t)b * nch + c];
+    W = block_sum<256>(W, red);
   }
-  __syncthreads();
+  const bool use_resid = i < G && W > 0.0;
+  float Mp = -INFINITY;
+  if (!use_resid) {                                  // target row i (bonus: row G) from its chunk statistics
+    for (int c = tid; c < nch; c += 256) Mp = fmaxf(Mp, (float)pst[c].x);
+    Mp = block_max<256>(Mp, redf);
+    W = 0.0;
+    for (int c = tid; c < nch; c += 256)
+      if (pst[c].x != -INFINITY) W += pst[c].y * exp((pst[c].x - (double)Mp) / T);
+    W = block_sum<256>(W, red);
+  }
+  const double t = u * W;
+  double before;
+  const int cstar = select_chunk(
+      nch, t,
+      [&](int c) -> double {
+        if (use_resid) return a.r_chunk[(size_t)b * nch + c];
+        return pst[c].x == -INFINITY ? 0.0 : pst[c].y * exp((pst[c].x - (double)Mp) / T);
+      },
+      &before, red, smi);
+  const float* prow = a.p + ((size_t)b * (G + 1) + i) * a.V;
   int tok;
-  if (use_resid_sh) {
-    ResidualWeight w;
-    w.prow = a.p + ((size_t)b * (G + 1) + i) * a.V;
-    w.qrow = a.q + ((size_t)b * G + i) * a.V;
-    w.Mp = a.rowinfo[b * 4];
-    w.Mq = a.rowinfo[b * 4 + 2];
-    w.T = T;
-    row_sums(a, b, nch, &w.Sp, &w.Sq);
-    tok = chunk_search(c_sh, a.V, before_sh, t_sh, w, red, smi);
+  if (use_resid) {
+    double Sp, Sq;
+    row_sums(a, b, nch, &Sp, &Sq, red);
+    const float* qrow = a.q + ((size_t)b * G + i) * a.V;
+    const double Mpr = a.rowinfo[b * 4], Mq = a.rowinfo[b * 4 + 2];
+    tok = chunk_search(
+        cstar, a.V, before, t,
+        [&](int e0, double* w) { residual16(prow, qrow, a.V, e0, vec, Mpr, Mq, Sp, Sq, T, w); }, red, smi);
   } else {
-    TargetWeight w;
-    w.row = a.p + ((size_t)b * (G + 1) + i) * a.V;
-    w.M = (float)a.rowinfo[b * 4];
-    w.k = kLog2e / a.temperature;
-    tok = chunk_search(c_sh, a.V, before_sh, t_sh, w, red, smi);
+    const float k = kLog2e / a.temperature;
+    tok = chunk_search(
+        cstar, a.V, before, t,
+        [&](int e0, double* w) {
+          float v[kPer];
+          load_run(prow, a.V, e0, vec, v);
+#pragma unroll
+          for (int e = 0; e < kPer; ++e) w[e] = v[e] == -INFINITY ? 0.0 : (double)exp2f((v[e] - Mp) * k);
+        },
+        red, smi);
   }
   if (tid == 0) a.out_tokens[(size_t)b * (G + 1) + i] = tok < 0 ? 0 : tok;
 }
@@ -268,11 +252,12 @@ hipError_t launch_verify(const VerifyArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(decide_kernel, dim3(a.B), dim3(64), 0, s, a, nch);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (a.temperature == 0.f) return hipSuccess;
-  hipLaunchKernelGGL(reject_sums_kernel, dim3(nch * a.B), dim3(256), 0, s, a, nch);
+  const bool vec = (a.V & 3) == 0 && ((uintptr_t)a.p & 15) == 0 && ((uintptr_t)a.q & 15) == 0;
+  hipLaunchKernelGGL(reject_sums_kernel, dim3(nch * a.B), dim3(256), 0, s, a, nch, vec);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(residual_kernel, dim3(nch * a.B), dim3(256), 0, s, a, nch);
+  hipLaunchKernelGGL(residual_kernel, dim3(nch * a.B), dim3(256), 0, s, a, nch, vec);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(final_kernel, dim3(a.B), dim3(256), 0, s, a, nch);
+  hipLaunchKernelGGL(final_kernel, dim3(a.B), dim3(256), 0, s, a, nch, vec);
   return hipGetLastError();
 }
 

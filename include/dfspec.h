@@ -186,7 +186,8 @@ size_t markov_bias_sample_workspace_size(int32_t batch, int32_t n_draft, int32_t
  * row_stats   [B, gamma, 2] fp64 out, may be NULL: (max, sum exp((x - max)/T))
  *             of each final row (T == 0: (max, 1)); spec_verify can reuse them.
  *
- * DFS_EUNSUPPORTED for a bf16 head unless rank is a multiple of 64.
+ * DFS_EUNSUPPORTED for a bf16 head unless rank is a multiple of 64, and for
+ * vocab > 4194304.
  */
 int markov_bias_sample(int32_t batch, int32_t n_draft, int32_t vocab, int32_t rank,
                        float* logits, const void* U, const void* Wt, int32_t uw_dtype,
@@ -216,6 +217,8 @@ size_t spec_verify_workspace_size(int32_t batch, int32_t n_draft, int32_t vocab)
  * out_tokens     [B, gamma+1] int32 out: accepted drafts, the correction or bonus
  *                token, then -1.
  * n_accepted     [B] int32 out, in [0, gamma]; the cycle yields n_accepted + 1 tokens.
+ *
+ * DFS_EUNSUPPORTED for vocab > 4194304.
  */
 int spec_verify(int32_t batch, int32_t n_draft, int32_t vocab, const float* draft_logits,
                 const float* target_logits, const int32_t* draft_tokens, const float* u_accept,
