@@ -36,10 +36,13 @@ def algorithmic_bytes(w):
     Mb, Mc = B * S, B * S
     per_layer_w = (nq * d * H + 2 * nkv * d * H + H * nq * d + 3 * F * H) * es
     gemm_w = L * per_layer_w + (H * nT * H + V * H) * es
-    # activations in/out of every GEMM (X read once per launch, fp32 result written once)
+    # activations in/out of every GEMM (X read once per launch, fp32 result written once;
+    # the gate|up GEMM writes the bf16 SwiGLU product when its gated form applies)
+    gated = w.dtype == "bf16" and Mb <= 128
+    gateup_out = Mb * F * es if gated else Mb * 2 * F * 4
     gemm_act = (Mc * nT * H * es + Mc * H * 4
                 + L * ((Mc + Mb) * H * es + (Mc + Mb) * (nq + 2 * nkv) * d * 4
-                       + Mb * nq * d * es + Mb * H * 4 + Mb * H * es + Mb * 2 * F * 4
+                       + Mb * nq * d * es + Mb * H * 4 + Mb * H * es + gateup_out
                        + Mb * F * es + Mb * H * 4)
                 + B * G * H * es + B * G * V * 4)
     attn = L * (B * nkv * (C + S) * d * 2 * es + Mb * nq * d * es * 2)
@@ -189,6 +192,63 @@ def cpu_baseline(w, step, budget_s=20.0):
                       f"{cores} host cores visible"}
 
 
+# ---------------------------------------------------------------- rocprofv3 summaries
+
+GEMM_SOURCES = ["block_speculative_decoding_amd/csrc/gemm.hip", "block_speculative_decoding_amd/csrc/kernels.h",
+                "block_speculative_decoding_amd/csrc/common.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_stream_C1_hbm_traffic.txt")
+
+
+def gemm_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic():
+    """HBM bytes per GEMM launch recorded with the PMC counters, if the GEMM
+    sources still hash to the value recorded next to them (else None)."""
+    try:
+        kv = dict(l.split(":", 1) for l in open(TRAFFIC_FILE).read().splitlines() if ":" in l and not l.startswith(" "))
+        if kv.get("source_sha256", "").strip() != gemm_source_hash():
+            return None
+        return float(kv["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def _short(name):
+    import re
+    return re.sub(r"\(.*", "", name.replace("(anonymous namespace)::", "").replace("void ", ""))
+
+
+def summarize_rocprof(d, steps):
+    """Print the per-kernel table of a rocprofv3 --stats run, or the per-kernel
+    average counters of a --pmc run, found under directory d."""
+    import csv
+    import glob
+    stats = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)
+    pmc = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if stats:
+        rows = list(csv.DictReader(open(stats[0])))
+        print(f"{'kernel':60s} {'calls':>6s} {'calls/step':>10s} {'total us':>10s} {'avg us':>8s} {'us/step':>8s}")
+        for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+            n, tot = int(r["Calls"]), float(r["TotalDurationNs"]) / 1e3
+            print(f"{_short(r['Name'])[:60]:60s} {n:6d} {n / steps:10.2f} {tot:10.1f} {tot / n:8.2f} {tot / steps:8.1f}")
+    for f in pmc:
+        agg = {}
+        for r in csv.DictReader(open(f)):
+            k = (_short(r["Kernel_Name"])[:60], r["Counter_Name"])
+            a = agg.setdefault(k, [0, 0.0])
+            a[0] += 1
+            a[1] += float(r["Counter_Value"])
+        print(f"{'kernel':60s} {'counter':12s} {'dispatches':>10s} {'avg KiB/dispatch':>17s}")
+        for (k, c), (n, v) in sorted(agg.items(), key=lambda x: -x[1][1]):
+            print(f"{k:60s} {c:12s} {n:10d} {v / n:17.1f}")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -199,7 +259,12 @@ def main():
     ap.add_argument("--no-roofline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (reference for HBM byte counters)")
+    ap.add_argument("--summarize-rocprof", metavar="DIR",
+                    help="print the kernel table / counter averages of a rocprofv3 output directory and exit")
     args = ap.parse_args()
+    if args.summarize_rocprof:
+        summarize_rocprof(args.summarize_rocprof, args.steps + args.warmup)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build measures one GPU only; --gpus must be 1"}))
         sys.exit(2)
@@ -238,9 +303,11 @@ def main():
         launches_per_step = n / args.steps
         gemm_bytes_per_launch = ab["gemm"] / launches_per_step
         achieved = gemm_bytes_per_launch / (per_launch_ms * 1e-3) / 1e9
-        res["roofline"] = {"kernel": "gemm_bf16_nt (all drafter GEMM launches)", "bound": "hbm",
+        res["roofline"] = {"kernel": "gemm_stream_bf16 (all drafter GEMM launches)", "bound": "hbm",
                            "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                           "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                           "frac": achieved / HBM_PEAK_GBPS,
+                           "traffic": recorded_traffic() if w.name == WORKLOADS["C1"].name else None,
+                           "algorithmic_bytes_per_launch": gemm_bytes_per_launch,
                            "launches_per_step": launches_per_step, "avg_launch_us": per_launch_ms * 1e3,
                            "ms_per_step_profiled": ms_p}
         groups = {}
