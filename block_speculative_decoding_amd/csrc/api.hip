@@ -124,9 +124,10 @@ DraftWs carve_draft(void* base, const DraftDims& d, int dtype) {
 
 hipError_t run_gemm(const void* X, int ldx, int M, int N, int K, const void* w0, const void* w1, int n1,
                     const void* w2, int n2, float* Y, int dtype, int packed, hipStream_t s, int* splits_out,
-                    size_t* stride_out, int force_splits = 0, long ldy = 0) {
+                    size_t* stride_out, int force_splits = 0, long ldy = 0, int nt_store = 0) {
   GemmArgs a;
   a.packed = packed;
+  a.nt_store = nt_store;
   a.X = X;
   a.ldx = ldx;
   a.x_rows = M;
@@ -377,8 +378,9 @@ int dflash_draft_step(const dfs_drafter_cfg* cfg, const dfs_drafter_weights* wt,
     }
   }
   // 6. LM head on the mask rows -> base logits [B, S-1, V]
+  // (the logits are not re-read before the sampler's pass: non-temporal stores)
   DFS_TRY(run_gemm(w.z, d.H, d.B * d.G, d.V, d.H, wt->lm_head, nullptr, 0, nullptr, 0, base_logits, dt, pk, s,
-                   &sp, &pst, 1));
+                   &sp, &pst, 1, 0, 1));
   return DFS_OK;
 }
 
@@ -503,7 +505,7 @@ int spec_verify(int32_t batch, int32_t n_draft, int32_t vocab, const float* draf
   if (batch < 1 || n_draft < 1 || vocab < 1 || !draft_logits || !target_logits || !draft_tokens || !u_accept ||
       !u_final || !out_tokens || !n_accepted || !workspace)
     return DFS_EINVAL;
-  if (vocab > kMaxVocab) return DFS_EUNSUPPORTED;
+  if (vocab > kMaxVocab || n_draft > 64) return DFS_EUNSUPPORTED;   // one decide slot per position
   if (!(temperature >= 0.f)) return DFS_EINVAL;
   if (workspace_bytes < spec_verify_workspace_size(batch, n_draft, vocab)) return DFS_EWORKSPACE;
   VerifyArgs a;

@@ -381,7 +381,8 @@ void gemm_stream_bf16(GemmArgs a, int k_per_split, int mtiles, int ntiles) {
       if (vec && n + 3 < a.N) {
         f32x4 v = acc[i][j];
         if (a.accumulate) v += *(const f32x4*)(yrow + n);
-        *(f32x4*)(yrow + n) = v;
+        if (a.nt_store) __builtin_nontemporal_store(v, (f32x4*)(yrow + n));
+        else *(f32x4*)(yrow + n) = v;
       } else {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {

@@ -32,6 +32,7 @@ struct GemmArgs {
   // writes hout[m][n] = bf16(silu(gate) * up) (row stride ldy) instead of Y
   int gated = 0;
   void* hout = nullptr;
+  int nt_store = 0;                   // 1: results written with non-temporal stores (not re-read soon)
 };
 
 struct GemmPlan {

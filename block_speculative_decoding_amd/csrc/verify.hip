@@ -9,8 +9,9 @@
 // Launch sequence (all on the caller's stream):
 //   1. chunk statistics of every target row (and of the draft rows when the
 //      sampler's row statistics are not supplied)            — streams [B, G+1, V]
-//   2. decide: one wave per batch row walks i = 1..G, forming p(d_i) and q(d_i)
-//      in fp64 from the row statistics, and stops at the first rejection
+//   2. decide: one workgroup per batch row, one wave per position, forms
+//      p_i(d_i) and q_i(d_i) in fp64 for every position at once and keeps the
+//      prefix up to the first rejection
 //   3. fp64 exp-sums of the target and draft rows at each rejection (only B rows)
 //   4. residual mass max(0, p - q) per chunk, with p and q normalised by (3)
 //      (fp64 throughout: p - q cancels when the two are close)
@@ -47,29 +48,39 @@ __device__ __forceinline__ int argmax_chunks_wave(const double2* st, int nch) {
   return best == -INFINITY ? 0 : (int)(-best);
 }
 
-__global__ __launch_bounds__(64) void decide_kernel(VerifyArgs a, int nch) {
-  const int b = blockIdx.x, lane = threadIdx.x;
+// One workgroup (16 waves) per batch row; wave w takes positions w, w+16, ...
+// (position G is the bonus row).  Per position: the target row's exact (max,
+// sum) from its chunk statistics, the draft row's from the sampler (or its
+// chunks), p(d) / q(d) in fp64, and the accept test; then the prefix.
+constexpr int kDecideWaves = 16;
+__global__ __launch_bounds__(1024) void decide_kernel(VerifyArgs a, int nch) {
+  __shared__ int acc_sh[65];
+  __shared__ double info_sh[65][4];
+  __shared__ int arg_sh[65];
+  const int b = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int G = a.G, V = a.V;
   const double T = a.temperature;
-  int acc_end = G;
-  double info[4] = {0, 0, 0, 0};
-  for (int i = 0; i < G; ++i) {
+  for (int i = wave; i <= G; i += kDecideWaves) {
     const double2* pst = a.p_chunk + ((size_t)b * (G + 1) + i) * nch;
-    const int d = a.drafts[(size_t)b * G + i];
-    bool accept;
     if (a.temperature == 0.f) {
       const int arg = argmax_chunks_wave(pst, nch);
-      accept = d == arg;
-      if (!accept && lane == 0) a.out_tokens[(size_t)b * (G + 1) + i] = arg;
-    } else {
-      double Mp, Sp, Mq, Sq;
-      combine_chunks_wave(pst, nch, T, &Mp, &Sp);
+      if (lane == 0) {
+        arg_sh[i] = arg;
+        acc_sh[i] = i < G && a.drafts[(size_t)b * G + i] == arg;
+      }
+      continue;
+    }
+    double Mp, Sp, Mq = 0.0, Sq = 0.0;
+    combine_chunks_wave(pst, nch, T, &Mp, &Sp);
+    bool accept = false;
+    if (i < G) {
       if (a.q_stats) {
         Mq = a.q_stats[((size_t)b * G + i) * 2];
         Sq = a.q_stats[((size_t)b * G + i) * 2 + 1];
       } else {
         combine_chunks_wave(a.q_chunk + ((size_t)b * G + i) * nch, nch, T, &Mq, &Sq);
       }
+      const int d = a.drafts[(size_t)b * G + i];
       double r = 0.0;
       if (d >= 0 && d < V) {
         const double xp = a.p[((size_t)b * (G + 1) + i) * V + d];
@@ -79,34 +90,31 @@ __global__ __launch_bounds__(64) void decide_kernel(VerifyArgs a, int nch) {
         r = qd > 0.0 ? pd / qd : (pd > 0.0 ? INFINITY : 0.0);
       }
       accept = (double)a.u_accept[(size_t)b * G + i] < r;
-      info[0] = Mp;
-      info[1] = Sp;
-      info[2] = Mq;
-      info[3] = Sq;
     }
-    if (accept) {
-      if (lane == 0) a.out_tokens[(size_t)b * (G + 1) + i] = d;
-    } else {
+    if (lane == 0) {
+      acc_sh[i] = accept;
+      info_sh[i][0] = Mp;
+      info_sh[i][1] = Sp;
+      info_sh[i][2] = Mq;
+      info_sh[i][3] = Sq;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x != 0) return;
+  int acc_end = G;
+  for (int i = 0; i < G; ++i)
+    if (!acc_sh[i]) {
       acc_end = i;
       break;
     }
-  }
-  if (acc_end == G) {
-    const double2* pst = a.p_chunk + ((size_t)b * (G + 1) + G) * nch;
-    if (a.temperature == 0.f) {
-      const int arg = argmax_chunks_wave(pst, nch);
-      if (lane == 0) a.out_tokens[(size_t)b * (G + 1) + G] = arg;
-    } else {
-      combine_chunks_wave(pst, nch, T, &info[0], &info[1]);
-    }
-  }
-  if (lane == 0) {
-    a.state[b] = acc_end;
-    a.n_accepted[b] = acc_end;
-    for (int j = acc_end + 1; j <= G; ++j) a.out_tokens[(size_t)b * (G + 1) + j] = -1;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) a.rowinfo[b * 4 + k] = info[k];
-  }
+  int32_t* out = a.out_tokens + (size_t)b * (G + 1);
+  for (int i = 0; i < acc_end; ++i) out[i] = a.drafts[(size_t)b * G + i];
+  if (a.temperature == 0.f) out[acc_end] = arg_sh[acc_end];   // correction or bonus: the target argmax
+  for (int j = acc_end + 1; j <= G; ++j) out[j] = -1;
+  a.state[b] = acc_end;
+  a.n_accepted[b] = acc_end;
+  if (a.temperature != 0.f)
+    for (int k = 0; k < 4; ++k) a.rowinfo[b * 4 + k] = info_sh[acc_end][k];
 }
 
 // fp64 exp-sums over one chunk of the target and draft rows at the rejection
@@ -123,11 +131,12 @@ __global__ __launch_bounds__(256) void reject_sums_kernel(VerifyArgs a, int nch,
   float vp[kPer], vq[kPer];
   load_run(prow, a.V, e0, vec, vp);                  // -inf past V: no mass
   load_run(qrow, a.V, e0, vec, vq);
+  const double invT = 1.0 / T;
   double sp = 0.0, sq = 0.0;
 #pragma unroll
   for (int e = 0; e < kPer; ++e) {
-    if (vp[e] != -INFINITY) sp += exp(((double)vp[e] - Mp) / T);
-    if (vq[e] != -INFINITY) sq += exp(((double)vq[e] - Mq) / T);
+    if (vp[e] != -INFINITY) sp += exp(((double)vp[e] - Mp) * invT);
+    if (vq[e] != -INFINITY) sq += exp(((double)vq[e] - Mq) * invT);
   }
   sp = block_sum<256>(sp, red);
   sq = block_sum<256>(sq, red);
@@ -140,10 +149,11 @@ __device__ __forceinline__ void residual16(const float* prow, const float* qrow,
   float vp[kPer], vq[kPer];
   load_run(prow, V, e0, vec, vp);
   load_run(qrow, V, e0, vec, vq);
+  const double invT = 1.0 / T, invSp = 1.0 / Sp, invSq = 1.0 / Sq;
 #pragma unroll
   for (int e = 0; e < kPer; ++e) {
-    const double p = vp[e] == -INFINITY ? 0.0 : exp(((double)vp[e] - Mp) / T) / Sp;
-    const double q = vq[e] == -INFINITY ? 0.0 : exp(((double)vq[e] - Mq) / T) / Sq;
+    const double p = vp[e] == -INFINITY ? 0.0 : exp(((double)vp[e] - Mp) * invT) * invSp;
+    const double q = vq[e] == -INFINITY ? 0.0 : exp(((double)vq[e] - Mq) * invT) * invSq;
     w[e] = p > q ? p - q : 0.0;
   }
 }
@@ -249,7 +259,7 @@ hipError_t launch_verify(const VerifyArgs& a, hipStream_t s) {
     e = launch_chunk_stats(a.q, a.V, a.B * a.G, a.V, a.temperature, const_cast<double2*>(a.q_chunk), s);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(decide_kernel, dim3(a.B), dim3(64), 0, s, a, nch);
+  hipLaunchKernelGGL(decide_kernel, dim3(a.B), dim3(64 * kDecideWaves), 0, s, a, nch);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (a.temperature == 0.f) return hipSuccess;
   const bool vec = (a.V & 3) == 0 && ((uintptr_t)a.p & 15) == 0 && ((uintptr_t)a.q & 15) == 0;

@@ -218,7 +218,7 @@ size_t spec_verify_workspace_size(int32_t batch, int32_t n_draft, int32_t vocab)
  *                token, then -1.
  * n_accepted     [B] int32 out, in [0, gamma]; the cycle yields n_accepted + 1 tokens.
  *
- * DFS_EUNSUPPORTED for vocab > 4194304.
+ * DFS_EUNSUPPORTED for vocab > 4194304 or n_draft > 64.
  */
 int spec_verify(int32_t batch, int32_t n_draft, int32_t vocab, const float* draft_logits,
                 const float* target_logits, const int32_t* draft_tokens, const float* u_accept,
