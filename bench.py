@@ -54,7 +54,9 @@ def algorithmic_bytes(w):
 
 
 class Step:
-    def __init__(self, w, seed=0):
+    def __init__(self, w, seed=0, reuse=None):
+        """reuse: another Step of a workload with the same drafter weights (block
+        or Markov-head sweeps), whose host and device weights are shared."""
         import torch
         from block_speculative_decoding_amd import dfspec as D
         self.D, self.torch, self.w = D, torch, w
@@ -67,11 +69,14 @@ class Step:
                 return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
             return torch.from_numpy(a).to(dev)
 
-        self.np_weights = inputs.drafter_weights(w, seed)
         self.cfg = D.DrafterConfig.of(w)
-        # bf16 matrices in the tile-packed layout the matrix-core kernels stream (packed once here)
-        self.wdev = D.DrafterWeights(self.cfg, {k: up(v, w.dtype) for k, v in self.np_weights.items()},
-                                     packed=w.dtype == "bf16")
+        if reuse is not None:
+            self.np_weights, self.wdev = reuse.np_weights, reuse.wdev   # the block is not part of them
+        else:
+            self.np_weights = inputs.drafter_weights(w, seed)
+            # bf16 matrices in the tile-packed layout the matrix-core kernels stream (packed once here)
+            self.wdev = D.DrafterWeights(self.cfg, {k: up(v, w.dtype) for k, v in self.np_weights.items()},
+                                         packed=w.dtype == "bf16")
         step = inputs.step_inputs(w, seed)
         self.np_step = step
         kc, vc = inputs.cache_prefix(w, seed, step["ctx_len"])
@@ -249,6 +254,35 @@ def summarize_rocprof(d, steps):
             print(f"{k:60s} {c:12s} {n:10d} {v / n:17.1f}")
 
 
+def sweeps(steps, warmup):
+    """Secondary measurements: draft time vs block size (the block drafter's cost
+    should be nearly flat in the block size) and the Markov head's share of the
+    step at draft lengths 4 and 15 (the pages quote a 0.2-1.3 % latency cost for
+    going from 4 to 16 draft tokens).  One JSON line per point."""
+    base = None
+    for S in (4, 8, 16):
+        w = WORKLOADS["C1"].with_(name=f"dflash_bf16_b8_s{S}_c4096_v151936", block=S)
+        st = Step(w, reuse=base)
+        base = base or st
+        for _ in range(warmup):
+            st()
+        ms = time_steps(st, steps)
+        n, tot, _ = profile_group(st, "gemm", steps, 64)
+        print(json.dumps({"sweep": "block", "workload": w.name, "block": S, "gamma": S - 1,
+                          "ms_per_step": ms, "gemm_ms_per_step": tot / steps}), flush=True)
+    base = None
+    for S in (5, 16):
+        w = WORKLOADS["C2"].with_(name=f"dspark_markov_bf16_b32_s{S}_c4096_v129280", block=S)
+        st = Step(w, reuse=base)
+        base = base or st
+        for _ in range(warmup):
+            st()
+        ms = time_steps(st, steps)
+        n, tot, _ = profile_group(st, "markov", steps, 64 * S)
+        print(json.dumps({"sweep": "markov", "workload": w.name, "gamma": S - 1, "ms_per_step": ms,
+                          "markov_ms_per_step": tot / steps, "markov_share": tot / steps / ms}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -259,11 +293,16 @@ def main():
     ap.add_argument("--no-roofline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (reference for HBM byte counters)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="secondary measurements: block-size and Markov draft-length sweeps (JSON line per point)")
     ap.add_argument("--summarize-rocprof", metavar="DIR",
                     help="print the kernel table / counter averages of a rocprofv3 output directory and exit")
     args = ap.parse_args()
     if args.summarize_rocprof:
         summarize_rocprof(args.summarize_rocprof, args.steps + args.warmup)
+        return
+    if args.sweep:
+        sweeps(args.steps, args.warmup)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this build measures one GPU only; --gpus must be 1"}))
