@@ -1,15 +1,12 @@
 // Drafter GEMMs: Y = X . W^T with X [M, K] activations and W [N, K] weights
 // ([out, in] storage, inputs contiguous), fp32 accumulation.
 //
-// bf16: a matrix-core kernel.  A workgroup of 4 waves owns a BM x BN output tile
-// and walks K in steps of 64, staging both operand tiles in LDS (double
-// buffered: the global loads of step k+1 are in flight while step k computes).
-// Each wave computes a (BM/2) x (BN/2) sub-tile with v_mfma_f32_16x16x32_bf16;
-// the "NT" operand layout means every lane feeds the matrix core 8 consecutive
-// k values of one row with a single 16-byte LDS read, for X and for W alike.
-// At the drafter's small M the kernel streams W from HBM once; K is split over
-// workgroups (fp32 partial slices reduced by the consumer kernel) when there
-// are too few output tiles to keep every CU loading.
+// bf16: one matrix-core kernel (v_mfma_f32_16x16x32_bf16) that streams W from
+// HBM straight into MFMA operand registers while producer waves stage X tiles
+// in LDS.  At the drafter's small M it reads W once and is bound by HBM; at
+// M in the hundreds to thousands it runs 128 x 128 output tiles and is bound by
+// the matrix cores.  K is split over workgroups (fp32 partial slices reduced by
+// the consumer kernel) when there are too few output tiles to fill the chip.
 //
 // fp32: a plain LDS-tiled VALU kernel (the fp32 configuration is tiny).
 #include "kernels.h"
@@ -48,124 +45,7 @@ __device__ __forceinline__ int x_row(const GemmArgs& a, int m) {
   return r < 0 ? 0 : (r >= a.x_rows ? a.x_rows - 1 : r);
 }
 
-template <int BM, int BN, bool PACKED>
-__global__ __launch_bounds__(256) void gemm_bf16_nt(GemmArgs a, int k_per_split) {
-  constexpr int WSTEP = PACKED ? kTileElems : BK;     // W elements per k step
-  constexpr int TM = BM / 32, TN = BN / 32;            // 16x16 tiles per wave (2x2 waves)
-  constexpr int A_CH = BM * BK / 8 / 256;               // 16-byte chunks per thread
-  constexpr int B_CH = BN * BK / 8 / 256;
-  __shared__ __attribute__((aligned(16))) bf16_t As[2][BM * LDK];
-  __shared__ __attribute__((aligned(16))) bf16_t Bs[2][BN * LDK];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int n0 = blockIdx.x * BN, m0 = blockIdx.y * BM, z = blockIdx.z;
-  const int kbeg = z * k_per_split;
-  const int kend = min(a.K, kbeg + k_per_split);
-  const int nk = kend > kbeg ? (kend - kbeg) / BK : 0;
-
-  const bf16_t* a_src[A_CH];
-  bool a_ok[A_CH];
-  int a_dst[A_CH];
-#pragma unroll
-  for (int i = 0; i < A_CH; ++i) {
-    const int c = tid + i * 256, row = c >> 3, col = (c & 7) * 8, m = m0 + row;
-    a_ok[i] = m < a.M;
-    a_src[i] = (const bf16_t*)a.X + (size_t)x_row(a, a_ok[i] ? m : 0) * a.ldx + kbeg + col;
-    a_dst[i] = row * LDK + col;
-  }
-  const bf16_t* b_src[B_CH];
-  bool b_ok[B_CH];
-  int b_dst[B_CH];
-#pragma unroll
-  for (int i = 0; i < B_CH; ++i) {
-    const int c = tid + i * 256;
-    if constexpr (PACKED) {
-      // chunk c of the step: tile c / 128, operand slot (ks, lane) = c % 128
-      const int t = c >> 7, q = c & 127, l = q & 63;
-      const int row = t * 16 + (l & 15), n = n0 + row;
-      b_ok[i] = n < a.N;
-      b_src[i] = seg_tile(a, b_ok[i] ? n : 0) + (size_t)(kbeg / BK) * kTileElems + q * 8;
-      b_dst[i] = row * LDK + (q >> 6) * 32 + (l >> 4) * 8;
-    } else {
-      const int row = c >> 3, col = (c & 7) * 8, n = n0 + row;
-      b_ok[i] = n < a.N;
-      b_src[i] = (const bf16_t*)seg_row(a, b_ok[i] ? n : 0, 2) + kbeg + col;
-      b_dst[i] = row * LDK + col;
-    }
-  }
-
-  uint4 ra[A_CH], rb[B_CH];
-  auto gload = [&](int kt) {
-#pragma unroll
-    for (int i = 0; i < A_CH; ++i)
-      ra[i] = a_ok[i] ? ldg16(a_src[i] + kt * BK) : make_uint4(0, 0, 0, 0);
-#pragma unroll
-    for (int i = 0; i < B_CH; ++i)
-      rb[i] = b_ok[i] ? ldg16(b_src[i] + (size_t)kt * WSTEP) : make_uint4(0, 0, 0, 0);
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < A_CH; ++i) *(uint4*)&As[buf][a_dst[i]] = ra[i];
-#pragma unroll
-    for (int i = 0; i < B_CH; ++i) *(uint4*)&Bs[buf][b_dst[i]] = rb[i];
-  };
-
-  f32x4 acc[TM][TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  if (nk > 0) {
-    gload(0);
-    sstore(0);
-  }
-  __syncthreads();
-  const int frag_row = lane & 15, frag_k = (lane >> 4) * 8;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
-#pragma unroll
-    for (int ks = 0; ks < BK / 32; ++ks) {
-      bf16x8 af[TM], bfg[TN];
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-        af[i] = *(const bf16x8*)&As[buf][(wm * (BM / 2) + i * 16 + frag_row) * LDK + ks * 32 + frag_k];
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-        bfg[j] = *(const bf16x8*)&Bs[buf][(wn * (BN / 2) + j * 16 + frag_row) * LDK + ks * 32 + frag_k];
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfg[j], acc[i][j], 0, 0, 0);
-    }
-    if (kt + 1 < nk) sstore(buf ^ 1);
-    __syncthreads();
-  }
-
-  // D layout of a 16x16 tile: lane holds column (lane & 15), rows 4*(lane >> 4) + r
-  float* Y = a.Y + (size_t)z * a.y_split_stride;
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int n = n0 + wn * (BN / 2) + j * 16 + (lane & 15);
-      if (n >= a.N) continue;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = m0 + wm * (BM / 2) + i * 16 + (lane >> 4) * 4 + r;
-        if (m >= a.M) continue;
-        float* y = Y + (size_t)m * a.ldy + n;
-        if (a.accumulate) *y = *y + acc[i][j][r];
-        else *y = acc[i][j][r];
-      }
-    }
-}
-
-// Weight-streaming kernel for the drafter's small M (<= 256 rows), with
-// producer/consumer waves.  A workgroup has 8 waves:
+// Weight-streaming kernel with producer/consumer waves.  A workgroup has 8 waves:
 //   waves 4..7 (producers) stream the X tile (all BM rows x 64 k per step)
 //     global -> registers -> LDS, XPD steps ahead;
 //   waves 0..3 (consumers) stream their own 16*NW rows of W straight into MFMA
@@ -465,22 +345,26 @@ __global__ __launch_bounds__(256) void pack_kernel(const bf16_t* __restrict__ sr
 
 }  // namespace
 
-// Kernel configurations the planner chooses from.
-//   kind 0: LDS-tiled (both operands staged), BM x BN in {128,64}^2 — large M.
-//   kind 1: weight streaming, BM = 16*MT rows, BN = 64*NW columns — M <= 256.
+// Kernel configurations the planner chooses from: weight streaming with
+// BM = 16*MT rows and BN = 64*NW columns per workgroup.
 struct Cand {
-  int kind, bm, bn, mt, nw;
+  int bm, bn, mt, nw;
 };
 static const Cand kCands[] = {
-    {1, 128, 128, 8, 2}, {1, 128, 64, 8, 1}, {1, 64, 128, 4, 2}, {1, 64, 64, 4, 1},
-    {1, 32, 128, 2, 2},  {1, 32, 64, 2, 1},  {1, 256, 64, 16, 1},
-    {0, 128, 128, 0, 0}, {0, 128, 64, 0, 0}, {0, 64, 128, 0, 0}, {0, 64, 64, 0, 0},
+    {128, 128, 8, 2}, {128, 64, 8, 1}, {64, 128, 4, 2}, {64, 64, 4, 1}, {32, 128, 2, 2}, {32, 64, 2, 1}, {256, 64, 16, 1},
 };
 
-// Cost model (seconds at the HBM roofline): weights once per M tile, X staged
-// once per column tile (mostly L2 hits, weighted 1/4), fp32 split partials
-// written and read back (mostly MALL-resident, weighted 1/2), the dense product
-// at ~half the bf16 peak, all divided by how well the grid fills 256 CUs.
+// Cost model, two regimes.
+// M <= 256 (HBM bound): seconds at the HBM roofline for W (once per M tile, the
+// M tiles of one W slab sharing an XCD's L2), staged X (mostly L2 hits,
+// weighted 1/2) and the fp32 split partials (written and read back, mostly
+// MALL resident), against the dense product at about half the bf16 peak, all
+// divided by how well the grid fills the chip.
+// M > 256 (matrix-core bound): the 128 x 128 tile only (measured fastest at
+// every such drafter shape), at its measured ~0.8 PFLOP/s; one 512-thread
+// workgroup occupies a CU, so the compute time is counted in whole waves of
+// 256 workgroups and K splits pay off when they round the grid up to full
+// waves.
 GemmPlan gemm_plan(int M, int N, int K, int dtype, int force_splits) {
   GemmPlan best;
   if (dtype != 1) {   // fp32 VALU kernel
@@ -492,7 +376,7 @@ GemmPlan gemm_plan(int M, int N, int K, int dtype, int force_splits) {
   }
   const int kb = K / BK;
 #ifdef DFS_TUNING
-  // tuning builds only: DFS_GEMM_FORCE="kind,bm,bn,mt,nw,splits" selects a configuration
+  // tuning builds only: DFS_GEMM_FORCE="kind,bm,bn,mt,nw,splits[,pd,xd]" selects a configuration
   if (const char* f = getenv("DFS_GEMM_FORCE")) {
     GemmPlan p;
     int sp = 1;
@@ -504,9 +388,10 @@ GemmPlan gemm_plan(int M, int N, int K, int dtype, int force_splits) {
     }
   }
 #endif
+  const bool big = M > 256;
   double best_cost = 1e300;
   for (const Cand& c : kCands) {
-    if (c.kind == 1 && M > 256) continue;
+    if (big && !(c.mt == 8 && c.nw == 2)) continue;
     const int mt = ceil_div(M, c.bm), nt = ceil_div(N, c.bn);
     for (int sp = 1; sp <= 32; ++sp) {
       if (force_splits && sp != force_splits) continue;
@@ -514,24 +399,26 @@ GemmPlan gemm_plan(int M, int N, int K, int dtype, int force_splits) {
       const int real_sp = ceil_div(kb, kps_blocks);
       if (real_sp != sp) continue;
       if (sp > 1 && kps_blocks < 4 && !force_splits) continue;
-      // the streaming kernel runs the M tiles of one W slab on the same XCD
-      // (partial L2 reuse); staged X is mostly L2 hits
-      const double w = 2.0 * N * K * (c.kind == 1 ? 1.0 + 0.5 * (mt - 1) : mt);
+      const double w = 2.0 * N * K * (1.0 + 0.5 * (mt - 1));
       const double x = 2.0 * (double)mt * c.bm * K * nt;
       const double flops = 2.0 * (double)mt * c.bm * nt * c.bn * K;
       // fp32 output: one slice, or sp slices written and read back by the consumer
       const double part = sp > 1 ? 1.5 * 4.0 * M * N * sp : 4.0 * M * N;
       const double wgs = (double)mt * nt * sp;
-      // one 512-thread streaming workgroup per CU already saturates its share;
-      // the LDS-tiled kernel runs two 256-thread workgroups per CU
-      const double full = c.kind == 1 ? 192.0 : 512.0;
-      const double fill = wgs >= full ? 1.0 : wgs / full;
+      // one 512-thread streaming workgroup per CU already saturates its share of HBM
+      const double fill = wgs >= 192.0 ? 1.0 : wgs / 192.0;
       const double mem = (w + 0.5 * x + part) / 8.0e12;
-      const double cmp = flops / 1.2e15;
-      const double cost = (mem > cmp ? mem : cmp) / fill;
+      double cost;
+      if (big) {
+        const double waves = ceil(wgs / 256.0);
+        const double cmp = flops / 0.8e15 * (waves * 256.0 / wgs);
+        cost = fmax(mem / fill, cmp);
+      } else {
+        cost = fmax(mem, flops / 1.2e15) / fill;
+      }
       if (cost < best_cost * 0.999) {
         best_cost = cost;
-        best.kind = c.kind;
+        best.kind = 1;
         best.bm = c.bm;
         best.bn = c.bn;
         best.mt = c.mt;
@@ -539,14 +426,17 @@ GemmPlan gemm_plan(int M, int N, int K, int dtype, int force_splits) {
         best.splits = sp;
         best.k_per_split = kps_blocks * BK;
         // X prefetched as deep as W where that variant is built (measured a little faster)
-        best.xd = (c.kind == 1 && ((c.mt == 8 && c.nw == 2) || (c.mt == 16 && c.nw == 1))) ? 4 : 2;
+        best.xd = ((c.mt == 8 && c.nw == 2) || (c.mt == 16 && c.nw == 1)) ? 4 : 2;
       }
     }
   }
   if (best_cost == 1e300) {   // forced split count not representable
-    best.kind = 0;
+    best.kind = 1;
     best.bm = 128;
     best.bn = 128;
+    best.mt = 8;
+    best.nw = 2;
+    best.xd = 4;
     best.splits = 1;
     best.k_per_split = K;
   }
@@ -554,11 +444,12 @@ GemmPlan gemm_plan(int M, int N, int K, int dtype, int force_splits) {
 }
 
 // Gated gate|up GEMM: the weight-streaming kernel with paired tiles, no K split
-// (the SwiGLU needs complete sums); 64 features per workgroup.
+// (the SwiGLU needs complete sums); 64 features per workgroup, 128-row tiles
+// beyond M = 64.
 GemmPlan gemm_plan_gated(int M, int N, int K, int dtype) {
   GemmPlan p;
   p.kind = -1;
-  if (dtype != 1 || M > 128 || K % BK) return p;
+  if (dtype != 1 || K % BK) return p;
   p.kind = 1;
   p.nw = 2;
   p.mt = M <= 32 ? 2 : (M <= 64 ? 4 : 8);
@@ -599,7 +490,6 @@ hipError_t launch_gemm(const GemmArgs& a, const GemmPlan& p, int dtype, hipStrea
     hipLaunchKernelGGL(gemm_f32_nt, grid, dim3(256), 0, s, a, p.k_per_split);
     return hipGetLastError();
   }
-  dim3 grid(ceil_div(a.N, p.bn), ceil_div(a.M, p.bm), p.splits);
   const int kps = p.k_per_split;
   if (p.kind == 1) {
     const int mtl = ceil_div(a.M, p.bm), ntl = ceil_div(a.N, p.bn);
@@ -617,20 +507,6 @@ hipError_t launch_gemm(const GemmArgs& a, const GemmPlan& p, int dtype, hipStrea
 #undef DFS_STREAM
     return hipErrorInvalidValue;
   }
-  if (a.gated) return hipErrorInvalidValue;
-#define DFS_TILED(BM_, BN_)                                                                              \
-  if (p.bm == BM_ && p.bn == BN_) {                                                                       \
-    if (a.packed)                                                                                         \
-      hipLaunchKernelGGL((gemm_bf16_nt<BM_, BN_, true>), grid, dim3(256), 0, s, a, kps);                  \
-    else                                                                                                  \
-      hipLaunchKernelGGL((gemm_bf16_nt<BM_, BN_, false>), grid, dim3(256), 0, s, a, kps);                 \
-    return hipGetLastError();                                                                             \
-  }
-  DFS_TILED(128, 128)
-  DFS_TILED(128, 64)
-  DFS_TILED(64, 128)
-  DFS_TILED(64, 64)
-#undef DFS_TILED
   return hipErrorInvalidValue;
 }
 

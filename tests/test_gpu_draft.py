@@ -25,6 +25,9 @@ CASES = {
     # weights in the tile-packed layout (V = 5000 leaves a partial last row tile)
     "medium_packed": (MEDIUM, 2, None, None, None, True),
     "medium_ragged_packed": (MEDIUM, 3, [284, 131, 7], [16, 5, 0], 16, True),
+    # 320 block rows: every GEMM in its matrix-core-bound plan (128-row tiles,
+    # ragged last tile), the gated MLP GEMM over three M tiles
+    "medium_b20_packed": (MEDIUM.with_(batch=20), 6, None, None, None, True),
 }
 
 
