@@ -24,6 +24,7 @@ sys.path.insert(0, ROOT)
 from synth import WORKLOADS, inputs  # noqa: E402
 
 HBM_PEAK_GBPS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0       # dense bf16 matrix-core peak (no sparsity)
 METRIC = "draft-verify steps/sec + HBM GB/s, B=8 block=16 ctx=4K vocab=152K (1 GPU)"
 
 
@@ -37,8 +38,8 @@ def algorithmic_bytes(w):
     per_layer_w = (nq * d * H + 2 * nkv * d * H + H * nq * d + 3 * F * H) * es
     gemm_w = L * per_layer_w + (H * nT * H + V * H) * es
     # activations in/out of every GEMM (X read once per launch, fp32 result written once;
-    # the gate|up GEMM writes the bf16 SwiGLU product when its gated form applies)
-    gated = w.dtype == "bf16" and Mb <= 128
+    # the gate|up GEMM writes the bf16 SwiGLU product in its gated (bf16) form)
+    gated = w.dtype == "bf16"
     gateup_out = Mb * F * es if gated else Mb * 2 * F * 4
     gemm_act = (Mc * nT * H * es + Mc * H * 4
                 + L * ((Mc + Mb) * H * es + (Mc + Mb) * (nq + 2 * nkv) * d * 4
@@ -49,8 +50,15 @@ def algorithmic_bytes(w):
     sample = B * G * V * 4                               # read final logits once
     markov = (V * r * es + B * G * V * 4 * 2) if r > 0 else 0
     verify = B * (G + 1) * V * 4 + 2 * B * V * 4        # target rows + the two rows at the rejection
-    return {"gemm": gemm_w + gemm_act, "gemm_weights": gemm_w, "attention": attn, "sample": sample,
-            "markov": markov, "verify": verify}
+    # dense products of the drafter GEMMs (the QKV GEMM runs over context and block rows)
+    gemm_flops = 2.0 * (Mc * H * nT * H + B * G * V * H
+                        + L * ((Mc + Mb) * (nq + 2 * nkv) * d * H + Mb * H * nq * d + Mb * 2 * F * H + Mb * H * F))
+    # the Markov head's per-position GEMM: W once, gathered U rows, logits rows read and written
+    markov_gemm = (V * r * es + B * G * r * es + 2 * B * G * V * 4) if r > 0 else 0
+    markov_flops = 2.0 * B * G * V * r
+    return {"gemm": gemm_w + gemm_act, "gemm_weights": gemm_w, "gemm_flops": gemm_flops, "attention": attn,
+            "sample": sample, "markov": markov, "markov_gemm": markov_gemm, "markov_flops": markov_flops,
+            "verify": verify}
 
 
 class Step:
@@ -337,17 +345,31 @@ def main():
     }
     if not args.no_roofline:
         L = w.n_layers
-        n, tot, ms_p = profile_group(step, "gemm", args.steps, 4 * L + 2)
+        # GEMM launches of one step: fc, 4 per layer, LM head, and with a Markov head
+        # one per drafted position (its GEMMs run through the same launcher)
+        per_step = 4 * L + 2 + (w.gamma if w.markov_rank > 0 else 0)
+        n, tot, ms_p = profile_group(step, "gemm", args.steps, per_step)
         per_launch_ms = tot / max(n, 1)
         launches_per_step = n / args.steps
-        gemm_bytes_per_launch = ab["gemm"] / launches_per_step
-        achieved = gemm_bytes_per_launch / (per_launch_ms * 1e-3) / 1e9
-        res["roofline"] = {"kernel": "gemm_stream_bf16 (all drafter GEMM launches)", "bound": "hbm",
-                           "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                           "frac": achieved / HBM_PEAK_GBPS,
-                           "traffic": recorded_traffic() if w.name == WORKLOADS["C1"].name else None,
-                           "algorithmic_bytes_per_launch": gemm_bytes_per_launch,
-                           "launches_per_step": launches_per_step, "avg_launch_us": per_launch_ms * 1e3,
+        step_bytes_g = ab["gemm"] + ab["markov_gemm"]
+        step_flops_g = ab["gemm_flops"] + ab["markov_flops"]
+        bytes_per_launch = step_bytes_g / launches_per_step
+        flops_per_launch = step_flops_g / launches_per_step
+        kernel = "drafter GEMM launches (gemm_stream_bf16" + (", gemm_tile_bf16" if w.batch * w.block > 256 else "") \
+            + (", Markov-head GEMMs" if w.markov_rank > 0 else "") + ")"
+        if w.batch * w.block > 256 and w.dtype == "bf16":
+            # M > 256: the drafter GEMMs are bound by the matrix cores
+            achieved = flops_per_launch / (per_launch_ms * 1e-3) / 1e12
+            roof = {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": None}
+        else:
+            achieved = bytes_per_launch / (per_launch_ms * 1e-3) / 1e9
+            roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                    "frac": achieved / HBM_PEAK_GBPS,
+                    "traffic": recorded_traffic() if w.name == WORKLOADS["C1"].name else None}
+        res["roofline"] = {"kernel": kernel, **roof, "algorithmic_bytes_per_launch": bytes_per_launch,
+                           "flops_per_launch": flops_per_launch, "launches_per_step": launches_per_step,
+                           "avg_launch_us": per_launch_ms * 1e3, "gemm_ms_per_step": tot / args.steps,
                            "ms_per_step_profiled": ms_p}
         groups = {}
         for g, per_step in (("attention", L), ("verify", 1), ("sample", 1), ("markov", 1), ("elementwise", 0)):

@@ -346,7 +346,7 @@ int dflash_draft_step(const dfs_drafter_cfg* cfg, const dfs_drafter_weights* wt,
     // 5. SwiGLU MLP: gate and up in one weight pass (the product formed in the
     //    GEMM epilogue when a gated plan fits, else by a separate pass over the
     //    fp32 results), then down, residual add, next pre-norm
-    if (gated.kind == 1) {
+    if (gated.kind > 0) {
       DFS_TRY(run_gemm_gated(w.mlp_in, d.H, d.Mb, d.F, d.H, wt->w_gate[l], wt->w_up[l], w.hmid, pk, gated, s));
     } else {
       DFS_TRY(run_gemm(w.mlp_in, d.H, d.Mb, 2 * d.F, d.H, wt->w_gate[l], wt->w_up[l], d.F, nullptr, 0, w.part, dt,
@@ -616,6 +616,16 @@ int dfs_gemm(int32_t M, int32_t N, int32_t K, int32_t dtype, const void* X, cons
   size_t pst;
   DFS_TRY(run_gemm(X, K, M, N, K, W, nullptr, 0, nullptr, 0, target, dtype, w_packed, s, &sp, &pst, splits));
   if (sp > 1) DFS_TRY(launch_reduce(target, sp, pst, (size_t)M * N, Y, s));
+  return DFS_OK;
+}
+
+int dfs_gemm_swiglu(int32_t M, int32_t F, int32_t K, const void* X, const void* Wg, const void* Wu, void* H,
+                    int32_t w_packed, void* stream) {
+  if (M < 1 || F < 1 || K < 1 || !X || !Wg || !Wu || !H || (w_packed != 0 && w_packed != 1)) return DFS_EINVAL;
+  if (K % 64) return DFS_EUNSUPPORTED;
+  const GemmPlan p = gemm_plan_gated(M, F, K, DFS_BF16);
+  if (p.kind < 0) return DFS_EUNSUPPORTED;
+  DFS_TRY(run_gemm_gated(X, K, M, F, K, Wg, Wu, H, w_packed, p, (hipStream_t)stream));
   return DFS_OK;
 }
 

@@ -275,6 +275,204 @@ void gemm_stream_bf16(GemmArgs a, int k_per_split, int mtiles, int ntiles) {
   }
 }
 
+// Matrix-core-bound GEMM for M in the hundreds to thousands: a BM x BN output
+// tile per 512-thread workgroup (8 waves, 2 along M x 4 along N, all of them
+// loading and multiplying).  K is walked in half steps of 32 through a ring of
+// NS LDS stages filled by direct global->LDS loads (global_load_lds_dwordx4:
+// each lane's 16 bytes land at lane*16 of a wave-uniform LDS address), issued
+// NS-1 half steps ahead, so no registers hold operands in flight.
+// A stage holds each operand in matrix-core fragment order: 16-row groups of
+// 1 KB, lane l's 16 bytes being row l % 16, k 8*(l/16) .. +7 of the half step —
+// one half of a tile-packed weight tile, copied verbatim; a row-major operand
+// is gathered into it by per-lane addresses.  Every fragment read is one
+// linear, conflict-free 16-byte LDS read per lane.
+// Synchronisation per half step: each wave waits for its own loads of the
+// stage (vmcnt counts them in issue order: (NS-2) half steps of younger loads
+// may stay in flight), then a workgroup barrier; the stage read NS-1 half
+// steps later is refilled only after that barrier.  The stages are distinct
+// LDS arrays so that the compiler's own load/LDS-read ordering does not
+// serialise the ring.
+// W is the A operand (16 output columns) and X the B operand (16 rows), so a
+// lane's result is 4 consecutive columns of one row, stored as one 16-byte
+// vector as in the streaming kernel.
+// GATED: the tile covers BN/2 features; each wave's BN/4 W rows are the gate
+// rows of its BN/8 features followed by their up rows, so its epilogue holds
+// gate and up of the same outputs and writes bf16(silu(gate) * up).
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+
+template <int BM, int BN, bool PACKED, bool GATED>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void gemm_tile_bf16(GemmArgs a, int k_per_split, int mtiles, int ntiles) {
+  constexpr int NS = 4;                                 // LDS ring depth (half steps)
+  constexpr int NA = BN / 64, MB = BM / 32;             // 16-wide W / X fragments per wave
+  constexpr int GW = BN / 16, GX = BM / 16;             // 1 KB units per half step
+  constexpr int UPS = (GW + GX) / 8;                    // units per wave per half step
+  constexpr int SE = (BN + BM) * 32;                    // stage size (bf16 elements)
+  static_assert((GW % 8) == 0 && (GX % 8) == 0, "units split evenly over the waves");
+  static_assert(!GATED || NA % 2 == 0, "gated tiles pair gate and up fragments");
+  // a wave's vmcnt wait before reading a stage: younger half steps still in flight
+  constexpr int kWait = (NS - 2) * UPS;
+  static_assert(kWait < 16, "wait count fits the low vmcnt field");
+  __shared__ __attribute__((aligned(1024))) bf16_t S0[SE];
+  __shared__ __attribute__((aligned(1024))) bf16_t S1[SE];
+  __shared__ __attribute__((aligned(1024))) bf16_t S2[SE];
+  __shared__ __attribute__((aligned(1024))) bf16_t S3[SE];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 2, wn = wave & 3;
+  const int c = lane & 15, g4 = lane >> 4;
+  const int lid = xcd_logical_id(blockIdx.x, gridDim.x);
+  const int mtile = lid % mtiles, rest = lid / mtiles;
+  const int ntile = rest % ntiles, z = rest / ntiles;
+  const int m0 = mtile * BM;
+  const int kbeg = z * k_per_split;
+  const int kend = min(a.K, kbeg + k_per_split);
+  const int nh = kend > kbeg ? (kend - kbeg) / 32 : 0;  // half steps
+  if (nh == 0) return;                                   // uniform over the workgroup
+
+  // Unit u = wave + 8*i of a half step: u < GW is W row group u, else X row
+  // group u - GW.  src[i] is the lane's address at half step 0; hstep[i] the
+  // advance per half step (elements); dsto[i] the unit's offset in a stage.
+  const bf16_t* src[UPS];
+  int dsto[UPS];
+  int hstep[UPS];
+#pragma unroll
+  for (int i = 0; i < UPS; ++i) {
+    const int u = wave + 8 * i;
+    if (i < GW / 8) {
+      const int g = u;
+      if constexpr (GATED) {
+        const int wg = g / NA, jj = g % NA;
+        const int f = min(ntile * (BN / 2) + wg * (NA / 2) * 16 + (jj % (NA / 2)) * 16, (a.N - 1) & ~15);
+        const bf16_t* w = (const bf16_t*)a.seg[jj < NA / 2 ? 0 : 1].w;
+        if constexpr (PACKED)
+          src[i] = w + ((size_t)(f >> 4) * (a.K / BK) + kbeg / BK) * kTileElems + lane * 8;
+        else
+          src[i] = w + (size_t)min(f + c, a.N - 1) * a.K + kbeg + g4 * 8;
+      } else {
+        const int n = min(ntile * BN + g * 16, (a.N - 1) & ~15);
+        if constexpr (PACKED)
+          src[i] = seg_tile(a, n) + (size_t)(kbeg / BK) * kTileElems + lane * 8;
+        else
+          src[i] = (const bf16_t*)seg_row(a, min(n + c, a.N - 1), 2) + kbeg + g4 * 8;
+      }
+      dsto[i] = g * 512;
+      hstep[i] = PACKED ? kTileElems / 2 : 32;
+    } else {
+      const int g = u - GW;
+      const int m = min(m0 + g * 16 + c, a.M - 1);
+      src[i] = (const bf16_t*)a.X + (size_t)x_row(a, m) * a.ldx + kbeg + g4 * 8;
+      dsto[i] = BN * 32 + g * 512;
+      hstep[i] = 32;
+    }
+  }
+  // packed W: half step h of tile kt = h/2 sits at kt * kTileElems + (h%2) * 512
+  auto src_at = [&](int i, int h) -> const bf16_t* {
+    if (PACKED && i < GW / 8) return src[i] + (size_t)(h >> 1) * kTileElems + (h & 1) * 512;
+    return src[i] + (size_t)h * 32;
+  };
+  auto fill = [&](bf16_t* stage, int h) {
+    const int hh = min(h, nh - 1);                       // past the end: reload the last (unused)
+#pragma unroll
+    for (int i = 0; i < UPS; ++i)
+      __builtin_amdgcn_global_load_lds((glb_void_t*)src_at(i, hh), (lds_void_t*)(stage + dsto[i]), 16, 0, 0);
+  };
+  (void)hstep;
+
+  f32x4 acc[NA][MB];
+#pragma unroll
+  for (int j = 0; j < NA; ++j)
+#pragma unroll
+    for (int i = 0; i < MB; ++i) acc[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  fill(S0, 0);
+  fill(S1, 1);
+  fill(S2, 2);
+#define DFS_TILE_STEP(CUR, NXT, H)                                                            \
+  {                                                                                           \
+    __builtin_amdgcn_s_waitcnt(0x0070 | kWait); /* own loads of stage H done; lgkm drained */ \
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);                                                  \
+    __builtin_amdgcn_s_barrier();                                                             \
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);                                                  \
+    fill(NXT, (H) + NS - 1);                                                                  \
+    if ((H) < nh) {                                                                           \
+      const bf16_t* ws = CUR + wn * NA * 512 + lane * 8;                                      \
+      const bf16_t* xs = CUR + BN * 32 + wm * MB * 512 + lane * 8;                            \
+      bf16x8 af[NA], bx[MB];                                                                  \
+      _Pragma("unroll") for (int j = 0; j < NA; ++j) af[j] = *(const bf16x8*)(ws + j * 512);  \
+      _Pragma("unroll") for (int i = 0; i < MB; ++i) bx[i] = *(const bf16x8*)(xs + i * 512);  \
+      _Pragma("unroll") for (int i = 0; i < MB; ++i)                                          \
+        _Pragma("unroll") for (int j = 0; j < NA; ++j)                                        \
+          acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[j], bx[i], acc[j][i], 0, 0, 0); \
+    }                                                                                         \
+  }
+  for (int h = 0; h < nh; h += NS) {
+    DFS_TILE_STEP(S0, S3, h)
+    DFS_TILE_STEP(S1, S0, h + 1)
+    DFS_TILE_STEP(S2, S1, h + 2)
+    DFS_TILE_STEP(S3, S2, h + 3)
+  }
+#undef DFS_TILE_STEP
+  // drain the ring's trailing (unused) loads before the workgroup can exit
+  __builtin_amdgcn_s_waitcnt(0x0070);
+
+  if constexpr (GATED) {
+    // h = bf16(silu(gate) * up) for features f .. f+3 of row m (one 8-byte store)
+    constexpr int per = NA * 16 / 2;
+#pragma unroll
+    for (int i = 0; i < MB; ++i) {
+      const int m = m0 + (wm * MB + i) * 16 + c;
+      if (m >= a.M) continue;
+      bf16_t* hrow = (bf16_t*)a.hout + (size_t)m * a.ldy;
+#pragma unroll
+      for (int j = 0; j < NA / 2; ++j) {
+        const int f = ntile * (BN / 2) + wn * per + j * 16 + g4 * 4;
+        bf16_t hv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float g = acc[j][i][e], u = acc[j + NA / 2][i][e];
+          hv[e] = f2bf(g / (1.f + expf(-g)) * u);
+        }
+        if (f + 3 < a.N) {
+          *(uint2*)(hrow + f) =
+              make_uint2((uint32_t)hv[0] | ((uint32_t)hv[1] << 16), (uint32_t)hv[2] | ((uint32_t)hv[3] << 16));
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (f + e < a.N) hrow[f + e] = hv[e];
+        }
+      }
+    }
+    return;
+  }
+  float* Y = a.Y + (size_t)z * a.y_split_stride;
+  const bool vec = (a.ldy & 3) == 0 && ((uintptr_t)Y & 15) == 0;
+#pragma unroll
+  for (int i = 0; i < MB; ++i) {
+    const int m = m0 + (wm * MB + i) * 16 + c;
+    if (m >= a.M) continue;
+    float* yrow = Y + (size_t)m * a.ldy;
+#pragma unroll
+    for (int j = 0; j < NA; ++j) {
+      const int n = ntile * BN + (wn * NA + j) * 16 + g4 * 4;
+      if (vec && n + 3 < a.N) {
+        f32x4 v = acc[j][i];
+        if (a.accumulate) v += *(const f32x4*)(yrow + n);
+        if (a.nt_store) __builtin_nontemporal_store(v, (f32x4*)(yrow + n));
+        else *(f32x4*)(yrow + n) = v;
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          if (n + r >= a.N) break;
+          if (a.accumulate) yrow[n + r] += acc[j][i][r];
+          else yrow[n + r] = acc[j][i][r];
+        }
+      }
+    }
+  }
+}
+
 // fp32: 64x64 output tile, 256 threads each computing a 4x4 block, BK = 16.
 __global__ __launch_bounds__(256) void gemm_f32_nt(GemmArgs a, int k_per_split) {
   constexpr int T = 64, KT = 16;
@@ -345,26 +543,65 @@ __global__ __launch_bounds__(256) void pack_kernel(const bf16_t* __restrict__ sr
 
 }  // namespace
 
-// Kernel configurations the planner chooses from: weight streaming with
-// BM = 16*MT rows and BN = 64*NW columns per workgroup.
+// Kernel configurations the planner chooses from: weight streaming (kind 1)
+// with BM = 16*MT rows and BN = 64*NW columns per workgroup, and the
+// LDS-ring tile kernel (kind 3, 256 x 256) for M > 256.
 struct Cand {
-  int bm, bn, mt, nw;
+  int kind, bm, bn, mt, nw;
 };
 static const Cand kCands[] = {
-    {128, 128, 8, 2}, {128, 64, 8, 1}, {64, 128, 4, 2}, {64, 64, 4, 1}, {32, 128, 2, 2}, {32, 64, 2, 1}, {256, 64, 16, 1},
+    {1, 128, 128, 8, 2}, {1, 128, 64, 8, 1}, {1, 64, 128, 4, 2}, {1, 64, 64, 4, 1},
+    {1, 32, 128, 2, 2},  {1, 32, 64, 2, 1},  {1, 256, 64, 16, 1}, {3, 256, 256, 0, 0},
 };
 
 // Cost model, two regimes.
-// M <= 256 (HBM bound): seconds at the HBM roofline for W (once per M tile, the
-// M tiles of one W slab sharing an XCD's L2), staged X (mostly L2 hits,
-// weighted 1/2) and the fp32 split partials (written and read back, mostly
-// MALL resident), against the dense product at about half the bf16 peak, all
-// divided by how well the grid fills the chip.
-// M > 256 (matrix-core bound): the 128 x 128 tile only (measured fastest at
-// every such drafter shape), at its measured ~0.8 PFLOP/s; one 512-thread
-// workgroup occupies a CU, so the compute time is counted in whole waves of
-// 256 workgroups and K splits pay off when they round the grid up to full
-// waves.
+// M <= 256 (HBM bound, weight streaming only): seconds at the HBM roofline for
+// W (once per M tile, the M tiles of one W slab sharing an XCD's L2), staged X
+// (mostly L2 hits, weighted 1/2) and the fp32 split partials (written and read
+// back, mostly MALL resident), against the dense product at about half the
+// bf16 peak, all divided by how well the grid fills the chip.
+// M > 256 (matrix-core bound): the 128 x 128 streaming tile at its measured
+// ~0.85 PFLOP/s or the 256 x 256 LDS-ring tile at ~1.1 PFLOP/s.  One workgroup
+// occupies a CU, so compute time is counted in whole waves of 256 workgroups,
+// plus a fixed ~4 us per wave (pipeline ramp, epilogue); split partials cost
+// one more pass over M x N x splits fp32.  Fitted to measurements of the
+// drafter shapes at M = 480 .. 2048 (every pick within 2 % of the fastest).
+static double plan_cost(const Cand& c, int sp, int M, int N, int K) {
+  const bool big = M > 256;
+  const int mt = ceil_div(M, c.bm), nt = ceil_div(N, c.bn);
+  const double w = 2.0 * N * K * (1.0 + 0.5 * (mt - 1));
+  const double x = 2.0 * (double)mt * c.bm * K * nt;
+  const double flops = 2.0 * (double)mt * c.bm * nt * c.bn * K;
+  // fp32 output: one slice, or sp slices written and read back by the consumer
+  const double part = sp > 1 ? 1.5 * 4.0 * M * N * sp : 4.0 * M * N;
+  const double wgs = (double)mt * nt * sp;
+  // one 512-thread streaming workgroup per CU already saturates its share of HBM
+  const double fill = wgs >= 192.0 ? 1.0 : wgs / 192.0;
+  const double mem = (w + 0.5 * x + part) / 8.0e12;
+  if (!big) return fmax(mem, flops / 1.2e15) / fill;
+  const double waves = ceil(wgs / 256.0);
+  const double rate = c.kind == 3 ? 1.1e15 : 0.85e15;
+  const double cmp = flops / rate * (waves * 256.0 / wgs) + waves * 4.0e-6;
+  return fmax(mem / fill, cmp) + (sp > 1 ? 4.0 * M * N * sp / 8.0e12 : 0.0);
+}
+
+static bool plan_allows(const Cand& c, int M) {
+  if (M > 256) return (c.kind == 1 && c.mt == 8 && c.nw == 2) || c.kind == 3;
+  return c.kind == 1;
+}
+
+static void plan_take(GemmPlan& p, const Cand& c, int sp, int kps_blocks) {
+  p.kind = c.kind;
+  p.bm = c.bm;
+  p.bn = c.bn;
+  p.mt = c.mt;
+  p.nw = c.nw;
+  p.splits = sp;
+  p.k_per_split = kps_blocks * BK;
+  // X prefetched as deep as W where that streaming variant is built (measured a little faster)
+  p.xd = ((c.mt == 8 && c.nw == 2) || (c.mt == 16 && c.nw == 1)) ? 4 : 2;
+}
+
 GemmPlan gemm_plan(int M, int N, int K, int dtype, int force_splits) {
   GemmPlan best;
   if (dtype != 1) {   // fp32 VALU kernel
@@ -388,45 +625,19 @@ GemmPlan gemm_plan(int M, int N, int K, int dtype, int force_splits) {
     }
   }
 #endif
-  const bool big = M > 256;
   double best_cost = 1e300;
   for (const Cand& c : kCands) {
-    if (big && !(c.mt == 8 && c.nw == 2)) continue;
-    const int mt = ceil_div(M, c.bm), nt = ceil_div(N, c.bn);
+    if (!plan_allows(c, M)) continue;
     for (int sp = 1; sp <= 32; ++sp) {
       if (force_splits && sp != force_splits) continue;
       const int kps_blocks = ceil_div(kb, sp);
       const int real_sp = ceil_div(kb, kps_blocks);
       if (real_sp != sp) continue;
       if (sp > 1 && kps_blocks < 4 && !force_splits) continue;
-      const double w = 2.0 * N * K * (1.0 + 0.5 * (mt - 1));
-      const double x = 2.0 * (double)mt * c.bm * K * nt;
-      const double flops = 2.0 * (double)mt * c.bm * nt * c.bn * K;
-      // fp32 output: one slice, or sp slices written and read back by the consumer
-      const double part = sp > 1 ? 1.5 * 4.0 * M * N * sp : 4.0 * M * N;
-      const double wgs = (double)mt * nt * sp;
-      // one 512-thread streaming workgroup per CU already saturates its share of HBM
-      const double fill = wgs >= 192.0 ? 1.0 : wgs / 192.0;
-      const double mem = (w + 0.5 * x + part) / 8.0e12;
-      double cost;
-      if (big) {
-        const double waves = ceil(wgs / 256.0);
-        const double cmp = flops / 0.8e15 * (waves * 256.0 / wgs);
-        cost = fmax(mem / fill, cmp);
-      } else {
-        cost = fmax(mem, flops / 1.2e15) / fill;
-      }
+      const double cost = plan_cost(c, sp, M, N, K);
       if (cost < best_cost * 0.999) {
         best_cost = cost;
-        best.kind = 1;
-        best.bm = c.bm;
-        best.bn = c.bn;
-        best.mt = c.mt;
-        best.nw = c.nw;
-        best.splits = sp;
-        best.k_per_split = kps_blocks * BK;
-        // X prefetched as deep as W where that variant is built (measured a little faster)
-        best.xd = ((c.mt == 8 && c.nw == 2) || (c.mt == 16 && c.nw == 1)) ? 4 : 2;
+        plan_take(best, c, sp, kps_blocks);
       }
     }
   }
@@ -443,9 +654,10 @@ GemmPlan gemm_plan(int M, int N, int K, int dtype, int force_splits) {
   return best;
 }
 
-// Gated gate|up GEMM: the weight-streaming kernel with paired tiles, no K split
-// (the SwiGLU needs complete sums); 64 features per workgroup, 128-row tiles
-// beyond M = 64.
+// Gated gate|up GEMM (N = features): no K split (the SwiGLU needs complete
+// sums).  Weight streaming with paired tiles (64 features per workgroup,
+// 128-row tiles beyond M = 64), or for M > 256 the tile kernel (128 features
+// per workgroup) when the same cost model prefers it.
 GemmPlan gemm_plan_gated(int M, int N, int K, int dtype) {
   GemmPlan p;
   p.kind = -1;
@@ -459,6 +671,16 @@ GemmPlan gemm_plan_gated(int M, int N, int K, int dtype) {
   p.k_per_split = K;
   p.pd = 4;
   p.xd = p.mt == 8 ? 4 : 2;
+  if (M > 256) {
+    // both read 2N weight rows; the streaming tile covers 64 features, the LDS tile 128
+    const Cand stream = {1, 128, 128, 8, 2}, tile = {3, 256, 256, 0, 0};
+    if (plan_cost(tile, 1, M, 2 * N, K) < plan_cost(stream, 1, M, 2 * N, K)) {
+      p.kind = 3;
+      p.bm = 256;
+      p.bn = 256;
+      p.mt = p.nw = 0;
+    }
+  }
   return p;
 }
 
@@ -480,6 +702,22 @@ hipError_t launch_stream(const GemmArgs& a, dim3 g1, int kps, int mtl, int ntl, 
     hipLaunchKernelGGL((gemm_stream_bf16<MT, NW, PD, XD, true, false>), g1, dim3(512), 0, s, a, kps, mtl, ntl);
   else
     hipLaunchKernelGGL((gemm_stream_bf16<MT, NW, PD, XD, false, false>), g1, dim3(512), 0, s, a, kps, mtl, ntl);
+  return hipGetLastError();
+}
+
+template <int BM, int BN>
+hipError_t launch_tile(const GemmArgs& a, dim3 g1, int kps, int mtl, int ntl, hipStream_t s) {
+  if (a.gated) {
+    if (a.packed)
+      hipLaunchKernelGGL((gemm_tile_bf16<BM, BN, true, true>), g1, dim3(512), 0, s, a, kps, mtl, ntl);
+    else
+      hipLaunchKernelGGL((gemm_tile_bf16<BM, BN, false, true>), g1, dim3(512), 0, s, a, kps, mtl, ntl);
+  } else {
+    if (a.packed)
+      hipLaunchKernelGGL((gemm_tile_bf16<BM, BN, true, false>), g1, dim3(512), 0, s, a, kps, mtl, ntl);
+    else
+      hipLaunchKernelGGL((gemm_tile_bf16<BM, BN, false, false>), g1, dim3(512), 0, s, a, kps, mtl, ntl);
+  }
   return hipGetLastError();
 }
 
@@ -505,6 +743,27 @@ hipError_t launch_gemm(const GemmArgs& a, const GemmPlan& p, int dtype, hipStrea
     DFS_STREAM(8, 2, 4, 4)
     DFS_STREAM(16, 1, 4, 4)
 #undef DFS_STREAM
+    return hipErrorInvalidValue;
+  }
+  if (p.kind == 3) {   // LDS-ring tile kernel; gated tiles cover bn/2 features
+    // its direct-to-LDS loads take 16-byte aligned rows; otherwise the 128 x 128
+    // streaming tile with the same split count (same workspace)
+    bool aligned = ((uintptr_t)a.X & 15) == 0 && (a.ldx & 7) == 0;
+    for (int i = 0; i < (a.gated ? 2 : a.nseg); ++i) aligned = aligned && ((uintptr_t)a.seg[i].w & 15) == 0;
+    if (!aligned) {
+      GemmPlan q = p;
+      q.kind = 1;
+      q.bm = 128;
+      q.bn = a.gated ? 64 : 128;
+      q.mt = 8;
+      q.nw = 2;
+      q.pd = 4;
+      q.xd = 4;
+      return launch_gemm(a, q, dtype, s);
+    }
+    const int mtl = ceil_div(a.M, p.bm), ntl = ceil_div(a.N, a.gated ? p.bn / 2 : p.bn);
+    const dim3 g1(mtl * ntl * p.splits);
+    if (p.bm == 256 && p.bn == 256) return launch_tile<256, 256>(a, g1, kps, mtl, ntl, s);
     return hipErrorInvalidValue;
   }
   return hipErrorInvalidValue;

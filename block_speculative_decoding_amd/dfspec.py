@@ -25,7 +25,7 @@ EXPORTS = [
     "spec_verify_workspace_size", "spec_verify", "dfs_status_string",
     "dfs_block_attention_workspace_size", "dfs_block_attention",
     "dfs_gemm_workspace_size", "dfs_gemm", "dfs_profile_begin", "dfs_profile_end",
-    "dfs_packed_matrix_bytes", "dfs_pack_matrix",
+    "dfs_packed_matrix_bytes", "dfs_pack_matrix", "dfs_gemm_swiglu",
 ]
 
 
@@ -71,6 +71,7 @@ def _load():
                                                vp, vp, vp, vp, sz, vp]),
         "dfs_gemm_workspace_size": (sz, [i32, i32, i32, i32, i32]),
         "dfs_gemm": (ctypes.c_int, [i32, i32, i32, i32, vp, vp, vp, i32, i32, vp, sz, vp]),
+        "dfs_gemm_swiglu": (ctypes.c_int, [i32, i32, i32, vp, vp, vp, vp, i32, vp]),
         "dfs_packed_matrix_bytes": (sz, [i32, i32]),
         "dfs_pack_matrix": (ctypes.c_int, [i32, i32, vp, vp, vp]),
         "dfs_profile_begin": (ctypes.c_int, [ctypes.c_char_p, i32]),
@@ -290,6 +291,20 @@ def dfs_gemm(X, W, Y, splits: int, workspace, stream=None, w_packed: bool = Fals
                       _ptr(Y, torch.float32, M * N, "Y"), splits, int(w_packed),
                       _ptr(workspace, torch.uint8, None, "workspace"), workspace.numel(), _stream(stream))
     _check(st, "dfs_gemm")
+
+
+def dfs_gemm_swiglu(X, Wg, Wu, H, stream=None, w_packed: bool = False):
+    """H = bf16(silu(X . Wg^T) * (X . Wu^T)); X [M, K], H [M, F] bf16; Wg, Wu [F, K]
+    bf16, or with w_packed their pack_matrix copies."""
+    M, K = X.shape
+    F = H.shape[1]
+    if X.dtype != torch.bfloat16 or H.dtype != torch.bfloat16 or H.shape[0] != M:
+        raise TypeError("dfs_gemm_swiglu takes bf16 X [M, K] and H [M, F]")
+    wn = packed_matrix_bytes(F, K) // 2 if w_packed else F * K
+    st = LIB.dfs_gemm_swiglu(M, F, K, _ptr(X, torch.bfloat16, M * K, "X"), _ptr(Wg, torch.bfloat16, wn, "Wg"),
+                             _ptr(Wu, torch.bfloat16, wn, "Wu"), _ptr(H, torch.bfloat16, M * F, "H"),
+                             int(w_packed), _stream(stream))
+    _check(st, "dfs_gemm_swiglu")
 
 
 def packed_matrix_bytes(rows: int, cols: int) -> int:

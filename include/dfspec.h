@@ -253,6 +253,17 @@ int dfs_gemm(int32_t M, int32_t N, int32_t K, int32_t dtype, const void* X, cons
              float* Y, int32_t splits, int32_t w_packed, void* workspace, size_t workspace_bytes,
              void* stream);
 
+/* H[M, F] bf16 = silu(X . Wg^T) * (X . Wu^T), the gated gate|up product of the
+ * drafter's SwiGLU MLP (the layer form read for the DFlash drafter: pre-norm
+ * attention then a SwiGLU MLP), computed in the epilogue of the drafter's
+ * matrix-core GEMM: fp32 sums, silu and product in fp32, one rounding to bf16.
+ * X [M, K] bf16 row-major; Wg, Wu [F, K] bf16, both row-major or both
+ * tile-packed (w_packed = 1, see below); H [M, F] bf16 row-major.  All device
+ * pointers, caller-owned, no workspace; runs on `stream`.  DFS_EINVAL for null
+ * pointers or non-positive sizes, DFS_EUNSUPPORTED unless K is a multiple of 64. */
+int dfs_gemm_swiglu(int32_t M, int32_t F, int32_t K, const void* X, const void* Wg, const void* Wu,
+                    void* H, int32_t w_packed, void* stream);
+
 /* Weight layout for the matrix-core kernels.  A bf16 matrix W [rows, cols]
  * (cols a multiple of 64) becomes ceil(rows/16) x (cols/64) tiles of 16 rows x
  * 64 columns, row-tile major; each 2 KB tile holds [half h = 0..1][lane l =

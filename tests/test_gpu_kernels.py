@@ -23,8 +23,12 @@ def D():
 
 # ---------------------------------------------------------------- GEMM (matrix cores)
 
+# M > 256 with enough columns is planned onto the LDS-ring tile kernel (256 x 256
+# tiles): (640, 8200, 1024) with its automatic 2-way K split and a forced 3-way
+# one, (600, 16400, 512) unsplit; ragged in both M and N.
 @pytest.mark.parametrize("M,N,K,splits", [(1, 64, 64, 0), (120, 300, 256, 0), (120, 300, 256, 3),
-                                          (256, 1000, 512, 7), (64, 128, 4096, 0), (130, 4096, 1024, 0)])
+                                          (256, 1000, 512, 7), (64, 128, 4096, 0), (130, 4096, 1024, 0),
+                                          (640, 8200, 1024, 0), (640, 8200, 1024, 3), (600, 16400, 512, 0)])
 def test_gemm_bf16_matches_fp64_product(D, M, N, K, splits):
     say(f"gemm bf16 M={M} N={N} K={K} splits={splits}")
     X = rng.normal(1, "gx", (M, K), 1.0, dtype="bf16")
@@ -62,7 +66,8 @@ def test_pack_matrix_layout(D, N, K):
 
 
 @pytest.mark.parametrize("M,N,K,splits", [(1, 64, 64, 0), (120, 300, 256, 3), (128, 1000, 512, 0),
-                                          (256, 1000, 512, 7), (300, 200, 256, 0), (130, 4096, 1024, 0)])
+                                          (256, 1000, 512, 7), (300, 200, 256, 0), (130, 4096, 1024, 0),
+                                          (640, 8200, 1024, 0)])
 def test_gemm_packed_weights_bit_identical(D, M, N, K, splits):
     # same operands in the same order: the packed and row-major kernels agree bit for bit
     import torch
@@ -78,6 +83,33 @@ def test_gemm_packed_weights_bit_identical(D, M, N, K, splits):
     assert np.array_equal(down(Y0).view(np.uint32), down(Y1).view(np.uint32))
     want = as_f64(X, "bf16") @ as_f64(W, "bf16").T
     np.testing.assert_allclose(down(Y1).astype(np.float64), want, atol=2e-5 * np.sqrt(K), rtol=1e-5)
+
+
+# (48, 1000, 256) and (320, 1536, 512) run the weight-streaming kernel with paired
+# gate/up tiles; (700, 8200, 1024) is planned onto the LDS-ring tile kernel
+# (ragged M, and F not a multiple of 16).
+@pytest.mark.parametrize("M,F,K", [(48, 1000, 256), (320, 1536, 512), (700, 8200, 1024)])
+def test_gemm_swiglu_matches_fp64(D, M, F, K):
+    import torch
+    say(f"gemm swiglu M={M} F={F} K={K}")
+    X = rng.normal(3, "sx", (M, K), 1.0, dtype="bf16")
+    Wg = rng.normal(3, "sg", (F, K), 0.05, dtype="bf16")
+    Wu = rng.normal(3, "su", (F, K), 0.05, dtype="bf16")
+    Xd, Wgd, Wud = up(X, "bf16").view(M, K), up(Wg, "bf16").view(F, K), up(Wu, "bf16").view(F, K)
+    H0 = torch.full((M, F), float("nan"), dtype=torch.bfloat16, device=DEV)
+    H1 = torch.full((M, F), float("nan"), dtype=torch.bfloat16, device=DEV)
+    D.dfs_gemm_swiglu(Xd, Wgd, Wud, H0)
+    D.dfs_gemm_swiglu(Xd, D.pack_matrix(Wgd), D.pack_matrix(Wud), H1, w_packed=True)
+    torch.cuda.synchronize()
+    # same sums in the same order: packed and row-major agree bit for bit
+    assert torch.equal(H0.view(torch.int16), H1.view(torch.int16))
+    x = as_f64(X, "bf16")
+    g = x @ as_f64(Wg, "bf16").T
+    u = x @ as_f64(Wu, "bf16").T
+    want = g / (1.0 + np.exp(-g)) * u
+    got = H0.float().cpu().numpy().astype(np.float64)
+    # one bf16 rounding (<= 2^-9 relative) of a value whose fp32 sums carry ~1e-6 relative error
+    np.testing.assert_allclose(got, want, rtol=2.0 ** -8, atol=3e-4)
 
 
 def test_gemm_f32(D):
