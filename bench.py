@@ -265,10 +265,10 @@ def summarize_rocprof(d, steps):
 def sweeps(steps, warmup):
     """Secondary measurements: draft time vs block size (the block drafter's cost
     should be nearly flat in the block size) and the Markov head's share of the
-    step at draft lengths 4 and 15 (the pages quote a 0.2-1.3 % latency cost for
+    step at draft lengths 4 and 16 (the pages quote a 0.2-1.3 % latency cost for
     going from 4 to 16 draft tokens).  One JSON line per point."""
     base = None
-    for S in (4, 8, 16):
+    for S in (4, 8, 16, 32):
         w = WORKLOADS["C1"].with_(name=f"dflash_bf16_b8_s{S}_c4096_v151936", block=S)
         st = Step(w, reuse=base)
         base = base or st
@@ -279,7 +279,7 @@ def sweeps(steps, warmup):
         print(json.dumps({"sweep": "block", "workload": w.name, "block": S, "gamma": S - 1,
                           "ms_per_step": ms, "gemm_ms_per_step": tot / steps}), flush=True)
     base = None
-    for S in (5, 16):
+    for S in (5, 17):   # draft lengths 4 and 16
         w = WORKLOADS["C2"].with_(name=f"dspark_markov_bf16_b32_s{S}_c4096_v129280", block=S)
         st = Step(w, reuse=base)
         base = base or st

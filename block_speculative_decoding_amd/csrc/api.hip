@@ -36,7 +36,7 @@ int check_cfg(const dfs_drafter_cfg* c) {
   const long R = (long)(c->n_q_heads / c->n_kv_heads) * c->block;
   if (c->dtype == DFS_BF16) {
     if (c->head_dim != 128 || c->hidden % 64 || (c->n_q_heads * c->head_dim) % 64 || c->mlp_dim % 64 ||
-        ((long)c->n_target_layers * c->hidden) % 64 || R > 64)
+        ((long)c->n_target_layers * c->hidden) % 64 || R > 256)
       return DFS_EUNSUPPORTED;
   } else {
     if (c->head_dim > 256 || R > 256) return DFS_EUNSUPPORTED;
@@ -275,7 +275,8 @@ int dflash_draft_step(const dfs_drafter_cfg* cfg, const dfs_drafter_weights* wt,
     na.eps = cfg->rms_eps;
     DFS_TRY(launch_norm(na, dt, s));
   }
-  const AttnPlan ap = attn_plan(d.B, d.nkv, ctx_bound, dt);
+  const int rgs = dt == DFS_BF16 ? ceil_div(d.R, 64) : 1;   // 64-row groups of the R query rows
+  const AttnPlan ap = attn_plan(d.B, d.nkv, ctx_bound, dt, rgs);
   const GemmPlan gated = gemm_plan_gated(d.Mb, d.F, d.H, dt);
   const size_t layer_cache = (size_t)d.B * d.nkv * d.max_ctx * d.d * es;
   for (int l = 0; l < d.L; ++l) {
@@ -325,6 +326,7 @@ int dflash_draft_step(const dfs_drafter_cfg* cfg, const dfs_drafter_weights* wt,
     aa.Rpad = d.Rpad;
     aa.keys_per_split = ap.keys_per_split;
     aa.n_ctx_splits = ap.n_ctx_splits;
+    aa.row_groups = rgs;
     DFS_TRY(launch_attention(aa, dt, s));
     // 4. O projection, residual add, MLP pre-norm
     DFS_TRY(run_gemm(w.attn_o, d.nq * d.d, d.Mb, d.H, d.nq * d.d, wt->wo[l], nullptr, 0, nullptr, 0, w.part, dt,
@@ -538,7 +540,8 @@ size_t dfs_block_attention_workspace_size(int32_t batch, int32_t block, int32_t 
   cv.take<char>((size_t)batch * n_kv_heads * Rpad * head_dim * es);
   cv.take<char>((size_t)batch * n_kv_heads * 64 * head_dim * es);
   cv.take<char>((size_t)batch * n_kv_heads * head_dim * 64 * es);
-  const AttnPlan ap = attn_plan(batch, n_kv_heads, ctx_bound, dtype);
+  const int rgs = dtype == DFS_BF16 ? ceil_div(R, 64) : 1;   // 64-row groups of the R query rows
+  const AttnPlan ap = attn_plan(batch, n_kv_heads, ctx_bound, dtype, rgs);
   cv.take<float>(attn_partial_elems(ap.n_ctx_splits + 1, batch, n_kv_heads, Rpad, head_dim));
   cv.take<float>((size_t)batch * n_kv_heads * (ap.n_ctx_splits + 1) * Rpad * 2);
   return cv.off + 256;
@@ -554,7 +557,7 @@ int dfs_block_attention(int32_t batch, int32_t block, int32_t n_q_heads, int32_t
     return DFS_EINVAL;
   const int R = n_q_heads / n_kv_heads * block, Rpad = (R + 15) / 16 * 16;
   if (block > 64 || max_ctx % 64 || batch > 65535) return DFS_EUNSUPPORTED;
-  if (dtype == DFS_BF16 && (head_dim != 128 || R > 64)) return DFS_EUNSUPPORTED;
+  if (dtype == DFS_BF16 && (head_dim != 128 || R > 256)) return DFS_EUNSUPPORTED;
   if (dtype == DFS_F32 && (head_dim > 256 || R > 256)) return DFS_EUNSUPPORTED;
   if (workspace_bytes <
       dfs_block_attention_workspace_size(batch, block, n_q_heads, n_kv_heads, head_dim, ctx_bound, dtype))
@@ -565,7 +568,8 @@ int dfs_block_attention(int32_t batch, int32_t block, int32_t n_q_heads, int32_t
   char* q_att = cv.take<char>((size_t)batch * n_kv_heads * Rpad * head_dim * es);
   char* kb = cv.take<char>((size_t)batch * n_kv_heads * 64 * head_dim * es);
   char* vb = cv.take<char>((size_t)batch * n_kv_heads * head_dim * 64 * es);
-  const AttnPlan ap = attn_plan(batch, n_kv_heads, ctx_bound, dtype);
+  const int rgs = dtype == DFS_BF16 ? ceil_div(R, 64) : 1;   // 64-row groups of the R query rows
+  const AttnPlan ap = attn_plan(batch, n_kv_heads, ctx_bound, dtype, rgs);
   float* po = cv.take<float>(attn_partial_elems(ap.n_ctx_splits + 1, batch, n_kv_heads, Rpad, head_dim));
   float* pml = cv.take<float>((size_t)batch * n_kv_heads * (ap.n_ctx_splits + 1) * Rpad * 2);
   DFS_TRY(launch_attn_stage(q, k_blk, v_blk, q_att, kb, vb, batch, block, n_q_heads, n_kv_heads, head_dim, Rpad,
@@ -591,6 +595,7 @@ int dfs_block_attention(int32_t batch, int32_t block, int32_t n_q_heads, int32_t
   aa.Rpad = Rpad;
   aa.keys_per_split = ap.keys_per_split;
   aa.n_ctx_splits = ap.n_ctx_splits;
+  aa.row_groups = rgs;
   DFS_TRY(launch_attention(aa, dtype, s));
   return DFS_OK;
 }

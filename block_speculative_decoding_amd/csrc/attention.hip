@@ -4,8 +4,9 @@
 // and all S block keys).
 //
 // bf16 path (matrix cores, v_mfma_f32_16x16x32_bf16).  The work unit is
-// (batch row b, key/value head g, key range); its queries are the
-// R = (nq/nkv)*S rows of the GQA group (<= 64).  A 4-wave workgroup streams the
+// (batch row b, key/value head g, key range, group of 64 query rows); its
+// queries are up to 64 of the R = (nq/nkv)*S rows of the GQA group (R > 64
+// — long blocks — takes several groups, each reading the unit's keys).  A 4-wave workgroup streams the
 // unit's K and V^T tiles through LDS once and each wave multiplies them against
 // its own 16 query rows (details at the kernel).  Context keys are split over
 // units so that the grid fills the GPU; one extra unit per (b, g) takes the S
@@ -57,10 +58,11 @@ __global__ __launch_bounds__(256) void attn_bf16_d128(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) bf16_t Ks[2][KS * kKLd];
   __shared__ __attribute__((aligned(16))) bf16_t Vs[2][D * kVLd];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, c = lane & 15, g4 = lane >> 4;
-  const int pairs = a.B * a.nkv, nctx = pairs * a.n_ctx_splits;
+  const int pairs = a.B * a.nkv, rgs = a.row_groups, nctx = pairs * rgs * a.n_ctx_splits;
   const int id = blockIdx.x;
   const int unit = id < nctx ? id % a.n_ctx_splits : a.n_ctx_splits;
-  const int pair = id < nctx ? id / a.n_ctx_splits : id - nctx;
+  const int rest = id < nctx ? id / a.n_ctx_splits : id - nctx;
+  const int rg = rest % rgs, pair = rest / rgs;          // 64-row group of the R query rows
   const int g = pair % a.nkv, b = pair / a.nkv;
   const int units = a.n_ctx_splits + 1;
   const size_t bg = (size_t)b * a.nkv + g;
@@ -122,9 +124,9 @@ __global__ __launch_bounds__(256) void attn_bf16_d128(AttnArgs a) {
     }
   };
 
-  // this wave's queries as the B operand of S^T: row 16*wave + c, dims ds*32 + g4*8 .. +8
-  const int row = wave * 16 + c;
-  const bool active = wave * 16 < a.R;
+  // this wave's queries as the B operand of S^T: row 64*rg + 16*wave + c, dims ds*32 + g4*8 .. +8
+  const int row = rg * 64 + wave * 16 + c;
+  const bool active = rg * 64 + wave * 16 < a.R;
   bf16x8 qf[4];
   const bf16_t* Q = (const bf16_t*)a.q + (bg * a.Rpad + min(row, a.Rpad - 1)) * D;
 #pragma unroll
@@ -371,14 +373,14 @@ hipError_t launch_attn_stage(const void* q, const void* k, const void* v, void* 
   return hipGetLastError();
 }
 
-AttnPlan attn_plan(int B, int nkv, int ctx_bound, int dtype) {
+AttnPlan attn_plan(int B, int nkv, int ctx_bound, int dtype, int row_groups) {
   AttnPlan p;
   if (dtype != 1) {
     p.keys_per_split = ctx_bound;
     p.n_ctx_splits = 0;
     return p;
   }
-  const int pairs = B * nkv;
+  const int pairs = B * nkv * row_groups;
   int splits = ceil_div(kAttnTargetUnits, pairs);    // ~one four-wave context unit per CU
 #ifdef DFS_TUNING
   if (const char* f = getenv("DFS_ATTN_SPLITS")) splits = atoi(f);
@@ -417,7 +419,7 @@ hipError_t launch_attention(const AttnArgs& a, int dtype, hipStream_t s) {
     hipLaunchKernelGGL(attn_f32, dim3(a.S, a.nq, a.B), dim3(256), 0, s, a);
     return hipGetLastError();
   }
-  const dim3 grid((unsigned)(a.B * a.nkv * (a.n_ctx_splits + 1)));
+  const dim3 grid((unsigned)(a.B * a.nkv * a.row_groups * (a.n_ctx_splits + 1)));
   hipLaunchKernelGGL(attn_bf16_d128, grid, dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

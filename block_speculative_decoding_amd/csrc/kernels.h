@@ -36,7 +36,7 @@ struct GemmArgs {
 };
 
 struct GemmPlan {
-  int kind = 1;            // 1: bf16 weight streaming, 3: bf16 LDS-ring tile, 2: fp32 VALU
+  int kind = 1;            // 1: bf16 weight streaming, 3: bf16 LDS-ring tile, 4: bf16 small-M rows, 2: fp32 VALU
   int bm = 128, bn = 128, mt = 8, nw = 2, splits = 1, k_per_split = 0;
   int pd = 4, xd = 2;      // weight-streaming kernel: k steps of W / X in flight per wave
 };
@@ -67,11 +67,12 @@ struct AttnArgs {
   int B, S, nq, nkv, d, max_ctx, ctx_bound;
   int R, Rpad;          // rows per kv head = (nq/nkv)*S, padded to 16
   int keys_per_split, n_ctx_splits;   // units = n_ctx_splits + 1 (last = block keys)
+  int row_groups = 1;   // bf16: the R rows in groups of 64, one workgroup per (unit, group)
 };
 struct AttnPlan {
   int keys_per_split, n_ctx_splits;
 };
-AttnPlan attn_plan(int B, int nkv, int ctx_bound, int dtype);
+AttnPlan attn_plan(int B, int nkv, int ctx_bound, int dtype, int row_groups = 1);
 int attn_max_units(int B, int nkv, int max_ctx, int dtype);
 size_t attn_partial_elems(int units, int B, int nkv, int Rpad, int d);
 hipError_t launch_attention(const AttnArgs& a, int dtype, hipStream_t s);

@@ -154,7 +154,7 @@ size_t dflash_draft_workspace_size(const dfs_drafter_cfg* cfg, int32_t batch, in
  * base_logits [B, S-1, V] fp32, out.
  *
  * DFS_EUNSUPPORTED for cfg.dtype == DFS_BF16 unless head_dim == 128,
- * hidden, nq*d, mlp_dim, nT*H are multiples of 64 and (nq/nkv)*S <= 64;
+ * hidden, nq*d, mlp_dim, nT*H are multiples of 64 and (nq/nkv)*S <= 256;
  * for DFS_F32 unless head_dim <= 256 and (nq/nkv)*S <= 256.
  */
 int dflash_draft_step(const dfs_drafter_cfg* cfg, const dfs_drafter_weights* weights,

@@ -28,6 +28,8 @@ CASES = {
     # 320 block rows: every GEMM in its matrix-core-bound plan (128-row tiles,
     # ragged last tile), the gated MLP GEMM over three M tiles
     "medium_b20_packed": (MEDIUM.with_(batch=20), 6, None, None, None, True),
+    # a 32-token block: 128 query rows per kv head, attention in two 64-row groups
+    "medium_s32": (MEDIUM.with_(batch=2, block=32), 7, None, None, None),
 }
 
 
