@@ -291,6 +291,114 @@ def sweeps(steps, warmup):
                           "markov_ms_per_step": tot / steps, "markov_share": tot / steps / ms}), flush=True)
 
 
+def loop_bench(wl, K, R, sigma=1.0, seed=0):
+    """On-device multi-step loop: K cycles of draft -> sample -> [synthetic target]
+    -> verify -> advance captured into one HIP graph and replayed R times, the
+    accepted count of each cycle driving the next append on the device.  Targets
+    are the final draft rows plus N(0, sigma^2) noise, the bonus row N(0, 3^2),
+    so acceptance is partial.  Reports time per cycle (graph and eager), the
+    synthetic-target time alone, the mean tokens committed per cycle (tau) and
+    L = (cycle time without the synthetic target) / tau.  One JSON line."""
+    import torch
+    from block_speculative_decoding_amd import dfspec as D
+    from block_speculative_decoding_amd.loop import SpecLoop
+    w0 = WORKLOADS[wl]
+    B, S, G, V = w0.batch, w0.block, w0.gamma, w0.vocab
+    total = K * (R + 2)                      # eager warm-up, eager timed, R graph replays
+    w = w0.with_(ctx=w0.ctx + total * S + 64)   # cache capacity for every cycle's append
+    dev = "cuda"
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+
+    def up(a, kind):
+        a = np.ascontiguousarray(a)
+        if kind == "bf16":
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    cfg = D.DrafterConfig.of(w)
+    np_w = inputs.drafter_weights(w0, seed)
+    wdev = D.DrafterWeights(cfg, {k: up(v, w.dtype) for k, v in np_w.items()}, packed=w.dtype == "bf16")
+    del np_w
+    L, nkv, d, M = w.n_layers, w.n_kv_heads, w.head_dim, w.max_ctx
+    # cache contents below the starting context (device-generated; their values do not matter here)
+    kl = (torch.randn((L, B, M, nkv, d), generator=gen, device=dev) * 1.28).to(tdt)
+    vl = (torch.randn((L, B, M, nkv, d), generator=gen, device=dev) * 1.28).to(tdt)
+    k, v = D.cache_from_logical(kl, vl)
+    del kl, vl
+    ctx0 = torch.full((B,), w0.ctx - S, dtype=torch.int32, device=dev)
+    last0 = torch.randint(0, V - 1, (B,), generator=gen, device=dev, dtype=torch.int32)
+    n0 = torch.full((B,), S, dtype=torch.int32, device=dev)
+    U = Wt = None
+    packed = False
+    if w.markov_rank > 0:
+        Un, Wn = inputs.markov_factors(w0, seed)
+        U, Wt = up(Un, w.dtype).view(V, w.markov_rank), up(Wn, w.dtype).view(V, w.markov_rank)
+        packed = w.dtype == "bf16"
+        if packed:
+            Wt = D.pack_matrix(Wt)
+    lp = SpecLoop(cfg, wdev, k, v, ctx0, last0, n0, w.temperature, U, Wt, wt_packed=packed)
+    nT_H = w.n_target_layers * w.hidden
+    pool = [dict(h=torch.randn((B, S, nT_H), generator=gen, device=dev).to(tdt),
+                 ud=torch.rand((B, G), generator=gen, device=dev) * 0.999999,
+                 ua=torch.rand((B, G), generator=gen, device=dev) * 0.999999,
+                 uf=torch.rand((B,), generator=gen, device=dev) * 0.999999,
+                 nz=torch.randn((B, S, V), generator=gen, device=dev)) for _ in range(K)]
+    for p_ in pool:
+        p_["nz"][:, :G].mul_(sigma)
+        p_["nz"][:, G].mul_(3.0)
+
+    def target_fn(nz):
+        def f(final, target):
+            target[:, :G].copy_(final)
+            target[:, :G].add_(nz[:, :G])
+            target[:, G].copy_(nz[:, G])
+        return f
+
+    def run():
+        for p_ in pool:
+            lp.cycle(p_["h"], p_["ud"], p_["ua"], p_["uf"], target_fn(p_["nz"]))
+
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    run()                                     # eager warm-up
+    torch.cuda.synchronize()
+    ev[0].record()
+    run()
+    ev[1].record()
+    torch.cuda.synchronize()
+    eager_ms = ev[0].elapsed_time(ev[1]) / K
+    ev[0].record()
+    for p_ in pool:
+        target_fn(p_["nz"])(lp.logits, lp.target)
+    ev[1].record()
+    torch.cuda.synchronize()
+    synth_ms = ev[0].elapsed_time(ev[1]) / K
+    g = torch.cuda.CUDAGraph()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        with torch.cuda.graph(g, stream=st):
+            run()
+    torch.cuda.current_stream().wait_stream(st)
+    torch.cuda.synchronize()
+    lp.tau_sum.zero_()
+    ev[0].record()
+    for _ in range(R):
+        g.replay()
+    ev[1].record()
+    torch.cuda.synchronize()
+    graph_ms = ev[0].elapsed_time(ev[1]) / (K * R)
+    tau = float(lp.tau_sum.double().sum().item()) / (B * K * R)
+    core_ms = graph_ms - synth_ms
+    print(json.dumps({"loop": w0.name, "cycles": K * R, "cycles_per_graph": K, "graph": True,
+                      "ms_per_cycle": graph_ms, "ms_per_cycle_eager": eager_ms,
+                      "target_synthesis_ms": synth_ms, "mean_tau": tau, "acceptance_rate": (tau - 1.0) / G,
+                      "L_ms_per_token": core_ms / tau, "tokens_per_s": B * tau / (core_ms * 1e-3),
+                      "target": f"final draft logits + N(0, {sigma}^2), bonus row N(0, 3^2)",
+                      "final_ctx_len_max": int(lp.ctx_len.max().item())}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -301,6 +409,10 @@ def main():
     ap.add_argument("--no-roofline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (reference for HBM byte counters)")
+    ap.add_argument("--loop", action="store_true",
+                    help="on-device multi-step loop: cycles captured in a HIP graph, tau and L (JSON line)")
+    ap.add_argument("--loop-cycles", type=int, default=8, help="cycles per captured graph")
+    ap.add_argument("--loop-replays", type=int, default=8, help="graph replays timed")
     ap.add_argument("--sweep", action="store_true",
                     help="secondary measurements: block-size and Markov draft-length sweeps (JSON line per point)")
     ap.add_argument("--summarize-rocprof", metavar="DIR",
@@ -309,12 +421,15 @@ def main():
     if args.summarize_rocprof:
         summarize_rocprof(args.summarize_rocprof, args.steps + args.warmup)
         return
-    if args.sweep:
-        sweeps(args.steps, args.warmup)
-        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build measures one GPU only; --gpus must be 1"}))
         sys.exit(2)
+    if args.sweep:
+        sweeps(args.steps, args.warmup)
+        return
+    if args.loop:
+        loop_bench(args.workload, args.loop_cycles, args.loop_replays)
+        return
     if args.calibrate_copy:
         import torch
         src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")

@@ -324,7 +324,6 @@ int dflash_draft_step(const dfs_drafter_cfg* cfg, const dfs_drafter_weights* wt,
     aa.ctx_bound = ctx_bound;
     aa.R = d.R;
     aa.Rpad = d.Rpad;
-    aa.keys_per_split = ap.keys_per_split;
     aa.n_ctx_splits = ap.n_ctx_splits;
     aa.row_groups = rgs;
     DFS_TRY(launch_attention(aa, dt, s));
@@ -528,6 +527,16 @@ int spec_verify(int32_t batch, int32_t n_draft, int32_t vocab, const float* draf
   return DFS_OK;
 }
 
+// ------------------------------------------------------------------ multi-step loop
+
+int spec_cycle_advance(int32_t batch, int32_t n_draft, const int32_t* n_accepted, const int32_t* out_tokens,
+                       int32_t* n_new, int32_t* last_token, int64_t* tau_sum, void* stream) {
+  if (batch < 1 || n_draft < 0 || !n_accepted || !out_tokens || !n_new || !last_token) return DFS_EINVAL;
+  if (n_draft > 64) return DFS_EUNSUPPORTED;
+  DFS_TRY(launch_advance(batch, n_draft, n_accepted, out_tokens, n_new, last_token, tau_sum, (hipStream_t)stream));
+  return DFS_OK;
+}
+
 // ------------------------------------------------------------------ kernel-level hooks
 
 size_t dfs_block_attention_workspace_size(int32_t batch, int32_t block, int32_t n_q_heads, int32_t n_kv_heads,
@@ -593,7 +602,6 @@ int dfs_block_attention(int32_t batch, int32_t block, int32_t n_q_heads, int32_t
   aa.ctx_bound = ctx_bound;
   aa.R = R;
   aa.Rpad = Rpad;
-  aa.keys_per_split = ap.keys_per_split;
   aa.n_ctx_splits = ap.n_ctx_splits;
   aa.row_groups = rgs;
   DFS_TRY(launch_attention(aa, dtype, s));

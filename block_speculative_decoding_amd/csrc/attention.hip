@@ -76,12 +76,17 @@ __global__ __launch_bounds__(256) void attn_bf16_d128(AttnArgs a) {
     ldv = 64;
     k_begin = 0;
     k_end = a.S;
-  } else {                                   // context keys [unit*kps, (unit+1)*kps) ∩ [0, C_b)
+  } else {
+    // context keys [unit*kps, (unit+1)*kps) ∩ [0, C_b): the row's own C_b split
+    // evenly over the planned units (a loose host bound — a graph-captured loop
+    // passes the cache capacity — then costs no imbalance)
     K = (const bf16_t*)a.k_cache + bg * a.max_ctx * D;
     Vt = (const bf16_t*)a.v_cache + bg * D * a.max_ctx;
     ldv = a.max_ctx;
-    k_begin = unit * a.keys_per_split;
-    k_end = min(min(a.ctx_len[b], a.ctx_bound), k_begin + a.keys_per_split);
+    const int cb = max(0, min(a.ctx_len[b], a.ctx_bound));
+    const int kps = (ceil_div(cb, a.n_ctx_splits) + KS - 1) / KS * KS;
+    k_begin = unit * kps;
+    k_end = min(cb, k_begin + kps);
   }
   const int nsteps = k_end > k_begin ? (k_end - k_begin + KS - 1) / KS : 0;
 

@@ -66,7 +66,7 @@ struct AttnArgs {
   float* part_ml;       // [B][nkv][nunits][Rpad][2]
   int B, S, nq, nkv, d, max_ctx, ctx_bound;
   int R, Rpad;          // rows per kv head = (nq/nkv)*S, padded to 16
-  int keys_per_split, n_ctx_splits;   // units = n_ctx_splits + 1 (last = block keys)
+  int n_ctx_splits;     // units = n_ctx_splits + 1 (last = block keys); a row's C_b is split evenly
   int row_groups = 1;   // bf16: the R rows in groups of 64, one workgroup per (unit, group)
 };
 struct AttnPlan {
@@ -176,5 +176,9 @@ struct VerifyArgs {
   int B, G, V;
 };
 hipError_t launch_verify(const VerifyArgs& a, hipStream_t s);
+
+// ------------------------------------------------------------------ cycle bookkeeping
+hipError_t launch_advance(int B, int G, const int32_t* n_accepted, const int32_t* out_tokens, int32_t* n_new,
+                          int32_t* last_token, int64_t* tau_sum, hipStream_t s);
 
 }  // namespace dfs

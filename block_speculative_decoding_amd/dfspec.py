@@ -25,7 +25,7 @@ EXPORTS = [
     "spec_verify_workspace_size", "spec_verify", "dfs_status_string",
     "dfs_block_attention_workspace_size", "dfs_block_attention",
     "dfs_gemm_workspace_size", "dfs_gemm", "dfs_profile_begin", "dfs_profile_end",
-    "dfs_packed_matrix_bytes", "dfs_pack_matrix", "dfs_gemm_swiglu",
+    "dfs_packed_matrix_bytes", "dfs_pack_matrix", "dfs_gemm_swiglu", "spec_cycle_advance",
 ]
 
 
@@ -72,6 +72,7 @@ def _load():
         "dfs_gemm_workspace_size": (sz, [i32, i32, i32, i32, i32]),
         "dfs_gemm": (ctypes.c_int, [i32, i32, i32, i32, vp, vp, vp, i32, i32, vp, sz, vp]),
         "dfs_gemm_swiglu": (ctypes.c_int, [i32, i32, i32, vp, vp, vp, vp, i32, vp]),
+        "spec_cycle_advance": (ctypes.c_int, [i32, i32, vp, vp, vp, vp, vp, vp]),
         "dfs_packed_matrix_bytes": (sz, [i32, i32]),
         "dfs_pack_matrix": (ctypes.c_int, [i32, i32, vp, vp, vp]),
         "dfs_profile_begin": (ctypes.c_int, [ctypes.c_char_p, i32]),
@@ -305,6 +306,18 @@ def dfs_gemm_swiglu(X, Wg, Wu, H, stream=None, w_packed: bool = False):
                              _ptr(Wu, torch.bfloat16, wn, "Wu"), _ptr(H, torch.bfloat16, M * F, "H"),
                              int(w_packed), _stream(stream))
     _check(st, "dfs_gemm_swiglu")
+
+
+def spec_cycle_advance(n_accepted, out_tokens, n_new, last_token, tau_sum=None, stream=None):
+    """Next cycle's n_new = n_accepted + 1 and last_token = out_tokens[b, n_accepted]
+    (device, no sync); tau_sum (int64, optional) accumulates n_accepted + 1."""
+    B = n_accepted.numel()
+    G = out_tokens.shape[1] - 1
+    st = LIB.spec_cycle_advance(B, G, _ptr(n_accepted, torch.int32, B, "n_accepted"),
+                                _ptr(out_tokens, torch.int32, B * (G + 1), "out_tokens"),
+                                _ptr(n_new, torch.int32, B, "n_new"), _ptr(last_token, torch.int32, B, "last_token"),
+                                _ptr(tau_sum, torch.int64, B, "tau_sum"), _stream(stream))
+    _check(st, "spec_cycle_advance")
 
 
 def packed_matrix_bytes(rows: int, cols: int) -> int:

@@ -226,6 +226,28 @@ int spec_verify(int32_t batch, int32_t n_draft, int32_t vocab, const float* draf
                 int32_t* out_tokens, int32_t* n_accepted, void* workspace,
                 size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------ multi-step loop */
+
+/* Device-side bookkeeping between two cycles, so that draft -> sample -> verify
+ * -> advance -> draft ... runs on one stream with no host synchronisation (and
+ * can be captured into a HIP graph).  Same DSpark page, section "Jak działa
+ * spekulatywne dekodowanie DSpark?": a cycle commits the accepted prefix plus
+ * one token, tau = n_accepted + 1 tokens; the committed tokens are what the
+ * next drafter call appends as context (their target hidden states) and the
+ * last of them starts the next block.  For each row b, a = n_accepted[b]
+ * clamped to [0, n_draft]:
+ *   n_new[b]       = a + 1              (rows the next dflash_draft_step appends)
+ *   last_token[b]  = out_tokens[b, a]   (the correction or bonus token)
+ *   tau_sum[b]    += a + 1              (running count of committed tokens)
+ * n_accepted [B] int32, out_tokens [B, n_draft+1] int32 (spec_verify's outputs,
+ * may alias nothing written here); n_new, last_token [B] int32 out; tau_sum [B]
+ * int64 in/out, or NULL.  No workspace.  DFS_EINVAL for null required pointers,
+ * batch < 1 or n_draft < 0; DFS_EUNSUPPORTED for n_draft > 64.
+ * A graph-captured chain needs host-side bounds that hold for every captured
+ * cycle: dflash_draft_step's n_new_max = S and ctx_bound = the cache capacity. */
+int spec_cycle_advance(int32_t batch, int32_t n_draft, const int32_t* n_accepted, const int32_t* out_tokens,
+                       int32_t* n_new, int32_t* last_token, int64_t* tau_sum, void* stream);
+
 /* ------------------------------------------------------------------ misc */
 
 const char* dfs_status_string(int status);

@@ -121,3 +121,23 @@ def target_logits(w: Workload, seed: int, draft_logits=None, batch=None):
                            dtype="f32")
         t[:, :w.gamma] = np.asarray(draft_logits, np.float32) + noise
     return t
+
+
+def cycle_inputs(w: Workload, seed: int, cycle: int, batch=None) -> dict:
+    """Inputs of cycle ``cycle`` of a multi-step loop, independent across cycles:
+    hidden_new [B, S, nT*H] (target hidden states of the rows the previous cycle
+    committed; rows >= n_new[b] unused), uniforms u_draft, u_accept [B, gamma] and
+    u_final [B], target logits [B, S, V] ~ N(0, std^2), and noise [B, S, V] ~ N(0, 1)
+    for targets built from the draft logits (draft + noise_std * noise)."""
+    B = w.batch if batch is None else batch
+    G, S = w.gamma, w.block
+    k = f"cycle{cycle}."
+    return {
+        "hidden_new": rng.normal(seed, k + "hidden_new", (B, S, w.n_target_layers * w.hidden), w.hidden_std,
+                                 dtype=w.dtype),
+        "u_draft": rng.uniform01(seed, k + "u_draft", (B, G)),
+        "u_accept": rng.uniform01(seed, k + "u_accept", (B, G)),
+        "u_final": rng.uniform01(seed, k + "u_final", (B,)),
+        "target_logits": rng.normal(seed, k + "target_logits", (B, S, w.vocab), w.target_logit_std, dtype="f32"),
+        "noise": rng.normal(seed, k + "target_noise", (B, S, w.vocab), 1.0, dtype="f32"),
+    }

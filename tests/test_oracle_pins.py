@@ -540,3 +540,86 @@ def test_latency_bookkeeping_closed_forms_and_page_figures():
         L = oracle.latency_per_token(0.3 * (1 + ov), 0.7 * (1 + ov), tau0 * (1 + gain))
         assert np.isclose(L / base_L, (1 + ov) / (1 + gain))
     assert 0.770 < (1 + lo) / (1 + gain) < (1 + hi) / (1 + gain) < 0.780
+
+
+# ---------------------------------------------------------------- multi-step loop
+
+def test_loop_advance_hand_cases():
+    from oracle import loop
+    # gamma = 3: out_tokens = accepted drafts, then the correction/bonus token, then -1
+    out = np.array([[7, -1, -1, -1],        # rejected at the first draft: correction 7
+                    [4, 5, 6, 9],           # all three accepted: bonus 9
+                    [4, 5, 8, -1],          # two accepted, correction 8
+                    [3, -1, -1, -1]])       # an out-of-range count (-2) is clamped to 0
+    n_new, last, tau = loop.advance(np.array([0, 3, 2, -2]), out, 3)
+    assert n_new.tolist() == [1, 4, 3, 1]
+    assert last.tolist() == [7, 9, 8, 3]
+    assert tau.tolist() == [1, 4, 3, 1]
+    # a count above gamma is clamped to gamma (the bonus slot)
+    n_new, last, _ = loop.advance(np.array([5]), np.array([[1, 2, 3, 4]]), 3)
+    assert n_new.tolist() == [4] and last.tolist() == [4]
+
+
+def _loop_setup(cycles, seed=3):
+    w = TINY.with_(batch=2)
+    weights = inputs.drafter_weights(w, seed, gain_std=0.1)
+    ctx0 = np.array([100, 61], np.int32)                 # room for every cycle's append below max_ctx
+    kc, vc = inputs.cache_prefix(w, seed, ctx0)
+    U, Wt = inputs.markov_factors(w, seed, std=w.markov_rank ** -0.25)
+    last0 = rng.integers(seed, "last_token", (w.batch,), 0, w.vocab - 1)
+    n0 = np.full(w.batch, w.block, np.int32)
+    cins = [inputs.cycle_inputs(w, seed, c) for c in range(cycles)]
+    return w, weights, ctx0, kc, vc, U, Wt, last0, n0, cins
+
+
+def test_loop_identical_distributions_commit_the_whole_block_each_cycle():
+    # target rows = the final draft rows (p = q): every draft is accepted, each
+    # cycle commits S tokens, the next block starts from the bonus token and the
+    # context grows by S per cycle (closed form of the loop under p = q)
+    from oracle import loop
+    w, weights, ctx0, kc, vc, U, Wt, last0, n0, cins = _loop_setup(3)
+    S, G = w.block, w.gamma
+
+    def same(c, final):
+        t = cins[c]["target_logits"].copy()
+        t[:, :G] = final
+        return t
+
+    recs = loop.run_cycles(od.DrafterShape.of(w), weights, U, Wt, "f32", kc, vc, ctx0, last0, n0, cins, 1.0,
+                           target_fn=same)
+    for c, r in enumerate(recs):
+        assert r["n_accepted"].tolist() == [G, G]
+        assert np.array_equal(r["out_tokens"][:, :G], r["draft_tokens"])
+        assert r["n_new"].tolist() == [S, S] and r["tau"].tolist() == [S, S]
+        assert np.array_equal(r["last_token"], r["out_tokens"][:, G])
+        assert np.array_equal(r["ctx_len"], ctx0 + S * (c + 1))     # the first cycle appends n0 = S rows
+    # the state each cycle starts from is what the previous cycle left
+    assert np.array_equal(recs[0]["last_token_in"], last0) and np.array_equal(recs[0]["n_new_in"], n0)
+    for prev, nxt in zip(recs, recs[1:]):
+        assert np.array_equal(nxt["last_token_in"], prev["last_token"])
+        assert np.array_equal(nxt["n_new_in"], prev["n_new"])
+
+
+def test_loop_point_mass_target_commits_one_token_per_cycle():
+    # target = a point mass on token t*: a first draft other than t* is rejected
+    # (p = 0), the residual max(0, p - q) is the point mass, so the cycle commits
+    # exactly t*, n_new = 1 and the next block starts from t*
+    from oracle import loop
+    w, weights, ctx0, kc, vc, U, Wt, last0, n0, cins = _loop_setup(3, seed=4)
+    t_star = 17
+
+    def point(c, final):
+        t = np.full((w.batch, w.block, w.vocab), -np.inf, np.float32)
+        t[:, :, t_star] = 0.0
+        return t
+
+    recs = loop.run_cycles(od.DrafterShape.of(w), weights, U, Wt, "f32", kc, vc, ctx0, last0, n0, cins, 1.0,
+                           target_fn=point)
+    ctx = ctx0 + n0
+    for r in recs:
+        for b in range(w.batch):
+            if r["draft_tokens"][b, 0] != t_star:
+                assert r["n_accepted"][b] == 0 and r["out_tokens"][b, 0] == t_star
+                assert r["n_new"][b] == 1 and r["last_token"][b] == t_star
+        assert np.array_equal(r["ctx_len"], ctx)
+        ctx = ctx + r["n_new"]
