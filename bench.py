@@ -46,7 +46,8 @@ def algorithmic_bytes(w):
                        + Mb * nq * d * es + Mb * H * 4 + Mb * H * es + gateup_out
                        + Mb * F * es + Mb * H * 4)
                 + B * G * H * es + B * G * V * 4)
-    attn = L * (B * nkv * (C + S) * d * 2 * es + Mb * nq * d * es * 2)
+    Ck = min(C, w.window) if w.window > 0 else C        # context keys a block row attends
+    attn = L * (B * nkv * (Ck + S) * d * 2 * es + Mb * nq * d * es * 2)
     sample = B * G * V * 4                               # read final logits once
     markov = (V * r * es + B * G * V * 4 * 2) if r > 0 else 0
     verify = B * (G + 1) * V * 4 + 2 * B * V * 4        # target rows + the two rows at the rejection

@@ -31,7 +31,7 @@ int check_cfg(const dfs_drafter_cfg* c) {
   if (c->n_q_heads % c->n_kv_heads != 0 || c->head_dim % 2 != 0) return DFS_EINVAL;
   if (c->mask_token_id < 0 || c->mask_token_id >= c->vocab) return DFS_EINVAL;
   if (c->dtype != DFS_F32 && c->dtype != DFS_BF16) return DFS_EINVAL;
-  if (!(c->rms_eps >= 0.f)) return DFS_EINVAL;
+  if (!(c->rms_eps >= 0.f) || c->window < 0) return DFS_EINVAL;
   if (c->max_ctx % 64 != 0 || c->block > 64 || c->hidden > 8192) return DFS_EUNSUPPORTED;
   const long R = (long)(c->n_q_heads / c->n_kv_heads) * c->block;
   if (c->dtype == DFS_BF16) {
@@ -276,7 +276,7 @@ int dflash_draft_step(const dfs_drafter_cfg* cfg, const dfs_drafter_weights* wt,
     DFS_TRY(launch_norm(na, dt, s));
   }
   const int rgs = dt == DFS_BF16 ? ceil_div(d.R, 64) : 1;   // 64-row groups of the R query rows
-  const AttnPlan ap = attn_plan(d.B, d.nkv, ctx_bound, dt, rgs);
+  const AttnPlan ap = attn_plan(d.B, d.nkv, ctx_bound, dt, rgs, cfg->window);
   const GemmPlan gated = gemm_plan_gated(d.Mb, d.F, d.H, dt);
   const size_t layer_cache = (size_t)d.B * d.nkv * d.max_ctx * d.d * es;
   for (int l = 0; l < d.L; ++l) {
@@ -326,6 +326,7 @@ int dflash_draft_step(const dfs_drafter_cfg* cfg, const dfs_drafter_weights* wt,
     aa.Rpad = d.Rpad;
     aa.n_ctx_splits = ap.n_ctx_splits;
     aa.row_groups = rgs;
+    aa.window = cfg->window;
     DFS_TRY(launch_attention(aa, dt, s));
     // 4. O projection, residual add, MLP pre-norm
     DFS_TRY(run_gemm(w.attn_o, d.nq * d.d, d.Mb, d.H, d.nq * d.d, wt->wo[l], nullptr, 0, nullptr, 0, w.part, dt,
@@ -557,12 +558,12 @@ size_t dfs_block_attention_workspace_size(int32_t batch, int32_t block, int32_t 
 }
 
 int dfs_block_attention(int32_t batch, int32_t block, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
-                        int32_t max_ctx, int32_t ctx_bound, int32_t dtype, const void* q, const void* k_blk,
-                        const void* v_blk, const void* k_cache, const void* v_cache, const int32_t* ctx_len,
-                        void* out, void* workspace, size_t workspace_bytes, void* stream) {
+                        int32_t max_ctx, int32_t ctx_bound, int32_t dtype, int32_t window, const void* q,
+                        const void* k_blk, const void* v_blk, const void* k_cache, const void* v_cache,
+                        const int32_t* ctx_len, void* out, void* workspace, size_t workspace_bytes, void* stream) {
   if (!q || !k_blk || !v_blk || !k_cache || !v_cache || !ctx_len || !out || !workspace) return DFS_EINVAL;
   if (batch < 1 || block < 1 || n_q_heads < 1 || n_kv_heads < 1 || n_q_heads % n_kv_heads || max_ctx < 1 ||
-      ctx_bound < 1 || ctx_bound > max_ctx || (dtype != DFS_F32 && dtype != DFS_BF16))
+      ctx_bound < 1 || ctx_bound > max_ctx || (dtype != DFS_F32 && dtype != DFS_BF16) || window < 0)
     return DFS_EINVAL;
   const int R = n_q_heads / n_kv_heads * block, Rpad = (R + 15) / 16 * 16;
   if (block > 64 || max_ctx % 64 || batch > 65535) return DFS_EUNSUPPORTED;
@@ -578,7 +579,7 @@ int dfs_block_attention(int32_t batch, int32_t block, int32_t n_q_heads, int32_t
   char* kb = cv.take<char>((size_t)batch * n_kv_heads * 64 * head_dim * es);
   char* vb = cv.take<char>((size_t)batch * n_kv_heads * head_dim * 64 * es);
   const int rgs = dtype == DFS_BF16 ? ceil_div(R, 64) : 1;   // 64-row groups of the R query rows
-  const AttnPlan ap = attn_plan(batch, n_kv_heads, ctx_bound, dtype, rgs);
+  const AttnPlan ap = attn_plan(batch, n_kv_heads, ctx_bound, dtype, rgs, window);
   float* po = cv.take<float>(attn_partial_elems(ap.n_ctx_splits + 1, batch, n_kv_heads, Rpad, head_dim));
   float* pml = cv.take<float>((size_t)batch * n_kv_heads * (ap.n_ctx_splits + 1) * Rpad * 2);
   DFS_TRY(launch_attn_stage(q, k_blk, v_blk, q_att, kb, vb, batch, block, n_q_heads, n_kv_heads, head_dim, Rpad,
@@ -604,6 +605,7 @@ int dfs_block_attention(int32_t batch, int32_t block, int32_t n_q_heads, int32_t
   aa.Rpad = Rpad;
   aa.n_ctx_splits = ap.n_ctx_splits;
   aa.row_groups = rgs;
+  aa.window = window;
   DFS_TRY(launch_attention(aa, dtype, s));
   return DFS_OK;
 }

@@ -69,7 +69,7 @@ __global__ __launch_bounds__(256) void attn_bf16_d128(AttnArgs a) {
 
   const bf16_t* K;
   const bf16_t* Vt;
-  int ldv, k_begin, k_end;
+  int ldv, k_begin, k_end, k_lo = 0;
   if (unit == a.n_ctx_splits) {              // the S block keys
     K = (const bf16_t*)a.k_blk + bg * 64 * D;
     Vt = (const bf16_t*)a.v_blk + bg * D * 64;
@@ -83,9 +83,14 @@ __global__ __launch_bounds__(256) void attn_bf16_d128(AttnArgs a) {
     K = (const bf16_t*)a.k_cache + bg * a.max_ctx * D;
     Vt = (const bf16_t*)a.v_cache + bg * D * a.max_ctx;
     ldv = a.max_ctx;
+    // with a sliding window only keys [C_b - window, C_b) count: the range starts
+    // at that key rounded down to a 64-key step (aligned tiles), and the keys in
+    // front of it inside the first step are masked
     const int cb = max(0, min(a.ctx_len[b], a.ctx_bound));
-    const int kps = (ceil_div(cb, a.n_ctx_splits) + KS - 1) / KS * KS;
-    k_begin = unit * kps;
+    k_lo = a.window > 0 ? max(0, cb - a.window) : 0;
+    const int lo = k_lo / KS * KS;
+    const int kps = (ceil_div(cb - lo, a.n_ctx_splits) + KS - 1) / KS * KS;
+    k_begin = lo + unit * kps;
     k_end = min(cb, k_begin + kps);
   }
   const int nsteps = k_end > k_begin ? (k_end - k_begin + KS - 1) / KS : 0;
@@ -163,7 +168,7 @@ __global__ __launch_bounds__(256) void attn_bf16_d128(AttnArgs a) {
     // lane's scores: tile t, reg i -> key k0 + 32*(t/2) + 8*g4 + 4*(t%2) + i of query row `row`
     float v[16];
     float mx = -INFINITY;
-    if (k0 + KS <= k_end) {                              // full step (uniform): no masking
+    if (k0 >= k_lo && k0 + KS <= k_end) {               // full step (uniform): no masking
 #pragma unroll
       for (int t = 0; t < 4; ++t)
 #pragma unroll
@@ -177,7 +182,7 @@ __global__ __launch_bounds__(256) void attn_bf16_d128(AttnArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int key = k0 + 32 * (t >> 1) + 8 * g4 + 4 * (t & 1) + i;
-          v[4 * t + i] = key < k_end ? s[t][i] * sc : -INFINITY;
+          v[4 * t + i] = key < k_end && key >= k_lo ? s[t][i] * sc : -INFINITY;
           mx = fmaxf(mx, v[4 * t + i]);
         }
     }
@@ -311,9 +316,10 @@ __global__ __launch_bounds__(256) void attn_f32(AttnArgs a) {
   __syncthreads();
   const int C = max(0, min(a.ctx_len[b], a.ctx_bound));
   const int total = C + a.S;
+  const int lo = a.window > 0 ? max(0, C - a.window) : 0;   // first context key attended
   const float scale = 1.f / sqrtf((float)d);
   float m_run = -INFINITY, l_run = 0.f, acc = 0.f;   // acc: output dim tid (tid < d)
-  for (int k0 = 0; k0 < total; k0 += CH) {
+  for (int k0 = lo; k0 < total; k0 += CH) {
     const int key = k0 + tid;
     float sv = -INFINITY;
     if (key < total) {
@@ -378,7 +384,8 @@ hipError_t launch_attn_stage(const void* q, const void* k, const void* v, void* 
   return hipGetLastError();
 }
 
-AttnPlan attn_plan(int B, int nkv, int ctx_bound, int dtype, int row_groups) {
+AttnPlan attn_plan(int B, int nkv, int ctx_bound, int dtype, int row_groups, int window) {
+  if (window > 0 && window + 64 < ctx_bound) ctx_bound = window + 64;   // keys a row can attend (step-aligned)
   AttnPlan p;
   if (dtype != 1) {
     p.keys_per_split = ctx_bound;

@@ -68,11 +68,12 @@ struct AttnArgs {
   int R, Rpad;          // rows per kv head = (nq/nkv)*S, padded to 16
   int n_ctx_splits;     // units = n_ctx_splits + 1 (last = block keys); a row's C_b is split evenly
   int row_groups = 1;   // bf16: the R rows in groups of 64, one workgroup per (unit, group)
+  int window = 0;       // > 0: only the last `window` of a row's C_b context keys are attended
 };
 struct AttnPlan {
   int keys_per_split, n_ctx_splits;
 };
-AttnPlan attn_plan(int B, int nkv, int ctx_bound, int dtype, int row_groups = 1);
+AttnPlan attn_plan(int B, int nkv, int ctx_bound, int dtype, int row_groups = 1, int window = 0);
 int attn_max_units(int B, int nkv, int max_ctx, int dtype);
 size_t attn_partial_elems(int units, int B, int nkv, int Rpad, int d);
 hipError_t launch_attention(const AttnArgs& a, int dtype, hipStream_t s);

@@ -39,7 +39,8 @@ class CDrafterCfg(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "n_layers", "hidden", "n_q_heads", "n_kv_heads", "head_dim", "mlp_dim", "vocab",
         "n_target_layers", "block", "max_ctx", "mask_token_id")] + [
-        ("rms_eps", ctypes.c_float), ("rope_theta", ctypes.c_float), ("dtype", ctypes.c_int32)]
+        ("rms_eps", ctypes.c_float), ("rope_theta", ctypes.c_float), ("dtype", ctypes.c_int32),
+        ("window", ctypes.c_int32)]
 
 
 _PP = ctypes.POINTER(ctypes.c_void_p)
@@ -67,7 +68,7 @@ def _load():
         "spec_verify": (ctypes.c_int, [i32, i32, i32, vp, vp, vp, vp, vp, f32, vp, vp, vp, vp, sz, vp]),
         "dfs_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "dfs_block_attention_workspace_size": (sz, [i32, i32, i32, i32, i32, i32, i32]),
-        "dfs_block_attention": (ctypes.c_int, [i32, i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp,
+        "dfs_block_attention": (ctypes.c_int, [i32, i32, i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp,
                                                vp, vp, vp, vp, sz, vp]),
         "dfs_gemm_workspace_size": (sz, [i32, i32, i32, i32, i32]),
         "dfs_gemm": (ctypes.c_int, [i32, i32, i32, i32, vp, vp, vp, i32, i32, vp, sz, vp]),
@@ -139,6 +140,7 @@ class DrafterConfig:
     rms_eps: float
     rope_theta: float
     dtype: int          # DFS_F32 / DFS_BF16
+    window: int = 0     # > 0: sliding attention window over the context (DSpark drafter variant)
 
     @classmethod
     def of(cls, w) -> "DrafterConfig":
@@ -151,7 +153,7 @@ class DrafterConfig:
     def c(self) -> CDrafterCfg:
         return CDrafterCfg(self.n_layers, self.hidden, self.n_q_heads, self.n_kv_heads, self.head_dim,
                            self.mlp_dim, self.vocab, self.n_target_layers, self.block, self.max_ctx,
-                           self.mask_token_id, self.rms_eps, self.rope_theta, self.dtype)
+                           self.mask_token_id, self.rms_eps, self.rope_theta, self.dtype, self.window)
 
 
 class DrafterWeights:
@@ -264,13 +266,13 @@ def dfs_block_attention_workspace_size(batch, block, nq, nkv, d, ctx_bound, dtyp
 
 
 def dfs_block_attention(q, k_blk, v_blk, k_cache, v_cache, ctx_len, out, max_ctx: int, ctx_bound: int,
-                        workspace, stream=None):
+                        workspace, stream=None, window: int = 0):
     B, S, nq, d = q.shape
     nkv = k_blk.shape[2]
     dtype = DFS_BF16 if q.dtype == torch.bfloat16 else DFS_F32
     dt = q.dtype
     st = LIB.dfs_block_attention(
-        B, S, nq, nkv, d, max_ctx, ctx_bound, dtype, _ptr(q, dt, name="q"), _ptr(k_blk, dt, name="k_blk"),
+        B, S, nq, nkv, d, max_ctx, ctx_bound, dtype, int(window), _ptr(q, dt, name="q"), _ptr(k_blk, dt, name="k_blk"),
         _ptr(v_blk, dt, name="v_blk"), _ptr(k_cache, dt, B * nkv * max_ctx * d, "k_cache"),
         _ptr(v_cache, dt, B * nkv * max_ctx * d, "v_cache"), _ptr(ctx_len, torch.int32, B, "ctx_len"),
         _ptr(out, dt, B * S * nq * d, "out"), _ptr(workspace, torch.uint8, None, "workspace"),

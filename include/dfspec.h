@@ -88,6 +88,9 @@ typedef struct {
   float rms_eps;           /* RMSNorm: y = x / sqrt(mean(x^2) + eps) * g */
   float rope_theta;        /* rotate-half rotary base; <= 0 disables rotary embedding */
   int32_t dtype;           /* dfs_dtype of weights, hidden states, caches and activations */
+  int32_t window;          /* > 0: block rows attend only the last `window` context keys (the
+                              DSpark drafter's sliding window, DeepSeek-V4.1 notes page, section
+                              "DSpark — le décodage spéculatif"); 0: the whole context */
 } dfs_drafter_cfg;
 
 /* Drafter weights, all in cfg.dtype, matrices stored [out, in] (row = output
@@ -257,12 +260,13 @@ const char* dfs_status_string(int status);
 /* Block attention alone, same math and layouts as inside dflash_draft_step:
  * q [B, S, nq, d], k_blk [B, S, nkv, d], v_blk [B, S, nkv, d] (all cfg dtype),
  * caches as above for ONE layer ([B, nkv, max_ctx, d] and [B, nkv, d, max_ctx]),
- * ctx_len [B] int32 = context keys of each row, out [B, S, nq, d] cfg dtype. */
+ * ctx_len [B] int32 = context keys of each row, out [B, S, nq, d] cfg dtype;
+ * window > 0 restricts each row to its last `window` context keys (cfg.window). */
 size_t dfs_block_attention_workspace_size(int32_t batch, int32_t block, int32_t n_q_heads,
                                           int32_t n_kv_heads, int32_t head_dim, int32_t ctx_bound,
                                           int32_t dtype);
 int dfs_block_attention(int32_t batch, int32_t block, int32_t n_q_heads, int32_t n_kv_heads,
-                        int32_t head_dim, int32_t max_ctx, int32_t ctx_bound, int32_t dtype,
+                        int32_t head_dim, int32_t max_ctx, int32_t ctx_bound, int32_t dtype, int32_t window,
                         const void* q, const void* k_blk, const void* v_blk, const void* k_cache,
                         const void* v_cache, const int32_t* ctx_len, void* out, void* workspace,
                         size_t workspace_bytes, void* stream);

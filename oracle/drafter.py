@@ -27,7 +27,11 @@ the design notes of the repository):
   and mask token j at C_b + j;
 * mask slot j (j = 1..S-1) predicts the token at slot j; slot 0 (the last
   decoded token) produces no logits;
-* the mask token is a row of the shared embedding (mask_token_id).
+* the mask token is a row of the shared embedding (mask_token_id);
+* sliding window (the DSpark drafter variant of the DeepSeek-V4.1 notes page,
+  section "DSpark — le décodage spéculatif": a 128-token window): with
+  window > 0 a block row attends the last min(C_b, window) context keys and all
+  S block keys; every appended row is still cached; positions are unchanged.
 
 Storage boundaries (rounded exactly where the GPU path stores a tensor):
 features, K/V, attention inputs/outputs, MLP input and SwiGLU product in the
@@ -64,6 +68,7 @@ class DrafterShape:
     rms_eps: float
     rope_theta: float
     dtype: str
+    window: int = 0          # > 0: the block sees only the last `window` context keys
 
     @classmethod
     def of(cls, w) -> "DrafterShape":
@@ -210,8 +215,9 @@ def draft_step(shape: DrafterShape, weights, hidden_new, n_new, k_cache, v_cache
         o = np.empty_like(q)
         for i, b in enumerate(rows):
             cb = int(new_len[b])
-            kc = as_f64(k_cache[l, b, :cb], dt)
-            vc = as_f64(v_cache[l, b, :cb], dt)
+            lo = max(0, cb - sh.window) if sh.window > 0 else 0     # sliding window: the last `window` keys
+            kc = as_f64(k_cache[l, b, lo:cb], dt)
+            vc = as_f64(v_cache[l, b, lo:cb], dt)
             o[i] = block_attention(q[i], kc, vc, k[i], v[i], F)
         o = rnd(o).reshape(-1, S, nq * d)
         x = round_f32(x + o @ wt(p + "wo").T).astype(F)

@@ -38,6 +38,7 @@ class Workload:
     hidden_std: float = 1.0
     base_logit_std: float = 1.28    # std of synthetic base logits fed to the sampler alone
     markov_factor_std: float = 0.02
+    window: int = 0                 # > 0: block rows attend only the last `window` context keys
 
     @property
     def gamma(self) -> int:
@@ -77,7 +78,13 @@ HIGHBATCH = Workload("highbatch_bf16_b128_s8_c2048_v129280", batch=128, block=8,
                      vocab=129280, markov_rank=256, target_logit_std=3.0,
                      target_noise_std=1.0, **_BIG)
 
-WORKLOADS = {"C0": TINY, "C1": DFLASH, "C2": DSPARK, "C3": LONGCTX, "C4": HIGHBATCH}
+# the DSpark drafter variant: 3 layers attending a 128-token window of the
+# context, 5-token block (1 last token + 4 drafts), otherwise as C2
+DSPARK_WINDOW = Workload("dspark_window_bf16_b32_s5_c4096_w128_v129280", batch=32, block=5, ctx=4096,
+                         vocab=129280, markov_rank=256, target_logit_std=3.0,
+                         **{**_BIG, "n_layers": 3}, window=128)
+
+WORKLOADS = {"C0": TINY, "C1": DFLASH, "C2": DSPARK, "C3": LONGCTX, "C4": HIGHBATCH, "C5": DSPARK_WINDOW}
 
 # a bf16 drafter with the big configs' structure (GQA 32/8 x 128) at a size the
 # oracle finishes in seconds, spanning several GEMM and attention tiles with ragged tails

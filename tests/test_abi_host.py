@@ -36,13 +36,14 @@ class Cfg(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "n_layers", "hidden", "n_q_heads", "n_kv_heads", "head_dim", "mlp_dim", "vocab",
         "n_target_layers", "block", "max_ctx", "mask_token_id")] + [
-        ("rms_eps", ctypes.c_float), ("rope_theta", ctypes.c_float), ("dtype", ctypes.c_int32)]
+        ("rms_eps", ctypes.c_float), ("rope_theta", ctypes.c_float), ("dtype", ctypes.c_int32),
+        ("window", ctypes.c_int32)]
 
 
 def _cfg(**kw):
     base = dict(n_layers=5, hidden=4096, n_q_heads=32, n_kv_heads=8, head_dim=128, mlp_dim=12288,
                 vocab=151936, n_target_layers=5, block=16, max_ctx=4096, mask_token_id=151935,
-                rms_eps=1e-6, rope_theta=1e6, dtype=1)
+                rms_eps=1e-6, rope_theta=1e6, dtype=1, window=0)
     base.update(kw)
     return Cfg(**base)
 
@@ -58,6 +59,10 @@ def test_workspace_sizes(lib):
     assert lib.dflash_draft_workspace_size(ctypes.byref(_cfg(head_dim=64)), 8, 16) == 0   # bf16 needs d=128
     assert lib.dflash_draft_workspace_size(ctypes.byref(_cfg(max_ctx=100)), 8, 16) == 0
     assert lib.dflash_draft_workspace_size(ctypes.byref(_cfg(n_q_heads=30)), 8, 16) == 0
+    assert lib.dflash_draft_workspace_size(ctypes.byref(_cfg(window=-1)), 8, 16) == 0     # window >= 0
+    assert lib.dflash_draft_workspace_size(ctypes.byref(_cfg(window=128)), 8, 16) > 0
+    assert lib.dflash_draft_workspace_size(ctypes.byref(_cfg(block=32)), 8, 16) > 0      # R = 128 rows
+    assert lib.dflash_draft_workspace_size(ctypes.byref(_cfg(block=64, n_q_heads=40)), 8, 16) == 0   # R > 256
     assert lib.dflash_draft_workspace_size(None, 8, 16) == 0
     assert lib.markov_bias_sample_workspace_size(32, 15, 129280) > 0
     assert lib.markov_bias_sample_workspace_size(0, 15, 129280) == 0

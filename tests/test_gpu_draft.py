@@ -30,6 +30,9 @@ CASES = {
     "medium_b20_packed": (MEDIUM.with_(batch=20), 6, None, None, None, True),
     # a 32-token block: 128 query rows per kv head, attention in two 64-row groups
     "medium_s32": (MEDIUM.with_(batch=2, block=32), 7, None, None, None),
+    # sliding-window drafter (64 context keys): ragged contexts above and below the window
+    "medium_window": (MEDIUM.with_(window=64), 9, [284, 131, 7], [16, 5, 0], 16),
+    "medium_window_packed": (MEDIUM.with_(window=100), 9, [284, 131, 7], [16, 5, 0], 16, True),
 }
 
 

@@ -33,7 +33,7 @@ from synth import WORKLOADS, inputs, rng
 
 from _gpu_common import DEV, FLAG, as_f64, compare_sequential_draws, down, flag_budget, say, up, upload_weights, workspace
 
-BIG = ["C1", "C2", "C3", "C4"]
+BIG = ["C1", "C2", "C3", "C4", "C5"]
 
 
 @pytest.fixture(scope="module")

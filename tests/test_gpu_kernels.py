@@ -126,18 +126,23 @@ def test_gemm_f32(D):
 
 # ---------------------------------------------------------------- block attention
 
-@pytest.mark.parametrize("dtype,B,S,nq,nkv,d,max_ctx,ctx", [
-    ("bf16", 3, 16, 8, 2, 128, 640, [600, 37, 0]),
-    ("bf16", 2, 8, 8, 2, 128, 2112, [2100, 1031]),
-    ("bf16", 2, 4, 4, 4, 128, 128, [128, 65]),
-    ("bf16", 2, 32, 8, 2, 128, 640, [600, 37]),      # R = 128 query rows per kv head: two 64-row groups
-    ("bf16", 1, 24, 8, 2, 128, 256, [200]),          # R = 96: a partial second group
-    ("f32", 2, 4, 4, 4, 64, 128, [124, 50]),
-    ("f32", 1, 5, 6, 2, 32, 320, [300]),
+@pytest.mark.parametrize("dtype,B,S,nq,nkv,d,max_ctx,ctx,window", [
+    ("bf16", 3, 16, 8, 2, 128, 640, [600, 37, 0], 0),
+    ("bf16", 2, 8, 8, 2, 128, 2112, [2100, 1031], 0),
+    ("bf16", 2, 4, 4, 4, 128, 128, [128, 65], 0),
+    ("bf16", 2, 32, 8, 2, 128, 640, [600, 37], 0),      # R = 128 query rows per kv head: two 64-row groups
+    ("bf16", 1, 24, 8, 2, 128, 256, [200], 0),          # R = 96: a partial second group
+    ("f32", 2, 4, 4, 4, 64, 128, [124, 50], 0),
+    ("f32", 1, 5, 6, 2, 32, 320, [300], 0),
+    # sliding window: first key not step-aligned (600 - 128 = 472), shorter and empty contexts
+    ("bf16", 3, 16, 8, 2, 128, 640, [600, 37, 0], 128),
+    ("bf16", 2, 8, 8, 2, 128, 2112, [2100, 1031], 100),
+    ("bf16", 2, 32, 8, 2, 128, 640, [600, 37], 64),
+    ("f32", 2, 4, 4, 4, 64, 128, [124, 50], 30),
 ])
-def test_block_attention_matches_oracle(D, dtype, B, S, nq, nkv, d, max_ctx, ctx):
+def test_block_attention_matches_oracle(D, dtype, B, S, nq, nkv, d, max_ctx, ctx, window):
     import torch
-    say(f"attention {dtype} B={B} S={S} nq={nq} nkv={nkv} ctx={ctx}")
+    say(f"attention {dtype} B={B} S={S} nq={nq} nkv={nkv} ctx={ctx} window={window}")
     ctx = np.array(ctx, np.int32)
     q = rng.normal(3, "aq", (B, S, nq, d), 1.0, dtype=dtype)
     kb = rng.normal(3, "akb", (B, S, nkv, d), 1.0, dtype=dtype)
@@ -153,13 +158,14 @@ def test_block_attention_matches_oracle(D, dtype, B, S, nq, nkv, d, max_ctx, ctx
     ws = workspace(D.dfs_block_attention_workspace_size(B, S, nq, nkv, d, int(ctx.max()),
                                                         1 if dtype == "bf16" else 0))
     D.dfs_block_attention(up(q, dtype), up(kb, dtype), up(vb, dtype), up(kc, dtype), up(vc, dtype),
-                          up(ctx, "i32"), out, max_ctx, int(max(ctx.max(), 1)), ws)
+                          up(ctx, "i32"), out, max_ctx, int(max(ctx.max(), 1)), ws, window=window)
     got = as_f64(down(out), dtype)
     tol = 2e-2 if dtype == "bf16" else 1e-4
     for b in range(B):
         c = ctx[b]
-        want = od.block_attention(as_f64(q[b], dtype), as_f64(kc[b, :, :c], dtype).transpose(1, 0, 2),
-                                  as_f64(vc[b, :, :, :c], dtype).transpose(2, 0, 1),
+        lo = max(0, c - window) if window > 0 else 0
+        want = od.block_attention(as_f64(q[b], dtype), as_f64(kc[b, :, lo:c], dtype).transpose(1, 0, 2),
+                                  as_f64(vc[b, :, :, lo:c], dtype).transpose(2, 0, 1),
                                   as_f64(kb[b], dtype), as_f64(vb[b], dtype))
         np.testing.assert_allclose(got[b], want, atol=tol, rtol=0)
 

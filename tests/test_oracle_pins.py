@@ -100,9 +100,10 @@ def test_rope_scores_depend_on_relative_position():
 
 # ---------------------------------------------------------------- attention
 
-def _bruteforce_block_attention(q, k_ctx, v_ctx, k_blk, v_blk):
+def _bruteforce_block_attention(q, k_ctx, v_ctx, k_blk, v_blk, window=0):
     """Whole sequence [context ; block] with an explicit 0/-inf mask matrix built
-    from the rule: full attention inside the block, causal toward the context."""
+    from the rule: full attention inside the block, causal toward the context
+    (with a sliding window: only the last `window` context keys)."""
     C = k_ctx.shape[0]
     S, nq, d = q.shape
     nkv = k_ctx.shape[1]
@@ -118,8 +119,8 @@ def _bruteforce_block_attention(q, k_ctx, v_ctx, k_blk, v_blk):
             in_block_i, in_block_j = i >= C, j >= C
             if in_block_i and in_block_j:
                 mask[i, j] = 0.0                 # full attention inside the block
-            elif j <= i and not in_block_j:
-                mask[i, j] = 0.0                 # causal toward the (earlier) context
+            elif j <= i and not in_block_j and (window <= 0 or j >= C - window):
+                mask[i, j] = 0.0                 # causal toward the (earlier) context, within the window
     qfull = np.zeros((n, nq, d))
     qfull[C:] = q
     out = np.zeros((S, nq, d))
@@ -255,18 +256,20 @@ def _bruteforce_one_layer_drafter(w, weights, hidden_all, last_token):
     k = f32(_rope_complex((rows @ W["layers.0.wk"].T).reshape(-1, nkv, d), pos, w.rope_theta))
     v = f32((rows @ W["layers.0.wv"].T).reshape(-1, nkv, d))
     q = f32(_rope_complex((a @ W["layers.0.wq"].T).reshape(-1, nq, d), pos[C:], w.rope_theta))
-    o = _bruteforce_block_attention(q, k[:C], v[:C], k[C:], v[C:])
+    o = _bruteforce_block_attention(q, k[:C], v[:C], k[C:], v[C:], window=w.window)
     x = f32(x + f32(o).reshape(S, nq * d) @ W["layers.0.wo"].T)
     z = f32(_rms(x[1:], W["final_norm"], w.rms_eps))
     return (z @ W["lm_head"].T).astype(np.float32)
 
 
-@pytest.mark.parametrize("split,arith", [(None, np.float64), (9, np.float64), (None, np.float32)])
-def test_drafter_matches_sequence_level_bruteforce(split, arith):
+@pytest.mark.parametrize("split,arith,window", [(None, np.float64, 0), (9, np.float64, 0), (None, np.float32, 0),
+                                                (None, np.float64, 6), (9, np.float64, 6), (None, np.float64, 30)])
+def test_drafter_matches_sequence_level_bruteforce(split, arith, window):
     # one layer, MLP output off, fp32 storage; the context is appended in one
     # call (prefill) or in two calls; positions come out of the cache
     # bookkeeping.  The fp32-arithmetic evaluation computes the same function.
-    w = _tiny(batch=1, ctx=21, dtype="f32", rope_theta=100.0)
+    # window > 0: the sliding-window variant (30 > C: the whole context)
+    w = _tiny(batch=1, ctx=21, dtype="f32", rope_theta=100.0, window=window)
     weights = inputs.drafter_weights(w, 2, gain_std=0.1)
     weights["layers.0.w_down"] = np.zeros_like(weights["layers.0.w_down"])
     C = 17
