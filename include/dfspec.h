@@ -133,8 +133,9 @@ size_t dflash_draft_workspace_size(const dfs_drafter_cfg* cfg, int32_t batch, in
  *    written to cache slots ctx_len[b] + j (positions ctx_len[b] + j).
  * 3. The block [last_token[b], mask x (S-1)] at positions C_b .. C_b+S-1, where
  *    C_b = ctx_len[b] + n_new[b], runs through the L pre-norm layers
- *    (attention over the C_b cached keys and the S block keys, full inside the
- *    block; then a SwiGLU MLP; fp32 residual stream).
+ *    (attention over the C_b cached keys — the last min(C_b, cfg.window) of them
+ *    when cfg.window > 0 — and the S block keys, full inside the block; then a
+ *    SwiGLU MLP; fp32 residual stream).
  * 4. base_logits[b, j-1] = RMSNorm(x_j; final_norm) . lm_head^T for mask slot
  *    j = 1..S-1 (slot j predicts the token at slot j).
  * 5. ctx_len[b] is advanced to C_b.
