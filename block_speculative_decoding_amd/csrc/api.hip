@@ -502,8 +502,8 @@ size_t spec_verify_workspace_size(int32_t batch, int32_t n_draft, int32_t vocab)
 
 int spec_verify(int32_t batch, int32_t n_draft, int32_t vocab, const float* draft_logits,
                 const float* target_logits, const int32_t* draft_tokens, const float* u_accept,
-                const float* u_final, float temperature, const double* draft_row_stats, int32_t* out_tokens,
-                int32_t* n_accepted, void* workspace, size_t workspace_bytes, void* stream) {
+                const float* u_final, float temperature, const double* draft_row_stats, const int32_t* n_verify,
+                int32_t* out_tokens, int32_t* n_accepted, void* workspace, size_t workspace_bytes, void* stream) {
   if (batch < 1 || n_draft < 1 || vocab < 1 || !draft_logits || !target_logits || !draft_tokens || !u_accept ||
       !u_final || !out_tokens || !n_accepted || !workspace)
     return DFS_EINVAL;
@@ -519,6 +519,7 @@ int spec_verify(int32_t batch, int32_t n_draft, int32_t vocab, const float* draf
   a.u_final = u_final;
   a.temperature = temperature;
   a.q_stats = draft_row_stats;
+  a.n_verify = n_verify;
   a.out_tokens = out_tokens;
   a.n_accepted = n_accepted;
   a.B = batch;
@@ -535,6 +536,27 @@ int spec_cycle_advance(int32_t batch, int32_t n_draft, const int32_t* n_accepted
   if (batch < 1 || n_draft < 0 || !n_accepted || !out_tokens || !n_new || !last_token) return DFS_EINVAL;
   if (n_draft > 64) return DFS_EUNSUPPORTED;
   DFS_TRY(launch_advance(batch, n_draft, n_accepted, out_tokens, n_new, last_token, tau_sum, (hipStream_t)stream));
+  return DFS_OK;
+}
+
+int spec_schedule_verify(int32_t batch, int32_t n_draft, const float* survival, int32_t n_curve,
+                         const float* curve_rows, const float* curve_sps, int32_t* n_verify, void* stream) {
+  if (batch < 1 || n_draft < 1 || !survival || !curve_rows || !curve_sps || !n_verify || n_curve < 1)
+    return DFS_EINVAL;
+  if ((long)batch * n_draft > 8192 || n_curve > kSchedCurve) return DFS_EUNSUPPORTED;
+  SchedArgs a;
+  a.surv = survival;
+  a.n_verify = n_verify;
+  a.B = batch;
+  a.G = n_draft;
+  a.ncurve = n_curve;
+  for (int i = 0; i < n_curve; ++i) {
+    if (!(curve_sps[i] >= 0.f) || !(curve_rows[i] > 0.f)) return DFS_EINVAL;
+    if (i > 0 && !(curve_rows[i] > curve_rows[i - 1])) return DFS_EINVAL;
+    a.xs[i] = curve_rows[i];
+    a.ys[i] = curve_sps[i];
+  }
+  DFS_TRY(launch_schedule(a, (hipStream_t)stream));
   return DFS_OK;
 }
 

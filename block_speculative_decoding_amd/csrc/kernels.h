@@ -164,6 +164,7 @@ struct VerifyArgs {
   const int32_t* drafts;   // [B][G]
   const float* u_accept;   // [B][G]
   const float* u_final;    // [B]
+  const int32_t* n_verify; // [B] drafts verified per row (clamped to [0, G]), or null = G
   float temperature;
   const double* q_stats;   // [B][G][2] (max, sum) of the draft rows, or null -> q_chunk
   const double2* q_chunk;  // [B*G][nch]
@@ -171,7 +172,7 @@ struct VerifyArgs {
   double* rowinfo;         // [B][4]: target (max, sum), draft (max, sum) at the decided position
   double2* sums;           // [B][nch]: fp64 sums of exp for target / draft row at the rejection
   double* r_chunk;         // [B][nch]: residual mass max(0, p - q) per chunk
-  int32_t* state;          // [B]: first rejected position (G = all accepted)
+  int32_t* state;          // [B]: first rejected position (= the row's verify length: all accepted)
   int32_t* out_tokens;     // [B][G+1]
   int32_t* n_accepted;     // [B]
   int B, G, V;
@@ -181,5 +182,15 @@ hipError_t launch_verify(const VerifyArgs& a, hipStream_t s);
 // ------------------------------------------------------------------ cycle bookkeeping
 hipError_t launch_advance(int B, int G, const int32_t* n_accepted, const int32_t* out_tokens, int32_t* n_new,
                           int32_t* last_token, int64_t* tau_sum, hipStream_t s);
+
+constexpr int kSchedCurve = 32;   // throughput-curve points passed by value
+struct SchedArgs {
+  const float* surv;       // [B][G] per-position survival scores
+  int32_t* n_verify;       // [B] out: drafts to verify per request
+  int B, G, ncurve;
+  float xs[kSchedCurve];   // rows in the verify batch, increasing
+  float ys[kSchedCurve];   // verify passes per second at xs
+};
+hipError_t launch_schedule(const SchedArgs& a, hipStream_t s);
 
 }  // namespace dfs

@@ -23,7 +23,106 @@ __global__ __launch_bounds__(256) void advance_kernel(int B, int G, const int32_
   if (tau_sum) tau_sum[b] += a + 1;
 }
 
+// ------------------------------------------------------------------ prefix scheduler
+// Verify length per request (DSpark page, section "Optymalizacja weryfikacji i
+// wydajności"; DeepSeek-V4.1 notes page, section "DSpark — le décodage
+// spéculatif"): maximise SPS(N) * sum_b (1 + sum_{j < k_b} P[b, j]), P the
+// prefix survival products of the per-position survival scores and N =
+// sum_b (k_b + 1) the rows verified.  P does not increase along a request, so
+// the optimum for M verified drafts takes the M largest P (ties: lower index
+// first, which keeps every request's choice a prefix): sort, then scan M.  One
+// workgroup; the scan runs on one thread in index order so that the argmax —
+// an integer decision — does not depend on a parallel summation order.
+constexpr int kSchedMax = 8192;
+
+__device__ __forceinline__ bool sched_before(double va, int ka, double vb, int kb) {
+  return va > vb || (va == vb && ka < kb);
+}
+
+__device__ double sched_sps(const SchedArgs& a, double n, int* seg) {
+  if (n <= (double)a.xs[0]) return a.ys[0];
+  if (n >= (double)a.xs[a.ncurve - 1]) return a.ys[a.ncurve - 1];
+  int i = *seg;                                          // n only grows along the scan
+  while ((double)a.xs[i + 1] <= n) ++i;
+  *seg = i;
+  const double x0 = a.xs[i], x1 = a.xs[i + 1], y0 = a.ys[i], y1 = a.ys[i + 1];
+  return y0 + (y1 - y0) * ((n - x0) / (x1 - x0));
+}
+
+__global__ __launch_bounds__(1024) void schedule_kernel(SchedArgs a) {
+  __shared__ double val[kSchedMax];
+  __shared__ int key[kSchedMax];
+  __shared__ int cnt[kSchedMax];
+  __shared__ int best_m;
+  const int tid = threadIdx.x, B = a.B, G = a.G, n = B * G;
+  int np2 = 1;
+  while (np2 < n) np2 <<= 1;
+  for (int b = tid; b < B; b += 1024) {                  // prefix survival products, fp64
+    double P = 1.0;
+    for (int j = 0; j < G; ++j) {
+      const float c = a.surv[(size_t)b * G + j];
+      const double cc = c >= 0.f ? (c <= 1.f ? (double)c : 1.0) : 0.0;   // NaN -> 0
+      P = P * cc;
+      val[b * G + j] = P;
+      key[b * G + j] = b * G + j;
+    }
+    cnt[b] = 0;
+  }
+  for (int i = n + tid; i < np2; i += 1024) {
+    val[i] = -1.0;
+    key[i] = 0x7fffffff;
+  }
+  __syncthreads();
+  // bitonic sort into (value descending, index ascending)
+  for (int k = 2; k <= np2; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = tid; i < np2; i += 1024) {
+        const int ixj = i ^ j;
+        if (ixj > i) {
+          const bool up = (i & k) == 0;
+          const bool swap = up ? sched_before(val[ixj], key[ixj], val[i], key[i])
+                               : sched_before(val[i], key[i], val[ixj], key[ixj]);
+          if (swap) {
+            const double tv = val[i];
+            val[i] = val[ixj];
+            val[ixj] = tv;
+            const int tk = key[i];
+            key[i] = key[ixj];
+            key[ixj] = tk;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  if (tid == 0) {
+    int seg = 0;
+    double acc = 0.0, best = sched_sps(a, (double)B, &seg) * (double)B;
+    int bm = 0;
+    for (int m = 1; m <= n; ++m) {
+      acc = acc + val[m - 1];
+      const double o = sched_sps(a, (double)(B + m), &seg) * ((double)B + acc);
+      if (o > best) {
+        best = o;
+        bm = m;
+      }
+    }
+    best_m = bm;
+  }
+  __syncthreads();
+  for (int r = tid; r < best_m; r += 1024) atomicAdd(&cnt[key[r] / G], 1);
+  __syncthreads();
+  for (int b = tid; b < B; b += 1024) a.n_verify[b] = cnt[b];
+}
+
 }  // namespace
+
+hipError_t launch_schedule(const SchedArgs& a, hipStream_t s) {
+  ProfScope ps("verify", s);
+  if (a.B * a.G > kSchedMax || a.ncurve < 1 || a.ncurve > kSchedCurve) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(1024), 0, s, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_advance(int B, int G, const int32_t* n_accepted, const int32_t* out_tokens, int32_t* n_new,
                           int32_t* last_token, int64_t* tau_sum, hipStream_t s) {

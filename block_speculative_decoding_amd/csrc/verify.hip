@@ -18,10 +18,18 @@
 //   5. final draw per row: residual (or p at the rejection when the residual has
 //      no mass), or the bonus token from p_{G+1}
 // Greedy (T == 0) finishes in step 2.
+// A row may verify only its first k drafts (n_verify, the prefix scheduler's
+// early stopping): the first rejection among them, else the bonus token from
+// target row k — the same rule on a shorter draft, so still lossless.
 #include "stream.h"
 
 namespace dfs {
 namespace {
+
+// drafts verified in row b
+__device__ __forceinline__ int verify_len(const VerifyArgs& a, int b) {
+  return a.n_verify ? min(max(a.n_verify[b], 0), a.G) : a.G;
+}
 
 __device__ __forceinline__ void combine_chunks_wave(const double2* st, int nch, double T, double* M, double* S) {
   const int lane = threadIdx.x & 63;
@@ -101,8 +109,9 @@ __global__ __launch_bounds__(1024) void decide_kernel(VerifyArgs a, int nch) {
   }
   __syncthreads();
   if (threadIdx.x != 0) return;
-  int acc_end = G;
-  for (int i = 0; i < G; ++i)
+  const int kb = verify_len(a, b);
+  int acc_end = kb;
+  for (int i = 0; i < kb; ++i)
     if (!acc_sh[i]) {
       acc_end = i;
       break;
@@ -122,7 +131,7 @@ __global__ __launch_bounds__(256) void reject_sums_kernel(VerifyArgs a, int nch,
   __shared__ double red[4];
   const int c = blockIdx.x % nch, b = blockIdx.x / nch, tid = threadIdx.x;
   const int i = a.state[b];
-  if (i >= a.G) return;
+  if (i >= verify_len(a, b)) return;
   const double T = a.temperature;
   const double Mp = a.rowinfo[b * 4], Mq = a.rowinfo[b * 4 + 2];
   const float* prow = a.p + ((size_t)b * (a.G + 1) + i) * a.V;
@@ -173,7 +182,7 @@ __global__ __launch_bounds__(256) void residual_kernel(VerifyArgs a, int nch, bo
   __shared__ double red[4];
   const int c = blockIdx.x % nch, b = blockIdx.x / nch, tid = threadIdx.x;
   const int i = a.state[b];
-  if (i >= a.G) return;
+  if (i >= verify_len(a, b)) return;
   double Sp, Sq;
   row_sums(a, b, nch, &Sp, &Sq, red);
   double w[kPer];
@@ -198,14 +207,15 @@ __global__ __launch_bounds__(256) void final_kernel(VerifyArgs a, int nch, bool 
   const double T = a.temperature;
   const double u = a.u_final[b];
   const double2* pst = a.p_chunk + ((size_t)b * (G + 1) + i) * nch;
+  const bool rejected = i < verify_len(a, b);       // else: bonus token from target row i
   double W = 0.0;
-  if (i < G) {
+  if (rejected) {
     for (int c = tid; c < nch; c += 256) W += a.r_chunk[(size_t)b * nch + c];
     W = block_sum<256>(W, red);
   }
-  const bool use_resid = i < G && W > 0.0;
+  const bool use_resid = rejected && W > 0.0;
   float Mp = -INFINITY;
-  if (!use_resid) {                                  // target row i (bonus: row G) from its chunk statistics
+  if (!use_resid) {                                  // target row i (bonus: the row after the verified drafts)
     for (int c = tid; c < nch; c += 256) Mp = fmaxf(Mp, (float)pst[c].x);
     Mp = block_max<256>(Mp, redf);
     W = 0.0;

@@ -25,7 +25,7 @@ EXPORTS = [
     "spec_verify_workspace_size", "spec_verify", "dfs_status_string",
     "dfs_block_attention_workspace_size", "dfs_block_attention",
     "dfs_gemm_workspace_size", "dfs_gemm", "dfs_profile_begin", "dfs_profile_end",
-    "dfs_packed_matrix_bytes", "dfs_pack_matrix", "dfs_gemm_swiglu", "spec_cycle_advance",
+    "dfs_packed_matrix_bytes", "dfs_pack_matrix", "dfs_gemm_swiglu", "spec_cycle_advance", "spec_schedule_verify",
 ]
 
 
@@ -65,7 +65,7 @@ def _load():
         "markov_bias_sample": (ctypes.c_int, [i32, i32, i32, i32, vp, vp, vp, i32, vp, vp, f32, vp, vp,
                                               vp, sz, vp]),
         "spec_verify_workspace_size": (sz, [i32, i32, i32]),
-        "spec_verify": (ctypes.c_int, [i32, i32, i32, vp, vp, vp, vp, vp, f32, vp, vp, vp, vp, sz, vp]),
+        "spec_verify": (ctypes.c_int, [i32, i32, i32, vp, vp, vp, vp, vp, f32, vp, vp, vp, vp, vp, sz, vp]),
         "dfs_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "dfs_block_attention_workspace_size": (sz, [i32, i32, i32, i32, i32, i32, i32]),
         "dfs_block_attention": (ctypes.c_int, [i32, i32, i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp,
@@ -74,6 +74,8 @@ def _load():
         "dfs_gemm": (ctypes.c_int, [i32, i32, i32, i32, vp, vp, vp, i32, i32, vp, sz, vp]),
         "dfs_gemm_swiglu": (ctypes.c_int, [i32, i32, i32, vp, vp, vp, vp, i32, vp]),
         "spec_cycle_advance": (ctypes.c_int, [i32, i32, vp, vp, vp, vp, vp, vp]),
+        "spec_schedule_verify": (ctypes.c_int, [i32, i32, vp, i32, ctypes.POINTER(f32), ctypes.POINTER(f32), vp,
+                                                vp]),
         "dfs_packed_matrix_bytes": (sz, [i32, i32]),
         "dfs_pack_matrix": (ctypes.c_int, [i32, i32, vp, vp, vp]),
         "dfs_profile_begin": (ctypes.c_int, [ctypes.c_char_p, i32]),
@@ -248,7 +250,8 @@ def spec_verify_workspace_size(batch: int, n_draft: int, vocab: int) -> int:
 
 
 def spec_verify(draft_logits, target_logits, draft_tokens, u_accept, u_final, temperature: float,
-                draft_row_stats, out_tokens, n_accepted, workspace, stream=None):
+                draft_row_stats, out_tokens, n_accepted, workspace, stream=None, n_verify=None):
+    """n_verify: optional device int32 [B], drafts verified per row (early stopping)."""
     B, G, V = draft_logits.shape
     st = LIB.spec_verify(
         B, G, V, _ptr(draft_logits, torch.float32, B * G * V, "draft_logits"),
@@ -256,6 +259,7 @@ def spec_verify(draft_logits, target_logits, draft_tokens, u_accept, u_final, te
         _ptr(draft_tokens, torch.int32, B * G, "draft_tokens"), _ptr(u_accept, torch.float32, B * G, "u_accept"),
         _ptr(u_final, torch.float32, B, "u_final"), float(temperature),
         _ptr(draft_row_stats, torch.float64, B * G * 2, "draft_row_stats") if draft_row_stats is not None else None,
+        _ptr(n_verify, torch.int32, B, "n_verify"),
         _ptr(out_tokens, torch.int32, B * (G + 1), "out_tokens"), _ptr(n_accepted, torch.int32, B, "n_accepted"),
         _ptr(workspace, torch.uint8, None, "workspace"), workspace.numel(), _stream(stream))
     _check(st, "spec_verify")
@@ -320,6 +324,20 @@ def spec_cycle_advance(n_accepted, out_tokens, n_new, last_token, tau_sum=None, 
                                 _ptr(n_new, torch.int32, B, "n_new"), _ptr(last_token, torch.int32, B, "last_token"),
                                 _ptr(tau_sum, torch.int64, B, "tau_sum"), _stream(stream))
     _check(st, "spec_cycle_advance")
+
+
+def spec_schedule_verify(survival, curve_rows, curve_sps, n_verify, stream=None):
+    """Verify lengths per request (device int32 [B] out) from survival scores
+    [B, gamma] (device fp32) and a host throughput curve (rows, passes/s)."""
+    B, G = survival.shape
+    xs = [float(x) for x in curve_rows]
+    ys = [float(y) for y in curve_sps]
+    if len(xs) != len(ys):
+        raise ValueError("curve_rows and curve_sps differ in length")
+    FA = ctypes.c_float * len(xs)
+    st = LIB.spec_schedule_verify(B, G, _ptr(survival, torch.float32, B * G, "survival"), len(xs), FA(*xs), FA(*ys),
+                                  _ptr(n_verify, torch.int32, B, "n_verify"), _stream(stream))
+    _check(st, "spec_schedule_verify")
 
 
 def packed_matrix_bytes(rows: int, cols: int) -> int:

@@ -29,7 +29,10 @@ class SpecLoop:
     capacity, so the same enqueued work is valid whatever the device-side state."""
 
     def __init__(self, cfg: D.DrafterConfig, weights: D.DrafterWeights, k_cache, v_cache, ctx_len, last_token, n_new,
-                 temperature: float = 1.0, U=None, Wt=None, wt_packed: bool = False):
+                 temperature: float = 1.0, U=None, Wt=None, wt_packed: bool = False, curve=None):
+        """curve: optional (rows, passes per second) throughput table for the prefix
+        scheduler; with it, a cycle given survival scores verifies per request only
+        the drafts spec_schedule_verify picks."""
         B = ctx_len.numel()
         S, V = cfg.block, cfg.vocab
         G = S - 1
@@ -46,20 +49,28 @@ class SpecLoop:
         self.out_tokens = torch.empty((B, S), dtype=torch.int32, device=dev)
         self.n_accepted = torch.empty(B, dtype=torch.int32, device=dev)
         self.tau_sum = torch.zeros(B, dtype=torch.int64, device=dev)
+        self.curve = curve
+        self.n_verify = torch.full((B,), G, dtype=torch.int32, device=dev)
         self.ws_draft = torch.empty(D.dflash_draft_workspace_size(cfg, B, S), dtype=torch.uint8, device=dev)
         self.ws_markov = torch.empty(D.markov_bias_sample_workspace_size(B, G, V), dtype=torch.uint8, device=dev)
         self.ws_verify = torch.empty(D.spec_verify_workspace_size(B, G, V), dtype=torch.uint8, device=dev)
 
-    def cycle(self, hidden_new, u_draft, u_accept, u_final, target_fn):
+    def cycle(self, hidden_new, u_draft, u_accept, u_final, target_fn, survival=None):
         """Enqueue one cycle.  hidden_new [B, S, nT*H]: target hidden states of the
         rows committed by the previous cycle (rows >= n_new[b] ignored); u_draft,
         u_accept [B, gamma], u_final [B]; target_fn(final_draft_logits, target)
-        enqueues the target logits [B, S, V] into ``target``."""
+        enqueues the target logits [B, S, V] into ``target``; survival [B, gamma]
+        (device fp32, with a curve): per-position survival scores for the
+        scheduler."""
         D.dflash_draft_step(self.cfg, self.weights, hidden_new, self.n_new, self.S, self.cfg.max_ctx, self.k_cache,
                             self.v_cache, self.ctx_len, self.last_token, self.logits, self.ws_draft)
         D.markov_bias_sample(self.logits, self.U, self.Wt, self.last_token, u_draft, self.temperature, self.tokens,
                              self.row_stats, self.ws_markov, wt_packed=self.wt_packed)
         target_fn(self.logits, self.target)
+        nv = None
+        if survival is not None and self.curve is not None:
+            D.spec_schedule_verify(survival, self.curve[0], self.curve[1], self.n_verify)
+            nv = self.n_verify
         D.spec_verify(self.logits, self.target, self.tokens, u_accept, u_final, self.temperature, self.row_stats,
-                      self.out_tokens, self.n_accepted, self.ws_verify)
+                      self.out_tokens, self.n_accepted, self.ws_verify, n_verify=nv)
         D.spec_cycle_advance(self.n_accepted, self.out_tokens, self.n_new, self.last_token, self.tau_sum)

@@ -218,16 +218,24 @@ size_t spec_verify_workspace_size(int32_t batch, int32_t n_draft, int32_t vocab)
  * draft_tokens   [B, gamma] int32.
  * u_accept       [B, gamma] fp32; u_final [B] fp32.
  * draft_row_stats[B, gamma, 2] fp64 from markov_bias_sample, or NULL to recompute.
+ * n_verify       [B] int32 or NULL: row b verifies only its first k_b = n_verify[b]
+ *                drafts (clamped to [0, gamma]; NULL = gamma) — the prefix
+ *                scheduler's early stopping (same DSpark page, section
+ *                "Optymalizacja weryfikacji i wydajności": per-request verify
+ *                length, losslessness kept).  If those k_b are all accepted the
+ *                bonus token is drawn from target row k_b, so target_logits rows
+ *                0..k_b must be valid; the rule is the one above on a k_b-draft
+ *                block, hence still exact.
  * out_tokens     [B, gamma+1] int32 out: accepted drafts, the correction or bonus
  *                token, then -1.
- * n_accepted     [B] int32 out, in [0, gamma]; the cycle yields n_accepted + 1 tokens.
+ * n_accepted     [B] int32 out, in [0, k_b]; the cycle yields n_accepted + 1 tokens.
  *
  * DFS_EUNSUPPORTED for vocab > 4194304 or n_draft > 64.
  */
 int spec_verify(int32_t batch, int32_t n_draft, int32_t vocab, const float* draft_logits,
                 const float* target_logits, const int32_t* draft_tokens, const float* u_accept,
                 const float* u_final, float temperature, const double* draft_row_stats,
-                int32_t* out_tokens, int32_t* n_accepted, void* workspace,
+                const int32_t* n_verify, int32_t* out_tokens, int32_t* n_accepted, void* workspace,
                 size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------ multi-step loop */
@@ -251,6 +259,29 @@ int spec_verify(int32_t batch, int32_t n_draft, int32_t vocab, const float* draf
  * cycle: dflash_draft_step's n_new_max = S and ctx_bound = the cache capacity. */
 int spec_cycle_advance(int32_t batch, int32_t n_draft, const int32_t* n_accepted, const int32_t* out_tokens,
                        int32_t* n_new, int32_t* last_token, int64_t* tau_sum, void* stream);
+
+/* Hardware-aware prefix scheduler: a verify length per request (same DSpark
+ * page, section "Optymalizacja weryfikacji i wydajności": the verify length of
+ * each request is set from a throughput curve SPS(B) profiled once at startup,
+ * more tokens when the GPUs are idle and fewer when busy, losslessness kept by
+ * early stopping; DeepSeek-V4.1 notes page, section "DSpark — le décodage
+ * spéculatif": prefix survival probabilities combined with the measured curve to
+ * maximise the expected system throughput).
+ * survival [B, n_draft] fp32 (device): per-position survival scores c[b, i] (the
+ *   chance that draft i survives given its predecessors did), clipped to [0, 1],
+ *   NaN = 0; P[b, j] = c[b, 0] * ... * c[b, j] (fp64).
+ * curve_rows, curve_sps [n_curve] (HOST, copied at the call; 1 <= n_curve <= 32):
+ *   verify passes per second at that many rows in the verify batch; rows strictly
+ *   increasing and > 0, sps >= 0; linear between points, constant past the ends.
+ * n_verify [B] int32 out (device): k_b in [0, n_draft] maximising
+ *   SPS(sum_b (k_b + 1)) * sum_b (1 + sum_{j < k_b} P[b, j]) — exact: P does not
+ *   increase along a request, so the best k for M verified drafts take the M
+ *   largest P (ties: lower request, then lower position) and M is scanned; the
+ *   first maximum wins.  Feed n_verify to spec_verify.
+ * DFS_EINVAL for null pointers, batch or n_draft < 1, a bad curve;
+ * DFS_EUNSUPPORTED for batch * n_draft > 8192 or n_curve > 32. */
+int spec_schedule_verify(int32_t batch, int32_t n_draft, const float* survival, int32_t n_curve,
+                         const float* curve_rows, const float* curve_sps, int32_t* n_verify, void* stream);
 
 /* ------------------------------------------------------------------ misc */
 

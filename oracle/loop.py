@@ -23,6 +23,7 @@ import numpy as np
 
 from . import drafter as od
 from .sampling import markov_sample
+from .scheduler import schedule
 from .verify import verify
 
 
@@ -40,13 +41,15 @@ def advance(n_accepted, out_tokens, n_draft):
 
 
 def run_cycles(shape, weights, U, Wt, uw_dtype, k_cache, v_cache, ctx_len, last_token, n_new, cycles,
-               temperature, target_fn=None):
+               temperature, target_fn=None, curve=None):
     """Run len(cycles) cycles of draft -> Markov sample -> verify -> advance.
 
     ``cycles[c]`` holds that cycle's inputs: hidden_new [B, S, nT*H] (rows
     < n_new[b] used), u_draft [B, gamma], u_accept [B, gamma], u_final [B], and
     target_logits [B, S, V] unless ``target_fn(c, final_draft_logits)`` supplies
-    them.  k_cache, v_cache (logical layout) are updated in place; ctx_len,
+    them.  With ``curve`` = (rows, passes per second) each cycle's ``survival``
+    [B, gamma] goes through the prefix scheduler and only the chosen drafts are
+    verified.  k_cache, v_cache (logical layout) are updated in place; ctx_len,
     last_token, n_new are the state before the first cycle.  Returns one record
     per cycle with everything either side emits plus the draws' margins."""
     G = shape.block - 1
@@ -59,9 +62,13 @@ def run_cycles(shape, weights, U, Wt, uw_dtype, k_cache, v_cache, ctx_len, last_
         base, ctx = od.draft_step(shape, weights, cin["hidden_new"], nn, k_cache, v_cache, ctx, last)
         final, tokens, m_draft = markov_sample(base, U, Wt, uw_dtype, last, cin["u_draft"], temperature)
         target = target_fn(c, final) if target_fn is not None else cin["target_logits"]
-        out_tok, n_acc, m_ver = verify(final, target, tokens, cin["u_accept"], cin["u_final"], temperature)
+        n_verify = None
+        if curve is not None:
+            n_verify = schedule(cin["survival"], curve[0], curve[1])
+        out_tok, n_acc, m_ver = verify(final, target, tokens, cin["u_accept"], cin["u_final"], temperature,
+                                       n_verify=n_verify)
         nn, last, tau = advance(n_acc, out_tok, G)
         out.append(dict(draft_tokens=tokens, n_accepted=n_acc, out_tokens=out_tok, n_new=nn, last_token=last,
                         tau=tau, ctx_len=ctx.copy(), margins_draft=m_draft, margins_verify=m_ver,
-                        final_logits=final, last_token_in=last_in, n_new_in=n_new_in))
+                        final_logits=final, last_token_in=last_in, n_new_in=n_new_in, n_verify=n_verify))
     return out

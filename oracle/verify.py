@@ -30,10 +30,15 @@ import numpy as np
 from .sampling import softmax_weights, inverse_cdf, argmax_with_gap
 
 
-def verify(draft_logits, target_logits, draft_tokens, u_accept, u_final, temperature):
+def verify(draft_logits, target_logits, draft_tokens, u_accept, u_final, temperature, n_verify=None):
     """Returns (out_tokens [B, gamma+1] int32, n_accepted [B] int32,
-    margins [B, gamma+1] float64 (accept tests, then the final draw; inf for
-    positions not reached))."""
+    margins [B, gamma+1] float64 (accept tests, then the final draw in the last
+    column; inf for positions not reached)).
+
+    ``n_verify`` [B] (optional): row b verifies only its first k_b drafts
+    (clamped to [0, gamma]) — the prefix scheduler's early stopping ([DSpark]
+    "Optymalizacja weryfikacji i wydajności"); if all k_b are accepted the bonus
+    token is drawn from target row k_b.  The rule on a k_b-draft block."""
     q_all = np.asarray(draft_logits, np.float32)
     p_all = np.asarray(target_logits, np.float32)
     B, G, V = q_all.shape
@@ -41,8 +46,9 @@ def verify(draft_logits, target_logits, draft_tokens, u_accept, u_final, tempera
     n_acc = np.zeros(B, np.int32)
     margins = np.full((B, G + 1), np.inf)
     for b in range(B):
-        a = G
-        for i in range(G):
+        kb = G if n_verify is None else int(np.clip(n_verify[b], 0, G))
+        a = kb
+        for i in range(kb):
             d = int(draft_tokens[b, i])
             if temperature == 0:
                 t_arg, gap = argmax_with_gap(p_all[b, i])
@@ -78,12 +84,12 @@ def verify(draft_logits, target_logits, draft_tokens, u_accept, u_final, tempera
             margins[b, G] = m
             a = i
             break
-        if a == G:
+        if a == kb:                                   # every verified draft accepted: bonus from row kb
             if temperature == 0:
-                tok, m = argmax_with_gap(p_all[b, G])
+                tok, m = argmax_with_gap(p_all[b, kb])
             else:
-                tok, m = inverse_cdf(softmax_weights(p_all[b, G], temperature), u_final[b])
-            out[b, G] = tok
+                tok, m = inverse_cdf(softmax_weights(p_all[b, kb], temperature), u_final[b])
+            out[b, kb] = tok
             margins[b, G] = m
         n_acc[b] = a
     return out, n_acc, margins

@@ -127,8 +127,10 @@ def cycle_inputs(w: Workload, seed: int, cycle: int, batch=None) -> dict:
     """Inputs of cycle ``cycle`` of a multi-step loop, independent across cycles:
     hidden_new [B, S, nT*H] (target hidden states of the rows the previous cycle
     committed; rows >= n_new[b] unused), uniforms u_draft, u_accept [B, gamma] and
-    u_final [B], target logits [B, S, V] ~ N(0, std^2), and noise [B, S, V] ~ N(0, 1)
-    for targets built from the draft logits (draft + noise_std * noise)."""
+    u_final [B], target logits [B, S, V] ~ N(0, std^2), noise [B, S, V] ~ N(0, 1)
+    for targets built from the draft logits (draft + noise_std * noise), and
+    per-position survival scores [B, gamma] ~ U[0, 1) standing in for a
+    confidence head."""
     B = w.batch if batch is None else batch
     G, S = w.gamma, w.block
     k = f"cycle{cycle}."
@@ -140,4 +142,5 @@ def cycle_inputs(w: Workload, seed: int, cycle: int, batch=None) -> dict:
         "u_final": rng.uniform01(seed, k + "u_final", (B,)),
         "target_logits": rng.normal(seed, k + "target_logits", (B, S, w.vocab), w.target_logit_std, dtype="f32"),
         "noise": rng.normal(seed, k + "target_noise", (B, S, w.vocab), 1.0, dtype="f32"),
+        "survival": rng.uniform01(seed, k + "survival", (B, G)),
     }

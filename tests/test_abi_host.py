@@ -95,10 +95,10 @@ def test_invalid_arguments_rejected_on_host(lib):
     assert lib.markov_bias_sample(4, 3, 1000, 0, fake, None, None, 1, fake, fake, -1.0, fake, None,
                                   fake, 1 << 20, None) == -1
     lib.spec_verify.argtypes = [ctypes.c_int32] * 3 + [ctypes.c_void_p] * 5 + [ctypes.c_float] + \
-        [ctypes.c_void_p] * 4 + [ctypes.c_size_t, ctypes.c_void_p]
-    assert lib.spec_verify(4, 3, 1000, fake, fake, None, fake, fake, 1.0, None, fake, fake, fake,
+        [ctypes.c_void_p] * 5 + [ctypes.c_size_t, ctypes.c_void_p]
+    assert lib.spec_verify(4, 3, 1000, fake, fake, None, fake, fake, 1.0, None, None, fake, fake, fake,
                            1 << 20, None) == -1
-    assert lib.spec_verify(4, 3, 1000, fake, fake, fake, fake, fake, 1.0, None, fake, fake, fake,
+    assert lib.spec_verify(4, 3, 1000, fake, fake, fake, fake, fake, 1.0, None, None, fake, fake, fake,
                            16, None) == -4
     lib.dfs_status_string.restype = ctypes.c_char_p
     assert lib.dfs_status_string(-4) == b"workspace too small"

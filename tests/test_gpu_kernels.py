@@ -269,12 +269,15 @@ def _drafts_from_q(q_logits, ud, T):
     return np.minimum(out, V - 1)
 
 
-@pytest.mark.parametrize("B,G,V,T,with_stats", [(64, 7, 3000, 1.0, False), (16, 15, 20000, 1.0, True),
-                                                (32, 7, 3000, 0.0, False), (8, 3, 8, 1.0, False),
-                                                (16, 5, 4096, 0.8, False)])
-def test_verify_matches_oracle(D, B, G, V, T, with_stats):
+# early: every row verifies only its first n_verify[b] drafts (random in -1 .. G+1,
+# clamped), the prefix scheduler's early stopping
+@pytest.mark.parametrize("B,G,V,T,with_stats,early", [(64, 7, 3000, 1.0, False, False), (16, 15, 20000, 1.0, True, False),
+                                                      (32, 7, 3000, 0.0, False, False), (8, 3, 8, 1.0, False, False),
+                                                      (16, 5, 4096, 0.8, False, False), (64, 7, 3000, 1.0, False, True),
+                                                      (16, 15, 20000, 1.0, True, True), (32, 7, 3000, 0.0, False, True)])
+def test_verify_matches_oracle(D, B, G, V, T, with_stats, early):
     import torch
-    say(f"verify B={B} G={G} V={V} T={T} stats={with_stats}")
+    say(f"verify B={B} G={G} V={V} T={T} stats={with_stats} early={early}")
     q = rng.normal(6, f"vq{V}", (B, G, V), 2.0)
     p = np.empty((B, G + 1, V), np.float32)
     p[:, :G] = q + rng.normal(6, f"vn{V}", (B, G, V), 1.0)
@@ -292,9 +295,11 @@ def test_verify_matches_oracle(D, B, G, V, T, with_stats):
     out = torch.empty((B, G + 1), dtype=torch.int32, device=DEV)
     nacc = torch.empty((B,), dtype=torch.int32, device=DEV)
     ws = workspace(D.spec_verify_workspace_size(B, G, V))
+    nv = rng.integers(6, f"vnv{V}", (B,), -1, G + 2).astype(np.int32) if early else None
     D.spec_verify(up(q, "f32"), up(p, "f32"), up(drafts, "i32"), up(ua, "f32"), up(uf, "f32"), T,
-                  up(stats, "f64") if stats is not None else None, out, nacc, ws)
-    oout, onacc, margins = oracle.verify(q, p, drafts, ua, uf, T)
+                  up(stats, "f64") if stats is not None else None, out, nacc, ws,
+                  n_verify=up(nv, "i32") if early else None)
+    oout, onacc, margins = oracle.verify(q, p, drafts, ua, uf, T, n_verify=nv)
     gout, gnacc = down(out), down(nacc)
     flagged = 0
     for b in range(B):

@@ -38,6 +38,36 @@ def test_cycle_advance_matches_oracle(D):
     assert np.array_equal(down(tau), tau0 + want_tau)
 
 
+@pytest.mark.parametrize("B,G,curve", [(32, 15, "busy"), (128, 7, "rising"), (1, 64, "busy"), (8, 3, "flat"),
+                                       (128, 64, "busy"), (40, 15, "random")])
+def test_schedule_matches_oracle(D, B, G, curve):
+    # the verify lengths are integers decided in fp64 on both sides: bit-exact
+    import torch
+    from oracle import scheduler as osch
+    g = np.random.default_rng(B * 100 + G)
+    c = rng.uniform01(9, f"surv{B}_{G}", (B, G))
+    c[0, :2] = [np.nan, 1.5] if G >= 2 else c[0, :2]         # NaN -> 0, above 1 -> 1
+    n_max = B * (G + 1)
+    if curve == "busy":       # throughput falls with the batch
+        xs = np.array([1, 8, 64, n_max + 1], np.float32)
+        ys = (1000.0 / (1.0 + 0.02 * xs)).astype(np.float32)
+    elif curve == "rising":   # batching helps up to a point
+        xs = np.array([1, n_max // 3 + 1, n_max + 1], np.float32)
+        ys = np.array([10, 400, 420], np.float32)
+    elif curve == "flat":
+        xs, ys = np.array([1.0], np.float32), np.array([100.0], np.float32)
+    else:
+        xs = np.sort(g.choice(np.arange(1, n_max + 8), size=12, replace=False)).astype(np.float32)
+        ys = (g.random(12) * 500 + 1).astype(np.float32)
+    nv = torch.full((B,), -9, dtype=torch.int32, device=DEV)
+    D.spec_schedule_verify(up(c, "f32").view(B, G), xs, ys, nv)
+    torch.cuda.synchronize()
+    want = osch.schedule(c, xs, ys)
+    got = down(nv)
+    say(f"schedule B={B} G={G} {curve}: verified {int(got.sum())} of {B * G} drafts")
+    assert np.array_equal(got, want)
+
+
 def _state(w, seed, ctx0, packed=False):
     """Device state of a loop over workload w: weights, caches, Markov factors."""
     import torch
@@ -61,7 +91,7 @@ def D_cache(w, kc, vc):
     return dfspec.cache_from_logical(up(kc, w.dtype), up(vc, w.dtype))
 
 
-@pytest.mark.parametrize("targets", ["independent", "draft_plus_noise"])
+@pytest.mark.parametrize("targets", ["independent", "draft_plus_noise", "scheduled"])
 def test_loop_tiny_matches_oracle(D, targets):
     # four cycles of the tiny fp32 drafter with the Markov head.  Targets either
     # independent random rows each cycle (mostly one committed token), or each
@@ -77,8 +107,11 @@ def test_loop_tiny_matches_oracle(D, targets):
     st = _state(w, seed, ctx0)
     cins = [inputs.cycle_inputs(w, seed, c) for c in range(cycles)]
     say(f"loop tiny: {cycles} cycles")
+    # scheduled: draft + noise targets, and the prefix scheduler picks per-request
+    # verify lengths from seeded survival scores and a falling throughput curve
+    curve = (np.array([1, 4, 16], np.float32), np.array([100, 60, 20], np.float32)) if targets == "scheduled" else None
     lp = SpecLoop(st["cfg"], st["wdev"], st["kd"], st["vd"], up(ctx0, "i32"), up(st["last0"], "i32"), up(n0, "i32"),
-                  1.0, st["Ud"], st["Wd"])
+                  1.0, st["Ud"], st["Wd"], curve=curve)
     gpu = []
     sigma = 0.5
     for c in range(cycles):
@@ -87,28 +120,31 @@ def test_loop_tiny_matches_oracle(D, targets):
 
         def tgt(final, target, t=t, nz=nz):
             target.copy_(t)
-            if targets == "draft_plus_noise":
+            if targets != "independent":
                 target[:, :w.gamma].copy_(final)
                 target[:, :w.gamma].add_(nz[:, :w.gamma], alpha=sigma)
         lp.cycle(up(cins[c]["hidden_new"], "f32"), up(cins[c]["u_draft"], "f32"), up(cins[c]["u_accept"], "f32"),
-                 up(cins[c]["u_final"], "f32"), tgt)
+                 up(cins[c]["u_final"], "f32"), tgt,
+                 survival=up(cins[c]["survival"], "f32").view(w.batch, w.gamma) if curve else None)
         torch.cuda.synchronize()
         gpu.append({k: down(getattr(lp, a)).copy() for k, a in (("draft_tokens", "tokens"), ("n_accepted", "n_accepted"),
                     ("out_tokens", "out_tokens"), ("n_new", "n_new"), ("last_token", "last_token"),
-                    ("ctx_len", "ctx_len"))})
+                    ("ctx_len", "ctx_len"), ("n_verify", "n_verify"))})
     kc, vc = st["kc"].copy(), st["vc"].copy()
     def ora_target(c, final):
         t = cins[c]["target_logits"].copy()
-        if targets == "draft_plus_noise":    # the oracle's own final rows, the same noise (fp32 add)
+        if targets != "independent":         # the oracle's own final rows, the same noise (fp32 add)
             t[:, :w.gamma] = (final.astype(np.float32) + np.float32(sigma) * cins[c]["noise"][:, :w.gamma]
                               ).astype(np.float32)
         return t
     ora = ol.run_cycles(od.DrafterShape.of(w), st["weights"], st["U"], st["Wt"], "f32", kc, vc, ctx0, st["last0"], n0,
-                        cins, 1.0, target_fn=ora_target)
+                        cins, 1.0, target_fn=ora_target, curve=curve)
     alive = np.ones(w.batch, bool)
     n_cmp = n_flag = 0
     for c in range(cycles):
         g, o = gpu[c], ora[c]
+        if curve is not None:                    # scheduler decisions: same inputs, exact
+            assert np.array_equal(g["n_verify"], o["n_verify"]), f"cycle {c} verify lengths"
         for b in range(w.batch):
             if not alive[b]:
                 continue
@@ -140,7 +176,7 @@ def test_loop_tiny_matches_oracle(D, targets):
         np.testing.assert_allclose(vg[:, b, :n], vc[:, b, :n], atol=1e-4, rtol=1e-4)
 
 
-def _medium_loop(D, packed=True):
+def _medium_loop(D, packed=True, curve=None):
     from block_speculative_decoding_amd.loop import SpecLoop
     w = MEDIUM
     seed = 8
@@ -148,7 +184,7 @@ def _medium_loop(D, packed=True):
     n0 = np.full(w.batch, w.block, np.int32)
     st = _state(w, seed, ctx0, packed=packed)
     lp = SpecLoop(st["cfg"], st["wdev"], st["kd"], st["vd"], up(ctx0, "i32"), up(st["last0"], "i32"), up(n0, "i32"),
-                  1.0, st["Ud"], st["Wd"], wt_packed=packed)
+                  1.0, st["Ud"], st["Wd"], wt_packed=packed, curve=curve)
     return w, seed, lp
 
 
@@ -177,16 +213,20 @@ def test_loop_identical_distributions_commit_every_draft(D):
     assert down(lp.tau_sum).tolist() == [3 * w.block] * w.batch
 
 
-def test_loop_graph_replay_matches_eager(D):
+@pytest.mark.parametrize("scheduled", [False, True])
+def test_loop_graph_replay_matches_eager(D, scheduled):
     # three cycles with targets = draft + N(0, 1) noise (partial acceptance), run
-    # eagerly and as one captured HIP graph replayed twice from the same start
+    # eagerly and as one captured HIP graph replayed twice from the same start;
+    # scheduled: the prefix scheduler sets the verify lengths inside the graph
     import torch
-    w, seed, lp = _medium_loop(D)
+    curve = (np.array([4, 16, 49], np.float32), np.array([300, 200, 90], np.float32)) if scheduled else None
+    w, seed, lp = _medium_loop(D, curve=curve)
     G = w.gamma
     cyc = [inputs.cycle_inputs(w, seed, c) for c in range(3)]
     dev_in = [dict(h=up(ci["hidden_new"], w.dtype).view(w.batch, w.block, -1), ud=up(ci["u_draft"], "f32"),
                    ua=up(ci["u_accept"], "f32"), uf=up(ci["u_final"], "f32"),
-                   nz=up(ci["noise"], "f32").view(w.batch, w.block, w.vocab)) for ci in cyc]
+                   nz=up(ci["noise"], "f32").view(w.batch, w.block, w.vocab),
+                   sv=up(ci["survival"], "f32").view(w.batch, G)) for ci in cyc]
 
     def run():
         for d in dev_in:
@@ -195,12 +235,12 @@ def test_loop_graph_replay_matches_eager(D):
                 target[:, :G].add_(nz[:, :G])
                 target[:, G].copy_(nz[:, G])
                 target[:, G].mul_(3.0)
-            lp.cycle(d["h"], d["ud"], d["ua"], d["uf"], tgt)
+            lp.cycle(d["h"], d["ud"], d["ua"], d["uf"], tgt, survival=d["sv"] if scheduled else None)
 
     state = (lp.k_cache, lp.v_cache, lp.ctx_len, lp.last_token, lp.n_new, lp.tau_sum)
     start = [t.clone() for t in state]
     outs = (lp.k_cache, lp.v_cache, lp.ctx_len, lp.last_token, lp.n_new, lp.tau_sum, lp.logits, lp.tokens,
-            lp.out_tokens, lp.n_accepted)
+            lp.out_tokens, lp.n_accepted, lp.n_verify)
 
     def restore():
         for t, s0 in zip(state, start):

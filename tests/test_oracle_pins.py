@@ -456,6 +456,55 @@ def test_verify_is_lossless_chi_square_and_acceptance_matches_tv():
         assert np.all(out[n, nacc[n] + 1:] == -1) and np.all(out[n, :nacc[n] + 1] >= 0)
 
 
+def test_verify_early_stopping_is_the_rule_on_the_truncated_block():
+    # n_verify = k: the outcome equals verifying the k-draft block (drafts and
+    # draft rows 0..k-1, target rows 0..k, row k acting as the bonus row);
+    # n_verify = gamma reproduces the unbounded call
+    g = np.random.default_rng(21)
+    B, G, V = 40, 4, 12
+    q = g.standard_normal((B, G, V)).astype(np.float32)
+    p = g.standard_normal((B, G + 1, V)).astype(np.float32)
+    d = g.integers(0, V, (B, G)).astype(np.int32)
+    ua = g.random((B, G)).astype(np.float32)
+    uf = g.random(B).astype(np.float32)
+    full = oracle.verify(q, p, d, ua, uf, 1.0)
+    same = oracle.verify(q, p, d, ua, uf, 1.0, n_verify=np.full(B, G))
+    assert np.array_equal(full[0], same[0]) and np.array_equal(full[1], same[1])
+    kv = g.integers(-1, G + 2, B)                        # includes out-of-range lengths (clamped)
+    out, nacc, _ = oracle.verify(q, p, d, ua, uf, 1.0, n_verify=kv)
+    for b in range(B):
+        k = int(np.clip(kv[b], 0, G))
+        o1, n1, _ = oracle.verify(q[b:b + 1, :k] if k else np.zeros((1, 0, V), np.float32), p[b:b + 1, :k + 1],
+                                  d[b:b + 1, :k], ua[b:b + 1, :k], uf[b:b + 1], 1.0)
+        assert nacc[b] == n1[0] and nacc[b] <= k
+        assert np.array_equal(out[b, :k + 1], o1[0]) and np.all(out[b, k + 1:] == -1)
+    for T in (0.0,):                                     # greedy: the same truncation
+        o0, n0, _ = oracle.verify(q, p, d, ua, uf, T, n_verify=kv)
+        assert np.all(n0 <= np.clip(kv, 0, G))
+
+
+def test_verify_early_stopping_stays_lossless_chi_square():
+    # random verify lengths per trial (0..gamma): the first emitted token is still
+    # distributed as the target's first row
+    V, G, N = 8, 3, 20_000
+    g = np.random.default_rng(12)
+    p_logits = g.standard_normal((G + 1, V)).astype(np.float32)
+    q_logits = g.standard_normal((G, V)).astype(np.float32)
+    ud = rng.uniform01(12, "es_draft", (N, G))
+    qw = special.softmax(q_logits.astype(np.float64), axis=1)
+    cum = np.cumsum(qw, axis=1)
+    drafts = np.array([[int(np.searchsorted(cum[i], ud[n, i] * cum[i, -1], side="right")) for i in range(G)]
+                       for n in range(N)], np.int32)
+    kv = g.integers(0, G + 1, N)
+    out, nacc, _ = oracle.verify(np.broadcast_to(q_logits, (N, G, V)), np.broadcast_to(p_logits, (N, G + 1, V)),
+                                 drafts, rng.uniform01(12, "es_acc", (N, G)), rng.uniform01(12, "es_fin", (N,)),
+                                 1.0, n_verify=kv)
+    p = special.softmax(p_logits.astype(np.float64), axis=1)
+    assert _chi2_pvalue(np.bincount(out[:, 0], minlength=V), p[0]) > 1e-4
+    assert np.all(nacc <= kv)
+    assert np.all(nacc[kv == 0] == 0)
+
+
 def test_verify_identical_and_disjoint_distributions():
     V, G, N = 8, 3, 2000
     g = np.random.default_rng(12)
@@ -626,3 +675,42 @@ def test_loop_point_mass_target_commits_one_token_per_cycle():
                 assert r["n_new"][b] == 1 and r["last_token"][b] == t_star
         assert np.array_equal(r["ctx_len"], ctx)
         ctx = ctx + r["n_new"]
+
+
+# ---------------------------------------------------------------- prefix scheduler
+
+def test_scheduler_scan_finds_the_brute_force_optimum():
+    from oracle import scheduler as osch
+    g = np.random.default_rng(31)
+    for trial in range(60):
+        B, G = int(g.integers(1, 4)), int(g.integers(1, 4))
+        c = g.random((B, G)).astype(np.float32)
+        xs = np.sort(g.choice(np.arange(1, 20), size=int(g.integers(2, 6)), replace=False)).astype(np.float32)
+        shape = trial % 3       # decreasing (busy), increasing then flat (idle: batching helps), random
+        if shape == 0:
+            ys = (100.0 / (1.0 + 0.3 * xs)).astype(np.float32)
+        elif shape == 1:
+            ys = np.minimum(10.0 * xs, 40.0).astype(np.float32)
+        else:
+            ys = (g.random(len(xs)) * 50 + 1).astype(np.float32)
+        k = osch.schedule(c, xs, ys)
+        P = osch.prefix_survival(c)
+        assert np.all((k >= 0) & (k <= G))
+        assert np.isclose(osch.objective(k, P, xs, ys), osch.brute_force(c, xs, ys), rtol=1e-12, atol=0)
+
+
+def test_scheduler_idle_verifies_everything_busy_verifies_less():
+    from oracle import scheduler as osch
+    g = np.random.default_rng(32)
+    B, G = 16, 7
+    c = (0.2 + 0.8 * g.random((B, G))).astype(np.float32)
+    xs = np.array([1, 1000], np.float32)
+    assert np.array_equal(osch.schedule(c, xs, np.array([50, 50], np.float32)), np.full(B, G))   # flat curve
+    totals = []
+    for alpha in (0.0, 0.01, 0.05, 0.2, 1.0, 5.0):          # SPS(N) = 1 / (1 + alpha N): heavier load
+        xs = np.arange(1, B * (G + 1) + 2, dtype=np.float32)
+        ys = (1.0 / (1.0 + alpha * xs)).astype(np.float32)
+        totals.append(int(osch.schedule(c, xs, ys).sum()))
+    assert totals[0] == B * G and all(a >= b for a, b in zip(totals, totals[1:])) and totals[-1] < totals[0]
+    # nothing survives: nothing is verified
+    assert np.array_equal(osch.schedule(np.zeros((B, G), np.float32), xs, ys), np.zeros(B))
