@@ -292,14 +292,41 @@ def sweeps(steps, warmup):
                           "markov_ms_per_step": tot / steps, "markov_share": tot / steps / ms}), flush=True)
 
 
-def loop_bench(wl, K, R, sigma=1.0, seed=0):
+def sps_profile(wl, steps=10, warmup=2, seed=0):
+    """The throughput curve the prefix scheduler uses, measured once at startup:
+    this build's whole step (draft + sample + verify) at batch sizes 1, 2, 4, ...
+    up to the workload's, as verify passes per second against the rows verified
+    (batch x block)."""
+    w0 = WORKLOADS[wl]
+    batches = [b for b in (1, 2, 4, 8, 16, 32, 64, 128) if b < w0.batch] + [w0.batch]
+    rows, sps = [], []
+    base = None
+    for b in batches:
+        w = w0.with_(name=f"{w0.name}_sps_b{b}", batch=b)
+        st = Step(w, seed=seed, reuse=base)
+        for _ in range(warmup):
+            st()
+        ms = time_steps(st, steps)
+        rows.append(b * w.block)
+        sps.append(1000.0 / ms)
+        if base is None:
+            base = st
+        else:
+            del st
+    return rows, sps
+
+
+def loop_bench(wl, K, R, sigma=1.0, seed=0, schedule=False):
     """On-device multi-step loop: K cycles of draft -> sample -> [synthetic target]
     -> verify -> advance captured into one HIP graph and replayed R times, the
     accepted count of each cycle driving the next append on the device.  Targets
     are the final draft rows plus N(0, sigma^2) noise, the bonus row N(0, 3^2),
     so acceptance is partial.  Reports time per cycle (graph and eager), the
     synthetic-target time alone, the mean tokens committed per cycle (tau) and
-    L = (cycle time without the synthetic target) / tau.  One JSON line."""
+    L = (cycle time without the synthetic target) / tau.  With ``schedule`` the
+    prefix scheduler sets each request's verify length every cycle from seeded
+    survival scores (standing in for a confidence head) and the SPS curve of
+    this build's step profiled first.  One JSON line."""
     import torch
     from block_speculative_decoding_amd import dfspec as D
     from block_speculative_decoding_amd.loop import SpecLoop
@@ -339,13 +366,15 @@ def loop_bench(wl, K, R, sigma=1.0, seed=0):
         packed = w.dtype == "bf16"
         if packed:
             Wt = D.pack_matrix(Wt)
-    lp = SpecLoop(cfg, wdev, k, v, ctx0, last0, n0, w.temperature, U, Wt, wt_packed=packed)
+    curve = sps_profile(wl, seed=seed) if schedule else None
+    lp = SpecLoop(cfg, wdev, k, v, ctx0, last0, n0, w.temperature, U, Wt, wt_packed=packed, curve=curve)
     nT_H = w.n_target_layers * w.hidden
     pool = [dict(h=torch.randn((B, S, nT_H), generator=gen, device=dev).to(tdt),
                  ud=torch.rand((B, G), generator=gen, device=dev) * 0.999999,
                  ua=torch.rand((B, G), generator=gen, device=dev) * 0.999999,
                  uf=torch.rand((B,), generator=gen, device=dev) * 0.999999,
-                 nz=torch.randn((B, S, V), generator=gen, device=dev)) for _ in range(K)]
+                 nz=torch.randn((B, S, V), generator=gen, device=dev),
+                 sv=torch.rand((B, G), generator=gen, device=dev)) for _ in range(K)]
     for p_ in pool:
         p_["nz"][:, :G].mul_(sigma)
         p_["nz"][:, G].mul_(3.0)
@@ -359,7 +388,7 @@ def loop_bench(wl, K, R, sigma=1.0, seed=0):
 
     def run():
         for p_ in pool:
-            lp.cycle(p_["h"], p_["ud"], p_["ua"], p_["uf"], target_fn(p_["nz"]))
+            lp.cycle(p_["h"], p_["ud"], p_["ua"], p_["uf"], target_fn(p_["nz"]), survival=p_["sv"] if schedule else None)
 
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     run()                                     # eager warm-up
@@ -375,6 +404,14 @@ def loop_bench(wl, K, R, sigma=1.0, seed=0):
     ev[1].record()
     torch.cuda.synchronize()
     synth_ms = ev[0].elapsed_time(ev[1]) / K
+    sched_us = None
+    if schedule:
+        ev[0].record()
+        for p_ in pool:
+            D.spec_schedule_verify(p_["sv"], curve[0], curve[1], lp.n_verify)
+        ev[1].record()
+        torch.cuda.synchronize()
+        sched_us = ev[0].elapsed_time(ev[1]) / K * 1e3
     g = torch.cuda.CUDAGraph()
     st = torch.cuda.Stream()
     st.wait_stream(torch.cuda.current_stream())
@@ -397,7 +434,10 @@ def loop_bench(wl, K, R, sigma=1.0, seed=0):
                       "target_synthesis_ms": synth_ms, "mean_tau": tau, "acceptance_rate": (tau - 1.0) / G,
                       "L_ms_per_token": core_ms / tau, "tokens_per_s": B * tau / (core_ms * 1e-3),
                       "target": f"final draft logits + N(0, {sigma}^2), bonus row N(0, 3^2)",
-                      "final_ctx_len_max": int(lp.ctx_len.max().item())}), flush=True)
+                      "final_ctx_len_max": int(lp.ctx_len.max().item()),
+                      **({"schedule": {"curve_rows": curve[0], "curve_steps_per_s": [round(x, 1) for x in curve[1]],
+                                       "mean_verify_length_last_cycle": float(lp.n_verify.double().mean().item()),
+                                       "scheduler_kernel_us": sched_us}} if schedule else {})}), flush=True)
 
 
 def main():
@@ -413,6 +453,8 @@ def main():
     ap.add_argument("--loop", action="store_true",
                     help="on-device multi-step loop: cycles captured in a HIP graph, tau and L (JSON line)")
     ap.add_argument("--loop-cycles", type=int, default=8, help="cycles per captured graph")
+    ap.add_argument("--schedule", action="store_true",
+                    help="with --loop: per-request verify lengths from the prefix scheduler (SPS profiled first)")
     ap.add_argument("--loop-replays", type=int, default=8, help="graph replays timed")
     ap.add_argument("--sweep", action="store_true",
                     help="secondary measurements: block-size and Markov draft-length sweeps (JSON line per point)")
@@ -429,7 +471,7 @@ def main():
         sweeps(args.steps, args.warmup)
         return
     if args.loop:
-        loop_bench(args.workload, args.loop_cycles, args.loop_replays)
+        loop_bench(args.workload, args.loop_cycles, args.loop_replays, schedule=args.schedule)
         return
     if args.calibrate_copy:
         import torch

@@ -31,20 +31,21 @@ __global__ __launch_bounds__(256) void advance_kernel(int B, int G, const int32_
 // sum_b (k_b + 1) the rows verified.  P does not increase along a request, so
 // the optimum for M verified drafts takes the M largest P (ties: lower index
 // first, which keeps every request's choice a prefix): sort, then scan M.  One
-// workgroup; the scan runs on one thread in index order so that the argmax —
-// an integer decision — does not depend on a parallel summation order.
+// workgroup; the running sum over the sorted values is taken by one thread in
+// order (so the argmax — an integer decision — does not depend on a parallel
+// summation order), the objective of every M is then evaluated in parallel and
+// reduced to its first maximum.
 constexpr int kSchedMax = 8192;
 
 __device__ __forceinline__ bool sched_before(double va, int ka, double vb, int kb) {
   return va > vb || (va == vb && ka < kb);
 }
 
-__device__ double sched_sps(const SchedArgs& a, double n, int* seg) {
+__device__ double sched_sps(const SchedArgs& a, double n) {
   if (n <= (double)a.xs[0]) return a.ys[0];
   if (n >= (double)a.xs[a.ncurve - 1]) return a.ys[a.ncurve - 1];
-  int i = *seg;                                          // n only grows along the scan
+  int i = 0;                                             // xs[i] <= n < xs[i+1]
   while ((double)a.xs[i + 1] <= n) ++i;
-  *seg = i;
   const double x0 = a.xs[i], x1 = a.xs[i + 1], y0 = a.ys[i], y1 = a.ys[i + 1];
   return y0 + (y1 - y0) * ((n - x0) / (x1 - x0));
 }
@@ -53,7 +54,8 @@ __global__ __launch_bounds__(1024) void schedule_kernel(SchedArgs a) {
   __shared__ double val[kSchedMax];
   __shared__ int key[kSchedMax];
   __shared__ int cnt[kSchedMax];
-  __shared__ int best_m;
+  __shared__ double red_v[16];
+  __shared__ int red_m[16];
   const int tid = threadIdx.x, B = a.B, G = a.G, n = B * G;
   int np2 = 1;
   while (np2 < n) np2 <<= 1;
@@ -95,21 +97,44 @@ __global__ __launch_bounds__(1024) void schedule_kernel(SchedArgs a) {
       __syncthreads();
     }
   }
-  if (tid == 0) {
-    int seg = 0;
-    double acc = 0.0, best = sched_sps(a, (double)B, &seg) * (double)B;
-    int bm = 0;
-    for (int m = 1; m <= n; ++m) {
-      acc = acc + val[m - 1];
-      const double o = sched_sps(a, (double)(B + m), &seg) * ((double)B + acc);
-      if (o > best) {
-        best = o;
-        bm = m;
-      }
+  if (tid == 0) {                                        // running sums in place: val[m-1] = sum of the top m
+    double acc = 0.0;
+    for (int m = 0; m < n; ++m) {
+      acc = acc + val[m];
+      val[m] = acc;
     }
-    best_m = bm;
   }
   __syncthreads();
+  // objective of every M = 0 .. n; first maximum (larger value, else smaller M)
+  double bv = -1.0;
+  int bmi = 0x7fffffff;
+  for (int m = tid; m <= n; m += 1024) {
+    const double o = sched_sps(a, (double)(B + m)) * ((double)B + (m > 0 ? val[m - 1] : 0.0));
+    if (o > bv) {
+      bv = o;
+      bmi = m;
+    }
+  }
+  for (int off = 32; off > 0; off >>= 1) {
+    const double ov = __shfl_xor(bv, off, 64);
+    const int om = __shfl_xor(bmi, off, 64);
+    if (ov > bv || (ov == bv && om < bmi)) {
+      bv = ov;
+      bmi = om;
+    }
+  }
+  if ((tid & 63) == 0) {
+    red_v[tid >> 6] = bv;
+    red_m[tid >> 6] = bmi;
+  }
+  __syncthreads();
+  double best = red_v[0];
+  int best_m = red_m[0];
+  for (int w = 1; w < 16; ++w)
+    if (red_v[w] > best || (red_v[w] == best && red_m[w] < best_m)) {
+      best = red_v[w];
+      best_m = red_m[w];
+    }
   for (int r = tid; r < best_m; r += 1024) atomicAdd(&cnt[key[r] / G], 1);
   __syncthreads();
   for (int b = tid; b < B; b += 1024) a.n_verify[b] = cnt[b];
