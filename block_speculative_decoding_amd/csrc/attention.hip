@@ -66,6 +66,10 @@ __global__ __launch_bounds__(256) void attn_bf16_d128(AttnArgs a) {
   const int g = pair % a.nkv, b = pair / a.nkv;
   const int units = a.n_ctx_splits + 1;
   const size_t bg = (size_t)b * a.nkv + g;
+  // one context unit per (b, g, group) — the grid fills the GPU without splits —
+  // also walks the S block keys and writes the normalised output itself (no
+  // block units, no partials, no combine pass)
+  const bool fused = a.n_ctx_splits == 1;
 
   const bf16_t* K;
   const bf16_t* Vt;
@@ -93,7 +97,7 @@ __global__ __launch_bounds__(256) void attn_bf16_d128(AttnArgs a) {
     k_begin = lo + unit * kps;
     k_end = min(cb, k_begin + kps);
   }
-  const int nsteps = k_end > k_begin ? (k_end - k_begin + KS - 1) / KS : 0;
+  int nsteps = k_end > k_begin ? (k_end - k_begin + KS - 1) / KS : 0;
 
   // staging: 16-byte chunks, 4 of K and 4 of V^T per thread per step
   //   K chunk q: slot q/16, dims (q%16)*8..+8      V chunk q: dim q/8, slots (q%8)*8..+8
@@ -227,21 +231,50 @@ __global__ __launch_bounds__(256) void attn_bf16_d128(AttnArgs a) {
   // Two steps per iteration, both always staged (a step past the end stages
   // clamped, fully masked tiles) so loads and waits sit in straight-line code;
   // only the math is skipped.
-  if (nsteps > 0) {
-    issue(0, kr0, vr0);
-    issue(1, kr1, vr1);
-    for (int it = 0; it < nsteps; it += 2) {
-      stage(it, kr0, vr0, 0);
-      __syncthreads();
-      issue(it + 2, kr0, vr0);
-      if (active) compute(it, 0);
-      stage(it + 1, kr1, vr1, 1);
-      __syncthreads();
-      issue(it + 3, kr1, vr1);
-      if (active && it + 1 < nsteps) compute(it + 1, 1);
+  auto walk = [&]() {
+    if (nsteps > 0) {
+      issue(0, kr0, vr0);
+      issue(1, kr1, vr1);
+      for (int it = 0; it < nsteps; it += 2) {
+        stage(it, kr0, vr0, 0);
+        __syncthreads();
+        issue(it + 2, kr0, vr0);
+        if (active) compute(it, 0);
+        stage(it + 1, kr1, vr1, 1);
+        __syncthreads();
+        issue(it + 3, kr1, vr1);
+        if (active && it + 1 < nsteps) compute(it + 1, 1);
+      }
     }
+  };
+  walk();
+  if (fused) {                               // then the block keys, same running softmax
+    __syncthreads();                         // every wave is done with both LDS buffers
+    K = (const bf16_t*)a.k_blk + bg * 64 * D;
+    Vt = (const bf16_t*)a.v_blk + bg * D * 64;
+    ldv = 64;
+    k_begin = 0;
+    k_end = a.S;
+    k_lo = 0;
+    nsteps = 1;
+    walk();
   }
   if (!active || row >= a.R) return;
+
+  if (fused) {
+    // output tile dt: lane holds dims dt*16 + 4*g4 .. +3 of query row `row` = hh*S + s
+    const int group = a.nq / a.nkv, hh = row / a.S, s = row % a.S, h = g * group + hh;
+    bf16_t* out = (bf16_t*)a.out + (((size_t)b * a.S + s) * a.nq + h) * D;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      bf16_t v4[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v4[i] = f2bf(o[dt][i] / l_run);
+      *(uint2*)(out + dt * 16 + 4 * g4) =
+          make_uint2((uint32_t)v4[0] | ((uint32_t)v4[1] << 16), (uint32_t)v4[2] | ((uint32_t)v4[3] << 16));
+    }
+    return;
+  }
 
   // partial O^T tile dt: lane holds dims dt*16 + 4*g4 + i of row `row`
   const size_t ubase = (bg * units + unit) * a.Rpad;
@@ -431,10 +464,12 @@ hipError_t launch_attention(const AttnArgs& a, int dtype, hipStream_t s) {
     hipLaunchKernelGGL(attn_f32, dim3(a.S, a.nq, a.B), dim3(256), 0, s, a);
     return hipGetLastError();
   }
-  const dim3 grid((unsigned)(a.B * a.nkv * a.row_groups * (a.n_ctx_splits + 1)));
+  // with a single context unit it takes the block keys too and writes the output
+  const bool fused = a.n_ctx_splits == 1;
+  const dim3 grid((unsigned)(a.B * a.nkv * a.row_groups * (fused ? 1 : a.n_ctx_splits + 1)));
   hipLaunchKernelGGL(attn_bf16_d128, grid, dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || fused) return e;
   hipLaunchKernelGGL(attn_combine<bf16_t>, dim3(a.R, a.nkv, a.B), dim3(128), 0, s, a);
   return hipGetLastError();
 }
