@@ -202,6 +202,83 @@ __global__ __launch_bounds__(64) void qkv_kernel(QkvArgs a) {
   }
 }
 
+// The same epilogue for bf16 with d = 128, by tiles: one 256-thread workgroup per
+// (batch row, tile of up to 16 consecutive rows of one segment — appended context
+// rows, or block rows —, head).  Thread t takes row t/16 and dims 4*(t%16) .. +3
+// plus the same four of the other rotary half: 16-byte loads of each split
+// partial, 8-byte stores.  Values go through LDS and are written transposed so
+// that each V^T cache row receives the tile's consecutive slots together.
+__global__ __launch_bounds__(256) void qkv_tile_kernel(QkvArgs a) {
+  constexpr int D = 128, HALF = 64, TR = 16;
+  __shared__ bf16_t vt[D][TR + 2];
+  const int tid = threadIdx.x, hd = blockIdx.y;
+  const int ctx_tiles = (a.n_new_max + TR - 1) / TR, blk_tiles = (a.S + TR - 1) / TR;
+  const int per_b = ctx_tiles + blk_tiles;
+  const int b = blockIdx.x / per_b, tile = blockIdx.x % per_b;
+  const bool ctx = tile < ctx_tiles;
+  if (ctx && hd < a.nq) return;                          // no queries for context rows (uniform)
+  const int j0 = (ctx ? tile : tile - ctx_tiles) * TR;   // first row of the tile within its segment
+  const int nrows = ctx ? min(TR, a.meta[a.B + b] - j0) : min(TR, a.S - j0);   // appended / block rows
+  if (nrows <= 0) return;
+  const int Mc = a.B * a.n_new_max;
+  const int Nqkv = (a.nq + 2 * a.nkv) * D;
+  const bool is_q = hd < a.nq, is_k = !is_q && hd < a.nq + a.nkv;
+  const int g = is_q ? hd / (a.nq / a.nkv) : (is_k ? hd - a.nq : hd - a.nq - a.nkv);
+  const size_t bg = (size_t)b * a.nkv + g;
+  const int r = tid >> 4, i0 = (tid & 15) * 4;
+  const int j = j0 + r;
+  const bool valid = r < nrows;
+  const int row = ctx ? b * a.n_new_max + j : Mc + b * a.S + j;
+  const int slot0 = ctx ? a.meta[b] + j0 : j0;           // cache slot (or block slot) of the tile's first row
+  float x1[4] = {0.f, 0.f, 0.f, 0.f}, x2[4] = {0.f, 0.f, 0.f, 0.f};
+  if (valid) {
+    const size_t off = (size_t)row * Nqkv + hd * D + i0;
+    for (int z = 0; z < a.sp; ++z) {
+      const float4 u = *(const float4*)(a.part + z * a.part_stride + off);
+      const float4 w = *(const float4*)(a.part + z * a.part_stride + off + HALF);
+      x1[0] += u.x; x1[1] += u.y; x1[2] += u.z; x1[3] += u.w;
+      x2[0] += w.x; x2[1] += w.y; x2[2] += w.z; x2[3] += w.w;
+    }
+    if ((is_q || is_k) && a.use_rope) {
+      const float4 c01 = *(const float4*)(a.rope + (size_t)row * HALF + i0);
+      const float4 c23 = *(const float4*)(a.rope + (size_t)row * HALF + i0 + 2);
+      const float cs[4][2] = {{c01.x, c01.y}, {c01.z, c01.w}, {c23.x, c23.y}, {c23.z, c23.w}};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float y1 = x1[e] * cs[e][0] - x2[e] * cs[e][1];
+        const float y2 = x2[e] * cs[e][0] + x1[e] * cs[e][1];
+        x1[e] = y1;
+        x2[e] = y2;
+      }
+    }
+  }
+  auto pack4 = [](const float* v) {
+    return make_uint2((uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16),
+                      (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16));
+  };
+  if (is_q || is_k) {
+    if (!valid) return;
+    bf16_t* dst;
+    if (is_q) dst = (bf16_t*)a.q_att + (bg * a.Rpad + (hd % (a.nq / a.nkv)) * a.S + j) * D;
+    else dst = ctx ? (bf16_t*)a.k_cache + (bg * a.max_ctx + slot0 + r) * D : (bf16_t*)a.k_blk + (bg * 64 + j) * D;
+    *(uint2*)(dst + i0) = pack4(x1);
+    *(uint2*)(dst + HALF + i0) = pack4(x2);
+    return;
+  }
+  // values: transpose through LDS, then every lane group of 16 writes one dim's slots
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    vt[i0 + e][r] = f2bf(x1[e]);
+    vt[HALF + i0 + e][r] = f2bf(x2[e]);
+  }
+  __syncthreads();
+  const size_t ld = ctx ? (size_t)a.max_ctx : 64;
+  bf16_t* dst = (ctx ? (bf16_t*)a.v_cache : (bf16_t*)a.v_blk) + bg * D * ld + slot0;
+  const int rr = tid & 15;
+  if (rr < nrows)
+    for (int dim = tid >> 4; dim < D; dim += 16) dst[(size_t)dim * ld + rr] = vt[dim][rr];
+}
+
 // h = T(silu(gate) * up) with gate = sum_z part[z][m][f], up = sum_z part[z][m][F + f]
 template <typename T>
 __global__ __launch_bounds__(256) void swiglu_kernel(const float* part, int sp, size_t ps, int M, int F,
@@ -296,6 +373,12 @@ hipError_t launch_norm(const NormArgs& a, int dtype, hipStream_t s) {
 
 hipError_t launch_qkv_epilogue(const QkvArgs& a, int dtype, hipStream_t s) {
   ProfScope ps("elementwise", s);
+  const bool aligned = (((uintptr_t)a.part | (uintptr_t)a.rope) & 15) == 0 && a.part_stride % 4 == 0;
+  if (dtype == 1 && a.d == 128 && aligned) {
+    const int tiles = (a.n_new_max + 15) / 16 + (a.S + 15) / 16;
+    hipLaunchKernelGGL(qkv_tile_kernel, dim3(a.B * tiles, a.nq + 2 * a.nkv), dim3(256), 0, s, a);
+    return hipGetLastError();
+  }
   dim3 grid(a.B * a.n_new_max + a.B * a.S, a.nq + 2 * a.nkv);
   if (dtype == 1) hipLaunchKernelGGL(qkv_kernel<bf16_t>, grid, dim3(64), 0, s, a);
   else hipLaunchKernelGGL(qkv_kernel<float>, grid, dim3(64), 0, s, a);
