@@ -611,26 +611,40 @@ static const Cand kCands[] = {
 // W (once per M tile, the M tiles of one W slab sharing an XCD's L2), staged X
 // (mostly L2 hits, weighted 1/2) and the fp32 split partials (written and read
 // back, mostly MALL resident), against the dense product at about half the
-// bf16 peak, all divided by how well the grid fills the chip.
+// bf16 peak.  The streaming kernel walks k in bodies of 8 steps, so a split's
+// steps count rounded up to 8.  One workgroup occupies a CU: a grid of w < 256
+// workgroups reaches about (w/256)^0.55 of the chip's bandwidth (a CU alone
+// streams faster than its 1/256 share), a larger one runs in rounds of 256,
+// each with a fixed ~1.5 us (pipeline ramp, epilogue).  Fitted to sweeps of the
+// drafter shapes at M = 16 .. 256 (every pick within 3 % of the fastest
+// measured configuration, the sum within 0.3 %).
 // M > 256 (matrix-core bound): the 128 x 128 streaming tile at its measured
-// ~0.85 PFLOP/s or the 256 x 256 LDS-ring tile at ~1.1 PFLOP/s.  One workgroup
-// occupies a CU, so compute time is counted in whole waves of 256 workgroups,
-// plus a fixed ~4 us per wave (pipeline ramp, epilogue); split partials cost
-// one more pass over M x N x splits fp32.  Fitted to measurements of the
-// drafter shapes at M = 480 .. 2048 (every pick within 2 % of the fastest).
+// ~0.85 PFLOP/s or the 256 x 256 LDS-ring tile at ~1.1 PFLOP/s.  Compute time
+// is counted in whole waves of 256 workgroups, plus a fixed ~4 us per wave;
+// split partials cost one more pass over M x N x splits fp32.  Fitted to
+// measurements of the drafter shapes at M = 480 .. 2048 (every pick within 2 %
+// of the fastest).
 static double plan_cost(const Cand& c, int sp, int M, int N, int K) {
   const bool big = M > 256;
   const int mt = ceil_div(M, c.bm), nt = ceil_div(N, c.bn);
+  const double wgs = (double)mt * nt * sp;
+  // fp32 output: one slice, or sp slices written and read back by the consumer
+  const double part = sp > 1 ? 1.5 * 4.0 * M * N * sp : 4.0 * M * N;
+  if (!big) {
+    const int kps = ceil_div(K / BK, sp);
+    const double pad = (double)(ceil_div(kps, 8) * 8) / kps;
+    const double w = 2.0 * N * K * (1.0 + 0.5 * (mt - 1)) * pad;
+    const double x = 2.0 * (double)mt * c.bm * K * nt * pad;
+    const double flops = 2.0 * (double)mt * c.bm * nt * c.bn * K;
+    const double rounds = ceil(wgs / 256.0);
+    const double fill = wgs < 256.0 ? pow(wgs / 256.0, 0.55) : wgs / (rounds * 256.0);
+    return fmax((w + 0.5 * x + part) / 8.0e12, flops / 1.2e15) / fill + rounds * 1.5e-6;
+  }
   const double w = 2.0 * N * K * (1.0 + 0.5 * (mt - 1));
   const double x = 2.0 * (double)mt * c.bm * K * nt;
   const double flops = 2.0 * (double)mt * c.bm * nt * c.bn * K;
-  // fp32 output: one slice, or sp slices written and read back by the consumer
-  const double part = sp > 1 ? 1.5 * 4.0 * M * N * sp : 4.0 * M * N;
-  const double wgs = (double)mt * nt * sp;
-  // one 512-thread streaming workgroup per CU already saturates its share of HBM
   const double fill = wgs >= 192.0 ? 1.0 : wgs / 192.0;
   const double mem = (w + 0.5 * x + part) / 8.0e12;
-  if (!big) return fmax(mem, flops / 1.2e15) / fill;
   const double waves = ceil(wgs / 256.0);
   const double rate = c.kind == 3 ? 1.1e15 : 0.85e15;
   const double cmp = flops / rate * (waves * 256.0 / wgs) + waves * 4.0e-6;
@@ -734,6 +748,18 @@ GemmPlan gemm_plan_gated(int M, int N, int K, int dtype) {
   p.k_per_split = K;
   p.pd = 4;
   p.xd = p.mt == 8 ? 4 : 2;
+#ifdef DFS_TUNING
+  // tuning builds only: DFS_GATED_FORCE="mt" selects the streaming row tile
+  if (const char* f = getenv("DFS_GATED_FORCE")) {
+    int mt = 0;
+    if (sscanf(f, "%d", &mt) == 1) {
+      p.mt = mt;
+      p.bm = 16 * mt;
+      p.xd = mt == 8 ? 4 : 2;
+      return p;
+    }
+  }
+#endif
   if (M > 256) {
     // both read 2N weight rows; the streaming tile covers 64 features, the LDS tile 128
     const Cand stream = {1, 128, 128, 8, 2}, tile = {3, 256, 256, 0, 0};
