@@ -31,7 +31,8 @@ Citation key (the pages, by title; sections are named as they appear):
   L = (T_draft + T_verify) / tau), "Innowacje w tworzeniu tokenów" (parallel
   core emits base logits per position; light sequential head adds a
   prefix-dependent bias before each token is sampled; Markov head = previous
-  token only, rank-256 factorisation), "Optymalizacja weryfikacji i wydajności"
+  token only, rank-256 factorisation; an optional RNN head follows the whole
+  block prefix), "Optymalizacja weryfikacji i wydajności"
   (total-variation loss <-> acceptance rate), "Wyniki i zastosowania
   produkcyjne" (draft length 4 -> 16 costs 0.2-1.3 % latency per round for
   +30 % accepted length).
@@ -51,7 +52,7 @@ from .rounding import round_bf16, round_f32, bf16_bits_to_f64, f64_to_bf16_bits,
 from .drafter import (rmsnorm, rope_rotate, block_attention, context_features,
                       draft_step, DrafterShape)
 from .sampling import (softmax_weights, inverse_cdf, argmax_with_gap, sample_row,
-                       markov_sample)
+                       markov_sample, rnn_states, rnn_sample)
 from .verify import verify
 from .bookkeeping import (tau_from_accepted, latency_per_token, acceptance_rate,
                           expected_tau_independent, expected_tau_markov)
@@ -60,6 +61,6 @@ __all__ = [
     "round_bf16", "round_f32", "bf16_bits_to_f64", "f64_to_bf16_bits", "round_to",
     "rmsnorm", "rope_rotate", "block_attention", "context_features", "draft_step",
     "DrafterShape", "softmax_weights", "inverse_cdf", "argmax_with_gap", "sample_row",
-    "markov_sample", "verify", "tau_from_accepted", "latency_per_token",
+    "markov_sample", "rnn_states", "rnn_sample", "verify", "tau_from_accepted", "latency_per_token",
     "acceptance_rate", "expected_tau_independent", "expected_tau_markov",
 ]

@@ -105,3 +105,68 @@ def markov_sample(base_logits, U, Wt, uw_dtype, last_token, u_draft, temperature
             margins[b, i] = m
             prev = k
     return final, tokens, margins
+
+
+def rnn_states(U, A, uw_dtype, prev_tokens):
+    """States of the RNN sequential head along one block (float64).
+
+    [DSpark] "Innowacje w tworzeniu tokenów": besides the default Markov head
+    the page names an optional RNN head that follows the whole block prefix
+    (with only a marginal gain over the Markov head).  It gives no structure, so
+    the cell is a reading: an Elman cell whose state has the head's rank r,
+
+        h_0 = 0,   h_i = tanh(U[prev_i] + A h_{i-1})      i = 1 .. gamma
+
+    with the Markov head's input factor U [V, r] as the input embedding (so the
+    i-th input is the same previous token the Markov head looks up), a
+    recurrent matrix A [r, r] (row j holds the weights into state element j),
+    no bias; the state is kept in full precision.  prev_tokens [gamma] are the
+    previous tokens prev_1 .. prev_gamma (clamped to the vocabulary).
+    Returns [gamma, r].
+    """
+    Uf = as_f64(U, uw_dtype)
+    Af = as_f64(A, uw_dtype)
+    V, r = Uf.shape
+    h = np.zeros(r)
+    out = np.zeros((len(prev_tokens), r))
+    for i, p in enumerate(prev_tokens):
+        p = min(max(int(p), 0), V - 1)
+        h = np.tanh(Uf[p] + Af @ h)
+        out[i] = h
+    return out
+
+
+def rnn_sample(base_logits, U, Wt, A, uw_dtype, last_token, u_draft, temperature):
+    """Sequential sampling of the gamma draft positions with the RNN head.
+
+    final_i = base_i + W h_i (the Markov head's output factor, Wt [V, r]; the
+    bias rounded to fp32, then the sum, as for the Markov head), h_i from
+    ``rnn_states`` with prev_1 = last decoded token and prev_i = d_{i-1}; each
+    draw as in ``sample_row``.  Returns (final_logits [B, gamma, V] float32,
+    tokens [B, gamma] int32, margins [B, gamma] float64, states [B, gamma, r]).
+    """
+    base = np.asarray(base_logits, np.float32)
+    B, G, V = base.shape
+    Uf = as_f64(U, uw_dtype)
+    Wf = as_f64(Wt, uw_dtype)
+    Af = as_f64(A, uw_dtype)
+    r = Uf.shape[1]
+    final = base.copy()
+    tokens = np.zeros((B, G), np.int32)
+    margins = np.zeros((B, G), np.float64)
+    states = np.zeros((B, G, r))
+    for b in range(B):
+        prev = int(last_token[b])
+        h = np.zeros(r)
+        for i in range(G):
+            p = min(max(prev, 0), V - 1)
+            h = np.tanh(Uf[p] + Af @ h)
+            states[b, i] = h
+            bias = round_f32(Wf @ h)
+            row = round_f32(base[b, i].astype(np.float64) + bias)
+            final[b, i] = row.astype(np.float32)
+            k, m = sample_row(row, u_draft[b, i], temperature)
+            tokens[b, i] = k
+            margins[b, i] = m
+            prev = k
+    return final, tokens, margins, states

@@ -415,6 +415,94 @@ def test_markov_sequence_distribution_chi_square():
     assert _chi2_pvalue(np.bincount(idx, minlength=V ** G), probs) > 1e-4
 
 
+# ---------------------------------------------------------------- RNN head
+
+def _torch_elman_states(U, A, prev_tokens):
+    """States of torch.nn.RNN (tanh, no bias) on one-hot inputs, float64."""
+    import torch
+    V, r = U.shape
+    cell = torch.nn.RNN(V, r, nonlinearity="tanh", bias=False, dtype=torch.float64)
+    with torch.no_grad():
+        cell.weight_ih_l0.copy_(torch.from_numpy(np.asarray(U, np.float64).T.copy()))
+        cell.weight_hh_l0.copy_(torch.from_numpy(np.asarray(A, np.float64)))
+        x = torch.nn.functional.one_hot(torch.as_tensor(np.asarray(prev_tokens, np.int64)), V).double()
+        out, _ = cell(x[:, None, :])
+    return out[:, 0, :].numpy()
+
+
+def test_rnn_head_states_equal_a_library_elman_rnn():
+    # the head's recurrence is an Elman cell fed one-hot previous tokens: torch's
+    # RNN with W_ih = U^T and W_hh = A must produce the same states, and the
+    # bias added to each position must be W h of that state
+    V, r, G, B = 11, 5, 6, 3
+    g = np.random.default_rng(21)
+    U = (g.standard_normal((V, r)) * 0.8).astype(np.float32)
+    Wt = g.standard_normal((V, r)).astype(np.float32)
+    A = (g.standard_normal((r, r)) * 0.7).astype(np.float32)
+    base = g.standard_normal((B, G, V)).astype(np.float32)
+    last = np.array([0, 7, 10])
+    u = rng.uniform01(21, "rnn", (B, G))
+    final, tok, _, states = oracle.rnn_sample(base, U, Wt, A, "f32", last, u, 1.0)
+    for b in range(B):
+        prev = np.concatenate([[last[b]], tok[b, :-1]])
+        ref = _torch_elman_states(U, A, prev)
+        np.testing.assert_allclose(states[b], ref, rtol=0, atol=1e-13)
+        np.testing.assert_allclose(oracle.rnn_states(U, A, "f32", prev), ref, rtol=0, atol=1e-13)
+        bias = ref @ Wt.astype(np.float64).T
+        np.testing.assert_allclose(final[b].astype(np.float64) - base[b], bias, atol=2e-6)
+    # A transposed is a different head: the states must tell them apart
+    prev = np.concatenate([[last[0]], tok[0, :-1]])
+    assert np.abs(_torch_elman_states(U, A.T, prev) - states[0]).max() > 1e-3
+
+
+def test_rnn_head_sequence_distribution_chi_square():
+    # V = 6, gamma = 3: drafted sequences follow prod_i softmax(base_i + W h_i)(d_i)
+    # with h_i the library RNN's state on the sequence's own prefix
+    V, G, r, N = 6, 3, 4, 30_000
+    g = np.random.default_rng(22)
+    U = (g.standard_normal((V, r)) * 0.9).astype(np.float32)
+    Wt = (g.standard_normal((V, r)) * 0.9).astype(np.float32)
+    A = (g.standard_normal((r, r)) * 0.6).astype(np.float32)
+    base1 = (g.standard_normal((G, V)) * 0.5).astype(np.float32)
+    last = 4
+    probs = np.zeros(V ** G)
+    for idx in range(V ** G):
+        seq = np.unravel_index(idx, (V,) * G)
+        h = _torch_elman_states(U, A, [last] + list(seq[:-1]))
+        pr = 1.0
+        for i in range(G):
+            pr *= special.softmax(base1[i] + h[i] @ Wt.astype(np.float64).T)[seq[i]]
+        probs[idx] = pr
+    base = np.broadcast_to(base1, (N, G, V))
+    u = rng.uniform01(22, "rnn_seq", (N, G))
+    _, tok, _, _ = oracle.rnn_sample(base, U, Wt, A, "f32", np.full(N, last), u, 1.0)
+    idx = np.ravel_multi_index(tuple(tok.T), (V,) * G)
+    assert _chi2_pvalue(np.bincount(idx, minlength=V ** G), probs) > 1e-4
+
+
+def test_rnn_head_degenerate_cases():
+    V, r, G = 9, 4, 5
+    g = np.random.default_rng(23)
+    U = g.standard_normal((V, r)).astype(np.float32)
+    Wt = g.standard_normal((V, r)).astype(np.float32)
+    base = g.standard_normal((2, G, V)).astype(np.float32)
+    last = np.array([1, 8])
+    u = rng.uniform01(23, "rnn_deg", (2, G))
+    # no recurrence: the head is a Markov head whose input factor is tanh(U)
+    f0, t0, m0, _ = oracle.rnn_sample(base, U, Wt, np.zeros((r, r), np.float32), "f32", last, u, 1.0)
+    f1, t1, m1 = oracle.markov_sample(base, np.tanh(U.astype(np.float64)).astype(np.float32), Wt, "f32", last, u, 1.0)
+    np.testing.assert_allclose(f0, f1, atol=1e-5)
+    ok = (m0 > 1e-5) & (m1 > 1e-5)
+    assert np.array_equal(t0[ok], t1[ok]) and ok.mean() > 0.9
+    # zero input factor: the state stays 0 and positions are independent draws
+    f2, t2, _, st = oracle.rnn_sample(base, np.zeros_like(U), Wt, g.standard_normal((r, r)).astype(np.float32),
+                                      "f32", last, u, 1.0)
+    assert not st.any() and np.array_equal(f2, base)
+    for b in range(2):
+        for i in range(G):
+            assert t2[b, i] == oracle.sample_row(base[b, i], u[b, i], 1.0)[0]
+
+
 # ---------------------------------------------------------------- verify
 
 def _verify_trials(p_logits, q_logits, N, seed, temperature=1.0):
