@@ -388,6 +388,30 @@ int dflash_draft_step(const dfs_drafter_cfg* cfg, const dfs_drafter_weights* wt,
 
 // ------------------------------------------------------------------ Markov head + sampling
 
+// Draw position i of every request from its final logits: chunk statistics,
+// then the inverse-CDF (or greedy) pick; writes d_i and the row's (max, sum).
+static hipError_t sample_position(int batch, int n_draft, int vocab, int i, const float* logits,
+                                  const float* u_draft, float temperature, int32_t* draft_tokens,
+                                  double* row_stats, double2* stats, hipStream_t s) {
+  const long rowV = (long)n_draft * vocab;
+  const hipError_t e = launch_chunk_stats(logits + (size_t)i * vocab, rowV, batch, vocab, temperature, stats, s);
+  if (e != hipSuccess) return e;
+  PickArgs pa;
+  pa.x = logits + (size_t)i * vocab;
+  pa.row_stride = rowV;
+  pa.rows = batch;
+  pa.V = vocab;
+  pa.temperature = temperature;
+  pa.stats = stats;
+  pa.u = u_draft + i;
+  pa.u_stride = n_draft;
+  pa.tokens = draft_tokens + i;
+  pa.tok_stride = n_draft;
+  pa.row_stats = row_stats ? row_stats + 2 * i : nullptr;
+  pa.rs_stride = 2 * (long)n_draft;
+  return launch_pick(pa, s);
+}
+
 size_t markov_bias_sample_workspace_size(int32_t batch, int32_t n_draft, int32_t vocab) {
   if (batch < 1 || n_draft < 1 || vocab < 1) return 0;
   const size_t nch = (size_t)ceil_div(vocab, kChunk);
@@ -454,21 +478,88 @@ int markov_bias_sample(int32_t batch, int32_t n_draft, int32_t vocab, int32_t ra
     ga.accumulate = 1;
     ga.packed = uw_packed;
     DFS_TRY(launch_gemm(ga, plan, uw_dtype, s));
-    DFS_TRY(launch_chunk_stats(logits + (size_t)i * vocab, rowV, batch, vocab, temperature, stats, s));
-    PickArgs pa;
-    pa.x = logits + (size_t)i * vocab;
-    pa.row_stride = rowV;
-    pa.rows = batch;
-    pa.V = vocab;
-    pa.temperature = temperature;
-    pa.stats = stats;
-    pa.u = u_draft + i;
-    pa.u_stride = n_draft;
-    pa.tokens = draft_tokens + i;
-    pa.tok_stride = n_draft;
-    pa.row_stats = row_stats ? row_stats + 2 * i : nullptr;
-    pa.rs_stride = 2 * (long)n_draft;
-    DFS_TRY(launch_pick(pa, s));
+    DFS_TRY(sample_position(batch, n_draft, vocab, i, logits, u_draft, temperature, draft_tokens, row_stats, stats,
+                            s));
+  }
+  return DFS_OK;
+}
+
+// ------------------------------------------------------------------ RNN head + sampling
+
+static size_t rnn_carve(int B, int G, int V, int r, void* base, double2** stats, float** h, bf16_t** split) {
+  Carver cv(base);
+  double2* st = cv.take<double2>((size_t)B * G * ceil_div(V, kChunk));
+  float* hh = cv.take<float>((size_t)B * r);
+  bf16_t* sp = cv.take<bf16_t>((size_t)3 * B * r);
+  if (stats) *stats = st;
+  if (h) *h = hh;
+  if (split) *split = sp;
+  return cv.off + 256;
+}
+
+size_t rnn_bias_sample_workspace_size(int32_t batch, int32_t n_draft, int32_t vocab, int32_t rank) {
+  if (batch < 1 || n_draft < 1 || vocab < 1 || rank < 1 || rank > kRnnMaxRank) return 0;
+  return rnn_carve(batch, n_draft, vocab, rank, nullptr, nullptr, nullptr, nullptr);
+}
+
+int rnn_bias_sample(int32_t batch, int32_t n_draft, int32_t vocab, int32_t rank, float* logits, const void* U,
+                    const void* Wt, const void* A, int32_t uw_dtype, const int32_t* last_token, const float* u_draft,
+                    float temperature, int32_t* draft_tokens, double* row_stats, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  if (batch < 1 || n_draft < 1 || vocab < 1 || rank < 1 || !logits || !U || !Wt || !A || !last_token ||
+      !u_draft || !draft_tokens || !workspace)
+    return DFS_EINVAL;
+  if (!(temperature >= 0.f)) return DFS_EINVAL;
+  if (uw_dtype != DFS_F32 && uw_dtype != DFS_BF16 && uw_dtype != DFS_BF16_PACKED) return DFS_EINVAL;
+  if (vocab > kMaxVocab || rank > kRnnMaxRank) return DFS_EUNSUPPORTED;
+  if (uw_dtype != DFS_F32 && rank % 64 != 0) return DFS_EUNSUPPORTED;
+  const int uw_packed = uw_dtype == DFS_BF16_PACKED;
+  if (uw_packed) uw_dtype = DFS_BF16;
+  if (workspace_bytes < rnn_bias_sample_workspace_size(batch, n_draft, vocab, rank)) return DFS_EWORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  double2* stats;
+  float* h;
+  bf16_t* split;
+  rnn_carve(batch, n_draft, vocab, rank, workspace, &stats, &h, &split);
+  const bool bf = uw_dtype == DFS_BF16;
+  const long rowV = (long)n_draft * vocab;
+  ProfScope ps("markov", s);
+  const GemmPlan plan = gemm_plan(batch, vocab, rank, uw_dtype, 1);
+  for (int i = 0; i < n_draft; ++i) {
+    // h_i = tanh(U[prev_i] + A h_{i-1}), then final_i = base_i + W h_i
+    RnnArgs ra;
+    ra.U = U;
+    ra.A = A;
+    ra.prev = i == 0 ? last_token : draft_tokens + (i - 1);
+    ra.prev_stride = i == 0 ? 1 : n_draft;
+    ra.h = h;
+    ra.split = bf ? split : nullptr;
+    ra.first = i == 0;
+    ra.B = batch;
+    ra.V = vocab;
+    ra.r = rank;
+    DFS_TRY(launch_rnn_state(ra, uw_dtype, s));
+    // fp32: one pass with the state itself; bf16: the three bf16 terms of the
+    // state, accumulated in turn (hi, mid, lo) into the fp32 logits
+    for (int t = 0; t < (bf ? 3 : 1); ++t) {
+      GemmArgs ga;
+      ga.X = bf ? (const void*)(split + (size_t)t * batch * rank) : (const void*)h;
+      ga.ldx = rank;
+      ga.x_rows = batch;
+      ga.M = batch;
+      ga.N = vocab;
+      ga.K = rank;
+      ga.seg[0].w = Wt;
+      ga.nseg = 1;
+      ga.Y = logits + (size_t)i * vocab;
+      ga.ldy = rowV;
+      ga.y_split_stride = 0;
+      ga.accumulate = 1;
+      ga.packed = uw_packed;
+      DFS_TRY(launch_gemm(ga, plan, uw_dtype, s));
+    }
+    DFS_TRY(sample_position(batch, n_draft, vocab, i, logits, u_draft, temperature, draft_tokens, row_stats, stats,
+                            s));
   }
   return DFS_OK;
 }

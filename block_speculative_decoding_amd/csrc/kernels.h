@@ -193,4 +193,18 @@ struct SchedArgs {
 };
 hipError_t launch_schedule(const SchedArgs& a, hipStream_t s);
 
+// ------------------------------------------------------------------ RNN sequential head
+constexpr int kRnnMaxRank = 1024;
+struct RnnArgs {
+  const void* U;           // [V][r] input factor (dtype)
+  const void* A;           // [r][r] recurrent matrix (dtype), row j -> state element j
+  const int32_t* prev;     // previous token of request b at prev[b * prev_stride]
+  long prev_stride;
+  float* h;                // [B][r] fp32 state, updated in place
+  bf16_t* split;           // [3][B][r] bf16 terms hi, mid, lo of the new state, or null
+  int first;               // 1: previous state is zero (first position of the block)
+  int B, V, r;
+};
+hipError_t launch_rnn_state(const RnnArgs& a, int dtype, hipStream_t s);
+
 }  // namespace dfs

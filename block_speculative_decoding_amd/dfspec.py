@@ -21,7 +21,7 @@ DFS_F32, DFS_BF16, DFS_BF16_PACKED = 0, 1, 2
 
 EXPORTS = [
     "dflash_draft_workspace_size", "dflash_draft_step",
-    "markov_bias_sample_workspace_size", "markov_bias_sample",
+    "markov_bias_sample_workspace_size", "markov_bias_sample", "rnn_bias_sample_workspace_size", "rnn_bias_sample",
     "spec_verify_workspace_size", "spec_verify", "dfs_status_string",
     "dfs_block_attention_workspace_size", "dfs_block_attention",
     "dfs_gemm_workspace_size", "dfs_gemm", "dfs_profile_begin", "dfs_profile_end",
@@ -64,6 +64,9 @@ def _load():
         "markov_bias_sample_workspace_size": (sz, [i32, i32, i32]),
         "markov_bias_sample": (ctypes.c_int, [i32, i32, i32, i32, vp, vp, vp, i32, vp, vp, f32, vp, vp,
                                               vp, sz, vp]),
+        "rnn_bias_sample_workspace_size": (sz, [i32, i32, i32, i32]),
+        "rnn_bias_sample": (ctypes.c_int, [i32, i32, i32, i32, vp, vp, vp, vp, i32, vp, vp, f32, vp, vp,
+                                           vp, sz, vp]),
         "spec_verify_workspace_size": (sz, [i32, i32, i32]),
         "spec_verify": (ctypes.c_int, [i32, i32, i32, vp, vp, vp, vp, vp, f32, vp, vp, vp, vp, vp, sz, vp]),
         "dfs_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -243,6 +246,37 @@ def markov_bias_sample(logits, U, Wt, last_token, u_draft, temperature: float, d
         _ptr(row_stats, torch.float64, B * G * 2, "row_stats") if row_stats is not None else None,
         _ptr(workspace, torch.uint8, None, "workspace"), workspace.numel(), _stream(stream))
     _check(st, "markov_bias_sample")
+
+
+def rnn_bias_sample_workspace_size(batch: int, n_draft: int, vocab: int, rank: int) -> int:
+    return int(LIB.rnn_bias_sample_workspace_size(batch, n_draft, vocab, rank))
+
+
+def rnn_bias_sample(logits, U, Wt, A, last_token, u_draft, temperature: float, draft_tokens, row_stats,
+                    workspace, stream=None, wt_packed: bool = False):
+    """RNN sequential head + sampling; U, Wt [V, r] and A [r, r] all bf16 or all fp32.
+    wt_packed: Wt was packed by pack_matrix (bf16)."""
+    B, G, V = logits.shape
+    rank = U.shape[1]
+    uw_dtype = DFS_BF16 if U.dtype == torch.bfloat16 else DFS_F32
+    dt = torch_dtype(uw_dtype)
+    _ptr(U, dt, V * rank, "U")
+    _ptr(A, dt, rank * rank, "A")
+    if wt_packed:
+        if uw_dtype != DFS_BF16:
+            raise ValueError("a packed Wt must be bf16")
+        _ptr(Wt, torch.bfloat16, packed_matrix_bytes(V, rank) // 2, "Wt")
+        uw_dtype = DFS_BF16_PACKED
+    else:
+        _ptr(Wt, dt, V * rank, "Wt")
+    st = LIB.rnn_bias_sample(
+        B, G, V, rank, _ptr(logits, torch.float32, B * G * V, "logits"), _ptr(U, name="U"), _ptr(Wt, name="Wt"),
+        _ptr(A, name="A"), uw_dtype, _ptr(last_token, torch.int32, B, "last_token"),
+        _ptr(u_draft, torch.float32, B * G, "u_draft"), float(temperature),
+        _ptr(draft_tokens, torch.int32, B * G, "draft_tokens"),
+        _ptr(row_stats, torch.float64, B * G * 2, "row_stats") if row_stats is not None else None,
+        _ptr(workspace, torch.uint8, None, "workspace"), workspace.numel(), _stream(stream))
+    _check(st, "rnn_bias_sample")
 
 
 def spec_verify_workspace_size(batch: int, n_draft: int, vocab: int) -> int:

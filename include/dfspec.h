@@ -20,6 +20,8 @@
  *                       that depends on the previous token (Markov head,
  *                       low-rank factorisation, rank 256) to each position's base
  *                       logits before that position is sampled.
+ *   rnn_bias_sample     The optional RNN sequential head of the same section
+ *                       (it follows the whole block prefix), same sampling.
  *   spec_verify         Rejection-sampling verification.  Same DSpark page,
  *                       section "Jak działa spekulatywne dekodowanie DSpark?":
  *                       the target keeps the longest valid prefix and adds one
@@ -198,6 +200,38 @@ int markov_bias_sample(int32_t batch, int32_t n_draft, int32_t vocab, int32_t ra
                        const int32_t* last_token, const float* u_draft, float temperature,
                        int32_t* draft_tokens, double* row_stats, void* workspace,
                        size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------- RNN + sample */
+
+size_t rnn_bias_sample_workspace_size(int32_t batch, int32_t n_draft, int32_t vocab, int32_t rank);
+
+/* The optional RNN sequential head of the same DSpark page and section ("Innowacje
+ * w tworzeniu tokenów": a head that follows the whole block prefix instead of the
+ * previous token only).  The page gives no structure; the cell implemented is an
+ * Elman tanh cell whose state has the head's rank r, fed the previous token
+ * through the Markov head's input factor:
+ *   h_0 = 0,  h_i = tanh(U[prev_i] + A h_{i-1}),  final_i = base_i + W h_i
+ * (prev_1 = last_token[b], prev_i = d_{i-1}), each d_i drawn as in
+ * markov_bias_sample.  The state is kept in fp32; with bf16 factors W h_i is
+ * formed from three bf16 terms of h_i (hi + mid + lo), i.e. to fp32 accuracy.
+ *
+ * logits, last_token, u_draft, temperature, draft_tokens, row_stats: as for
+ *             markov_bias_sample.
+ * U, Wt       [V, rank] in uw_dtype (DFS_F32, DFS_BF16, or DFS_BF16_PACKED: Wt
+ *             tile-packed by dfs_pack_matrix, U row-major bf16).
+ * A           [rank, rank] row-major, fp32 for DFS_F32 else bf16; A[j][k]
+ *             weights state element k of h_{i-1} into element j of h_i.
+ * workspace   rnn_bias_sample_workspace_size bytes (holds the state between
+ *             positions; nothing persists across calls).
+ *
+ * DFS_EINVAL for rank < 1 or null pointers; DFS_EUNSUPPORTED for rank > 1024,
+ * a bf16 head unless rank is a multiple of 64, and vocab > 4194304.
+ */
+int rnn_bias_sample(int32_t batch, int32_t n_draft, int32_t vocab, int32_t rank, float* logits,
+                    const void* U, const void* Wt, const void* A, int32_t uw_dtype,
+                    const int32_t* last_token, const float* u_draft, float temperature,
+                    int32_t* draft_tokens, double* row_stats, void* workspace,
+                    size_t workspace_bytes, void* stream);
 
 /* ----------------------------------------------------------------- verify */
 

@@ -100,6 +100,21 @@ def test_invalid_arguments_rejected_on_host(lib):
                            1 << 20, None) == -1
     assert lib.spec_verify(4, 3, 1000, fake, fake, fake, fake, fake, 1.0, None, None, fake, fake, fake,
                            16, None) == -4
+    # RNN head: a state is needed (rank >= 1), rank <= 1024, bf16 rank a multiple of 64
+    lib.rnn_bias_sample_workspace_size.restype = ctypes.c_size_t
+    assert lib.rnn_bias_sample_workspace_size(4, 3, 1000, 0) == 0
+    assert lib.rnn_bias_sample_workspace_size(4, 3, 1000, 2048) == 0
+    assert lib.rnn_bias_sample_workspace_size(4, 3, 1000, 64) > lib.markov_bias_sample_workspace_size(4, 3, 1000)
+    lib.rnn_bias_sample.argtypes = [ctypes.c_int32] * 4 + [ctypes.c_void_p] * 4 + [ctypes.c_int32] + \
+        [ctypes.c_void_p] * 2 + [ctypes.c_float] + [ctypes.c_void_p] * 3 + [ctypes.c_size_t, ctypes.c_void_p]
+    rnn = lambda rank, dt, a, wsb, T=1.0: lib.rnn_bias_sample(4, 3, 1000, rank, fake, fake, fake, a, dt, fake, fake, T,
+                                                              fake, None, fake, wsb, None)
+    assert rnn(0, 0, fake, 1 << 20) == -1
+    assert rnn(64, 1, None, 1 << 20) == -1                     # A missing
+    assert rnn(64, 1, fake, 1 << 20, T=-1.0) == -1
+    assert rnn(32, 1, fake, 1 << 20) == -2                     # bf16 rank not a multiple of 64
+    assert rnn(2048, 0, fake, 1 << 30) == -2
+    assert rnn(64, 1, fake, 16) == -4
     lib.dfs_status_string.restype = ctypes.c_char_p
     assert lib.dfs_status_string(-4) == b"workspace too small"
 

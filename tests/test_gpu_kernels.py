@@ -253,6 +253,79 @@ def test_markov_head_packed_wt_bit_identical(D):
     assert np.array_equal(outs[0][1], outs[1][1])
 
 
+# ---------------------------------------------------------------- RNN head
+
+def _rnn_inputs(seed, dtype, B, G, V, r):
+    base = rng.normal(seed, f"rb{V}", (B, G, V), 1.5)
+    U = rng.normal(seed, f"rU{V}", (V, r), 0.6, dtype=dtype)
+    Wt = rng.normal(seed, f"rW{V}", (V, r), r ** -0.25, dtype=dtype)
+    A = rng.normal(seed, f"rA{r}", (r, r), 0.5 / np.sqrt(r), dtype=dtype)
+    last = rng.integers(seed, f"rl{V}", (B,), 0, V - 1)
+    u = rng.uniform01(seed, f"ru{V}", (B, G))
+    return base, U, Wt, A, last, u
+
+
+# the last case is the DSpark 5-token block at the full vocabulary, rank 256, packed W
+@pytest.mark.parametrize("dtype,B,G,V,r,packed", [("f32", 2, 3, 1000, 16, False), ("bf16", 4, 15, 5000, 64, False),
+                                                  ("bf16", 33, 7, 9000, 256, False),
+                                                  ("bf16", 32, 4, 129280, 256, True)])
+def test_rnn_head_matches_oracle(D, dtype, B, G, V, r, packed):
+    import torch
+    say(f"rnn {dtype} B={B} G={G} V={V} r={r} packed={packed}")
+    base, U, Wt, A, last, u = _rnn_inputs(7, dtype, B, G, V, r)
+    lt = up(base, "f32")
+    tok = torch.empty((B, G), dtype=torch.int32, device=DEV)
+    rs = torch.empty((B, G, 2), dtype=torch.float64, device=DEV)
+    ws = workspace(D.rnn_bias_sample_workspace_size(B, G, V, r))
+    wt = up(Wt, dtype)
+    if packed:
+        wt = D.pack_matrix(wt.view(V, r))
+    D.rnn_bias_sample(lt, up(U, dtype), wt, up(A, dtype), up(last, "i32"), up(u, "f32"), 1.0, tok, rs, ws,
+                      wt_packed=packed)
+    final, otok, margins, _ = oracle.rnn_sample(base, U, Wt, A, dtype, last, u, 1.0)
+    got_tok = down(tok)
+    got_final = down(lt)
+    n_cmp, n_flag = compare_sequential_draws(got_tok, otok, margins, "rnn tokens")
+    # final logits (and row statistics) where both sides used the same prefix
+    got_rs = down(rs)
+    for b in range(B):
+        for i in range(G):
+            if i > 0 and got_tok[b, i - 1] != otok[b, i - 1]:
+                break
+            np.testing.assert_allclose(got_final[b, i], final[b, i], atol=1e-4, rtol=0)
+            x = final[b, i].astype(np.float64)
+            np.testing.assert_allclose(got_rs[b, i, 0], x.max(), atol=1e-4)
+            np.testing.assert_allclose(got_rs[b, i, 1], np.exp(x - x.max()).sum(), rtol=1e-4)
+    assert n_flag <= flag_budget(V, B * G)
+    say(f"  compared {n_cmp} draws, {n_flag} flagged")
+
+
+def test_rnn_head_repeat_calls_identical_and_zero_recurrence_is_markov_on_tanh_u(D):
+    # the state lives in the workspace only for one call: a second call on the same
+    # workspace gives bit-identical results; with A = 0 the head equals the Markov
+    # head whose input factor is tanh(U) (fp32 factors, same kernels for W h)
+    import torch
+    B, G, V, r = 6, 5, 3000, 32
+    base, U, Wt, A, last, u = _rnn_inputs(8, "f32", B, G, V, r)
+    ws = workspace(D.rnn_bias_sample_workspace_size(B, G, V, r))
+    outs = []
+    for _ in range(2):
+        lt = up(base, "f32")
+        tok = torch.empty((B, G), dtype=torch.int32, device=DEV)
+        D.rnn_bias_sample(lt, up(U, "f32"), up(Wt, "f32"), up(A, "f32"), up(last, "i32"), up(u, "f32"), 1.0, tok,
+                          None, ws)
+        outs.append((down(lt), down(tok)))
+    assert np.array_equal(outs[0][0].view(np.uint32), outs[1][0].view(np.uint32))
+    assert np.array_equal(outs[0][1], outs[1][1])
+    lt = up(base, "f32")
+    tok = torch.empty((B, G), dtype=torch.int32, device=DEV)
+    D.rnn_bias_sample(lt, up(U, "f32"), up(Wt, "f32"), up(np.zeros((r, r), np.float32), "f32"), up(last, "i32"),
+                      up(u, "f32"), 1.0, tok, None, ws)
+    _, otok, margins = oracle.markov_sample(base, np.tanh(U.astype(np.float64)).astype(np.float32), Wt, "f32",
+                                            last, u, 1.0)
+    compare_sequential_draws(down(tok), otok, margins, "rnn A=0 vs markov(tanh U)")
+
+
 # ---------------------------------------------------------------- verify
 
 def _drafts_from_q(q_logits, ud, T):
