@@ -63,9 +63,10 @@ def algorithmic_bytes(w):
 
 
 class Step:
-    def __init__(self, w, seed=0, reuse=None):
+    def __init__(self, w, seed=0, reuse=None, head="markov"):
         """reuse: another Step of a workload with the same drafter weights (block
-        or Markov-head sweeps), whose host and device weights are shared."""
+        or Markov-head sweeps), whose host and device weights are shared.
+        head: the sequential head, "markov" (the default head) or "rnn"."""
         import torch
         from block_speculative_decoding_amd import dfspec as D
         self.D, self.torch, self.w = D, torch, w
@@ -104,6 +105,8 @@ class Step:
         self.nacc = torch.empty((B,), dtype=torch.int32, device=dev)
         ud, ua, uf = inputs.uniforms(w, seed)
         self.ud, self.ua, self.uf = up(ud, "f32"), up(ua, "f32"), up(uf, "f32")
+        self.head = head if w.markov_rank > 0 else "markov"
+        self.A = up(inputs.rnn_recurrence(w, seed), w.dtype) if self.head == "rnn" else None
         if w.markov_rank > 0:
             U, Wt = inputs.markov_factors(w, seed)
             self.U, self.Wt = up(U, w.dtype), up(Wt, w.dtype)
@@ -115,7 +118,8 @@ class Step:
             self.wt_packed = False
         self.ws_d = torch.empty(D.dflash_draft_workspace_size(self.cfg, B, step["n_new_max"]),
                                 dtype=torch.uint8, device=dev)
-        self.ws_m = torch.empty(D.markov_bias_sample_workspace_size(B, G, V), dtype=torch.uint8, device=dev)
+        self.ws_m = torch.empty(D.rnn_bias_sample_workspace_size(B, G, V, w.markov_rank) if self.head == "rnn"
+                                else D.markov_bias_sample_workspace_size(B, G, V), dtype=torch.uint8, device=dev)
         self.ws_v = torch.empty(D.spec_verify_workspace_size(B, G, V), dtype=torch.uint8, device=dev)
         if w.target_noise_std > 0:       # target = draft logits + noise: needs one draft pass first
             self.draft()
@@ -133,6 +137,10 @@ class Step:
                                  self.k, self.v, self.ctx, self.last, self.logits, self.ws_d)
 
     def sample(self):
+        if self.head == "rnn":
+            self.D.rnn_bias_sample(self.logits, self.U, self.Wt, self.A, self.last, self.ud, self.w.temperature,
+                                   self.tokens, self.row_stats, self.ws_m, wt_packed=self.wt_packed)
+            return
         self.D.markov_bias_sample(self.logits, self.U, self.Wt, self.last, self.ud, self.w.temperature,
                                   self.tokens, self.row_stats, self.ws_m, wt_packed=self.wt_packed)
 
@@ -189,7 +197,11 @@ def cpu_baseline(w, step, budget_s=20.0):
         base, _ = od.draft_step(od.DrafterShape.of(w.with_(batch=1)), step.np_weights, st["hidden_new"][:1],
                                 st["n_new"][:1], ko, vo, st["ctx_len"][:1], st["last_token"][:1])
         ud, ua, uf = (x[:1] for x in inputs.uniforms(w, 0))
-        if w.markov_rank > 0:
+        if w.markov_rank > 0 and step.head == "rnn":
+            U, Wt = inputs.markov_factors(w, 0)
+            final, tok, _, _ = oracle.rnn_sample(base, U, Wt, inputs.rnn_recurrence(w, 0), w.dtype,
+                                                 st["last_token"][:1], ud, w.temperature)
+        elif w.markov_rank > 0:
             U, Wt = inputs.markov_factors(w, 0)
             final, tok, _ = oracle.markov_sample(base, U, Wt, w.dtype, st["last_token"][:1], ud, w.temperature)
         else:
@@ -458,6 +470,8 @@ def main():
     ap.add_argument("--loop-replays", type=int, default=8, help="graph replays timed")
     ap.add_argument("--sweep", action="store_true",
                     help="secondary measurements: block-size and Markov draft-length sweeps (JSON line per point)")
+    ap.add_argument("--head", default="markov", choices=("markov", "rnn"),
+                    help="sequential head of workloads that have one (rnn: the optional RNN head)")
     ap.add_argument("--summarize-rocprof", metavar="DIR",
                     help="print the kernel table / counter averages of a rocprofv3 output directory and exit")
     args = ap.parse_args()
@@ -484,7 +498,7 @@ def main():
         return
     w = WORKLOADS[args.workload]
     print(f"[bench] setting up {w.name}", file=sys.stderr, flush=True)
-    step = Step(w)
+    step = Step(w, head=args.head)
     print(f"[bench] setup {step.setup_s:.1f}s; warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         step()
@@ -497,7 +511,8 @@ def main():
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": w.dtype, "data": "synthetic (seeded; weights N(0,0.02^2))",
         "config": {"workload": w.name, "batch": w.batch, "block": w.block, "ctx": w.ctx, "vocab": w.vocab,
-                   "drafter_layers": w.n_layers, "hidden": w.hidden, "markov_rank": w.markov_rank},
+                   "drafter_layers": w.n_layers, "hidden": w.hidden, "markov_rank": w.markov_rank,
+                   **({"head": "rnn"} if step.head == "rnn" else {})},
         "hbm_gbps": step_bytes / (ms * 1e-3) / 1e9,
         "hbm_frac": step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
     }

@@ -489,7 +489,7 @@ int markov_bias_sample(int32_t batch, int32_t n_draft, int32_t vocab, int32_t ra
 static size_t rnn_carve(int B, int G, int V, int r, void* base, double2** stats, float** h, bf16_t** split) {
   Carver cv(base);
   double2* st = cv.take<double2>((size_t)B * G * ceil_div(V, kChunk));
-  float* hh = cv.take<float>((size_t)B * r);
+  float* hh = cv.take<float>((size_t)2 * B * r);   // two state buffers, alternating by position
   bf16_t* sp = cv.take<bf16_t>((size_t)3 * B * r);
   if (stats) *stats = st;
   if (h) *h = hh;
@@ -524,7 +524,9 @@ int rnn_bias_sample(int32_t batch, int32_t n_draft, int32_t vocab, int32_t rank,
   const bool bf = uw_dtype == DFS_BF16;
   const long rowV = (long)n_draft * vocab;
   ProfScope ps("markov", s);
-  const GemmPlan plan = gemm_plan(batch, vocab, rank, uw_dtype, 1);
+  // bf16: X rows [hi | mid | lo] of the state (K = 3 rank) against W (rank columns, wrapping)
+  const int kx = bf ? 3 * rank : rank;
+  const GemmPlan plan = gemm_plan(batch, vocab, kx, uw_dtype, 1);
   for (int i = 0; i < n_draft; ++i) {
     // h_i = tanh(U[prev_i] + A h_{i-1}), then final_i = base_i + W h_i
     RnnArgs ra;
@@ -532,32 +534,32 @@ int rnn_bias_sample(int32_t batch, int32_t n_draft, int32_t vocab, int32_t rank,
     ra.A = A;
     ra.prev = i == 0 ? last_token : draft_tokens + (i - 1);
     ra.prev_stride = i == 0 ? 1 : n_draft;
-    ra.h = h;
+    float* h_new = h + (size_t)(i & 1) * batch * rank;
+    ra.h_in = h + (size_t)((i + 1) & 1) * batch * rank;
+    ra.h_out = h_new;
     ra.split = bf ? split : nullptr;
     ra.first = i == 0;
     ra.B = batch;
     ra.V = vocab;
     ra.r = rank;
     DFS_TRY(launch_rnn_state(ra, uw_dtype, s));
-    // fp32: one pass with the state itself; bf16: the three bf16 terms of the
-    // state, accumulated in turn (hi, mid, lo) into the fp32 logits
-    for (int t = 0; t < (bf ? 3 : 1); ++t) {
-      GemmArgs ga;
-      ga.X = bf ? (const void*)(split + (size_t)t * batch * rank) : (const void*)h;
-      ga.ldx = rank;
-      ga.x_rows = batch;
-      ga.M = batch;
-      ga.N = vocab;
-      ga.K = rank;
-      ga.seg[0].w = Wt;
-      ga.nseg = 1;
-      ga.Y = logits + (size_t)i * vocab;
-      ga.ldy = rowV;
-      ga.y_split_stride = 0;
-      ga.accumulate = 1;
-      ga.packed = uw_packed;
-      DFS_TRY(launch_gemm(ga, plan, uw_dtype, s));
-    }
+    // fp32: the state itself; bf16: its three bf16 terms in one pass over W
+    GemmArgs ga;
+    ga.X = bf ? (const void*)split : (const void*)h_new;
+    ga.ldx = kx;
+    ga.x_rows = batch;
+    ga.M = batch;
+    ga.N = vocab;
+    ga.K = kx;
+    ga.wk = rank;
+    ga.seg[0].w = Wt;
+    ga.nseg = 1;
+    ga.Y = logits + (size_t)i * vocab;
+    ga.ldy = rowV;
+    ga.y_split_stride = 0;
+    ga.accumulate = 1;
+    ga.packed = uw_packed;
+    DFS_TRY(launch_gemm(ga, plan, uw_dtype, s));
     DFS_TRY(sample_position(batch, n_draft, vocab, i, logits, u_draft, temperature, draft_tokens, row_stats, stats,
                             s));
   }

@@ -23,11 +23,15 @@ namespace {
 constexpr int BK = 64;
 constexpr int LDK = BK + 8;   // padded LDS row (bf16 elements): 144 bytes
 
+// columns of W: K, or wk when the K columns of X hold K / wk terms that all
+// multiply the same W (GEMM column k uses W column k % wk)
+__device__ __forceinline__ int w_cols(const GemmArgs& a) { return a.wk > 0 ? a.wk : a.K; }
+
 __device__ __forceinline__ const void* seg_row(const GemmArgs& a, int n, int es) {
   int s = 0;
   if (a.nseg > 1 && n >= a.seg[1].n0) s = 1;
   if (a.nseg > 2 && n >= a.seg[2].n0) s = 2;
-  return (const char*)a.seg[s].w + (size_t)(n - a.seg[s].n0) * a.K * es;
+  return (const char*)a.seg[s].w + (size_t)(n - a.seg[s].n0) * w_cols(a) * es;
 }
 
 // first element of the packed 16-row tile group that holds logical W row n
@@ -36,7 +40,7 @@ __device__ __forceinline__ const bf16_t* seg_tile(const GemmArgs& a, int n) {
   int s = 0;
   if (a.nseg > 1 && n >= a.seg[1].n0) s = 1;
   if (a.nseg > 2 && n >= a.seg[2].n0) s = 2;
-  return (const bf16_t*)a.seg[s].w + (size_t)((n - a.seg[s].n0) >> 4) * (a.K / BK) * kTileElems;
+  return (const bf16_t*)a.seg[s].w + (size_t)((n - a.seg[s].n0) >> 4) * (w_cols(a) / BK) * kTileElems;
 }
 
 __device__ __forceinline__ int x_row(const GemmArgs& a, int m) {
@@ -80,6 +84,8 @@ void gemm_stream_bf16(GemmArgs a, int k_per_split, int mtiles, int ntiles) {
   static_assert(!GATED || NW == 2, "gated tiles pair gate and up");
   // W elements per k step and between the two 32-wide k halves of a step
   constexpr int WSTEP = PACKED ? kTileElems : BK, WKS = PACKED ? kTileElems / 2 : 32;
+  // W offset of k step s of this split (relative to its first step): the
+  // identity unless W is narrower than X (k wraps around W's columns)
   static_assert(PD == 4 || PD == 8, "ring depth divides the 8-step loop body");
   static_assert(XD == 2 || XD == PD, "X ring depth");
   constexpr int BM = 16 * MT, BN = GATED ? 64 : 64 * NW;
@@ -97,6 +103,8 @@ void gemm_stream_bf16(GemmArgs a, int k_per_split, int mtiles, int ntiles) {
   const int nk = kend > kbeg ? (kend - kbeg) / BK : 0;
   if (nk == 0) return;                                   // uniform over the workgroup
   const int c = lane & 15, g4 = lane >> 4;
+  const int kb0 = kbeg / BK, wsteps = w_cols(a) / BK;
+  auto wofs = [&](int st) -> ptrdiff_t { return (ptrdiff_t)((kb0 + st) % wsteps - kb0) * WSTEP; };
 
   // producer state: X rows of this tile
   const bf16_t* x_src[XCH];
@@ -118,9 +126,9 @@ void gemm_stream_bf16(GemmArgs a, int k_per_split, int mtiles, int ntiles) {
         const int n = min(n0 + wave * 16 + c, a.N - 1);
         const bf16_t* w = (const bf16_t*)a.seg[j].w;
         if constexpr (PACKED)
-          w_src[j] = w + ((size_t)(n >> 4) * (a.K / BK) + kbeg / BK) * kTileElems + lane * 8;
+          w_src[j] = w + ((size_t)(n >> 4) * (w_cols(a) / BK) + kbeg / BK) * kTileElems + lane * 8;
         else
-          w_src[j] = w + (size_t)n * a.K + kbeg + g4 * 8;
+          w_src[j] = w + (size_t)n * w_cols(a) + kbeg + g4 * 8;
       } else {
         const int n = min(n0 + wave * 16 * NW + j * 16 + c, a.N - 1);
         if constexpr (PACKED)   // the wave's 16 rows: one contiguous run of tiles
@@ -181,7 +189,7 @@ void gemm_stream_bf16(GemmArgs a, int k_per_split, int mtiles, int ntiles) {
     for (int j = 0; j < NW; ++j)
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
-        wr[st][j][ks] = ldg_bf16x8(w_src[j] + (size_t)min(st, nk - 1) * WSTEP + ks * WKS);
+        wr[st][j][ks] = ldg_bf16x8(w_src[j] + wofs(min(st, nk - 1)) + ks * WKS);
     // keep the ring filled oldest-first: the loop's wait counts assume step 0
     // holds the oldest loads, also on entry
     __builtin_amdgcn_sched_barrier(0);
@@ -203,7 +211,7 @@ void gemm_stream_bf16(GemmArgs a, int k_per_split, int mtiles, int ntiles) {
       }                                                                                        \
     }                                                                                          \
     __builtin_amdgcn_sched_barrier(0); /* keep the refill after this step's math */            \
-    const size_t kk = (size_t)min(kt + PD, nk - 1) * WSTEP;                                    \
+    const ptrdiff_t kk = wofs(min(kt + PD, nk - 1));                                         \
     _Pragma("unroll") for (int j = 0; j < NW; ++j)                                             \
       _Pragma("unroll") for (int ks = 0; ks < 2; ++ks) wr[R][j][ks] = ldg_bf16x8(w_src[j] + kk + ks * WKS); \
   }
@@ -486,7 +494,7 @@ __global__ __launch_bounds__(256) void gemm_rows_bf16(GemmArgs a) {
   const int ng = blockIdx.x * 4 + wave;                  // 16-row group of W
   if (ng * 16 >= a.N) return;                            // uniform over the wave
   const int c = lane & 15, g4 = lane >> 4;
-  const int nk = a.K / BK;                               // 1 .. NKM
+  const int nk = a.K / BK, wsteps = w_cols(a) / BK;     // 1 .. NKM
   const int n0 = ng * 16, n = n0 + 4 * g4;
   const bf16_t* wsrc = PACKED ? seg_tile(a, n0) + lane * 8
                               : (const bf16_t*)seg_row(a, min(n0 + c, a.N - 1), 2) + g4 * 8;
@@ -496,7 +504,8 @@ __global__ __launch_bounds__(256) void gemm_rows_bf16(GemmArgs a) {
     if (kt >= nk) break;                                 // uniform
 #pragma unroll
     for (int h = 0; h < 2; ++h)
-      wf[2 * kt + h] = ldg_bf16x8(wsrc + (PACKED ? (size_t)kt * kTileElems + h * 512 : (size_t)kt * BK + h * 32));
+      wf[2 * kt + h] = ldg_bf16x8(wsrc + (PACKED ? (size_t)(kt % wsteps) * kTileElems + h * 512
+                                                 : (size_t)(kt % wsteps) * BK + h * 32));
   }
   // lane (c, g4) owns row m = c, columns n .. n+3; the values it adds to are
   // loaded in the same round trip as the operands
@@ -812,6 +821,21 @@ hipError_t launch_tile(const GemmArgs& a, dim3 g1, int kps, int mtl, int ntl, hi
 
 hipError_t launch_gemm(const GemmArgs& a, const GemmPlan& p, int dtype, hipStream_t s) {
   ProfScope ps("gemm", s);
+  if (a.wk > 0 && a.wk != a.K) {
+    // W narrower than X: only the bf16 weight-streaming and small-M kernels wrap k
+    if (dtype != 1 || a.gated || a.wk % BK || a.K % a.wk) return hipErrorInvalidValue;
+    if (p.kind == 3) {
+      GemmPlan q = p;
+      q.kind = 1;
+      q.bm = 128;
+      q.bn = 128;
+      q.mt = 8;
+      q.nw = 2;
+      q.pd = 4;
+      q.xd = 4;
+      return launch_gemm(a, q, dtype, s);
+    }
+  }
   if (dtype != 1) {
     dim3 grid(ceil_div(a.N, 64), ceil_div(a.M, 64), p.splits);
     hipLaunchKernelGGL(gemm_f32_nt, grid, dim3(256), 0, s, a, p.k_per_split);

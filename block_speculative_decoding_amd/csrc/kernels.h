@@ -33,6 +33,9 @@ struct GemmArgs {
   int gated = 0;
   void* hout = nullptr;
   int nt_store = 0;                   // 1: results written with non-temporal stores (not re-read soon)
+  // > 0 and < K: W has wk columns and GEMM column k multiplies W column k % wk
+  // (X's K columns hold K / wk terms of one operand; bf16 streaming / rows kernels)
+  int wk = 0;
 };
 
 struct GemmPlan {
@@ -200,8 +203,9 @@ struct RnnArgs {
   const void* A;           // [r][r] recurrent matrix (dtype), row j -> state element j
   const int32_t* prev;     // previous token of request b at prev[b * prev_stride]
   long prev_stride;
-  float* h;                // [B][r] fp32 state, updated in place
-  bf16_t* split;           // [3][B][r] bf16 terms hi, mid, lo of the new state, or null
+  const float* h_in;       // [B][r] fp32 previous state (ignored when first)
+  float* h_out;            // [B][r] fp32 new state (a different buffer)
+  bf16_t* split;           // [B][3][r] bf16 terms hi, mid, lo of the new state, or null
   int first;               // 1: previous state is zero (first position of the block)
   int B, V, r;
 };

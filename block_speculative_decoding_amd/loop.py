@@ -29,10 +29,12 @@ class SpecLoop:
     capacity, so the same enqueued work is valid whatever the device-side state."""
 
     def __init__(self, cfg: D.DrafterConfig, weights: D.DrafterWeights, k_cache, v_cache, ctx_len, last_token, n_new,
-                 temperature: float = 1.0, U=None, Wt=None, wt_packed: bool = False, curve=None):
+                 temperature: float = 1.0, U=None, Wt=None, wt_packed: bool = False, curve=None, A=None):
         """curve: optional (rows, passes per second) throughput table for the prefix
         scheduler; with it, a cycle given survival scores verifies per request only
-        the drafts spec_schedule_verify picks."""
+        the drafts spec_schedule_verify picks.  A: the RNN head's recurrent matrix
+        [r, r]; with it the drafts come from rnn_bias_sample instead of the Markov
+        head."""
         B = ctx_len.numel()
         S, V = cfg.block, cfg.vocab
         G = S - 1
@@ -41,7 +43,7 @@ class SpecLoop:
         self.k_cache, self.v_cache = k_cache, v_cache
         self.ctx_len, self.last_token, self.n_new = ctx_len, last_token, n_new
         self.temperature = float(temperature)
-        self.U, self.Wt, self.wt_packed = U, Wt, wt_packed
+        self.U, self.Wt, self.wt_packed, self.A = U, Wt, wt_packed, A
         self.logits = torch.empty((B, G, V), dtype=torch.float32, device=dev)
         self.tokens = torch.empty((B, G), dtype=torch.int32, device=dev)
         self.row_stats = torch.empty((B, G, 2), dtype=torch.float64, device=dev)
@@ -52,7 +54,9 @@ class SpecLoop:
         self.curve = curve
         self.n_verify = torch.full((B,), G, dtype=torch.int32, device=dev)
         self.ws_draft = torch.empty(D.dflash_draft_workspace_size(cfg, B, S), dtype=torch.uint8, device=dev)
-        self.ws_markov = torch.empty(D.markov_bias_sample_workspace_size(B, G, V), dtype=torch.uint8, device=dev)
+        ws_head = (D.rnn_bias_sample_workspace_size(B, G, V, U.shape[1]) if A is not None
+                   else D.markov_bias_sample_workspace_size(B, G, V))
+        self.ws_markov = torch.empty(ws_head, dtype=torch.uint8, device=dev)
         self.ws_verify = torch.empty(D.spec_verify_workspace_size(B, G, V), dtype=torch.uint8, device=dev)
 
     def cycle(self, hidden_new, u_draft, u_accept, u_final, target_fn, survival=None):
@@ -64,8 +68,12 @@ class SpecLoop:
         scheduler."""
         D.dflash_draft_step(self.cfg, self.weights, hidden_new, self.n_new, self.S, self.cfg.max_ctx, self.k_cache,
                             self.v_cache, self.ctx_len, self.last_token, self.logits, self.ws_draft)
-        D.markov_bias_sample(self.logits, self.U, self.Wt, self.last_token, u_draft, self.temperature, self.tokens,
-                             self.row_stats, self.ws_markov, wt_packed=self.wt_packed)
+        if self.A is not None:
+            D.rnn_bias_sample(self.logits, self.U, self.Wt, self.A, self.last_token, u_draft, self.temperature,
+                              self.tokens, self.row_stats, self.ws_markov, wt_packed=self.wt_packed)
+        else:
+            D.markov_bias_sample(self.logits, self.U, self.Wt, self.last_token, u_draft, self.temperature,
+                                 self.tokens, self.row_stats, self.ws_markov, wt_packed=self.wt_packed)
         target_fn(self.logits, self.target)
         nv = None
         if survival is not None and self.curve is not None:

@@ -213,7 +213,8 @@ size_t rnn_bias_sample_workspace_size(int32_t batch, int32_t n_draft, int32_t vo
  *   h_0 = 0,  h_i = tanh(U[prev_i] + A h_{i-1}),  final_i = base_i + W h_i
  * (prev_1 = last_token[b], prev_i = d_{i-1}), each d_i drawn as in
  * markov_bias_sample.  The state is kept in fp32; with bf16 factors W h_i is
- * formed from three bf16 terms of h_i (hi + mid + lo), i.e. to fp32 accuracy.
+ * formed from three bf16 terms of h_i (hi + mid + lo) in one matrix-core pass
+ * over W, i.e. to fp32 accuracy.
  *
  * logits, last_token, u_draft, temperature, draft_tokens, row_stats: as for
  *             markov_bias_sample.

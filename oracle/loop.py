@@ -22,7 +22,7 @@ from __future__ import annotations
 import numpy as np
 
 from . import drafter as od
-from .sampling import markov_sample
+from .sampling import markov_sample, rnn_sample
 from .scheduler import schedule
 from .verify import verify
 
@@ -41,8 +41,9 @@ def advance(n_accepted, out_tokens, n_draft):
 
 
 def run_cycles(shape, weights, U, Wt, uw_dtype, k_cache, v_cache, ctx_len, last_token, n_new, cycles,
-               temperature, target_fn=None, curve=None):
-    """Run len(cycles) cycles of draft -> Markov sample -> verify -> advance.
+               temperature, target_fn=None, curve=None, A=None):
+    """Run len(cycles) cycles of draft -> Markov sample -> verify -> advance
+    (with the RNN head's recurrent matrix ``A``: RNN-head sampling instead).
 
     ``cycles[c]`` holds that cycle's inputs: hidden_new [B, S, nT*H] (rows
     < n_new[b] used), u_draft [B, gamma], u_accept [B, gamma], u_final [B], and
@@ -60,7 +61,10 @@ def run_cycles(shape, weights, U, Wt, uw_dtype, k_cache, v_cache, ctx_len, last_
     for c, cin in enumerate(cycles):
         last_in, n_new_in = last.copy(), nn.copy()
         base, ctx = od.draft_step(shape, weights, cin["hidden_new"], nn, k_cache, v_cache, ctx, last)
-        final, tokens, m_draft = markov_sample(base, U, Wt, uw_dtype, last, cin["u_draft"], temperature)
+        if A is not None:
+            final, tokens, m_draft, _ = rnn_sample(base, U, Wt, A, uw_dtype, last, cin["u_draft"], temperature)
+        else:
+            final, tokens, m_draft = markov_sample(base, U, Wt, uw_dtype, last, cin["u_draft"], temperature)
         target = target_fn(c, final) if target_fn is not None else cin["target_logits"]
         n_verify = None
         if curve is not None:

@@ -105,6 +105,15 @@ def markov_factors(w: Workload, seed: int, std=None, rank=None, dtype=None):
             rng.normal(seed, "markov_Wt", (w.vocab, r), s, dtype=dt))
 
 
+def rnn_recurrence(w: Workload, seed: int, std=None, rank=None, dtype=None):
+    """[r, r] recurrent matrix of the RNN sequential head, N(0, (0.5/sqrt(r))^2)
+    entries (spectral radius about 1/2: the state neither dies out nor saturates)."""
+    r = w.markov_rank if rank is None else rank
+    dt = w.dtype if dtype is None else dtype
+    s = 0.5 / r ** 0.5 if std is None else std
+    return rng.normal(seed, "rnn_A", (r, r), s, dtype=dt)
+
+
 def base_logits(w: Workload, seed: int, std=None, batch=None):
     B = w.batch if batch is None else batch
     s = w.base_logit_std if std is None else std

@@ -91,7 +91,7 @@ def D_cache(w, kc, vc):
     return dfspec.cache_from_logical(up(kc, w.dtype), up(vc, w.dtype))
 
 
-@pytest.mark.parametrize("targets", ["independent", "draft_plus_noise", "scheduled"])
+@pytest.mark.parametrize("targets", ["independent", "draft_plus_noise", "scheduled", "rnn_head"])
 def test_loop_tiny_matches_oracle(D, targets):
     # four cycles of the tiny fp32 drafter with the Markov head.  Targets either
     # independent random rows each cycle (mostly one committed token), or each
@@ -110,8 +110,10 @@ def test_loop_tiny_matches_oracle(D, targets):
     # scheduled: draft + noise targets, and the prefix scheduler picks per-request
     # verify lengths from seeded survival scores and a falling throughput curve
     curve = (np.array([1, 4, 16], np.float32), np.array([100, 60, 20], np.float32)) if targets == "scheduled" else None
+    # rnn_head: draft + noise targets, drafts from the RNN sequential head
+    A = inputs.rnn_recurrence(w, seed) if targets == "rnn_head" else None
     lp = SpecLoop(st["cfg"], st["wdev"], st["kd"], st["vd"], up(ctx0, "i32"), up(st["last0"], "i32"), up(n0, "i32"),
-                  1.0, st["Ud"], st["Wd"], curve=curve)
+                  1.0, st["Ud"], st["Wd"], curve=curve, A=None if A is None else up(A, "f32"))
     gpu = []
     sigma = 0.5
     for c in range(cycles):
@@ -138,7 +140,7 @@ def test_loop_tiny_matches_oracle(D, targets):
                               ).astype(np.float32)
         return t
     ora = ol.run_cycles(od.DrafterShape.of(w), st["weights"], st["U"], st["Wt"], "f32", kc, vc, ctx0, st["last0"], n0,
-                        cins, 1.0, target_fn=ora_target, curve=curve)
+                        cins, 1.0, target_fn=ora_target, curve=curve, A=A)
     alive = np.ones(w.batch, bool)
     n_cmp = n_flag = 0
     for c in range(cycles):
