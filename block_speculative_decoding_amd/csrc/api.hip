@@ -93,12 +93,14 @@ DraftWs carve_draft(void* base, const DraftDims& d, int dtype) {
   DraftWs w;
   w.meta = cv.take<int32_t>(3 * (size_t)d.B);
   w.rope = cv.take<float2>((size_t)d.Mx * (d.d / 2));
-  w.xs = cv.take<char>((size_t)d.Mx * d.H * d.es);
+  // GEMM inputs: whole 16-row groups (room for the tile-packed layout)
+  auto r16 = [](int m) { return (size_t)ceil_div(m, 16) * 16; };
+  w.xs = cv.take<char>(r16(d.Mx) * d.H * d.es);
   w.resid = cv.take<float>((size_t)d.Mb * d.H);
-  w.mlp_in = cv.take<char>((size_t)d.Mb * d.H * d.es);
-  w.attn_o = cv.take<char>((size_t)d.Mb * d.nq * d.d * d.es);
-  w.hmid = cv.take<char>((size_t)d.Mb * d.F * d.es);
-  w.z = cv.take<char>((size_t)d.B * d.G * d.H * d.es);
+  w.mlp_in = cv.take<char>(r16(d.Mb) * d.H * d.es);
+  w.attn_o = cv.take<char>(r16(d.Mb) * d.nq * d.d * d.es);
+  w.hmid = cv.take<char>(r16(d.Mb) * d.F * d.es);
+  w.z = cv.take<char>(r16(d.B * d.G) * d.H * d.es);
   w.q_att = cv.take<char>((size_t)d.B * d.nkv * d.Rpad * d.d * d.es);
   w.k_blk = cv.take<char>((size_t)d.B * d.nkv * 64 * d.d * d.es);
   w.v_blk = cv.take<char>((size_t)d.B * d.nkv * d.d * 64 * d.es);
@@ -122,12 +124,20 @@ DraftWs carve_draft(void* base, const DraftDims& d, int dtype) {
   return w;
 }
 
+// Whether the GEMM's X is produced in the tile-packed layout: the LDS-ring tile
+// kernel loads a packed half tile as one contiguous kilobyte per wave instead of
+// gathering 16 row pieces (bf16 activations this library writes itself).
+bool pack_x(int M, int N, int K, int dtype, int force_splits = 0) {
+  return dtype == DFS_BF16 && M > 0 && K % 64 == 0 && gemm_plan(M, N, K, dtype, force_splits).kind == 3;
+}
+
 hipError_t run_gemm(const void* X, int ldx, int M, int N, int K, const void* w0, const void* w1, int n1,
                     const void* w2, int n2, float* Y, int dtype, int packed, hipStream_t s, int* splits_out,
-                    size_t* stride_out, int force_splits = 0, long ldy = 0, int nt_store = 0) {
+                    size_t* stride_out, int force_splits = 0, long ldy = 0, int nt_store = 0, int x_packed = 0) {
   GemmArgs a;
   a.packed = packed;
   a.nt_store = nt_store;
+  a.x_packed = x_packed;
   a.X = X;
   a.ldx = ldx;
   a.x_rows = M;
@@ -158,8 +168,10 @@ hipError_t run_gemm(const void* X, int ldx, int M, int N, int K, const void* w0,
 
 // SwiGLU MLP input: hout[m][f] = bf16(silu(X.Wg^T) * (X.Wu^T)) in one weight pass
 hipError_t run_gemm_gated(const void* X, int ldx, int M, int F, int K, const void* wg, const void* wu, void* hout,
-                          int packed, const GemmPlan& p, hipStream_t s) {
+                          int packed, const GemmPlan& p, hipStream_t s, int x_packed = 0, int h_packed = 0) {
   GemmArgs a;
+  a.x_packed = x_packed;
+  a.h_packed = h_packed;
   a.X = X;
   a.ldx = ldx;
   a.x_rows = M;
@@ -249,6 +261,13 @@ int dflash_draft_step(const dfs_drafter_cfg* cfg, const dfs_drafter_weights* wt,
 
   int sp;
   size_t pst;
+  // which GEMM inputs are written tile-packed (those read by the LDS-ring tile kernel)
+  const GemmPlan gated = gemm_plan_gated(d.Mb, d.F, d.H, dt);
+  const int xp_qkv = pack_x(d.Mx, d.Nqkv, d.H, dt);
+  const int xp_o = pack_x(d.Mb, d.H, d.nq * d.d, dt);
+  const int xp_mlp = dt == DFS_BF16 && gated.kind == 3;
+  const int xp_down = gated.kind > 0 && pack_x(d.Mb, d.H, d.F, dt);
+  const int xp_lm = pack_x(d.B * d.G, d.V, d.H, dt, 1);
   // 1. context features f = RMSNorm(concat(h) . fc^T) -> xs rows [0, Mc)
   if (d.Mc > 0) {
     DFS_TRY(run_gemm(hidden_new, d.nT * d.H, d.Mc, d.H, d.nT * d.H, wt->fc, nullptr, 0, nullptr, 0, w.part, dt, pk, s,
@@ -259,17 +278,21 @@ int dflash_draft_step(const dfs_drafter_cfg* cfg, const dfs_drafter_weights* wt,
     na.part_stride = pst;
     na.gain = wt->fc_norm;
     na.out = w.xs;
+    na.out_packed = xp_qkv;
     na.rows = d.Mc;
     na.H = d.H;
     na.eps = cfg->rms_eps;
     DFS_TRY(launch_norm(na, dt, s));
   }
-  char* xs_blk = w.xs + (size_t)d.Mc * d.H * es;
+  // block rows of xs: rows Mc.. (packed: same buffer, row offset Mc)
+  char* xs_blk = xp_qkv ? w.xs : w.xs + (size_t)d.Mc * d.H * es;
   {  // layer 0 attention pre-norm of the block rows
     NormArgs na;
     na.resid = w.resid;
     na.gain = wt->attn_norm[0];
     na.out = xs_blk;
+    na.out_packed = xp_qkv;
+    na.out_row0 = xp_qkv ? d.Mc : 0;
     na.rows = d.Mb;
     na.H = d.H;
     na.eps = cfg->rms_eps;
@@ -277,12 +300,11 @@ int dflash_draft_step(const dfs_drafter_cfg* cfg, const dfs_drafter_weights* wt,
   }
   const int rgs = dt == DFS_BF16 ? ceil_div(d.R, 64) : 1;   // 64-row groups of the R query rows
   const AttnPlan ap = attn_plan(d.B, d.nkv, ctx_bound, dt, rgs, cfg->window);
-  const GemmPlan gated = gemm_plan_gated(d.Mb, d.F, d.H, dt);
   const size_t layer_cache = (size_t)d.B * d.nkv * d.max_ctx * d.d * es;
   for (int l = 0; l < d.L; ++l) {
     // 2. Q|K|V of [features ; block rows] in one pass over wq|wk|wv
     DFS_TRY(run_gemm(w.xs, d.H, d.Mx, d.Nqkv, d.H, wt->wq[l], wt->wk[l], d.nq * d.d, wt->wv[l],
-                     (d.nq + d.nkv) * d.d, w.part, dt, pk, s, &sp, &pst));
+                     (d.nq + d.nkv) * d.d, w.part, dt, pk, s, &sp, &pst, 0, 0, 0, xp_qkv));
     QkvArgs qa;
     qa.part = w.part;
     qa.sp = sp;
@@ -327,10 +349,11 @@ int dflash_draft_step(const dfs_drafter_cfg* cfg, const dfs_drafter_weights* wt,
     aa.n_ctx_splits = ap.n_ctx_splits;
     aa.row_groups = rgs;
     aa.window = cfg->window;
+    aa.out_packed = xp_o;
     DFS_TRY(launch_attention(aa, dt, s));
     // 4. O projection, residual add, MLP pre-norm
     DFS_TRY(run_gemm(w.attn_o, d.nq * d.d, d.Mb, d.H, d.nq * d.d, wt->wo[l], nullptr, 0, nullptr, 0, w.part, dt,
-                     pk, s, &sp, &pst));
+                     pk, s, &sp, &pst, 0, 0, 0, xp_o));
     {
       NormArgs na;
       na.resid = w.resid;
@@ -340,6 +363,7 @@ int dflash_draft_step(const dfs_drafter_cfg* cfg, const dfs_drafter_weights* wt,
       na.update_resid = 1;
       na.gain = wt->mlp_norm[l];
       na.out = w.mlp_in;
+      na.out_packed = xp_mlp;
       na.rows = d.Mb;
       na.H = d.H;
       na.eps = cfg->rms_eps;
@@ -349,14 +373,15 @@ int dflash_draft_step(const dfs_drafter_cfg* cfg, const dfs_drafter_weights* wt,
     //    GEMM epilogue when a gated plan fits, else by a separate pass over the
     //    fp32 results), then down, residual add, next pre-norm
     if (gated.kind > 0) {
-      DFS_TRY(run_gemm_gated(w.mlp_in, d.H, d.Mb, d.F, d.H, wt->w_gate[l], wt->w_up[l], w.hmid, pk, gated, s));
+      DFS_TRY(run_gemm_gated(w.mlp_in, d.H, d.Mb, d.F, d.H, wt->w_gate[l], wt->w_up[l], w.hmid, pk, gated, s,
+                             xp_mlp, xp_down));
     } else {
       DFS_TRY(run_gemm(w.mlp_in, d.H, d.Mb, 2 * d.F, d.H, wt->w_gate[l], wt->w_up[l], d.F, nullptr, 0, w.part, dt,
                        pk, s, &sp, &pst));
       DFS_TRY(launch_swiglu(w.part, sp, pst, d.Mb, d.F, w.hmid, dt, s));
     }
     DFS_TRY(run_gemm(w.hmid, d.F, d.Mb, d.H, d.F, wt->w_down[l], nullptr, 0, nullptr, 0, w.part, dt, pk, s,
-                     &sp, &pst));
+                     &sp, &pst, 0, 0, 0, xp_down));
     {
       NormArgs na;
       na.resid = w.resid;
@@ -370,11 +395,14 @@ int dflash_draft_step(const dfs_drafter_cfg* cfg, const dfs_drafter_weights* wt,
       if (l + 1 < d.L) {
         na.gain = wt->attn_norm[l + 1];
         na.out = xs_blk;
+        na.out_packed = xp_qkv;
+        na.out_row0 = xp_qkv ? d.Mc : 0;
       } else {   // final norm of the mask rows only -> z [B*(S-1), H]
         na.gain = wt->final_norm;
         na.out = w.z;
         na.out_mode = 1;
         na.S = d.S;
+        na.out_packed = xp_lm;
       }
       DFS_TRY(launch_norm(na, dt, s));
     }
@@ -382,7 +410,7 @@ int dflash_draft_step(const dfs_drafter_cfg* cfg, const dfs_drafter_weights* wt,
   // 6. LM head on the mask rows -> base logits [B, S-1, V]
   // (the logits are not re-read before the sampler's pass: non-temporal stores)
   DFS_TRY(run_gemm(w.z, d.H, d.B * d.G, d.V, d.H, wt->lm_head, nullptr, 0, nullptr, 0, base_logits, dt, pk, s,
-                   &sp, &pst, 1, 0, 1));
+                   &sp, &pst, 1, 0, 1, xp_lm));
   return DFS_OK;
 }
 

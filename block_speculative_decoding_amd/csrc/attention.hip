@@ -264,14 +264,16 @@ __global__ __launch_bounds__(256) void attn_bf16_d128(AttnArgs a) {
   if (fused) {
     // output tile dt: lane holds dims dt*16 + 4*g4 .. +3 of query row `row` = hh*S + s
     const int group = a.nq / a.nkv, hh = row / a.S, s = row % a.S, h = g * group + hh;
-    bf16_t* out = (bf16_t*)a.out + (((size_t)b * a.S + s) * a.nq + h) * D;
+    const int orow = b * a.S + s;
+    bf16_t* out = (bf16_t*)a.out + ((size_t)orow * a.nq + h) * D;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
       bf16_t v4[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) v4[i] = f2bf(o[dt][i] / l_run);
-      *(uint2*)(out + dt * 16 + 4 * g4) =
-          make_uint2((uint32_t)v4[0] | ((uint32_t)v4[1] << 16), (uint32_t)v4[2] | ((uint32_t)v4[3] << 16));
+      const int col = dt * 16 + 4 * g4;
+      bf16_t* dst = a.out_packed ? (bf16_t*)a.out + xpk_index(orow, h * D + col, a.nq * D) : out + col;
+      *(uint2*)dst = make_uint2((uint32_t)v4[0] | ((uint32_t)v4[1] << 16), (uint32_t)v4[2] | ((uint32_t)v4[3] << 16));
     }
     return;
   }
@@ -330,7 +332,9 @@ __global__ __launch_bounds__(128) void attn_combine(AttnArgs a) {
       }
       M = mg;
     }
-    Elem<T>::store((T*)a.out, (((size_t)b * a.S + s) * a.nq + h) * a.d + dd, num / den);
+    const int orow = b * a.S + s, col = h * a.d + dd;
+    Elem<T>::store((T*)a.out, a.out_packed ? xpk_index(orow, col, a.nq * a.d) : (size_t)orow * a.nq * a.d + col,
+                   num / den);
   }
 }
 
@@ -460,6 +464,7 @@ size_t attn_partial_elems(int units, int B, int nkv, int Rpad, int d) {
 
 hipError_t launch_attention(const AttnArgs& a, int dtype, hipStream_t s) {
   ProfScope ps("attention", s);
+  if (a.out_packed && (dtype != 1 || (a.nq * a.d) % 64)) return hipErrorInvalidValue;
   if (dtype != 1) {
     hipLaunchKernelGGL(attn_f32, dim3(a.S, a.nq, a.B), dim3(256), 0, s, a);
     return hipGetLastError();

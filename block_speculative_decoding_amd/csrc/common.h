@@ -87,6 +87,18 @@ __device__ __forceinline__ float block_max(float v, float* smem) {
 __host__ __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
 __host__ __device__ __forceinline__ size_t align_up(size_t a, size_t b) { return (a + b - 1) / b * b; }
 
+// Tile-packed activation layout (bf16, K a multiple of 64): the rows in groups
+// of 16, each group's K in 64-wide tiles of 2 KB, a tile stored as [half h =
+// 0..1][lane l = 0..63][8 values] with lane l holding row 16 g + (l % 16),
+// columns 64 t + 32 h + 8 (l / 16) .. +7 — the matrix-core operand fragment
+// order, so a wave loads a 16-row x 32-column half tile as one contiguous
+// kilobyte.  Four consecutive columns k .. k+3 (k % 4 == 0) are contiguous.
+// A buffer holds ceil(rows / 16) whole groups.
+__host__ __device__ __forceinline__ size_t xpk_index(int m, int k, int K) {
+  return ((size_t)(m >> 4) * (K >> 6) + (k >> 6)) * 1024 + ((k >> 5) & 1) * 512 + ((m & 15) + 16 * ((k >> 3) & 3)) * 8 +
+         (k & 7);
+}
+
 // ----------------------------------------------------------------- host plumbing
 
 // Profiling hooks (events around launches of one kernel group); see profile.cpp.

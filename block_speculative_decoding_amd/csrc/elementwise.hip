@@ -131,6 +131,22 @@ __global__ __launch_bounds__(1024) void norm_kernel(NormArgs a) {
     if (s == 0) return;
     orow = (r / a.S) * (a.S - 1) + s - 1;
   }
+  if constexpr (sizeof(T) == 2) {
+    if (a.out_packed) {   // 4 consecutive columns are one 8-byte run of the packed layout
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int h = 4 * (tid + i * kNormThreads);
+        if (h >= a.H) continue;
+        uint32_t w[2];
+#pragma unroll
+        for (int e = 0; e < 4; e += 2)
+          w[e / 2] = (uint32_t)f2bf(v[i][e] * rs * Elem<T>::load((const T*)a.gain, h + e)) |
+                     ((uint32_t)f2bf(v[i][e + 1] * rs * Elem<T>::load((const T*)a.gain, h + e + 1)) << 16);
+        *(uint2*)((bf16_t*)a.out + xpk_index(orow + a.out_row0, h, a.H)) = make_uint2(w[0], w[1]);
+      }
+      return;
+    }
+  }
   T* out = (T*)a.out + (size_t)orow * a.H;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
@@ -365,6 +381,7 @@ hipError_t launch_embed(int dtype, const void* embed, const int32_t* last_token,
 }
 
 hipError_t launch_norm(const NormArgs& a, int dtype, hipStream_t s) {
+  if (a.out_packed && (dtype != 1 || a.H % 64)) return hipErrorInvalidValue;
   ProfScope ps("elementwise", s);
   if (dtype == 1) hipLaunchKernelGGL(norm_kernel<bf16_t>, dim3(a.rows), dim3(kNormThreads), 0, s, a);
   else hipLaunchKernelGGL(norm_kernel<float>, dim3(a.rows), dim3(kNormThreads), 0, s, a);

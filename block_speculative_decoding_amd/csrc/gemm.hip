@@ -246,12 +246,13 @@ void gemm_stream_bf16(GemmArgs a, int k_per_split, int mtiles, int ntiles) {
         const float g = acc[i][0][e], u = acc[i][1][e];
         h[e] = f2bf(g / (1.f + expf(-g)) * u);
       }
+      bf16_t* dst = a.h_packed ? (bf16_t*)a.hout + xpk_index(m, n, a.N) : hrow + n;
       if (n + 3 < a.N) {
-        *(uint2*)(hrow + n) = make_uint2((uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16));
+        *(uint2*)dst = make_uint2((uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16));
       } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          if (n + e < a.N) hrow[n + e] = h[e];
+          if (n + e < a.N) dst[e] = h[e];
       }
     }
     return;
@@ -369,16 +370,22 @@ void gemm_tile_bf16(GemmArgs a, int k_per_split, int mtiles, int ntiles) {
       hstep[i] = PACKED ? kTileElems / 2 : 32;
     } else {
       const int g = u - GW;
-      const int m = min(m0 + g * 16 + c, a.M - 1);
-      src[i] = (const bf16_t*)a.X + (size_t)x_row(a, m) * a.ldx + kbeg + g4 * 8;
+      if (a.x_packed) {   // the 16-row group's tiles: one contiguous kilobyte per half step
+        const int mg = min((m0 >> 4) + g, (a.M - 1) >> 4);
+        src[i] = (const bf16_t*)a.X + ((size_t)mg * (a.K / BK) + kbeg / BK) * kTileElems + lane * 8;
+        hstep[i] = kTileElems / 2;
+      } else {
+        const int m = min(m0 + g * 16 + c, a.M - 1);
+        src[i] = (const bf16_t*)a.X + (size_t)x_row(a, m) * a.ldx + kbeg + g4 * 8;
+        hstep[i] = 32;
+      }
       dsto[i] = BN * 32 + g * 512;
-      hstep[i] = 32;
     }
   }
-  // packed W: half step h of tile kt = h/2 sits at kt * kTileElems + (h%2) * 512
+  // a packed operand's half step h (of tile h/2) sits at h/2 * kTileElems + (h%2) * 512 = h * 512
   auto src_at = [&](int i, int h) -> const bf16_t* {
-    if (PACKED && i < GW / 8) return src[i] + (size_t)(h >> 1) * kTileElems + (h & 1) * 512;
-    return src[i] + (size_t)h * 32;
+    if (PACKED && i < GW / 8) return src[i] + (size_t)h * (kTileElems / 2);
+    return src[i] + (size_t)h * hstep[i];
   };
   auto fill = [&](bf16_t* stage, int h) {
     const int hh = min(h, nh - 1);                       // past the end: reload the last (unused)
@@ -386,7 +393,6 @@ void gemm_tile_bf16(GemmArgs a, int k_per_split, int mtiles, int ntiles) {
     for (int i = 0; i < UPS; ++i)
       __builtin_amdgcn_global_load_lds((glb_void_t*)src_at(i, hh), (lds_void_t*)(stage + dsto[i]), 16, 0, 0);
   };
-  (void)hstep;
 
   f32x4 acc[NA][MB];
 #pragma unroll
@@ -442,13 +448,14 @@ void gemm_tile_bf16(GemmArgs a, int k_per_split, int mtiles, int ntiles) {
           const float g = acc[j][i][e], u = acc[j + NA / 2][i][e];
           hv[e] = f2bf(g / (1.f + expf(-g)) * u);
         }
+        bf16_t* dst = a.h_packed ? (bf16_t*)a.hout + xpk_index(m, f, a.N) : hrow + f;
         if (f + 3 < a.N) {
-          *(uint2*)(hrow + f) =
+          *(uint2*)dst =
               make_uint2((uint32_t)hv[0] | ((uint32_t)hv[1] << 16), (uint32_t)hv[2] | ((uint32_t)hv[3] << 16));
         } else {
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            if (f + e < a.N) hrow[f + e] = hv[e];
+            if (f + e < a.N) dst[e] = hv[e];
         }
       }
     }
@@ -821,6 +828,10 @@ hipError_t launch_tile(const GemmArgs& a, dim3 g1, int kps, int mtl, int ntl, hi
 
 hipError_t launch_gemm(const GemmArgs& a, const GemmPlan& p, int dtype, hipStream_t s) {
   ProfScope ps("gemm", s);
+  // tile-packed X is read by the tile kernel only; a packed gated output needs whole 64-wide tiles
+  if (a.x_packed && (dtype != 1 || p.kind != 3 || a.row_idx || a.K % BK || (a.wk > 0 && a.wk != a.K)))
+    return hipErrorInvalidValue;
+  if (a.h_packed && (!a.gated || a.N % BK)) return hipErrorInvalidValue;
   if (a.wk > 0 && a.wk != a.K) {
     // W narrower than X: only the bf16 weight-streaming and small-M kernels wrap k
     if (dtype != 1 || a.gated || a.wk % BK || a.K % a.wk) return hipErrorInvalidValue;
@@ -874,9 +885,10 @@ hipError_t launch_gemm(const GemmArgs& a, const GemmPlan& p, int dtype, hipStrea
   if (p.kind == 3) {   // LDS-ring tile kernel; gated tiles cover bn/2 features
     // its direct-to-LDS loads take 16-byte aligned rows; otherwise the 128 x 128
     // streaming tile with the same split count (same workspace)
-    bool aligned = ((uintptr_t)a.X & 15) == 0 && (a.ldx & 7) == 0;
+    bool aligned = ((uintptr_t)a.X & 15) == 0 && (a.x_packed || (a.ldx & 7) == 0);
     for (int i = 0; i < (a.gated ? 2 : a.nseg); ++i) aligned = aligned && ((uintptr_t)a.seg[i].w & 15) == 0;
     if (!aligned) {
+      if (a.x_packed) return hipErrorInvalidValue;
       GemmPlan q = p;
       q.kind = 1;
       q.bm = 128;

@@ -36,6 +36,8 @@ struct GemmArgs {
   // > 0 and < K: W has wk columns and GEMM column k multiplies W column k % wk
   // (X's K columns hold K / wk terms of one operand; bf16 streaming / rows kernels)
   int wk = 0;
+  int x_packed = 0;                   // 1: X in the tile-packed layout (xpk_index; tile kernel only)
+  int h_packed = 0;                   // 1: gated output hout written tile-packed (K = N features)
 };
 
 struct GemmPlan {
@@ -72,6 +74,7 @@ struct AttnArgs {
   int n_ctx_splits;     // units = n_ctx_splits + 1 (last = block keys); a row's C_b is split evenly
   int row_groups = 1;   // bf16: the R rows in groups of 64, one workgroup per (unit, group)
   int window = 0;       // > 0: only the last `window` of a row's C_b context keys are attended
+  int out_packed = 0;   // bf16: out written tile-packed as rows b*S + s of nq*d columns (xpk_index)
 };
 struct AttnPlan {
   int keys_per_split, n_ctx_splits;
@@ -114,6 +117,8 @@ struct NormArgs {
   float eps = 0.f;
   int out_mode = 0;               // 0: out row = r; 1: only rows with r % S != 0 -> b*(S-1) + s-1
   int S = 1;
+  int out_packed = 0;             // bf16: out tile-packed (xpk_index), output row + out_row0 in it
+  int out_row0 = 0;
 };
 hipError_t launch_norm(const NormArgs& a, int dtype, hipStream_t s);
 

@@ -12,6 +12,9 @@ import oracle
 from oracle import drafter as od
 from synth import MEDIUM, TINY, inputs
 
+WIDE = MEDIUM.with_(name="wide_bf16_l1_h4096", hidden=4096, n_q_heads=32, n_kv_heads=8, mlp_dim=12288, n_layers=1,
+                    vocab=9000, n_target_layers=2)
+
 from _gpu_common import DEV, as_f64, down, say, up, upload_weights, workspace
 
 CASES = {
@@ -33,6 +36,11 @@ CASES = {
     # sliding-window drafter (64 context keys): ragged contexts above and below the window
     "medium_window": (MEDIUM.with_(window=64), 9, [284, 131, 7], [16, 5, 0], 16),
     "medium_window_packed": (MEDIUM.with_(window=100), 9, [284, 131, 7], [16, 5, 0], 16, True),
+    # one full-width layer (H 4096, 32/8 heads, F 12288) at batches where the planner
+    # gives the LDS-ring tile kernel the O, gate|up and down GEMMs (B = 20) or the
+    # Q|K|V, gate|up and down GEMMs (B = 24): their inputs are written tile-packed
+    "wide_b20_packed": (WIDE.with_(batch=20), 10, None, None, None, True),
+    "wide_b24_packed": (WIDE.with_(batch=24), 11, None, None, None, True),
 }
 
 
@@ -65,7 +73,12 @@ def run_case(D, w, seed, ctx_len, n_new, nmax, packed=False, gain_std=0.1):
     ko, vo = kc.copy(), vc.copy()
     ologits, onew = od.draft_step(od.DrafterShape.of(w), weights, step["hidden_new"], step["n_new"], ko, vo,
                                   step["ctx_len"], step["last_token"])
-    return gpu, dict(logits=ologits, ctx=onew, k=ko, v=vo), step
+    ora = dict(logits=ologits, ctx=onew, k=ko, v=vo)
+    if w.hidden >= 4096:   # the same steps in fp32 arithmetic: the spread any fp32 evaluation shows
+        ora["logits32"], _ = od.draft_step(od.DrafterShape.of(w), weights, step["hidden_new"], step["n_new"],
+                                           kc.copy(), vc.copy(), step["ctx_len"], step["last_token"],
+                                           arith=np.float32)
+    return gpu, ora, step
 
 
 @pytest.mark.parametrize("name", list(CASES))
@@ -77,7 +90,17 @@ def test_draft_step_matches_oracle(D, name):
     np.testing.assert_array_equal(gpu["ctx"], ora["ctx"])
     err = np.abs(gpu["logits"].astype(np.float64) - ora["logits"])
     say(f"  logits max abs err {err.max():.3g} (tol {tol})")
-    assert err.max() <= tol
+    if "logits32" in ora:
+        # full width (H = 4096, F = 12288): every bf16 storage rounding can flip by
+        # an ulp on a sub-ulp difference, so the logits are held to the yardstick of
+        # the full-size tests — within 1.5x the fp32-arithmetic oracle's own max and
+        # mean departure from the float64 oracle, never tighter than 2e-2 max
+        spread = np.abs(ora["logits32"].astype(np.float64) - ora["logits"])
+        say(f"  fp32 oracle max {spread.max():.4f} mean {spread.mean():.5f}; GPU mean {err.mean():.5f}")
+        assert err.max() <= max(tol, 1.5 * spread.max())
+        assert err.mean() <= 1.5 * spread.mean()
+    else:
+        assert err.max() <= tol
     # cache: appended slots within tolerance, every other slot bit-identical (NaN stays NaN)
     for b in range(w.batch):
         c0, c1 = int(step["ctx_len"][b]), int(ora["ctx"][b])

@@ -61,7 +61,7 @@ def test_draft_step_full_size(D, wl):
     D.dflash_draft_step(cfg, wdev, up(step["hidden_new"], w.dtype), up(step["n_new"], "i32"), step["n_new_max"],
                         w.ctx, kdev, vdev, ctx, up(step["last_token"], "i32"), logits, ws)
     torch.cuda.synchronize()
-    rows = [0, B - 1]
+    rows = [0, B // 2, B - 1]
     glog = logits[rows].cpu().numpy()
     gk, gv = D.cache_to_logical(kdev[:, rows], vdev[:, rows])
     gk, gv = down(gk), down(gv)
