@@ -78,10 +78,11 @@ __device__ __forceinline__ int xcd_logical_id(int id, int total) {
 // GATED (NW = 2): the workgroup covers 64 output features; wave w streams the
 // rows of features n0+16w .. +15 from W_gate (j = 0) and W_up (j = 1), so its
 // epilogue holds gate and up of the same outputs and writes the SwiGLU product.
-template <int MT, int NW, int PD, int XD, bool PACKED, bool GATED>
+template <int MT, int NW, int PD, int XD, bool PACKED, bool GATED, int LB>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_stream_bf16(GemmArgs a, int k_per_split, int mtiles, int ntiles) {
   static_assert(!GATED || NW == 2, "gated tiles pair gate and up");
+  static_assert(LB == 8 || (LB == 4 && PD == 4), "loop body: 8 steps, or 4 (one turn of a 4-deep ring)");
   // W elements per k step and between the two 32-wide k halves of a step
   constexpr int WSTEP = PACKED ? kTileElems : BK, WKS = PACKED ? kTileElems / 2 : 32;
   // W offset of k step s of this split (relative to its first step): the
@@ -163,15 +164,17 @@ void gemm_stream_bf16(GemmArgs a, int k_per_split, int mtiles, int ntiles) {
     _Pragma("unroll") for (int i = 0; i < XCH; ++i) xr[ST % XD][i] = ldg16(x_src[i] + kk);    \
   }
     // as many steps per iteration as the consumers run (same barrier sequence)
-    for (int kb = 0; kb < nk; kb += 8) {
+    for (int kb = 0; kb < nk; kb += LB) {
       DFS_PRODUCER_STEP(0)
       DFS_PRODUCER_STEP(1)
       DFS_PRODUCER_STEP(2)
       DFS_PRODUCER_STEP(3)
-      DFS_PRODUCER_STEP(4)
-      DFS_PRODUCER_STEP(5)
-      DFS_PRODUCER_STEP(6)
-      DFS_PRODUCER_STEP(7)
+      if constexpr (LB == 8) {
+        DFS_PRODUCER_STEP(4)
+        DFS_PRODUCER_STEP(5)
+        DFS_PRODUCER_STEP(6)
+        DFS_PRODUCER_STEP(7)
+      }
     }
 #undef DFS_PRODUCER_STEP
     return;
@@ -217,16 +220,19 @@ void gemm_stream_bf16(GemmArgs a, int k_per_split, int mtiles, int ntiles) {
   }
   // 8 steps (two turns of a 4-deep ring, one turn of an 8-deep one) per loop
   // iteration: the wait-count analysis is conservative across the loop back
-  // edge, so cross it less often
-  for (int kb = 0; kb < nk; kb += 8) {
+  // edge, so cross it less often; a split whose step count is not a multiple
+  // of 8 runs 4-step bodies instead (fewer idle steps past its end)
+  for (int kb = 0; kb < nk; kb += LB) {
     DFS_CONSUMER_STEP(0, 0)
     DFS_CONSUMER_STEP(1, 1)
     DFS_CONSUMER_STEP(2, 2)
     DFS_CONSUMER_STEP(3, 3)
-    DFS_CONSUMER_STEP(4, 4 % PD)
-    DFS_CONSUMER_STEP(5, 5 % PD)
-    DFS_CONSUMER_STEP(6, 6 % PD)
-    DFS_CONSUMER_STEP(7, 7 % PD)
+    if constexpr (LB == 8) {
+      DFS_CONSUMER_STEP(4, 4 % PD)
+      DFS_CONSUMER_STEP(5, 5 % PD)
+      DFS_CONSUMER_STEP(6, 6 % PD)
+      DFS_CONSUMER_STEP(7, 7 % PD)
+    }
   }
 #undef DFS_CONSUMER_STEP
 
@@ -627,8 +633,9 @@ static const Cand kCands[] = {
 // W (once per M tile, the M tiles of one W slab sharing an XCD's L2), staged X
 // (mostly L2 hits, weighted 1/2) and the fp32 split partials (written and read
 // back, mostly MALL resident), against the dense product at about half the
-// bf16 peak.  The streaming kernel walks k in bodies of 8 steps, so a split's
-// steps count rounded up to 8.  One workgroup occupies a CU: a grid of w < 256
+// bf16 peak.  The streaming kernel walks k in bodies of 8 steps (4 when the
+// split's step count is not a multiple of 8), so a split's steps count rounded
+// up to that body.  One workgroup occupies a CU: a grid of w < 256
 // workgroups reaches about (w/256)^0.55 of the chip's bandwidth (a CU alone
 // streams faster than its 1/256 share), a larger one runs in rounds of 256,
 // each with a fixed ~1.5 us (pipeline ramp, epilogue).  Fitted to sweeps of the
@@ -648,7 +655,7 @@ static double plan_cost(const Cand& c, int sp, int M, int N, int K) {
   const double part = sp > 1 ? 1.5 * 4.0 * M * N * sp : 4.0 * M * N;
   if (!big) {
     const int kps = ceil_div(K / BK, sp);
-    const double pad = (double)(ceil_div(kps, 8) * 8) / kps;
+    const double pad = (double)(kps % 8 == 0 ? kps : ceil_div(kps, 4) * 4) / kps;
     const double w = 2.0 * N * K * (1.0 + 0.5 * (mt - 1)) * pad;
     const double x = 2.0 * (double)mt * c.bm * K * nt * pad;
     const double flops = 2.0 * (double)mt * c.bm * nt * c.bn * K;
@@ -791,23 +798,29 @@ GemmPlan gemm_plan_gated(int M, int N, int K, int dtype) {
 
 size_t gemm_partial_elems(const GemmPlan& p, int M, int N) { return (size_t)p.splits * M * N; }
 
-template <int MT, int NW, int PD, int XD>
-hipError_t launch_stream(const GemmArgs& a, dim3 g1, int kps, int mtl, int ntl, hipStream_t s) {
+template <int MT, int NW, int PD, int XD, int LB>
+hipError_t launch_stream_lb(const GemmArgs& a, dim3 g1, int kps, int mtl, int ntl, hipStream_t s) {
   if constexpr (NW == 2) {
     if (a.gated) {
       if (a.packed)
-        hipLaunchKernelGGL((gemm_stream_bf16<MT, NW, PD, XD, true, true>), g1, dim3(512), 0, s, a, kps, mtl, ntl);
+        hipLaunchKernelGGL((gemm_stream_bf16<MT, NW, PD, XD, true, true, LB>), g1, dim3(512), 0, s, a, kps, mtl, ntl);
       else
-        hipLaunchKernelGGL((gemm_stream_bf16<MT, NW, PD, XD, false, true>), g1, dim3(512), 0, s, a, kps, mtl, ntl);
+        hipLaunchKernelGGL((gemm_stream_bf16<MT, NW, PD, XD, false, true, LB>), g1, dim3(512), 0, s, a, kps, mtl, ntl);
       return hipGetLastError();
     }
   }
   if (a.gated) return hipErrorInvalidValue;
   if (a.packed)
-    hipLaunchKernelGGL((gemm_stream_bf16<MT, NW, PD, XD, true, false>), g1, dim3(512), 0, s, a, kps, mtl, ntl);
+    hipLaunchKernelGGL((gemm_stream_bf16<MT, NW, PD, XD, true, false, LB>), g1, dim3(512), 0, s, a, kps, mtl, ntl);
   else
-    hipLaunchKernelGGL((gemm_stream_bf16<MT, NW, PD, XD, false, false>), g1, dim3(512), 0, s, a, kps, mtl, ntl);
+    hipLaunchKernelGGL((gemm_stream_bf16<MT, NW, PD, XD, false, false, LB>), g1, dim3(512), 0, s, a, kps, mtl, ntl);
   return hipGetLastError();
+}
+
+template <int MT, int NW, int PD, int XD>
+hipError_t launch_stream(const GemmArgs& a, dim3 g1, int kps, int mtl, int ntl, hipStream_t s) {
+  if ((kps / BK) % 8 != 0) return launch_stream_lb<MT, NW, PD, XD, 4>(a, g1, kps, mtl, ntl, s);
+  return launch_stream_lb<MT, NW, PD, XD, 8>(a, g1, kps, mtl, ntl, s);
 }
 
 template <int BM, int BN>
