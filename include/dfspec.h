@@ -85,7 +85,10 @@ typedef struct {
   int32_t vocab;           /* V */
   int32_t n_target_layers; /* nT: target layers whose hidden states are concatenated */
   int32_t block;           /* S = 1 last decoded token + (S-1) mask tokens, S >= 2 */
-  int32_t max_ctx;         /* cache slots per sequence, a multiple of 64 */
+  int32_t max_ctx;         /* cache slots per sequence, a multiple of 64; preferably not a
+                              multiple of 1024: at a large power-of-two stride every (row,
+                              head) cache block starts on the same HBM channels (measured
+                              ~10 % slower attention at 2048 than at 2112 slots) */
   int32_t mask_token_id;   /* embedding row used for every mask slot, in [0, V) */
   float rms_eps;           /* RMSNorm: y = x / sqrt(mean(x^2) + eps) * g */
   float rope_theta;        /* rotate-half rotary base; <= 0 disables rotary embedding */

@@ -50,8 +50,11 @@ class Workload:
 
     @property
     def max_ctx(self) -> int:
-        # cache rows are padded to a multiple of 64 slots
-        return (self.ctx + 63) // 64 * 64
+        # cache capacity: the context rounded up to 64 slots plus one more 64-slot
+        # step (room for the next append; it also keeps the per-head slot stride off
+        # large powers of two, which would put every head's block on the same HBM
+        # channels)
+        return (self.ctx + 63) // 64 * 64 + 64
 
     @property
     def ctx_before(self) -> int:
