@@ -627,6 +627,7 @@ struct Cand {
 static const Cand kCands[] = {
     {1, 128, 128, 8, 2}, {1, 128, 64, 8, 1}, {1, 64, 128, 4, 2}, {1, 64, 64, 4, 1},
     {1, 32, 128, 2, 2},  {1, 32, 64, 2, 1},  {1, 256, 64, 16, 1}, {3, 256, 256, 0, 0},
+    {1, 128, 96, 8, 2},  {1, 64, 96, 4, 2},   // 3 consumer waves: 96 columns per workgroup
 };
 
 // Cost model, two regimes.
@@ -676,7 +677,7 @@ static double plan_cost(const Cand& c, int sp, int M, int N, int K) {
 }
 
 static bool plan_allows(const Cand& c, int M) {
-  if (M > 256) return (c.kind == 1 && c.mt == 8 && c.nw == 2) || c.kind == 3;
+  if (M > 256) return (c.kind == 1 && c.mt == 8 && c.nw == 2 && c.bn == 128) || c.kind == 3;
   return c.kind == 1;
 }
 
@@ -891,7 +892,7 @@ hipError_t launch_gemm(const GemmArgs& a, const GemmPlan& p, int dtype, hipStrea
     const int mtl = ceil_div(a.M, p.bm), ntl = ceil_div(a.N, p.bn);
     const dim3 g1(mtl * ntl * p.splits);
 #define DFS_STREAM(MT_, NW_, PD_, XD_)                                                                   \
-  if (p.mt == MT_ && p.nw == NW_ && p.pd == PD_ && p.xd == XD_ && p.bn != 48)                             \
+  if (p.mt == MT_ && p.nw == NW_ && p.pd == PD_ && p.xd == XD_ && p.bn != 48 && p.bn != 96)              \
     return launch_stream<MT_, NW_, PD_, XD_>(a, g1, kps, mtl, ntl, s);
     DFS_STREAM(2, 2, 4, 2)
     DFS_STREAM(2, 1, 4, 2)
@@ -900,6 +901,12 @@ hipError_t launch_gemm(const GemmArgs& a, const GemmPlan& p, int dtype, hipStrea
     DFS_STREAM(8, 1, 4, 2)
     DFS_STREAM(8, 2, 4, 4)
     DFS_STREAM(16, 1, 4, 4)
+    // 96 columns per workgroup (3 consumer waves)
+    if (!a.gated && p.bn == 96) {
+      if (p.mt == 8 && p.nw == 2 && p.pd == 4 && p.xd == 4) return launch_stream<8, 2, 4, 4, 3>(a, g1, kps, mtl, ntl, s);
+      if (p.mt == 4 && p.nw == 2 && p.pd == 4 && p.xd == 2) return launch_stream<4, 2, 4, 2, 3>(a, g1, kps, mtl, ntl, s);
+      return hipErrorInvalidValue;
+    }
     // gated tiles of 48 features (3 consumer waves)
     if (a.gated && p.bn == 48) {
       if (p.mt == 8 && p.nw == 2 && p.pd == 4 && p.xd == 4) return launch_stream<8, 2, 4, 4, 3>(a, g1, kps, mtl, ntl, s);

@@ -27,10 +27,12 @@ def D():
 # tiles): (640, 8200, 1024) with its automatic 2-way K split and a forced 3-way
 # one, (600, 16400, 512) unsplit; ragged in both M and N.  M <= 16 with K <= 512
 # ((5, 3001, 512), (16, 1000, 256), (1, 64, 64)) runs the independent-wave small-M kernel, ragged N.
+# (100, 6000, 1024 / 2048) get 96-column streaming tiles (3 consumer waves, 64 and 128 rows).
 @pytest.mark.parametrize("M,N,K,splits", [(1, 64, 64, 0), (120, 300, 256, 0), (120, 300, 256, 3),
                                           (256, 1000, 512, 7), (64, 128, 4096, 0), (130, 4096, 1024, 0),
                                           (640, 8200, 1024, 0), (640, 8200, 1024, 3), (600, 16400, 512, 0),
-                                          (32, 1000, 256, 0), (5, 3001, 512, 0), (16, 1000, 256, 0), (17, 129, 192, 0)])
+                                          (32, 1000, 256, 0), (5, 3001, 512, 0), (16, 1000, 256, 0), (17, 129, 192, 0),
+                                          (100, 6000, 1024, 0), (100, 6000, 2048, 0)])
 def test_gemm_bf16_matches_fp64_product(D, M, N, K, splits):
     say(f"gemm bf16 M={M} N={N} K={K} splits={splits}")
     X = rng.normal(1, "gx", (M, K), 1.0, dtype="bf16")
@@ -69,7 +71,7 @@ def test_pack_matrix_layout(D, N, K):
 
 @pytest.mark.parametrize("M,N,K,splits", [(1, 64, 64, 0), (120, 300, 256, 3), (128, 1000, 512, 0),
                                           (256, 1000, 512, 7), (300, 200, 256, 0), (130, 4096, 1024, 0),
-                                          (640, 8200, 1024, 0), (16, 1000, 256, 0), (3, 100, 64, 0)])
+                                          (640, 8200, 1024, 0), (16, 1000, 256, 0), (3, 100, 64, 0), (100, 6000, 2048, 0)])
 def test_gemm_packed_weights_bit_identical(D, M, N, K, splits):
     # same operands in the same order: the packed and row-major kernels agree bit for bit
     import torch
