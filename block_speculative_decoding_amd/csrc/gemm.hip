@@ -644,11 +644,12 @@ static const Cand kCands[] = {
 // drafter shapes at M = 16 .. 256 (every pick within 3 % of the fastest
 // measured configuration, the sum within 0.3 %).
 // M > 256 (matrix-core bound): the 128 x 128 streaming tile at its measured
-// ~0.85 PFLOP/s or the 256 x 256 LDS-ring tile at ~1.1 PFLOP/s.  Compute time
-// is counted in whole waves of 256 workgroups, plus a fixed ~4 us per wave;
-// split partials cost one more pass over M x N x splits fp32.  Fitted to
-// measurements of the drafter shapes at M = 480 .. 2048 (every pick within 2 %
-// of the fastest).
+// ~0.85 PFLOP/s or the 256 x 256 LDS-ring tile (tile-packed inputs) at ~1.2
+// PFLOP/s.  Compute time is counted in whole waves of 256 workgroups, plus a
+// fixed ~4 us per wave; split partials cost a write and a read of M x N x
+// splits fp32 on top.  Fitted to measurements of the drafter shapes at M = 320
+// .. 2048, the cost of a split including its consumer's extra reads (the picks
+// sum to within 1.2 % of the fastest configurations').
 static double plan_cost(const Cand& c, int sp, int M, int N, int K) {
   const bool big = M > 256;
   const int mt = ceil_div(M, c.bm), nt = ceil_div(N, c.bn);
@@ -671,9 +672,11 @@ static double plan_cost(const Cand& c, int sp, int M, int N, int K) {
   const double fill = wgs >= 192.0 ? 1.0 : wgs / 192.0;
   const double mem = (w + 0.5 * x + part) / 8.0e12;
   const double waves = ceil(wgs / 256.0);
-  const double rate = c.kind == 3 ? 1.1e15 : 0.85e15;
+  const double rate = c.kind == 3 ? 1.2e15 : 0.85e15;
   const double cmp = flops / rate * (waves * 256.0 / wgs) + waves * 4.0e-6;
-  return fmax(mem / fill, cmp) + (sp > 1 ? 4.0 * M * N * sp / 8.0e12 : 0.0);
+  // split partials are written in the epilogue and read back by the consumer:
+  // neither overlaps the matrix-core work
+  return fmax(mem / fill, cmp) + (sp > 1 ? 2.0 * 4.0 * M * N * sp / 8.0e12 : 0.0);
 }
 
 static bool plan_allows(const Cand& c, int M) {
