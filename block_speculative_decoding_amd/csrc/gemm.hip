@@ -495,6 +495,89 @@ void gemm_tile_bf16(GemmArgs a, int k_per_split, int mtiles, int ntiles) {
   }
 }
 
+// Short-K GEMM (K = 256, 16 < M <= 16*MT; the sequential head's per-position
+// product at batches 17..128): a persistent grid where each workgroup stages all
+// of X (M x 256, at most 64 KB) in LDS once, then each wave walks W row groups
+// g, g + (waves in the grid), ...: one 8 KB contiguous load of the group's 16 W
+// rows (packed) and of the Y values it accumulates into, issued one group
+// ahead (two register buffers, unconditional loads: past the end the last group
+// is re-read), 8*MT matrix-core products against X fragments from LDS, a
+// 16-byte store per row.  No barrier after the X staging; nothing is re-read
+// per k step.  Requires N % 4 == 0 and a 16-byte aligned Y with ldy % 4 == 0.
+template <int MT, bool PACKED>
+__global__ __launch_bounds__(256) void gemm_short_bf16(GemmArgs a) {
+  constexpr int K = 4 * BK, LDX = K + 8;
+  __shared__ __attribute__((aligned(16))) bf16_t Xs[16 * MT * LDX];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, c = lane & 15, g4 = lane >> 4;
+  // X rows 0 .. 16*MT-1 (rows past M repeat row M-1; their results are not stored)
+  for (int ch = tid; ch < 16 * MT * (K / 8); ch += 256) {
+    const int row = ch / (K / 8), col = (ch % (K / 8)) * 8;
+    const int m = min(row, a.M - 1);
+    *(uint4*)&Xs[row * LDX + col] = ldg16((const bf16_t*)a.X + (size_t)x_row(a, m) * a.ldx + col);
+  }
+  __syncthreads();
+  const int ng = ceil_div(a.N, 16), tw = gridDim.x * 4;
+  int g = blockIdx.x * 4 + wave;
+  if (g >= ng) return;                                   // uniform over the wave; no barrier follows
+  bf16x8 wf[2][8];
+  f32x4 yv[2][MT];
+  auto load = [&](int buf, int gg) {
+    gg = min(gg, ng - 1);
+    const int n0 = gg * 16;
+    const bf16_t* w = PACKED ? (const bf16_t*)a.seg[0].w + (size_t)gg * 4 * kTileElems + lane * 8
+                             : (const bf16_t*)a.seg[0].w + (size_t)min(n0 + c, a.N - 1) * K + g4 * 8;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        bf16x8 v = ldg_bf16x8(w + (PACKED ? (size_t)kt * kTileElems + h * 512 : (size_t)kt * BK + h * 32));
+        if (buf == 0) wf[0][2 * kt + h] = v;
+        else wf[1][2 * kt + h] = v;
+      }
+    const int n = min(n0 + 4 * g4, a.N - 4);
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      f32x4 y = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (a.accumulate) y = *(const f32x4*)(a.Y + (size_t)min(i * 16 + c, a.M - 1) * a.ldy + n);
+      if (buf == 0) yv[0][i] = y;
+      else yv[1][i] = y;
+    }
+  };
+  auto compute_store = [&](int buf, int gg) {
+    f32x4 acc[MT];
+#pragma unroll
+    for (int i = 0; i < MT; ++i) acc[i] = buf == 0 ? yv[0][i] : yv[1][i];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const bf16x8 wa = buf == 0 ? wf[0][2 * kt + h] : wf[1][2 * kt + h];
+#pragma unroll
+        for (int i = 0; i < MT; ++i)
+          acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              wa, *(const bf16x8*)&Xs[(i * 16 + c) * LDX + kt * BK + h * 32 + g4 * 8], acc[i], 0, 0, 0);
+      }
+    const int n = gg * 16 + 4 * g4;
+    if (n >= a.N) return;
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      const int m = i * 16 + c;
+      if (m < a.M) *(f32x4*)(a.Y + (size_t)m * a.ldy + n) = acc[i];
+    }
+  };
+  load(0, g);
+  while (true) {
+    load(1, g + tw);
+    compute_store(0, g);
+    g += tw;
+    if (g >= ng) break;
+    load(0, g + tw);
+    compute_store(1, g);
+    g += tw;
+    if (g >= ng) break;
+  }
+}
+
 // Small-M GEMM (M <= 16 rows, K <= 512; the Markov head's per-position
 // U[prev] . W product): every wave is independent — it owns 16 W rows, loads
 // all their K at once (8 KB contiguous in the packed layout at K = 256), the
@@ -730,6 +813,16 @@ GemmPlan gemm_plan(int M, int N, int K, int dtype, int force_splits) {
     best.k_per_split = K;
     return best;
   }
+  // K = 256 and up to 128 rows (the sequential head's product at batches 17..128):
+  // the persistent short-K kernel (X staged once per workgroup)
+  if (M > 16 && M <= 128 && K == 4 * BK && force_splits <= 1) {
+    best.kind = 5;
+    best.bm = 16 * ceil_div(M, 16);
+    best.bn = 16;
+    best.splits = 1;
+    best.k_per_split = K;
+    return best;
+  }
   double best_cost = 1e300;
   for (const Cand& c : kCands) {
     if (!plan_allows(c, M)) continue;
@@ -918,6 +1011,36 @@ hipError_t launch_gemm(const GemmArgs& a, const GemmPlan& p, int dtype, hipStrea
       return hipErrorInvalidValue;
     }
 #undef DFS_STREAM
+    return hipErrorInvalidValue;
+  }
+  if (p.kind == 5) {   // persistent short-K kernel, K = 256, 16 < M <= 128
+    const bool ok = !a.gated && p.splits == 1 && a.K == 4 * BK && a.M <= 128 && a.N % 4 == 0 && (a.ldy & 3) == 0 &&
+                    ((uintptr_t)a.Y & 15) == 0 && !a.x_packed && (a.wk == 0 || a.wk == a.K) && a.nseg == 1;
+    if (!ok) {   // same product on the streaming kernel
+      GemmPlan q = p;
+      q.kind = 1;
+      q.mt = a.M <= 32 ? 2 : (a.M <= 64 ? 4 : 8);
+      q.bm = 16 * q.mt;
+      q.bn = 128;
+      q.nw = 2;
+      q.pd = 4;
+      q.xd = q.mt == 8 ? 4 : 2;
+      return launch_gemm(a, q, dtype, s);
+    }
+    const int ng = ceil_div(a.N, 16);
+    const int mt = ceil_div(a.M, 16);
+    // resident at once: two workgroups per CU with 32 rows, one with more (registers)
+    const dim3 g5(min(ceil_div(ng, 4), mt <= 2 ? 512 : 256));
+#define DFS_SHORT(MT_)                                                                               \
+  if (mt <= MT_) {                                                                                   \
+    if (a.packed) hipLaunchKernelGGL((gemm_short_bf16<MT_, true>), g5, dim3(256), 0, s, a);          \
+    else hipLaunchKernelGGL((gemm_short_bf16<MT_, false>), g5, dim3(256), 0, s, a);                  \
+    return hipGetLastError();                                                                        \
+  }
+    DFS_SHORT(2)
+    DFS_SHORT(4)
+    DFS_SHORT(8)
+#undef DFS_SHORT
     return hipErrorInvalidValue;
   }
   if (p.kind == 4) {   // independent waves, 16 W rows each, M <= 16, K <= 512

@@ -41,7 +41,8 @@ struct GemmArgs {
 };
 
 struct GemmPlan {
-  int kind = 1;            // 1: bf16 weight streaming, 3: bf16 LDS-ring tile, 4: bf16 small-M rows, 2: fp32 VALU
+  int kind = 1;            // 1: bf16 weight streaming, 3: bf16 LDS-ring tile, 4: bf16 small-M rows,
+                           // 5: bf16 persistent short-K (K = 256, M <= 128), 2: fp32 VALU
   int bm = 128, bn = 128, mt = 8, nw = 2, splits = 1, k_per_split = 0;
   int pd = 4, xd = 2;      // weight-streaming kernel: k steps of W / X in flight per wave
 };
