@@ -560,7 +560,7 @@ int rnn_bias_sample(int32_t batch, int32_t n_draft, int32_t vocab, int32_t rank,
   ProfScope ps("markov", s);
   // bf16: X rows [hi | mid | lo] of the state (K = 3 rank) against W (rank columns, wrapping)
   const int kx = bf ? 3 * rank : rank;
-  const GemmPlan plan = gemm_plan(batch, vocab, kx, uw_dtype, 1);
+  const GemmPlan plan = gemm_plan_wrapped(batch, vocab, kx, rank, uw_dtype);
   for (int i = 0; i < n_draft; ++i) {
     // h_i = tanh(U[prev_i] + A h_{i-1}), then final_i = base_i + W h_i
     RnnArgs ra;

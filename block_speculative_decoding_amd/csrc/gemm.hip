@@ -495,8 +495,8 @@ void gemm_tile_bf16(GemmArgs a, int k_per_split, int mtiles, int ntiles) {
   }
 }
 
-// Short-K GEMM (K = 256, 16 < M <= 16*MT; the sequential head's per-position
-// product at batches 17..128): a persistent grid where each workgroup stages all
+// Short-K GEMM (K = 256, M <= 16*MT; the sequential head's per-position
+// product at batches up to 128): a persistent grid where each workgroup stages all
 // of X (M x 256, at most 64 KB) in LDS once, then each wave walks W row groups
 // g, g + (waves in the grid), ...: one 8 KB contiguous load of the group's 16 W
 // rows (packed) and of the Y values it accumulates into, issued one group
@@ -504,14 +504,16 @@ void gemm_tile_bf16(GemmArgs a, int k_per_split, int mtiles, int ntiles) {
 // is re-read), 8*MT matrix-core products against X fragments from LDS, a
 // 16-byte store per row.  No barrier after the X staging; nothing is re-read
 // per k step.  Requires N % 4 == 0 and a 16-byte aligned Y with ldy % 4 == 0.
-template <int MT, bool PACKED>
+// T = 3: X holds three K = 256 terms side by side (wk = 256, the RNN head's state
+// split hi | mid | lo); each W group is loaded once and multiplies all three.
+template <int MT, bool PACKED, int T>
 __global__ __launch_bounds__(256) void gemm_short_bf16(GemmArgs a) {
-  constexpr int K = 4 * BK, LDX = K + 8;
+  constexpr int K = 4 * BK, KX = T * K, LDX = KX + 8;
   __shared__ __attribute__((aligned(16))) bf16_t Xs[16 * MT * LDX];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, c = lane & 15, g4 = lane >> 4;
   // X rows 0 .. 16*MT-1 (rows past M repeat row M-1; their results are not stored)
-  for (int ch = tid; ch < 16 * MT * (K / 8); ch += 256) {
-    const int row = ch / (K / 8), col = (ch % (K / 8)) * 8;
+  for (int ch = tid; ch < 16 * MT * (KX / 8); ch += 256) {
+    const int row = ch / (KX / 8), col = (ch % (KX / 8)) * 8;
     const int m = min(row, a.M - 1);
     *(uint4*)&Xs[row * LDX + col] = ldg16((const bf16_t*)a.X + (size_t)x_row(a, m) * a.ldx + col);
   }
@@ -548,15 +550,17 @@ __global__ __launch_bounds__(256) void gemm_short_bf16(GemmArgs a) {
 #pragma unroll
     for (int i = 0; i < MT; ++i) acc[i] = buf == 0 ? yv[0][i] : yv[1][i];
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
+    for (int t = 0; t < T; ++t)
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const bf16x8 wa = buf == 0 ? wf[0][2 * kt + h] : wf[1][2 * kt + h];
+      for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-        for (int i = 0; i < MT; ++i)
-          acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              wa, *(const bf16x8*)&Xs[(i * 16 + c) * LDX + kt * BK + h * 32 + g4 * 8], acc[i], 0, 0, 0);
-      }
+        for (int h = 0; h < 2; ++h) {
+          const bf16x8 wa = buf == 0 ? wf[0][2 * kt + h] : wf[1][2 * kt + h];
+#pragma unroll
+          for (int i = 0; i < MT; ++i)
+            acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                wa, *(const bf16x8*)&Xs[(i * 16 + c) * LDX + t * K + kt * BK + h * 32 + g4 * 8], acc[i], 0, 0, 0);
+        }
     const int n = gg * 16 + 4 * g4;
     if (n >= a.N) return;
 #pragma unroll
@@ -802,10 +806,10 @@ GemmPlan gemm_plan(int M, int N, int K, int dtype, int force_splits) {
     }
   }
 #endif
-  // M <= 16, K <= 512: one round of independent waves (measured 1.5x faster than the
-  // streaming kernel for the Markov head's 4 x 129280 x 256 product; at 32 rows
-  // the per-wave X fragments cost more than the streaming kernel's shared LDS tile)
-  if (M <= 16 && K <= 8 * BK && force_splits <= 1) {
+  // M <= 16, K <= 512 other than 256: one round of independent waves (1.5x faster
+  // than the streaming kernel on a 4 x 129280 x 256 product; at 32 rows the
+  // per-wave X fragments cost more than the streaming kernel's shared LDS tile)
+  if (M <= 16 && K <= 8 * BK && K != 4 * BK && force_splits <= 1) {
     best.kind = 4;
     best.bm = 16 * ceil_div(M, 16);
     best.bn = 64;
@@ -813,9 +817,10 @@ GemmPlan gemm_plan(int M, int N, int K, int dtype, int force_splits) {
     best.k_per_split = K;
     return best;
   }
-  // K = 256 and up to 128 rows (the sequential head's product at batches 17..128):
-  // the persistent short-K kernel (X staged once per workgroup)
-  if (M > 16 && M <= 128 && K == 4 * BK && force_splits <= 1) {
+  // K = 256 and up to 128 rows (the sequential head's product at batch <= 128):
+  // the persistent short-K kernel (X staged once per workgroup; measured faster
+  // than the small-M kernel too: 13.9 against 15.0 us at 4 rows)
+  if (M <= 128 && K == 4 * BK && force_splits <= 1) {
     best.kind = 5;
     best.bm = 16 * ceil_div(M, 16);
     best.bn = 16;
@@ -850,6 +855,22 @@ GemmPlan gemm_plan(int M, int N, int K, int dtype, int force_splits) {
     best.k_per_split = K;
   }
   return best;
+}
+
+// GEMM whose X holds K / wk terms against a W of wk columns (GemmArgs.wk):
+// the persistent short-K kernel for three 256-wide terms and up to 32 rows,
+// else the plan of the full-K product (the streaming kernels wrap k).
+GemmPlan gemm_plan_wrapped(int M, int N, int K, int wk, int dtype) {
+  if (dtype == 1 && wk == 4 * BK && K == 3 * wk && M <= 32) {
+    GemmPlan p;
+    p.kind = 5;
+    p.bm = 16 * ceil_div(M, 16);
+    p.bn = 16;
+    p.splits = 1;
+    p.k_per_split = K;
+    return p;
+  }
+  return gemm_plan(M, N, K, dtype, 1);
 }
 
 // Gated gate|up GEMM (N = features): no K split (the SwiGLU needs complete
@@ -1013,9 +1034,11 @@ hipError_t launch_gemm(const GemmArgs& a, const GemmPlan& p, int dtype, hipStrea
 #undef DFS_STREAM
     return hipErrorInvalidValue;
   }
-  if (p.kind == 5) {   // persistent short-K kernel, K = 256, 16 < M <= 128
-    const bool ok = !a.gated && p.splits == 1 && a.K == 4 * BK && a.M <= 128 && a.N % 4 == 0 && (a.ldy & 3) == 0 &&
-                    ((uintptr_t)a.Y & 15) == 0 && !a.x_packed && (a.wk == 0 || a.wk == a.K) && a.nseg == 1;
+  if (p.kind == 5) {   // persistent short-K kernel, K = 256, M <= 128
+    const bool three = a.wk == 4 * BK && a.K == 3 * a.wk;   // three terms against one W
+    const bool ok = !a.gated && p.splits == 1 && (a.K == 4 * BK || three) && a.M <= (three ? 32 : 128) &&
+                    a.N % 4 == 0 && (a.ldy & 3) == 0 && ((uintptr_t)a.Y & 15) == 0 && !a.x_packed &&
+                    (three || a.wk == 0 || a.wk == a.K) && a.nseg == 1;
     if (!ok) {   // same product on the streaming kernel
       GemmPlan q = p;
       q.kind = 1;
@@ -1029,17 +1052,21 @@ hipError_t launch_gemm(const GemmArgs& a, const GemmPlan& p, int dtype, hipStrea
     }
     const int ng = ceil_div(a.N, 16);
     const int mt = ceil_div(a.M, 16);
-    // resident at once: two workgroups per CU with 32 rows, one with more (registers)
-    const dim3 g5(min(ceil_div(ng, 4), mt <= 2 ? 512 : 256));
-#define DFS_SHORT(MT_)                                                                               \
+    // resident at once: two workgroups per CU with 32 rows and one term, else one (registers)
+    const dim3 g5(min(ceil_div(ng, 4), mt <= 2 && !three ? 512 : 256));
+#define DFS_SHORT(MT_, T_)                                                                           \
   if (mt <= MT_) {                                                                                   \
-    if (a.packed) hipLaunchKernelGGL((gemm_short_bf16<MT_, true>), g5, dim3(256), 0, s, a);          \
-    else hipLaunchKernelGGL((gemm_short_bf16<MT_, false>), g5, dim3(256), 0, s, a);                  \
+    if (a.packed) hipLaunchKernelGGL((gemm_short_bf16<MT_, true, T_>), g5, dim3(256), 0, s, a);      \
+    else hipLaunchKernelGGL((gemm_short_bf16<MT_, false, T_>), g5, dim3(256), 0, s, a);              \
     return hipGetLastError();                                                                        \
   }
-    DFS_SHORT(2)
-    DFS_SHORT(4)
-    DFS_SHORT(8)
+    if (three) {
+      DFS_SHORT(2, 3)
+    } else {
+      DFS_SHORT(2, 1)
+      DFS_SHORT(4, 1)
+      DFS_SHORT(8, 1)
+    }
 #undef DFS_SHORT
     return hipErrorInvalidValue;
   }

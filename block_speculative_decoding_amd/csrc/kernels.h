@@ -48,6 +48,8 @@ struct GemmPlan {
 };
 
 GemmPlan gemm_plan(int M, int N, int K, int dtype, int force_splits = 0);
+// plan of a single-split GEMM whose X holds K / wk terms against W's wk columns
+GemmPlan gemm_plan_wrapped(int M, int N, int K, int wk, int dtype);
 // plan of a gated gate|up GEMM (N = features), or kind < 0 when no gated kernel fits
 GemmPlan gemm_plan_gated(int M, int N, int K, int dtype);
 // Tile-packed bf16 weights: [ceil(N/16)][K/64] tiles of 16 rows x 64 columns,

@@ -26,7 +26,8 @@ def D():
 # M > 256 with enough columns is planned onto the LDS-ring tile kernel (256 x 256
 # tiles): (640, 8200, 1024) with its automatic 2-way K split and a forced 3-way
 # one, (600, 16400, 512) unsplit; ragged in both M and N.  M <= 16 with K <= 512
-# ((5, 3001, 512), (16, 1000, 256), (1, 64, 64)) runs the independent-wave small-M kernel, ragged N.
+# ((5, 3001, 512), (1, 64, 64)) runs the independent-wave small-M kernel, ragged N; K = 256 with
+# M <= 128 ((16, 1000, 256), (32, 1000, 256), (120, 300, 256)) the persistent short-K kernel.
 # (100, 6000, 1024 / 2048) get 96-column streaming tiles (3 consumer waves, 64 and 128 rows).
 @pytest.mark.parametrize("M,N,K,splits", [(1, 64, 64, 0), (120, 300, 256, 0), (120, 300, 256, 3),
                                           (256, 1000, 512, 7), (64, 128, 4096, 0), (130, 4096, 1024, 0),
@@ -267,9 +268,10 @@ def _rnn_inputs(seed, dtype, B, G, V, r):
     return base, U, Wt, A, last, u
 
 
-# the last case is the DSpark 5-token block at the full vocabulary, rank 256, packed W
+# rank 256 runs W h on the persistent short-K kernel up to 32 rows (B = 20 here, and the last case:
+# the DSpark 5-token block at the full vocabulary with packed W), on the streaming kernel above
 @pytest.mark.parametrize("dtype,B,G,V,r,packed", [("f32", 2, 3, 1000, 16, False), ("bf16", 4, 15, 5000, 64, False),
-                                                  ("bf16", 33, 7, 9000, 256, False),
+                                                  ("bf16", 33, 7, 9000, 256, False), ("bf16", 20, 5, 9000, 256, False),
                                                   ("bf16", 32, 4, 129280, 256, True)])
 def test_rnn_head_matches_oracle(D, dtype, B, G, V, r, packed):
     import torch
