@@ -28,6 +28,15 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0       # dense bf16 matrix-core peak (no sparsity)
 METRIC = "draft-verify steps/sec + HBM GB/s, B=8 block=16 ctx=4K vocab=152K (1 GPU)"
 
 
+def step_algorithmic_bytes(w, ab=None):
+    """Bytes of one whole step: the drafter GEMMs, attention, the sequential head
+    (its GEMM and logits update) or, without a head, the sampling pass, and verify.
+    The per-group entries that are parts of these (weights alone, the head's GEMM)
+    or flop counts are not added."""
+    ab = algorithmic_bytes(w) if ab is None else ab
+    return ab["gemm"] + ab["attention"] + ab["verify"] + (ab["markov"] if w.markov_rank > 0 else ab["sample"])
+
+
 def algorithmic_bytes(w):
     """Bytes the step must move at minimum, per kernel group (see the design notes)."""
     es = 2 if w.dtype == "bf16" else 4
@@ -505,7 +514,7 @@ def main():
     ms = time_steps(step, args.steps)
     print(f"[bench] {ms:.3f} ms/step", file=sys.stderr, flush=True)
     ab = algorithmic_bytes(w)
-    step_bytes = sum(v for k, v in ab.items() if k != "gemm_weights")
+    step_bytes = step_algorithmic_bytes(w, ab)
     res = {
         "metric": METRIC, "value": 1000.0 / ms, "unit": "steps/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
