@@ -175,6 +175,32 @@ def time_steps(step, K):
     return s.elapsed_time(e) / K
 
 
+def achievable_peaks(torch):
+    """Measured reference peaks of this GPU, for fractions beside the datasheet's:
+    a plain 1 GiB device copy (bytes read + written per second) and a large
+    square bf16 library GEMM (torch.mm, 8192^3, contiguous operands)."""
+    src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    a = torch.randn(8192, 8192, device="cuda").to(torch.bfloat16)
+    b = torch.randn(8192, 8192, device="cuda").to(torch.bfloat16)
+    c = torch.empty(8192, 8192, dtype=torch.bfloat16, device="cuda")
+    out = {}
+    for name, fn, units in (("copy_gbps", lambda: dst.copy_(src), 2.0 * src.numel() * 4 / 1e9),
+                            ("gemm_tflops", lambda: torch.mm(a, b, out=c), 2.0 * 8192 ** 3 / 1e12)):
+        for _ in range(3):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        out[name] = units / (e0.elapsed_time(e1) / 10 * 1e-3)
+    del src, dst, a, b, c
+    torch.cuda.empty_cache()
+    return out
+
+
 def profile_group(step, group, K, launches_per_step):
     D = step.D
     D.dfs_profile_begin(group, K * launches_per_step + 8)
@@ -539,16 +565,21 @@ def main():
         flops_per_launch = step_flops_g / launches_per_step
         kernel = "drafter GEMM launches (gemm_stream_bf16" + (", gemm_tile_bf16" if w.batch * w.block > 256 else "") \
             + (", Markov-head GEMMs" if w.markov_rank > 0 else "") + ")"
+        ach = achievable_peaks(step.torch)
         if w.batch * w.block > 256 and w.dtype == "bf16":
             # M > 256: the drafter GEMMs are bound by the matrix cores
             achieved = flops_per_launch / (per_launch_ms * 1e-3) / 1e12
             roof = {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                    "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": None}
+                    "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
+                    "achievable_peak": ach["gemm_tflops"], "achievable_peak_source": "torch.mm bf16 8192^3",
+                    "frac_of_achievable": achieved / ach["gemm_tflops"]}
         else:
             achieved = bytes_per_launch / (per_launch_ms * 1e-3) / 1e9
             roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                     "frac": achieved / HBM_PEAK_GBPS,
-                    "traffic": recorded_traffic() if w.name == WORKLOADS["C1"].name else None}
+                    "traffic": recorded_traffic() if w.name == WORKLOADS["C1"].name else None,
+                    "achievable_peak": ach["copy_gbps"], "achievable_peak_source": "1 GiB device copy",
+                    "frac_of_achievable": achieved / ach["copy_gbps"]}
         res["roofline"] = {"kernel": kernel, **roof, "algorithmic_bytes_per_launch": bytes_per_launch,
                            "flops_per_launch": flops_per_launch, "launches_per_step": launches_per_step,
                            "avg_launch_us": per_launch_ms * 1e3, "gemm_ms_per_step": tot / args.steps,
