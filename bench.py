@@ -341,7 +341,7 @@ def sweeps(steps, warmup):
 
 def sps_profile(wl, steps=10, warmup=2, seed=0):
     """The throughput curve the prefix scheduler uses, measured once at startup:
-    this build's whole step (draft + sample + verify) at batch sizes 1, 2, 4, ...
+    this library's whole step (draft + sample + verify) at batch sizes 1, 2, 4, ...
     up to the workload's, as verify passes per second against the rows verified
     (batch x block)."""
     w0 = WORKLOADS[wl]
@@ -373,7 +373,7 @@ def loop_bench(wl, K, R, sigma=1.0, seed=0, schedule=False):
     L = (cycle time without the synthetic target) / tau.  With ``schedule`` the
     prefix scheduler sets each request's verify length every cycle from seeded
     survival scores (standing in for a confidence head) and the SPS curve of
-    this build's step profiled first.  One JSON line."""
+    this library's step profiled first.  One JSON line."""
     import torch
     from block_speculative_decoding_amd import dfspec as D
     from block_speculative_decoding_amd.loop import SpecLoop
@@ -514,7 +514,7 @@ def main():
         summarize_rocprof(args.summarize_rocprof, args.steps + args.warmup)
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build measures one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "this benchmark measures one GPU only; --gpus must be 1"}))
         sys.exit(2)
     if args.sweep:
         sweeps(args.steps, args.warmup)
