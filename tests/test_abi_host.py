@@ -115,6 +115,10 @@ def test_invalid_arguments_rejected_on_host(lib):
     assert rnn(32, 1, fake, 1 << 20) == -2                     # bf16 rank not a multiple of 64
     assert rnn(2048, 0, fake, 1 << 30) == -2
     assert rnn(64, 1, fake, 16) == -4
+    # vocabulary limit: 1024 chunks of 4096 tokens
+    assert lib.markov_bias_sample(4, 3, 4194305, 0, fake, None, None, 1, fake, fake, 1.0, fake, None,
+                                  fake, 1 << 30, None) == -2
+    assert lib.markov_bias_sample_workspace_size(2, 2, 4194304) > 0
     lib.dfs_status_string.restype = ctypes.c_char_p
     assert lib.dfs_status_string(-4) == b"workspace too small"
 

@@ -175,10 +175,16 @@ def test_block_attention_matches_oracle(D, dtype, B, S, nq, nkv, d, max_ctx, ctx
 
 # ---------------------------------------------------------------- sampling (no head)
 
-@pytest.mark.parametrize("V,T", [(1000, 1.0), (10000, 0.7), (10000, 0.0), (8, 1.0)])
+# the largest vocabulary the library takes (1024 chunks of 4096 tokens; the pick merges
+# exactly that many per row), also ragged (V % 4 != 0: scalar loads, a partial last chunk)
+MAX_V = 1024 * 4096
+
+
+@pytest.mark.parametrize("V,T", [(1000, 1.0), (10000, 0.7), (10000, 0.0), (8, 1.0),
+                                 (MAX_V, 1.0), (MAX_V - 3, 0.8), (MAX_V, 0.0)])
 def test_parallel_sampling_matches_oracle(D, V, T):
     import torch
-    B, G = 6, 5
+    B, G = (6, 5) if V < MAX_V - 3 else (2, 2)
     say(f"sampling V={V} T={T}")
     logits = rng.normal(4, f"sl{V}", (B, G, V), 3.0)
     u = rng.uniform01(4, f"su{V}", (B, G))
@@ -348,7 +354,8 @@ def _drafts_from_q(q_logits, ud, T):
 
 # early: every row verifies only its first n_verify[b] drafts (random in -1 .. G+1,
 # clamped), the prefix scheduler's early stopping
-@pytest.mark.parametrize("B,G,V,T,with_stats,early", [(64, 7, 3000, 1.0, False, False), (16, 15, 20000, 1.0, True, False),
+@pytest.mark.parametrize("B,G,V,T,with_stats,early", [(2, 2, MAX_V, 1.0, False, False), (2, 3, MAX_V - 3, 0.9, True, False),
+                                                      (64, 7, 3000, 1.0, False, False), (16, 15, 20000, 1.0, True, False),
                                                       (32, 7, 3000, 0.0, False, False), (8, 3, 8, 1.0, False, False),
                                                       (16, 5, 4096, 0.8, False, False), (64, 7, 3000, 1.0, False, True),
                                                       (16, 15, 20000, 1.0, True, True), (32, 7, 3000, 0.0, False, True)])
