@@ -77,20 +77,6 @@ __global__ __launch_bounds__(256) void embed_kernel(const T* E, const int32_t* l
   }
 }
 
-// v[0..3] += the float4 at p + z * stride for z = 0 .. n-1, added in z order.
-// Four partials are loaded together (indexes clamped, extra loads discarded):
-// a loop with one load per iteration would wait for each before the next.
-__device__ __forceinline__ void add_partials(float* v, const float* p, size_t stride, int n) {
-  for (int z0 = 0; z0 < n; z0 += 4) {
-    float4 t[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) t[u] = *(const float4*)(p + (size_t)min(z0 + u, n - 1) * stride);
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      if (z0 + u < n) v[0] += t[u].x, v[1] += t[u].y, v[2] += t[u].z, v[3] += t[u].w;
-  }
-}
-
 // RMSNorm of one row per workgroup (1024 threads), fused with the reduction of
 // split-K GEMM partials and the fp32 residual update:
 //   x = (resid or 0) + sum_z part[z]   (partials summed in z order after resid)
@@ -118,7 +104,10 @@ __global__ __launch_bounds__(1024) void norm_kernel(NormArgs a) {
           const float4 t = *(const float4*)(a.resid + row0 + h);
           v[i][0] = t.x, v[i][1] = t.y, v[i][2] = t.z, v[i][3] = t.w;
         }
-        if (a.part) add_partials(v[i], a.part + row0 + h, a.part_stride, a.sp);
+        for (int z = 0; z < (a.part ? a.sp : 0); ++z) {
+          const float4 t = *(const float4*)(a.part + z * a.part_stride + row0 + h);
+          v[i][0] += t.x, v[i][1] += t.y, v[i][2] += t.z, v[i][3] += t.w;
+        }
         if (a.part && a.update_resid) *(float4*)(a.resid + row0 + h) = make_float4(v[i][0], v[i][1], v[i][2], v[i][3]);
       } else {
 #pragma unroll
@@ -260,20 +249,11 @@ __global__ __launch_bounds__(256) void qkv_tile_kernel(QkvArgs a) {
   float x1[4] = {0.f, 0.f, 0.f, 0.f}, x2[4] = {0.f, 0.f, 0.f, 0.f};
   if (valid) {
     const size_t off = (size_t)row * Nqkv + hd * D + i0;
-    for (int z0 = 0; z0 < a.sp; z0 += 4) {   // four partials' loads in flight together, summed in z order
-      float4 u[4], w[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float* pz = a.part + (size_t)min(z0 + q, a.sp - 1) * a.part_stride + off;
-        u[q] = *(const float4*)pz;
-        w[q] = *(const float4*)(pz + HALF);
-      }
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if (z0 + q >= a.sp) continue;
-        x1[0] += u[q].x; x1[1] += u[q].y; x1[2] += u[q].z; x1[3] += u[q].w;
-        x2[0] += w[q].x; x2[1] += w[q].y; x2[2] += w[q].z; x2[3] += w[q].w;
-      }
+    for (int z = 0; z < a.sp; ++z) {
+      const float4 u = *(const float4*)(a.part + z * a.part_stride + off);
+      const float4 w = *(const float4*)(a.part + z * a.part_stride + off + HALF);
+      x1[0] += u.x; x1[1] += u.y; x1[2] += u.z; x1[3] += u.w;
+      x2[0] += w.x; x2[1] += w.y; x2[2] += w.z; x2[3] += w.w;
     }
     if ((is_q || is_k) && a.use_rope) {
       const float4 c01 = *(const float4*)(a.rope + (size_t)row * HALF + i0);
