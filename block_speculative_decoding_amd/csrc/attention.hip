@@ -338,6 +338,63 @@ __global__ __launch_bounds__(128) void attn_combine(AttnArgs a) {
   }
 }
 
+// The same merge for d = 128, vectorised: 256 threads take 8 query rows, each
+// thread four consecutive dims (16-byte partial loads, one 8-byte store), so
+// the grid is a quarter of the size and each unit costs one load per thread.
+// Per element the arithmetic is that of attn_combine, in the same order.
+__global__ __launch_bounds__(256) void attn_combine4(AttnArgs a) {
+  constexpr int U = 8, D = 128;
+  const int r = blockIdx.x * 8 + (threadIdx.x >> 5), g = blockIdx.y, b = blockIdx.z;
+  if (r >= a.R) return;
+  const int dd = (threadIdx.x & 31) * 4;
+  const int units = a.n_ctx_splits + 1;
+  const size_t bg = (size_t)b * a.nkv + g;
+  const float* ml = a.part_ml + (bg * units * a.Rpad + r) * 2;
+  const size_t ustride = (size_t)a.Rpad * 2;
+  const float* po = a.part_o + (bg * units * a.Rpad + r) * D + dd;
+  const size_t pstride = (size_t)a.Rpad * D;
+  float M = -INFINITY, den = 0.f, num[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int u0 = 0; u0 < units; u0 += U) {
+    float m[U], l[U];
+    float4 o[U];
+#pragma unroll
+    for (int i = 0; i < U; ++i) {
+      const int u = min(u0 + i, units - 1);
+      m[i] = ml[u * ustride];
+      l[i] = ml[u * ustride + 1];
+      o[i] = *(const float4*)(po + u * pstride);
+    }
+    float mg = M;
+#pragma unroll
+    for (int i = 0; i < U; ++i)
+      if (u0 + i < units) mg = fmaxf(mg, m[i]);
+    if (mg == -INFINITY) continue;
+    const float alpha = M == -INFINITY ? 0.f : exp2f(M - mg);
+    den *= alpha;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) num[e] *= alpha;
+#pragma unroll
+    for (int i = 0; i < U; ++i) {
+      if (u0 + i >= units || m[i] == -INFINITY) continue;
+      const float w = exp2f(m[i] - mg);
+      den += w * l[i];
+      num[0] += w * o[i].x;
+      num[1] += w * o[i].y;
+      num[2] += w * o[i].z;
+      num[3] += w * o[i].w;
+    }
+    M = mg;
+  }
+  const int group = a.nq / a.nkv, hh = r / a.S, s = r % a.S, h = g * group + hh;
+  const int orow = b * a.S + s, col = h * D + dd;
+  uint32_t w2[2];
+#pragma unroll
+  for (int e = 0; e < 4; e += 2)
+    w2[e / 2] = (uint32_t)f2bf(num[e] / den) | ((uint32_t)f2bf(num[e + 1] / den) << 16);
+  bf16_t* out = (bf16_t*)a.out + (a.out_packed ? xpk_index(orow, col, a.nq * D) : (size_t)orow * a.nq * D + col);
+  *(uint2*)out = make_uint2(w2[0], w2[1]);
+}
+
 // fp32: one workgroup per (query row s, head h, batch b); keys in chunks of 256.
 __global__ __launch_bounds__(256) void attn_f32(AttnArgs a) {
   constexpr int CH = 256;
@@ -486,7 +543,10 @@ hipError_t launch_attention(const AttnArgs& a, int dtype, hipStream_t s) {
   hipLaunchKernelGGL(attn_bf16_d128, grid, dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || fused) return e;
-  hipLaunchKernelGGL(attn_combine<bf16_t>, dim3(a.R, a.nkv, a.B), dim3(128), 0, s, a);
+  if (a.d == 128 && ((uintptr_t)a.part_o & 15) == 0 && ((uintptr_t)a.out & 7) == 0)
+    hipLaunchKernelGGL(attn_combine4, dim3((a.R + 7) / 8, a.nkv, a.B), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(attn_combine<bf16_t>, dim3(a.R, a.nkv, a.B), dim3(128), 0, s, a);
   return hipGetLastError();
 }
 
