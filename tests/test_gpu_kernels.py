@@ -173,6 +173,34 @@ def test_block_attention_matches_oracle(D, dtype, B, S, nq, nkv, d, max_ctx, ctx
         np.testing.assert_allclose(got[b], want, atol=tol, rtol=0)
 
 
+@pytest.mark.parametrize("B,S,nq,nkv,ctx", [(3, 16, 8, 2, [600, 37, 300]),   # 64 rows per kv head
+                                            (2, 5, 4, 4, [700, 290])])          # 5 rows: a partial row group
+def test_attention_combine_paths_agree(D, B, S, nq, nkv, ctx):
+    """The key-chunk merge has a vectorised kernel (8-byte aligned output) and a
+    one-thread-per-dim kernel (any alignment; here the output sits 2 bytes off);
+    both do the same fp32 arithmetic in the same order, so the outputs agree
+    bit for bit.  Contexts of several hundred keys split into key chunks."""
+    import torch
+    d, max_ctx = 128, 704
+    say(f"attention combine paths B={B} S={S} nq={nq} nkv={nkv} ctx={ctx}")
+    ctx = np.array(ctx, np.int32)
+    args = [up(rng.normal(4, "cq", (B, S, nq, d), 1.0, dtype="bf16"), "bf16"),
+            up(rng.normal(4, "ckb", (B, S, nkv, d), 1.0, dtype="bf16"), "bf16"),
+            up(rng.normal(4, "cvb", (B, S, nkv, d), 1.0, dtype="bf16"), "bf16"),
+            up(rng.normal(4, "ckc", (B, nkv, max_ctx, d), 1.0, dtype="bf16"), "bf16"),
+            up(rng.normal(4, "cvc", (B, nkv, d, max_ctx), 1.0, dtype="bf16"), "bf16"),
+            up(ctx, "i32")]
+    n = B * S * nq * d
+    aligned = torch.empty(n, dtype=torch.bfloat16, device=DEV)
+    shifted = torch.empty(n + 1, dtype=torch.bfloat16, device=DEV)[1:]
+    assert aligned.data_ptr() % 8 == 0 and shifted.data_ptr() % 8 == 2
+    ws = workspace(D.dfs_block_attention_workspace_size(B, S, nq, nkv, d, int(ctx.max()), 1))
+    for out in (aligned, shifted):
+        D.dfs_block_attention(*args, out.view(B, S, nq, d), max_ctx, int(ctx.max()), ws)
+    torch.cuda.synchronize()
+    assert torch.equal(aligned.view(torch.int16), shifted.view(torch.int16))
+
+
 # ---------------------------------------------------------------- sampling (no head)
 
 # the largest vocabulary the library takes (1024 chunks of 4096 tokens; the pick merges
