@@ -93,7 +93,7 @@ def test_draft_step_full_size(D, wl):
                                        atol=2e-2, rtol=2.0 ** -7)
 
 
-@pytest.mark.parametrize("wl", ["C2", "C3", "C4"])
+@pytest.mark.parametrize("wl", ["C2", "C3", "C4", "C5"])
 def test_markov_sample_full_size(D, wl):
     import torch
     w = WORKLOADS[wl]
