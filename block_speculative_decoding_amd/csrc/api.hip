@@ -160,10 +160,6 @@ hipError_t run_gemm(const void* X, int ldx, int M, int N, int K, const void* w0,
     a.nseg = 3;
   }
   const GemmPlan p = gemm_plan(M, N, K, dtype, force_splits);
-#ifdef DFS_TUNING
-  // tuning builds only: DFS_X_PACKED times the tile kernel as if X were tile-packed
-  if (getenv("DFS_X_PACKED") && p.kind == 3) a.x_packed = 1;
-#endif
   a.Y = Y;
   a.ldy = ldy ? ldy : N;
   a.y_split_stride = (size_t)M * N;

@@ -16,9 +16,6 @@
 #include "kernels.h"
 
 #include <math.h>
-#ifdef DFS_TUNING
-#include <stdlib.h>
-#endif
 
 namespace dfs {
 namespace {
@@ -498,9 +495,6 @@ AttnPlan attn_plan(int B, int nkv, int ctx_bound, int dtype, int row_groups, int
   }
   const int pairs = B * nkv * row_groups;
   int splits = attn_target_splits(pairs, ctx_bound);
-#ifdef DFS_TUNING
-  if (const char* f = getenv("DFS_ATTN_SPLITS")) splits = atoi(f);
-#endif
   const int max_splits = ceil_div(ctx_bound, 256);   // at least 256 keys (4 steps) per unit
   if (splits > max_splits) splits = max_splits;
   if (splits < 1) splits = 1;
@@ -515,9 +509,6 @@ AttnPlan attn_plan(int B, int nkv, int ctx_bound, int dtype, int row_groups, int
 // count actually used never exceeds the target split count).
 int attn_max_units(int B, int nkv, int max_ctx, int dtype) {
   if (dtype != 1) return 1;
-#ifdef DFS_TUNING
-  if (getenv("DFS_ATTN_SPLITS")) return 65;
-#endif
   int splits = 0;
   for (int rg = 1; rg <= 4; ++rg) splits = max(splits, attn_target_splits(B * nkv * rg, max_ctx));
   const int max_splits = ceil_div(max_ctx, 256);

@@ -15,19 +15,21 @@ namespace {
 //   block row (b, s), s < S            -> position C_b + s,  C_b = ctx_len[b] + n_new[b]
 // Angles pos * theta^(-2i/d) are formed and evaluated in fp64 (positions reach
 // 32K, where an fp32 angle would already be off by ~1e-3 rad), then stored fp32.
-// Block 0 also publishes per-row bookkeeping (clamped): base, appended rows, C_b.
+// Block 0 also publishes per-row bookkeeping (clamped) of every batch row, its
+// threads striding over the rows: base, appended rows, C_b.
 __global__ void prep_kernel(MetaArgs a) {
   const int half = a.d / 2;
   const int Mc = a.B * a.n_new_max, Mx = Mc + a.B * a.S;
   const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (blockIdx.x == 0 && threadIdx.x < a.B) {
-    const int b = threadIdx.x;
-    const int base = min(max(a.ctx_len[b], 0), a.ctx_bound);
-    const int nn = min(max(a.n_new[b], 0), a.n_new_max);
-    const int cb = min(base + nn, a.ctx_bound);
-    a.meta[b] = base;
-    a.meta[a.B + b] = cb - base;
-    a.meta[2 * a.B + b] = cb;
+  if (blockIdx.x == 0) {
+    for (int b = threadIdx.x; b < a.B; b += blockDim.x) {
+      const int base = min(max(a.ctx_len[b], 0), a.ctx_bound);
+      const int nn = min(max(a.n_new[b], 0), a.n_new_max);
+      const int cb = min(base + nn, a.ctx_bound);
+      a.meta[b] = base;
+      a.meta[a.B + b] = cb - base;
+      a.meta[2 * a.B + b] = cb;
+    }
   }
   if (!a.rope || idx >= (long)Mx * half) return;
   const int row = (int)(idx / half), i = (int)(idx % half);

@@ -11,10 +11,6 @@
 // fp32: a plain LDS-tiled VALU kernel (the fp32 configuration is tiny).
 #include "kernels.h"
 
-#ifdef DFS_TUNING
-#include <stdio.h>
-#include <stdlib.h>
-#endif
 
 namespace dfs {
 
@@ -793,19 +789,6 @@ GemmPlan gemm_plan(int M, int N, int K, int dtype, int force_splits) {
     return best;
   }
   const int kb = K / BK;
-#ifdef DFS_TUNING
-  // tuning builds only: DFS_GEMM_FORCE="kind,bm,bn,mt,nw,splits[,pd,xd]" selects a configuration
-  if (const char* f = getenv("DFS_GEMM_FORCE")) {
-    GemmPlan p;
-    int sp = 1;
-    if (sscanf(f, "%d,%d,%d,%d,%d,%d,%d,%d", &p.kind, &p.bm, &p.bn, &p.mt, &p.nw, &sp, &p.pd, &p.xd) >= 6) {
-      const int kps_blocks = ceil_div(kb, sp);
-      p.splits = ceil_div(kb, kps_blocks);
-      p.k_per_split = kps_blocks * BK;
-      return p;
-    }
-  }
-#endif
   // M <= 16, K <= 512 other than 256: one round of independent waves (1.5x faster
   // than the streaming kernel on a 4 x 129280 x 256 product; at 32 rows the
   // per-wave X fragments cost more than the streaming kernel's shared LDS tile)
@@ -889,19 +872,6 @@ GemmPlan gemm_plan_gated(int M, int N, int K, int dtype) {
   p.splits = 1;
   p.k_per_split = K;
   p.pd = 4;
-#ifdef DFS_TUNING
-  // tuning builds only: DFS_GATED_FORCE="mt[,features per tile]" selects the streaming tile
-  if (const char* f = getenv("DFS_GATED_FORCE")) {
-    int mt = 0, bn = 64;
-    if (sscanf(f, "%d,%d", &mt, &bn) >= 1) {
-      p.mt = mt;
-      p.bm = 16 * mt;
-      p.bn = bn;
-      p.xd = mt == 8 ? 4 : 2;
-      return p;
-    }
-  }
-#endif
   // streaming tiles of 16*mt rows x 48 or 64 features (3 or 4 consumer waves, each
   // with 16 gate + 16 up rows), priced by the same model on the 2N weight rows:
   // 48 features make 256 workgroups of the drafter's 12288 features

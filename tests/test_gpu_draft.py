@@ -41,6 +41,10 @@ CASES = {
     # Q|K|V, gate|up and down GEMMs (B = 24): their inputs are written tile-packed
     "wide_b20_packed": (WIDE.with_(batch=20), 10, None, None, None, True),
     "wide_b24_packed": (WIDE.with_(batch=24), 11, None, None, None, True),
+    # more batch rows than one workgroup has threads: every row's bookkeeping
+    # (base, appended count, new length) must still be published
+    "tiny_b300_ragged": (TINY.with_(batch=300), 12, [(37 * b) % 125 for b in range(300)],
+                         [b % 5 for b in range(300)], 4),
 }
 
 

@@ -287,6 +287,129 @@ def test_drafter_matches_sequence_level_bruteforce(split, arith, window):
     np.testing.assert_allclose(logits[0], want, atol=2e-6 if arith is np.float64 else 1e-4, rtol=0)
 
 
+def _torch_swiglu(m, w_gate, w_up, w_down):
+    """SwiGLU MLP through torch's own SiLU (CPU, float64): (silu(m Wg^T) * (m Wu^T)) Wd^T,
+    with the gated product stored in fp32 as the drafter stores it."""
+    import torch
+    import torch.nn.functional as Fn
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float64))
+    mt = t(m)
+    h = Fn.silu(mt @ t(w_gate).T) * (mt @ t(w_up).T)
+    h = h.to(torch.float32).to(torch.float64)
+    return (h @ t(w_down).T).numpy()
+
+
+def _bruteforce_drafter(w, weights, hidden_all, last_token):
+    """Sequence-level formulation of an L-layer drafter with its MLP on.
+
+    The sequence is [context rows ; block rows].  KV injection: a context row's
+    state is its feature vector at EVERY layer (only the block rows evolve), and
+    layer l's keys/values of every row come from that layer's own Wk, Wv.  Only
+    block rows query; the explicit mask gives full-in-block / causal-to-context.
+    Each layer: pre-norm attention, residual, pre-norm SwiGLU MLP (torch's SiLU),
+    residual.  fp32 storage throughout, float64 arithmetic."""
+    f32 = lambda a: np.asarray(a, np.float64).astype(np.float32).astype(np.float64)
+    W = {k: np.asarray(v, np.float64) for k, v in weights.items()}
+    C = hidden_all.shape[0]
+    S, nq, nkv, d = w.block, w.n_q_heads, w.n_kv_heads, w.head_dim
+    feats = f32(_rms(hidden_all @ W["fc"].T, W["fc_norm"], w.rms_eps))
+    toks = [last_token] + [w.mask_token_id] * (S - 1)
+    x = f32(W["embed"][toks])
+    pos = np.arange(C + S)
+    for l in range(w.n_layers):
+        p = f"layers.{l}."
+        a = f32(_rms(x, W[p + "attn_norm"], w.rms_eps))
+        rows = np.concatenate([feats, a])                       # layer-l states of the whole sequence
+        k = f32(_rope_complex((rows @ W[p + "wk"].T).reshape(-1, nkv, d), pos, w.rope_theta))
+        v = f32((rows @ W[p + "wv"].T).reshape(-1, nkv, d))
+        q = f32(_rope_complex((a @ W[p + "wq"].T).reshape(-1, nq, d), pos[C:], w.rope_theta))
+        o = _bruteforce_block_attention(q, k[:C], v[:C], k[C:], v[C:], window=w.window)
+        x = f32(x + f32(o).reshape(S, nq * d) @ W[p + "wo"].T)
+        m = f32(_rms(x, W[p + "mlp_norm"], w.rms_eps))
+        x = f32(x + _torch_swiglu(m, W[p + "w_gate"], W[p + "w_up"], W[p + "w_down"]))
+    z = f32(_rms(x[1:], W["final_norm"], w.rms_eps))
+    return (z @ W["lm_head"].T).astype(np.float32)
+
+
+def _strong_mlp(weights, w, seed):
+    """Gate/up weights wide enough that SiLU works in its curved range (|g| ~ 3)
+    and a down projection that makes the MLP a large share of the residual."""
+    out = dict(weights)
+    for l in range(w.n_layers):
+        p = f"layers.{l}."
+        out[p + "w_gate"] = rng.normal(seed, p + "w_gate_strong", (w.mlp_dim, w.hidden), 0.5)
+        out[p + "w_up"] = rng.normal(seed, p + "w_up_strong", (w.mlp_dim, w.hidden), 0.5)
+        out[p + "w_down"] = rng.normal(seed, p + "w_down_strong", (w.hidden, w.mlp_dim), 0.01)
+    return out
+
+
+@pytest.mark.parametrize("n_layers,split", [(2, None), (3, None), (2, 9)])
+def test_drafter_mlp_and_layer_stacking_match_sequence_level_bruteforce(n_layers, split):
+    # L layers with the SwiGLU MLP on and distinct random norm gains per layer: a
+    # gate/up swap, sigmoid in place of SiLU, a dropped residual or a layer reading
+    # another layer's weights or gains changes the logits far beyond the bar
+    w = _tiny(batch=1, ctx=21, dtype="f32", rope_theta=100.0, n_layers=n_layers)
+    weights = _strong_mlp(inputs.drafter_weights(w, 11, gain_std=0.3), w, 11)
+    C = 17
+    hid = rng.normal(11, "pin_hidden_mlp", (1, C, w.n_target_layers * w.hidden), 1.0)
+    last = np.array([7], np.int32)
+    sh = _shape(w)
+    kc = np.zeros((n_layers, 1, w.max_ctx, w.n_kv_heads, w.head_dim), np.float32)
+    vc = np.zeros_like(kc)
+    ctx = np.zeros(1, np.int32)
+    for lo, hi in ([(0, C)] if split is None else [(0, split), (split, C)]):
+        logits, ctx = od.draft_step(sh, weights, hid[:, lo:hi], np.array([hi - lo]), kc, vc, ctx, last)
+    want = _bruteforce_drafter(w, weights, hid[0].astype(np.float64), 7)
+    np.testing.assert_allclose(logits[0], want, atol=2e-6, rtol=0)
+    # the MLP matters at this scale: switching it off moves the logits by far more
+    off = dict(weights)
+    for l in range(n_layers):
+        off[f"layers.{l}.w_down"] = np.zeros_like(weights[f"layers.{l}.w_down"])
+    kc2, vc2 = np.zeros_like(kc), np.zeros_like(vc)
+    l_off, _ = od.draft_step(sh, off, hid, np.array([C]), kc2, vc2, np.zeros(1, np.int32), last)
+    assert np.abs(l_off[0] - want).max() > 1e-2
+
+
+def test_drafter_swiglu_gate_and_up_roles():
+    # one layer, attention output off (Wo = 0), so a mask row's state after the
+    # layer is e + MLP(m) with e = E[MASK] and m = RMSNorm(e; g_mlp)
+    w = _tiny(dtype="f32", rope_theta=100.0)
+    base = _strong_mlp(inputs.drafter_weights(w, 12, gain_std=0.3), w, 12)
+    base["layers.0.wo"] = np.zeros_like(base["layers.0.wo"])
+    step = inputs.step_inputs(w, 12)
+    kc, vc = inputs.cache_prefix(w, 12, step["ctx_len"])
+
+    def run(**over):
+        wt = dict(base)
+        wt.update({f"layers.0.{k}": v for k, v in over.items()})
+        return _run(w, wt, step, kc, vc)[0]
+
+    Fd, H = w.mlp_dim, w.hidden
+    no_mlp = run(w_down=np.zeros((H, Fd), np.float32))
+    # silu(g) * 0 and silu(0) * u are exactly zero: the MLP adds nothing
+    np.testing.assert_array_equal(run(w_up=np.zeros((Fd, H), np.float32)), no_mlp)
+    np.testing.assert_array_equal(run(w_gate=np.zeros((Fd, H), np.float32)), no_mlp)
+    # a gate row g_f = lam for every feature of the mask rows: silu(lam) ~ lam when
+    # lam >> 0 and ~ 0 when lam << 0 (a gate/up swap would give silu(u) * lam instead)
+    e = base["embed"][w.mask_token_id].astype(np.float64)
+    m = (e / np.sqrt(np.mean(e * e) + w.rms_eps) * base["layers.0.mlp_norm"]).astype(np.float32)
+    m = m.astype(np.float64)
+    unit = np.broadcast_to(m / (m @ m), (Fd, H))
+    np.testing.assert_allclose(run(w_gate=(-60.0 * unit).astype(np.float32)), no_mlp, atol=1e-9, rtol=0)
+    lam = 60.0
+    wg = (lam * unit).astype(np.float32)
+    g = wg.astype(np.float64) @ m                                 # ~ lam for every feature
+    u = base["layers.0.w_up"].astype(np.float64) @ m
+    hmid = (g * u).astype(np.float32).astype(np.float64)          # silu(g) = g to ~1e-24 here
+    x = (e + hmid @ base["layers.0.w_down"].astype(np.float64).T).astype(np.float32).astype(np.float64)
+    z = (x / np.sqrt(np.mean(x * x) + w.rms_eps) * base["final_norm"]).astype(np.float32).astype(np.float64)
+    want = (base["lm_head"].astype(np.float64) @ z).astype(np.float32)
+    got = run(w_gate=wg)
+    for b in range(w.batch):
+        for j in range(w.gamma):
+            np.testing.assert_allclose(got[b, j], want, atol=2e-6, rtol=0)
+
+
 def test_drafter_batch_rows_independent_and_garbage_slots_ignored():
     w = _tiny(n_layers=2, ctx=40)
     weights = inputs.drafter_weights(w, 3, gain_std=0.1)
