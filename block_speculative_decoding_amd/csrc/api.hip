@@ -87,6 +87,7 @@ struct DraftWs {
   float* part;
   float* apart_o;
   float* apart_ml;
+  size_t resid_off, mlp_in_off, hmid_off;   // byte offsets in the workspace (trace hook)
   size_t bytes;
 };
 
@@ -99,9 +100,12 @@ DraftWs carve_draft(void* base, const DraftDims& d, int dtype) {
   auto r16 = [](int m) { return (size_t)ceil_div(m, 16) * 16; };
   w.xs = cv.take<char>(r16(d.Mx) * d.H * d.es);
   w.resid = cv.take<float>((size_t)d.Mb * d.H);
+  w.resid_off = cv.off - (size_t)d.Mb * d.H * sizeof(float);
   w.mlp_in = cv.take<char>(r16(d.Mb) * d.H * d.es);
+  w.mlp_in_off = cv.off - r16(d.Mb) * d.H * d.es;
   w.attn_o = cv.take<char>(r16(d.Mb) * d.nq * d.d * d.es);
   w.hmid = cv.take<char>(r16(d.Mb) * d.F * d.es);
+  w.hmid_off = cv.off - r16(d.Mb) * d.F * d.es;
   w.z = cv.take<char>(r16(d.B * d.G) * d.H * d.es);
   w.q_att = cv.take<char>((size_t)d.B * d.nkv * d.Rpad * d.d * d.es);
   w.k_blk = cv.take<char>((size_t)d.B * d.nkv * 64 * d.d * d.es);
@@ -214,6 +218,25 @@ size_t dflash_draft_workspace_size(const dfs_drafter_cfg* cfg, int32_t batch, in
   if (check_cfg(cfg) != DFS_OK || batch < 1 || n_new_max < 0) return 0;
   const DraftDims d = dims_of(cfg, batch, n_new_max);
   return carve_draft(nullptr, d, cfg->dtype).bytes;
+}
+
+int dfs_draft_trace_layout(const dfs_drafter_cfg* cfg, int32_t batch, int32_t n_new_max, size_t* offsets,
+                           int32_t* packed) {
+  if (!offsets || !packed || batch < 1 || n_new_max < 0) return DFS_EINVAL;
+  const int st = check_cfg(cfg);
+  if (st != DFS_OK) return st;
+  const DraftDims d = dims_of(cfg, batch, n_new_max);
+  const int dt = cfg->dtype;
+  const DraftWs w = carve_draft(nullptr, d, dt);
+  // the same layout decisions as dflash_draft_step's
+  const GemmPlan gated = gemm_plan_gated(d.Mb, d.F, d.H, dt);
+  offsets[0] = w.resid_off;
+  offsets[1] = w.mlp_in_off;
+  offsets[2] = w.hmid_off;
+  packed[0] = 0;
+  packed[1] = dt == DFS_BF16 && gated.kind == 3;
+  packed[2] = gated.kind > 0 && pack_x(d.Mb, d.H, d.F, dt);
+  return DFS_OK;
 }
 
 int dflash_draft_step(const dfs_drafter_cfg* cfg, const dfs_drafter_weights* wt, int32_t batch,
@@ -422,9 +445,10 @@ int dflash_draft_step(const dfs_drafter_cfg* cfg, const dfs_drafter_weights* wt,
 // then the inverse-CDF (or greedy) pick; writes d_i and the row's (max, sum).
 static hipError_t sample_position(int batch, int n_draft, int vocab, int i, const float* logits,
                                   const float* u_draft, float temperature, int32_t* draft_tokens,
-                                  double* row_stats, double2* stats, hipStream_t s) {
+                                  double* row_stats, double2* stats, double* sub, hipStream_t s) {
   const long rowV = (long)n_draft * vocab;
-  const hipError_t e = launch_chunk_stats(logits + (size_t)i * vocab, rowV, batch, vocab, temperature, stats, s);
+  const hipError_t e =
+      launch_chunk_stats(logits + (size_t)i * vocab, rowV, batch, vocab, temperature, stats, sub, s);
   if (e != hipSuccess) return e;
   PickArgs pa;
   pa.x = logits + (size_t)i * vocab;
@@ -433,6 +457,7 @@ static hipError_t sample_position(int batch, int n_draft, int vocab, int i, cons
   pa.V = vocab;
   pa.temperature = temperature;
   pa.stats = stats;
+  pa.sub = sub;
   pa.u = u_draft + i;
   pa.u_stride = n_draft;
   pa.tokens = draft_tokens + i;
@@ -442,10 +467,20 @@ static hipError_t sample_position(int batch, int n_draft, int vocab, int i, cons
   return launch_pick(pa, s);
 }
 
+// statistics of every sampled row: per chunk (max, sum) and per 64-token sub-chunk sums
+static size_t sample_carve(int B, int G, int V, void* base, double2** stats, double** sub) {
+  Carver cv(base);
+  const size_t nch = (size_t)ceil_div(V, kChunk);
+  double2* st = cv.take<double2>((size_t)B * G * nch);
+  double* sb = cv.take<double>((size_t)B * G * nch * 64);
+  if (stats) *stats = st;
+  if (sub) *sub = sb;
+  return cv.off + 256;
+}
+
 size_t markov_bias_sample_workspace_size(int32_t batch, int32_t n_draft, int32_t vocab) {
   if (batch < 1 || n_draft < 1 || vocab < 1) return 0;
-  const size_t nch = (size_t)ceil_div(vocab, kChunk);
-  return align_up((size_t)batch * n_draft * nch * sizeof(double2), 256) + 256;
+  return sample_carve(batch, n_draft, vocab, nullptr, nullptr, nullptr);
 }
 
 int markov_bias_sample(int32_t batch, int32_t n_draft, int32_t vocab, int32_t rank, float* logits, const void* U,
@@ -464,13 +499,13 @@ int markov_bias_sample(int32_t batch, int32_t n_draft, int32_t vocab, int32_t ra
   if (uw_packed) uw_dtype = DFS_BF16;
   if (workspace_bytes < markov_bias_sample_workspace_size(batch, n_draft, vocab)) return DFS_EWORKSPACE;
   hipStream_t s = (hipStream_t)stream;
-  Carver cv(workspace);
-  const int nch = ceil_div(vocab, kChunk);
-  double2* stats = cv.take<double2>((size_t)batch * n_draft * nch);
+  double2* stats;
+  double* sub;
+  sample_carve(batch, n_draft, vocab, workspace, &stats, &sub);
   const long rowV = (long)n_draft * vocab;
   if (rank == 0) {
     ProfScope ps("sample", s);
-    DFS_TRY(launch_chunk_stats(logits, vocab, batch * n_draft, vocab, temperature, stats, s));
+    DFS_TRY(launch_chunk_stats(logits, vocab, batch * n_draft, vocab, temperature, stats, sub, s));
     PickArgs pa;
     pa.x = logits;
     pa.row_stride = vocab;
@@ -478,6 +513,7 @@ int markov_bias_sample(int32_t batch, int32_t n_draft, int32_t vocab, int32_t ra
     pa.V = vocab;
     pa.temperature = temperature;
     pa.stats = stats;
+    pa.sub = sub;
     pa.u = u_draft;
     pa.u_stride = 1;
     pa.tokens = draft_tokens;
@@ -509,19 +545,22 @@ int markov_bias_sample(int32_t batch, int32_t n_draft, int32_t vocab, int32_t ra
     ga.packed = uw_packed;
     DFS_TRY(launch_gemm(ga, plan, uw_dtype, s));
     DFS_TRY(sample_position(batch, n_draft, vocab, i, logits, u_draft, temperature, draft_tokens, row_stats, stats,
-                            s));
+                            sub, s));
   }
   return DFS_OK;
 }
 
 // ------------------------------------------------------------------ RNN head + sampling
 
-static size_t rnn_carve(int B, int G, int V, int r, void* base, double2** stats, float** h, bf16_t** split) {
+static size_t rnn_carve(int B, int G, int V, int r, void* base, double2** stats, double** sub, float** h,
+                        bf16_t** split) {
   Carver cv(base);
   double2* st = cv.take<double2>((size_t)B * G * ceil_div(V, kChunk));
+  double* sb = cv.take<double>((size_t)B * G * ceil_div(V, kChunk) * 64);
   float* hh = cv.take<float>((size_t)2 * B * r);   // two state buffers, alternating by position
   bf16_t* sp = cv.take<bf16_t>((size_t)3 * B * r);
   if (stats) *stats = st;
+  if (sub) *sub = sb;
   if (h) *h = hh;
   if (split) *split = sp;
   return cv.off + 256;
@@ -529,7 +568,7 @@ static size_t rnn_carve(int B, int G, int V, int r, void* base, double2** stats,
 
 size_t rnn_bias_sample_workspace_size(int32_t batch, int32_t n_draft, int32_t vocab, int32_t rank) {
   if (batch < 1 || n_draft < 1 || vocab < 1 || rank < 1 || rank > kRnnMaxRank) return 0;
-  return rnn_carve(batch, n_draft, vocab, rank, nullptr, nullptr, nullptr, nullptr);
+  return rnn_carve(batch, n_draft, vocab, rank, nullptr, nullptr, nullptr, nullptr, nullptr);
 }
 
 int rnn_bias_sample(int32_t batch, int32_t n_draft, int32_t vocab, int32_t rank, float* logits, const void* U,
@@ -548,9 +587,10 @@ int rnn_bias_sample(int32_t batch, int32_t n_draft, int32_t vocab, int32_t rank,
   if (workspace_bytes < rnn_bias_sample_workspace_size(batch, n_draft, vocab, rank)) return DFS_EWORKSPACE;
   hipStream_t s = (hipStream_t)stream;
   double2* stats;
+  double* sub;
   float* h;
   bf16_t* split;
-  rnn_carve(batch, n_draft, vocab, rank, workspace, &stats, &h, &split);
+  rnn_carve(batch, n_draft, vocab, rank, workspace, &stats, &sub, &h, &split);
   const bool bf = uw_dtype == DFS_BF16;
   const long rowV = (long)n_draft * vocab;
   ProfScope ps("markov", s);
@@ -591,7 +631,7 @@ int rnn_bias_sample(int32_t batch, int32_t n_draft, int32_t vocab, int32_t rank,
     ga.packed = uw_packed;
     DFS_TRY(launch_gemm(ga, plan, uw_dtype, s));
     DFS_TRY(sample_position(batch, n_draft, vocab, i, logits, u_draft, temperature, draft_tokens, row_stats, stats,
-                            s));
+                            sub, s));
   }
   return DFS_OK;
 }
@@ -602,18 +642,20 @@ static size_t verify_carve(int B, int G, int V, void* base, VerifyArgs* a) {
   Carver cv(base);
   const size_t nch = (size_t)ceil_div(V, kChunk);
   double2* p_chunk = cv.take<double2>((size_t)B * (G + 1) * nch);
+  double* p_sub = cv.take<double>((size_t)B * (G + 1) * nch * 64);
   double2* q_chunk = cv.take<double2>((size_t)B * G * nch);
   double* rowinfo = cv.take<double>((size_t)B * 4);
-  double2* sums = cv.take<double2>((size_t)B * nch);
-  double* r_chunk = cv.take<double>((size_t)B * nch);
   int32_t* state = cv.take<int32_t>(B);
+  double* res = cv.take<double>((size_t)B * nch * 4);
+  double2* sub = cv.take<double2>((size_t)B * nch * 64);
   if (a) {
     a->p_chunk = p_chunk;
+    a->p_sub = p_sub;
     a->q_chunk = q_chunk;
     a->rowinfo = rowinfo;
-    a->sums = sums;
-    a->r_chunk = r_chunk;
     a->state = state;
+    a->res = res;
+    a->sub = sub;
   }
   return cv.off + 256;
 }
@@ -631,6 +673,8 @@ int spec_verify(int32_t batch, int32_t n_draft, int32_t vocab, const float* draf
       !u_final || !out_tokens || !n_accepted || !workspace)
     return DFS_EINVAL;
   if (vocab > kMaxVocab || n_draft > 64) return DFS_EUNSUPPORTED;   // one decide slot per position
+  // the statistics pass runs one workgroup per (row, chunk) of the target and draft rows
+  if ((size_t)batch * (2 * n_draft + 1) * ceil_div(vocab, kChunk) > 0x7fffffffu) return DFS_EUNSUPPORTED;
   if (!(temperature >= 0.f)) return DFS_EINVAL;
   if (workspace_bytes < spec_verify_workspace_size(batch, n_draft, vocab)) return DFS_EWORKSPACE;
   VerifyArgs a;

@@ -151,8 +151,10 @@ hipError_t launch_swiglu(const float* part, int sp, size_t part_stride, int M, i
 // Chunked row statistics: per (row, chunk): (max, sum exp((x-max)/T)) in fp64, or for
 // T == 0 (max, index of the first maximum).
 constexpr int kChunk = 4096;
+// sub (nullable, used when temperature > 0): [rows][nch][64] fp64 sums of each
+// 64-token sub-chunk relative to its chunk max
 hipError_t launch_chunk_stats(const float* x, long row_stride, int rows, int V, float temperature,
-                              double2* stats, hipStream_t s);
+                              double2* stats, double* sub, hipStream_t s);
 
 struct PickArgs {
   const float* x;          // logits rows
@@ -160,6 +162,7 @@ struct PickArgs {
   int rows, V;
   float temperature;
   const double2* stats;    // [rows][nchunks]
+  const double* sub;       // [rows][nchunks][64] sub-chunk sums (T > 0)
   const float* u;          // [rows] (stride u_stride)
   long u_stride;
   int32_t* tokens;         // [rows] (stride tok_stride)
@@ -178,12 +181,13 @@ struct VerifyArgs {
   const int32_t* n_verify; // [B] drafts verified per row (clamped to [0, G]), or null = G
   float temperature;
   const double* q_stats;   // [B][G][2] (max, sum) of the draft rows, or null -> q_chunk
-  const double2* q_chunk;  // [B*G][nch]
-  const double2* p_chunk;  // [B*(G+1)][nch]
-  double* rowinfo;         // [B][4]: target (max, sum), draft (max, sum) at the decided position
-  double2* sums;           // [B][nch]: fp64 sums of exp for target / draft row at the rejection
-  double* r_chunk;         // [B][nch]: residual mass max(0, p - q) per chunk
-  int32_t* state;          // [B]: first rejected position (= the row's verify length: all accepted)
+  double2* q_chunk;        // [B*G][nch]
+  double2* p_chunk;        // [B*(G+1)][nch]
+  double* p_sub;           // [B*(G+1)][nch][64] sub-chunk sums of the target rows
+  double* rowinfo;         // [B][4]: (Mp, Sp, Mq, Sq) at the rejected position, statistics-pass normalisers
+  int32_t* state;          // [B]: first rejected position (= the verify length when all are accepted)
+  double* res;             // [B][nch][4]: per chunk of the rejected rows, fp64 sums (see verify.hip)
+  double2* sub;            // [B][nch][64]: per 64-token sub-chunk of the rejected rows, fp64 sums
   int32_t* out_tokens;     // [B][G+1]
   int32_t* n_accepted;     // [B]
   int B, G, V;

@@ -26,6 +26,7 @@ EXPORTS = [
     "dfs_block_attention_workspace_size", "dfs_block_attention",
     "dfs_gemm_workspace_size", "dfs_gemm", "dfs_profile_begin", "dfs_profile_end",
     "dfs_packed_matrix_bytes", "dfs_pack_matrix", "dfs_gemm_swiglu", "spec_cycle_advance", "spec_schedule_verify",
+    "dfs_draft_trace_layout",
 ]
 
 
@@ -80,6 +81,7 @@ def _load():
         "spec_schedule_verify": (ctypes.c_int, [i32, i32, vp, i32, ctypes.POINTER(f32), ctypes.POINTER(f32), vp,
                                                 vp]),
         "dfs_packed_matrix_bytes": (sz, [i32, i32]),
+        "dfs_draft_trace_layout": (ctypes.c_int, [vp, i32, i32, ctypes.POINTER(sz), ctypes.POINTER(i32)]),
         "dfs_pack_matrix": (ctypes.c_int, [i32, i32, vp, vp, vp]),
         "dfs_profile_begin": (ctypes.c_int, [ctypes.c_char_p, i32]),
         "dfs_profile_end": (ctypes.c_int, [ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_double)]),
@@ -193,6 +195,23 @@ class DrafterWeights:
             *[ctypes.cast(self._arrays[n], _PP) for n in self.PER_LAYER], int(self.packed))
 
 
+    def layer_prefix(self, n: int) -> "DrafterWeights":
+        """The same device tensors as a drafter of only the first n layers."""
+        from dataclasses import replace
+        if not 1 <= n <= self.cfg.n_layers:
+            raise ValueError(f"layer prefix {n} outside 1..{self.cfg.n_layers}")
+        out = object.__new__(DrafterWeights)
+        out.cfg = replace(self.cfg, n_layers=n)
+        out.t = self.t
+        out.packed = self.packed
+        out._arrays = {k: (ctypes.c_void_p * n)(*list(v)[:n]) for k, v in self._arrays.items()}
+        out.c = CDrafterWeights(
+            self.t["embed"].data_ptr(), self.t["fc"].data_ptr(), self.t["fc_norm"].data_ptr(),
+            self.t["final_norm"].data_ptr(), self.t["lm_head"].data_ptr(),
+            *[ctypes.cast(out._arrays[k], _PP) for k in self.PER_LAYER], int(self.packed))
+        return out
+
+
 # ------------------------------------------------------------------ entry points
 
 def dflash_draft_workspace_size(cfg: DrafterConfig, batch: int, n_new_max: int) -> int:
@@ -216,6 +235,16 @@ def dflash_draft_step(cfg: DrafterConfig, weights: DrafterWeights, hidden_new, n
         _ptr(base_logits, torch.float32, B * (cfg.block - 1) * cfg.vocab, "base_logits"),
         _ptr(workspace, torch.uint8, None, "workspace"), workspace.numel(), _stream(stream))
     _check(st, "dflash_draft_step")
+
+
+def draft_trace_layout(cfg: DrafterConfig, batch: int, n_new_max: int):
+    """Workspace byte offsets and tile-packed flags of the last layer's residual
+    stream, MLP input and gated product left by dflash_draft_step (test hook)."""
+    c = cfg.c()
+    off = (ctypes.c_size_t * 3)()
+    pk = (ctypes.c_int32 * 3)()
+    _check(LIB.dfs_draft_trace_layout(ctypes.byref(c), batch, n_new_max, off, pk), "dfs_draft_trace_layout")
+    return list(off), list(pk)
 
 
 def markov_bias_sample_workspace_size(batch: int, n_draft: int, vocab: int) -> int:

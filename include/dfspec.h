@@ -34,10 +34,12 @@
  * Conventions for every function below
  *  - Tensor pointers are DEVICE pointers unless marked "host".  All tensors are
  *    dense, row-major, in the layouts stated.  The caller owns every buffer,
- *    including the workspace; the library allocates no device memory, keeps no
- *    mutable global state, never synchronises, and enqueues all work on
- *    `stream` (a hipStream_t; NULL = the null stream).  Results are valid once
- *    the caller has synchronised with that stream.
+ *    including the workspace; the library allocates no device memory, never
+ *    synchronises, and enqueues all work on `stream` (a hipStream_t; NULL = the
+ *    null stream).  Results are valid once the caller has synchronised with
+ *    that stream.  Its one piece of mutable global state is the opt-in timing
+ *    hook dfs_profile_begin/end (process-wide, not thread-safe; disarmed by
+ *    default, when it costs one flag test per launch).
  *  - Return value: DFS_OK (0) or a negative dfs_status.  Every shape, pointer
  *    and size check is done on the host before anything is enqueued; on error
  *    nothing is enqueued and no output is touched.  DFS_EHIP reports a failed
@@ -256,6 +258,11 @@ size_t spec_verify_workspace_size(int32_t batch, int32_t n_draft, int32_t vocab)
  * draft_tokens   [B, gamma] int32.
  * u_accept       [B, gamma] fp32; u_final [B] fp32.
  * draft_row_stats[B, gamma, 2] fp64 from markov_bias_sample, or NULL to recompute.
+ *                They hold the draft rows' (max, sum exp((x - max)/T)) at the
+ *                temperature of the markov_bias_sample call that wrote them, so
+ *                they may only be passed when that call used the same
+ *                temperature as this one (pass NULL otherwise); T == 0 stats
+ *                (max, 1) are not used by greedy verification.
  * n_verify       [B] int32 or NULL: row b verifies only its first k_b = n_verify[b]
  *                drafts (clamped to [0, gamma]; NULL = gamma) — the prefix
  *                scheduler's early stopping (same DSpark page, section
@@ -340,6 +347,22 @@ int dfs_block_attention(int32_t batch, int32_t block, int32_t n_q_heads, int32_t
                         const void* q, const void* k_blk, const void* v_blk, const void* k_cache,
                         const void* v_cache, const int32_t* ctx_len, void* out, void* workspace,
                         size_t workspace_bytes, void* stream);
+
+/* Where dflash_draft_step leaves three intermediates of its LAST layer in the
+ * workspace, for stage-by-stage parity tests (run the call with a prefix of the
+ * layers to see any layer).  After a call, at byte offsets[k] of the workspace:
+ *   k = 0  the fp32 residual stream [B*S, H] after the layer (the input of the
+ *          next layer, or of the final norm);
+ *   k = 1  the MLP input m = RMSNorm(x + attention output) [B*S, H] in cfg dtype;
+ *   k = 2  the gated product silu(m Wg^T) * (m Wu^T) [B*S, F] in cfg dtype.
+ * packed[k] = 1 when that tensor is stored in the tile-packed activation layout
+ * (rows in groups of 16, each group's columns in 64-wide 2 KB tiles in
+ * matrix-core operand order: element (r, c) of a tensor with C columns at
+ * ((r/16)*(C/64) + c/64)*1024 + ((c/32)%2)*512 + (r%16 + 16*((c/8)%4))*8 + c%8),
+ * else 0 (row-major).  offsets [3] and packed [3] are HOST arrays.
+ * DFS_EINVAL / DFS_EUNSUPPORTED as for dflash_draft_workspace_size's inputs. */
+int dfs_draft_trace_layout(const dfs_drafter_cfg* cfg, int32_t batch, int32_t n_new_max, size_t* offsets,
+                           int32_t* packed);
 
 /* Y[M, N] fp32 = X[M, K] . W[N, K]^T, both in `dtype`; the matrix-core kernel of
  * the drafter (split over K when `splits` > 1; splits = 0 picks automatically).

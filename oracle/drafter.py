@@ -204,35 +204,95 @@ def draft_step(shape: DrafterShape, weights, hidden_new, n_new, k_cache, v_cache
     tok[:, 0] = np.clip(np.asarray(last_token)[rows], 0, sh.vocab - 1)
     emb = wt("embed")
     x = round_f32(emb[tok]).astype(F)                         # [R, S, H] residual stream
-    pos = new_len[rows][:, None] + np.arange(S)[None, :]      # [R, S]
-
     for l in range(sh.n_layers):
-        p = f"layers.{l}."
-        a = rnd(rmsnorm(x, wt(p + "attn_norm"), sh.rms_eps, F))
-        q = rnd(rope_rotate((a @ wt(p + "wq").T).reshape(-1, S, nq, d), pos, sh.rope_theta, F))
-        k = rnd(rope_rotate((a @ wt(p + "wk").T).reshape(-1, S, nkv, d), pos, sh.rope_theta, F))
-        v = rnd((a @ wt(p + "wv").T).reshape(-1, S, nkv, d))
-        o = np.empty_like(q)
-        for i, b in enumerate(rows):
-            cb = int(new_len[b])
-            lo = max(0, cb - sh.window) if sh.window > 0 else 0     # sliding window: the last `window` keys
-            kc = as_f64(k_cache[l, b, lo:cb], dt)
-            vc = as_f64(v_cache[l, b, lo:cb], dt)
-            o[i] = block_attention(q[i], kc, vc, k[i], v[i], F)
-        o = rnd(o).reshape(-1, S, nq * d)
-        x = round_f32(x + o @ wt(p + "wo").T).astype(F)
-        m = rnd(rmsnorm(x, wt(p + "mlp_norm"), sh.rms_eps, F))
-        g = m @ wt(p + "w_gate").T
-        u = m @ wt(p + "w_up").T
-        with np.errstate(over="ignore"):
-            hmid = rnd(g / (F(1) + np.exp(-g)) * u)                # silu(g) * u
-        x = round_f32(x + hmid @ wt(p + "w_down").T).astype(F)
-
-    z = rnd(rmsnorm(x[:, 1:, :], wt("final_norm"), sh.rms_eps, F))
+        x = drafter_layer(sh, weights, l, x, k_cache, v_cache, new_len, rows, arith)
     out = np.full((B, S - 1, sh.vocab), np.nan, np.float32)
+    out[rows] = block_logits(sh, weights, x, arith)
+    return out, new_len.astype(np.int32)
+
+
+def drafter_layer(shape: DrafterShape, weights, l, x, k_cache, v_cache, new_len, rows, arith=np.float64):
+    """Layer l of the drafter on the block rows' residual stream.
+
+    x [R, S, H] (fp32 values) is the residual stream of batch rows ``rows`` on
+    entry; k_cache, v_cache [L, B, max_ctx, nkv, d] hold every cached context row
+    (the step's own appended rows included) and new_len [B] the context lengths
+    after the append (the block sits at positions new_len[b] .. new_len[b]+S-1).
+    Pre-norm attention over [cached context keys ; block keys], residual, pre-norm
+    SwiGLU MLP, residual.  Returns the residual stream after the layer."""
+    x1 = attention_half(shape, weights, l, x, k_cache, v_cache, new_len, rows, arith)
+    m = mlp_input(shape, weights, l, x1, arith)
+    return mlp_residual(shape, weights, l, x1, swiglu_product(shape, weights, l, m, arith), arith)
+
+
+def attention_half(shape: DrafterShape, weights, l, x, k_cache, v_cache, new_len, rows, arith=np.float64):
+    """x + Attention(RMSNorm(x)) . Wo of layer l (arguments as drafter_layer)."""
+    sh = shape
+    dt = sh.dtype
+    S = sh.block
+    nq, nkv, d = sh.n_q_heads, sh.n_kv_heads, sh.head_dim
+    F = arith
+    rows = list(rows)
+
+    def rnd(v):                     # storage rounding, back in the arithmetic type
+        return round_to(v, dt).astype(F)
+
+    def wt(name):
+        return _w(weights, name, dt, F)
+
+    x = np.asarray(x, F)
+    pos = np.asarray(new_len)[rows][:, None] + np.arange(S)[None, :]      # [R, S]
+    p = f"layers.{l}."
+    a = rnd(rmsnorm(x, wt(p + "attn_norm"), sh.rms_eps, F))
+    q = rnd(rope_rotate((a @ wt(p + "wq").T).reshape(-1, S, nq, d), pos, sh.rope_theta, F))
+    k = rnd(rope_rotate((a @ wt(p + "wk").T).reshape(-1, S, nkv, d), pos, sh.rope_theta, F))
+    v = rnd((a @ wt(p + "wv").T).reshape(-1, S, nkv, d))
+    o = np.empty_like(q)
+    for i, b in enumerate(rows):
+        cb = int(new_len[b])
+        lo = max(0, cb - sh.window) if sh.window > 0 else 0     # sliding window: the last `window` keys
+        kc = as_f64(k_cache[l, b, lo:cb], dt)
+        vc = as_f64(v_cache[l, b, lo:cb], dt)
+        o[i] = block_attention(q[i], kc, vc, k[i], v[i], F)
+    o = rnd(o).reshape(-1, S, nq * d)
+    return round_f32(x + o @ wt(p + "wo").T).astype(F)
+
+
+def mlp_input(shape: DrafterShape, weights, l, x1, arith=np.float64):
+    """m = RMSNorm(x1; g_mlp) of layer l, rounded to the weight dtype."""
+    return round_to(rmsnorm(np.asarray(x1, arith), _w(weights, f"layers.{l}.mlp_norm", shape.dtype, arith),
+                            shape.rms_eps, arith), shape.dtype).astype(arith)
+
+
+def swiglu_product(shape: DrafterShape, weights, l, m, arith=np.float64):
+    """silu(m . Wg^T) * (m . Wu^T) of layer l, rounded to the weight dtype."""
+    F = arith
+    m = np.asarray(m, F)
+    g = m @ _w(weights, f"layers.{l}.w_gate", shape.dtype, F).T
+    u = m @ _w(weights, f"layers.{l}.w_up", shape.dtype, F).T
+    with np.errstate(over="ignore"):
+        return round_to(g / (F(1) + np.exp(-g)) * u, shape.dtype).astype(F)       # silu(g) * u
+
+
+def mlp_residual(shape: DrafterShape, weights, l, x1, hmid, arith=np.float64):
+    """x1 + hmid . Wd^T of layer l, stored fp32."""
+    F = arith
+    return round_f32(np.asarray(x1, F) + np.asarray(hmid, F) @ _w(weights, f"layers.{l}.w_down", shape.dtype,
+                                                                   F).T).astype(F)
+
+
+def block_logits(shape: DrafterShape, weights, x, arith=np.float64):
+    """Final RMSNorm of the mask rows (slots 1..S-1) and the LM head:
+    x [R, S, H] residual stream -> base logits [R, S-1, V] float32."""
+    sh = shape
+    dt = sh.dtype
+    F = arith
+    z = round_to(rmsnorm(np.asarray(x, F)[:, 1:, :], _w(weights, "final_norm", dt, F), sh.rms_eps, F),
+                 dt).astype(F)
+    out = np.empty((z.shape[0], sh.block - 1, sh.vocab), np.float32)
     lm = weights["lm_head"]
     chunk = 16384
     for v0 in range(0, sh.vocab, chunk):
         wl = as_f64(lm[v0:v0 + chunk], dt).astype(F, copy=False)
-        out[rows, :, v0:v0 + chunk] = (z @ wl.T).astype(np.float32)
-    return out, new_len.astype(np.int32)
+        out[:, :, v0:v0 + chunk] = (z @ wl.T).astype(np.float32)
+    return out

@@ -72,3 +72,33 @@ def upload_weights(w, np_weights, packed=False):
     cfg = D.DrafterConfig.of(w)
     t = {k: up(v, w.dtype) for k, v in np_weights.items()}
     return cfg, D.DrafterWeights(cfg, t, packed=packed)
+
+
+def unpack_activations(buf, rows, cols):
+    """Row-major [rows, cols] from a tile-packed activation buffer (rows in groups
+    of 16, each group's columns in 64-wide 2 KB tiles in matrix-core operand
+    order; the layout the library's header states for its trace hook)."""
+    r = np.arange(rows)[:, None]
+    c = np.arange(cols)[None, :]
+    idx = (((r >> 4) * (cols >> 6) + (c >> 6)) * 1024 + ((c >> 5) & 1) * 512 + ((r & 15) + 16 * ((c >> 3) & 3)) * 8
+           + (c & 7))
+    return np.asarray(buf).reshape(-1)[idx]
+
+
+def draft_trace(D, cfg, batch, n_new_max, ws, dtype):
+    """The last layer's residual stream [B*S, H] (fp32), MLP input [B*S, H] and
+    gated product [B*S, F] (storage dtype) that dflash_draft_step left in ws."""
+    off, packed = D.draft_trace_layout(cfg, batch, n_new_max)
+    M, H, F = batch * cfg.block, cfg.hidden, cfg.mlp_dim
+    es = 2 if dtype == "bf16" else 4
+    host = down(ws).view(np.uint8)
+
+    def grab(k, cols, kind):
+        rows = (M + 15) // 16 * 16 if packed[k] else M
+        raw = host[off[k]:off[k] + rows * cols * (4 if kind == "f32" else es)]
+        arr = raw.view(np.float32 if kind == "f32" or es == 4 else np.uint16)
+        if packed[k]:
+            return unpack_activations(arr, M, cols)
+        return arr.reshape(M, cols)
+
+    return grab(0, H, "f32"), grab(1, H, dtype), grab(2, F, dtype)

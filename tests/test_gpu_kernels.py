@@ -142,6 +142,10 @@ def test_gemm_f32(D):
     ("bf16", 2, 8, 8, 2, 128, 2112, [2100, 1031], 100),
     ("bf16", 2, 32, 8, 2, 128, 640, [600, 37], 64),
     ("f32", 2, 4, 4, 4, 64, 128, [124, 50], 30),
+    # the full workload shapes: 8 rows x 4096 context keys (4 key chunks per row and
+    # kv head, merged), and 4 rows x 32768 keys (long-context plan: two resident units per CU)
+    ("bf16", 8, 16, 32, 8, 128, 4160, [4096] * 8, 0),
+    ("bf16", 4, 16, 32, 8, 128, 32832, [32768, 32768, 30001, 32768], 0),
 ])
 def test_block_attention_matches_oracle(D, dtype, B, S, nq, nkv, d, max_ctx, ctx, window):
     import torch
@@ -467,3 +471,134 @@ def test_verify_is_lossless_on_gpu_chi_square(D):
         assert stats.chisquare(cnt, pp[i] * cnt.sum()).pvalue > 1e-4
     alpha1 = np.minimum(pp[0], qp[0]).sum()
     assert abs(np.mean(n >= 1) - alpha1) < 4 * np.sqrt(alpha1 * (1 - alpha1) / B)
+
+
+# ---------------------------------------------------------------- verify / sampling edge cases
+
+U_TOP = 1.0 - 2.0 ** -24          # the largest uniform below 1 in fp32
+
+
+def _verify_case(name, B, G, V):
+    """Inputs of one verify edge case: q [B, G, V], p [B, G+1, V] (fp32, -inf where
+    masked), drafts, u_accept, u_final, and which of them are decided by construction."""
+    q = rng.normal(9, f"eq_{name}", (B, G, V), 2.0)
+    p = rng.normal(9, f"ep_{name}", (B, G + 1, V), 2.0)
+    ua = rng.uniform01(9, f"ea_{name}", (B, G))
+    uf = rng.uniform01(9, f"ef_{name}", (B,))
+    ud = rng.uniform01(9, f"ed_{name}", (B, G))
+    drafts = None
+    if name == "disjoint":             # target on even ids in [17, V - 23], draft on odd ids: p(d) = 0,
+        p[:, :, 1::2] = -np.inf        # residual = p, drawn at u_final 0 (first id 18), just below 1, random
+        p[:, :, :17] = -np.inf
+        p[:, :, V - 22:] = -np.inf
+        q[:, :, 0::2] = -np.inf
+        uf[0::4] = 0.0
+        uf[1::4] = U_TOP
+    elif name == "point_mass":         # every target row one finite logit: the emitted token is forced
+        t = rng.integers(9, "ept", (B, G + 1), 0, V)
+        p[:] = -np.inf
+        for b in range(B):
+            for i in range(G + 1):
+                p[b, i, t[b, i]] = 0.5
+        drafts = _drafts_from_q(q, ud, 1.0)
+        drafts[::2, :] = t[::2, :G]    # even rows draft the target's token: accepted (p(d) = 1 >= q(d))
+    elif name == "q_zero":             # drafts where q is -inf and p finite: p/q = +inf, always accepted
+        drafts = rng.integers(9, "eqd", (B, G), 0, V).astype(np.int32)
+        for b in range(B):
+            for i in range(G):
+                q[b, i, drafts[b, i]] = -np.inf
+    elif name == "zero_residual":      # p = q and an out-of-range draft: rejected with no residual mass
+        p[:, :G] = q
+        drafts = _drafts_from_q(q, ud, 1.0)
+        drafts[:, 0] = V + 3
+    elif name == "u_edges":            # u_accept 0: accepted while p/q > 0, so every block is; the
+        ua[:] = 0.0                    # bonus token at u_final 0 (the first token) or just below 1
+        uf[0::2] = 0.0
+        uf[1::2] = U_TOP
+    if drafts is None:
+        drafts = _drafts_from_q(np.where(np.isinf(q), -1e30, q), ud, 1.0)
+    return q, p, np.asarray(drafts, np.int32), ua, uf
+
+
+@pytest.mark.parametrize("name", ["disjoint", "point_mass", "q_zero", "zero_residual", "u_edges"])
+@pytest.mark.parametrize("with_stats", [False, True])
+def test_verify_edge_cases_match_oracle(D, name, with_stats):
+    """-inf-masked logits (disjoint supports, a point-mass target, q(d) = 0 < p(d)),
+    the residual with no mass (falls back to p), and the extreme uniforms.  Draws
+    whose threshold sits exactly at an end of the distribution (u = 0, u just below
+    1) are decided by the inverse-CDF convention itself, not by rounding, so they
+    are compared without the flag exclusion."""
+    import torch
+    B, G, V = 16, 4, 9000
+    say(f"verify edge case {name} stats={with_stats}")
+    q, p, drafts, ua, uf = _verify_case(name, B, G, V)
+    stats = None
+    if with_stats:
+        x = q.astype(np.float64)
+        mx = x.max(-1)
+        stats = np.stack([mx, np.exp(x - mx[..., None]).sum(-1)], -1)
+    out = torch.empty((B, G + 1), dtype=torch.int32, device=DEV)
+    nacc = torch.empty((B,), dtype=torch.int32, device=DEV)
+    D.spec_verify(up(q, "f32"), up(p, "f32"), up(drafts, "i32"), up(ua, "f32"), up(uf, "f32"), 1.0,
+                  up(stats, "f64") if stats is not None else None, out, nacc,
+                  workspace(D.spec_verify_workspace_size(B, G, V)))
+    oout, onacc, margins = oracle.verify(q, p, drafts, ua, uf, 1.0)
+    gout, gnacc = down(out), down(nacc)
+    edge_final = (uf == 0.0) | (uf == np.float32(U_TOP))
+    flagged = 0
+    for b in range(B):
+        reached = list(range(min(onacc[b], G - 1) + 1))
+        tests = [margins[b, i] for i in reached if np.isfinite(margins[b, i])]
+        if not edge_final[b]:
+            tests.append(margins[b, G])
+        if any(m < FLAG for m in tests):                     # a random uniform next to a threshold
+            flagged += 1
+            continue
+        assert gnacc[b] == onacc[b], (name, b, gnacc[b], onacc[b])
+        np.testing.assert_array_equal(gout[b], oout[b])
+    assert flagged <= flag_budget(V, B)
+    # what the construction forces, independently of the oracle
+    if name == "disjoint":
+        assert np.all(gnacc == 0) and np.all(gout[:, 0] % 2 == 0) and np.all(gout[0::4, 0] == 18)
+    elif name == "point_mass":
+        for b in range(B):
+            a = gnacc[b]
+            assert gout[b, a] == int(np.argmax(p[b, a]))
+        assert np.all(gnacc[::2] == G)
+    elif name == "q_zero":
+        assert np.all(gnacc == G)
+    elif name == "zero_residual":
+        assert np.all(gnacc == 0)
+    elif name == "u_edges":
+        assert np.all(gnacc == G) and np.all(gout[0::2, G] == 0)   # p/q > 0 everywhere; u = 0: token 0
+
+
+@pytest.mark.parametrize("T", [1.0, 0.0])
+def test_sampling_masked_logits_and_extreme_uniforms(D, T):
+    """Rank-0 sampling of rows with -inf entries (a one-hot row, a row with only
+    its odd ids finite, an unmasked row) at u = 0 (the first token with mass),
+    u just below 1 (the last one) and ordinary uniforms."""
+    import torch
+    B, G, V = 4, 6, 9000
+    logits = rng.normal(10, "sm", (B, G, V), 3.0)
+    logits[0, :] = -np.inf
+    logits[0, :, 4321] = 1.0                                  # one-hot rows
+    logits[1, :, 0::2] = -np.inf                              # odd ids only
+    u = rng.uniform01(10, "smu", (B, G))
+    u[:, 0] = 0.0
+    u[:, 1] = U_TOP
+    tok = torch.empty((B, G), dtype=torch.int32, device=DEV)
+    ws = workspace(D.markov_bias_sample_workspace_size(B, G, V))
+    D.markov_bias_sample(up(logits, "f32"), None, None, up(np.zeros(B, np.int32), "i32"), up(u, "f32"), T, tok,
+                         None, ws)
+    got = down(tok)
+    for b in range(B):
+        for i in range(G):
+            k, m = oracle.sample_row(logits[b, i], u[b, i], T)
+            if i >= 2:
+                assert m >= FLAG
+            assert got[b, i] == k, (b, i, got[b, i], k)
+    assert np.all(got[0] == 4321) and np.all(got[1] % 2 == 1)
+    if T > 0:
+        assert got[2, 0] == 0 and got[3, 0] == 0              # u = 0: the first token (all finite)
+        assert got[1, 0] == 1                                 # the first finite id
