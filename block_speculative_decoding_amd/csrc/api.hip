@@ -3,11 +3,37 @@
 #include "../../include/dfspec.h"
 #include "kernels.h"
 
-#include <stdlib.h>
+#include <mutex>
 
 using namespace dfs;
 
 namespace {
+
+// ------------------------------------------------------------------ static scratch
+// The scratch of spec_verify_static: a file-scope device array, one copy per
+// GPU the library runs on, held until the process ends.  Host code reaches it
+// only through the device address that hipGetSymbolAddress returns for the
+// current device (the array's own name is a host-side stand-in); the address
+// of each device is looked up once, on that device's first call.
+constexpr size_t kStaticScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) char scratch[kStaticScratchBytes];
+constexpr int kMaxDevices = 64;
+void* g_scratch_dev[kMaxDevices];
+std::mutex g_scratch_mu;
+
+int static_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return DFS_EHIP;
+  if (dev >= kMaxDevices) return DFS_EUNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return DFS_EHIP;
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return DFS_OK;
+}
 
 #define DFS_TRY(expr)                          \
   do {                                         \
@@ -665,18 +691,23 @@ size_t spec_verify_workspace_size(int32_t batch, int32_t n_draft, int32_t vocab)
   return verify_carve(batch, n_draft, vocab, nullptr, nullptr);
 }
 
-int spec_verify(int32_t batch, int32_t n_draft, int32_t vocab, const float* draft_logits,
-                const float* target_logits, const int32_t* draft_tokens, const float* u_accept,
-                const float* u_final, float temperature, const double* draft_row_stats, const int32_t* n_verify,
-                int32_t* out_tokens, int32_t* n_accepted, void* workspace, size_t workspace_bytes, void* stream) {
+static int verify_check(int32_t batch, int32_t n_draft, int32_t vocab, const float* draft_logits,
+                        const float* target_logits, const int32_t* draft_tokens, const float* u_accept,
+                        const float* u_final, float temperature, int32_t* out_tokens, int32_t* n_accepted) {
   if (batch < 1 || n_draft < 1 || vocab < 1 || !draft_logits || !target_logits || !draft_tokens || !u_accept ||
-      !u_final || !out_tokens || !n_accepted || !workspace)
+      !u_final || !out_tokens || !n_accepted)
     return DFS_EINVAL;
   if (vocab > kMaxVocab || n_draft > 64) return DFS_EUNSUPPORTED;   // one decide slot per position
   // the statistics pass runs one workgroup per (row, chunk) of the target and draft rows
   if ((size_t)batch * (2 * n_draft + 1) * ceil_div(vocab, kChunk) > 0x7fffffffu) return DFS_EUNSUPPORTED;
   if (!(temperature >= 0.f)) return DFS_EINVAL;
-  if (workspace_bytes < spec_verify_workspace_size(batch, n_draft, vocab)) return DFS_EWORKSPACE;
+  return DFS_OK;
+}
+
+static int verify_run(int32_t batch, int32_t n_draft, int32_t vocab, const float* draft_logits,
+                      const float* target_logits, const int32_t* draft_tokens, const float* u_accept,
+                      const float* u_final, float temperature, const double* draft_row_stats, const int32_t* n_verify,
+                      int32_t* out_tokens, int32_t* n_accepted, void* workspace, void* stream) {
   VerifyArgs a;
   verify_carve(batch, n_draft, vocab, workspace, &a);
   a.q = draft_logits;
@@ -694,6 +725,34 @@ int spec_verify(int32_t batch, int32_t n_draft, int32_t vocab, const float* draf
   a.V = vocab;
   DFS_TRY(launch_verify(a, (hipStream_t)stream));
   return DFS_OK;
+}
+
+int spec_verify(int32_t batch, int32_t n_draft, int32_t vocab, const float* draft_logits,
+                const float* target_logits, const int32_t* draft_tokens, const float* u_accept,
+                const float* u_final, float temperature, const double* draft_row_stats, const int32_t* n_verify,
+                int32_t* out_tokens, int32_t* n_accepted, void* workspace, size_t workspace_bytes, void* stream) {
+  const int st = verify_check(batch, n_draft, vocab, draft_logits, target_logits, draft_tokens, u_accept, u_final,
+                              temperature, out_tokens, n_accepted);
+  if (st != DFS_OK) return st;
+  if (!workspace) return DFS_EINVAL;
+  if (workspace_bytes < spec_verify_workspace_size(batch, n_draft, vocab)) return DFS_EWORKSPACE;
+  return verify_run(batch, n_draft, vocab, draft_logits, target_logits, draft_tokens, u_accept, u_final, temperature,
+                    draft_row_stats, n_verify, out_tokens, n_accepted, workspace, stream);
+}
+
+int spec_verify_static(int32_t batch, int32_t n_draft, int32_t vocab, const float* draft_logits,
+                       const float* target_logits, const int32_t* draft_tokens, const float* u_accept,
+                       const float* u_final, float temperature, const double* draft_row_stats,
+                       const int32_t* n_verify, int32_t* out_tokens, int32_t* n_accepted, void* stream) {
+  const int st = verify_check(batch, n_draft, vocab, draft_logits, target_logits, draft_tokens, u_accept, u_final,
+                              temperature, out_tokens, n_accepted);
+  if (st != DFS_OK) return st;
+  if (spec_verify_workspace_size(batch, n_draft, vocab) > kStaticScratchBytes) return DFS_EWORKSPACE;
+  void* ws = nullptr;
+  const int sc = static_scratch(&ws);
+  if (sc != DFS_OK) return sc;
+  return verify_run(batch, n_draft, vocab, draft_logits, target_logits, draft_tokens, u_accept, u_final, temperature,
+                    draft_row_stats, n_verify, out_tokens, n_accepted, ws, stream);
 }
 
 // ------------------------------------------------------------------ multi-step loop

@@ -26,7 +26,7 @@ EXPORTS = [
     "dfs_block_attention_workspace_size", "dfs_block_attention",
     "dfs_gemm_workspace_size", "dfs_gemm", "dfs_profile_begin", "dfs_profile_end",
     "dfs_packed_matrix_bytes", "dfs_pack_matrix", "dfs_gemm_swiglu", "spec_cycle_advance", "spec_schedule_verify",
-    "dfs_draft_trace_layout",
+    "dfs_draft_trace_layout", "spec_verify_static",
 ]
 
 
@@ -70,6 +70,7 @@ def _load():
                                            vp, sz, vp]),
         "spec_verify_workspace_size": (sz, [i32, i32, i32]),
         "spec_verify": (ctypes.c_int, [i32, i32, i32, vp, vp, vp, vp, vp, f32, vp, vp, vp, vp, vp, sz, vp]),
+        "spec_verify_static": (ctypes.c_int, [i32, i32, i32, vp, vp, vp, vp, vp, f32, vp, vp, vp, vp, vp]),
         "dfs_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "dfs_block_attention_workspace_size": (sz, [i32, i32, i32, i32, i32, i32, i32]),
         "dfs_block_attention": (ctypes.c_int, [i32, i32, i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp,
@@ -326,6 +327,22 @@ def spec_verify(draft_logits, target_logits, draft_tokens, u_accept, u_final, te
         _ptr(out_tokens, torch.int32, B * (G + 1), "out_tokens"), _ptr(n_accepted, torch.int32, B, "n_accepted"),
         _ptr(workspace, torch.uint8, None, "workspace"), workspace.numel(), _stream(stream))
     _check(st, "spec_verify")
+
+
+def spec_verify_static(draft_logits, target_logits, draft_tokens, u_accept, u_final, temperature: float,
+                       draft_row_stats, out_tokens, n_accepted, stream=None, n_verify=None):
+    """spec_verify on the library's static per-GPU scratch (no workspace, no allocation)."""
+    B, G, V = draft_logits.shape
+    st = LIB.spec_verify_static(
+        B, G, V, _ptr(draft_logits, torch.float32, B * G * V, "draft_logits"),
+        _ptr(target_logits, torch.float32, B * (G + 1) * V, "target_logits"),
+        _ptr(draft_tokens, torch.int32, B * G, "draft_tokens"), _ptr(u_accept, torch.float32, B * G, "u_accept"),
+        _ptr(u_final, torch.float32, B, "u_final"), float(temperature),
+        _ptr(draft_row_stats, torch.float64, B * G * 2, "draft_row_stats") if draft_row_stats is not None else None,
+        _ptr(n_verify, torch.int32, B, "n_verify"),
+        _ptr(out_tokens, torch.int32, B * (G + 1), "out_tokens"), _ptr(n_accepted, torch.int32, B, "n_accepted"),
+        _stream(stream))
+    _check(st, "spec_verify_static")
 
 
 def dfs_block_attention_workspace_size(batch, block, nq, nkv, d, ctx_bound, dtype) -> int:

@@ -37,9 +37,10 @@
  *    including the workspace; the library allocates no device memory, never
  *    synchronises, and enqueues all work on `stream` (a hipStream_t; NULL = the
  *    null stream).  Results are valid once the caller has synchronised with
- *    that stream.  Its one piece of mutable global state is the opt-in timing
- *    hook dfs_profile_begin/end (process-wide, not thread-safe; disarmed by
- *    default, when it costs one flag test per launch).
+ *    that stream.  Its mutable global state is the opt-in timing hook
+ *    dfs_profile_begin/end (process-wide, not thread-safe; disarmed by default,
+ *    when it costs one flag test per launch) and the per-GPU static scratch of
+ *    spec_verify_static (below).
  *  - Return value: DFS_OK (0) or a negative dfs_status.  Every shape, pointer
  *    and size check is done on the host before anything is enqueued; on error
  *    nothing is enqueued and no output is touched.  DFS_EHIP reports a failed
@@ -282,6 +283,23 @@ int spec_verify(int32_t batch, int32_t n_draft, int32_t vocab, const float* draf
                 const float* u_final, float temperature, const double* draft_row_stats,
                 const int32_t* n_verify, int32_t* out_tokens, int32_t* n_accepted, void* workspace,
                 size_t workspace_bytes, void* stream);
+
+/* spec_verify for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * arguments and results as spec_verify without the workspace.  Its scratch is a
+ * static device array of 64 MiB inside the library, one copy per GPU the library
+ * runs on, held until the process ends; the call allocates nothing (no
+ * hipMalloc, hipFree or allocating library routine).  Every call on one GPU
+ * shares that GPU's array, so calls that overlap on one GPU (different streams,
+ * threads or processes sharing the library instance) race and must be ordered by
+ * the caller; nothing in the array needs to start at zero and each call
+ * overwrites what it reads.  DFS_EWORKSPACE when spec_verify_workspace_size()
+ * of the arguments exceeds 64 MiB; otherwise the checks and errors of
+ * spec_verify, plus DFS_EHIP if the array's device address cannot be obtained. */
+int spec_verify_static(int32_t batch, int32_t n_draft, int32_t vocab, const float* draft_logits,
+                       const float* target_logits, const int32_t* draft_tokens, const float* u_accept,
+                       const float* u_final, float temperature, const double* draft_row_stats,
+                       const int32_t* n_verify, int32_t* out_tokens, int32_t* n_accepted, void* stream);
 
 /* ------------------------------------------------------------ multi-step loop */
 
