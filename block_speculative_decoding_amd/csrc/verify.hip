@@ -11,10 +11,11 @@
 //      draft row when the sampler's row statistics are not supplied) the chunk
 //      max and sum exp((x - max)/T), and for the target rows the same sum per
 //      64-token sub-chunk.  The one full read of the target logits.
-//   2. resolve: one 1024-thread workgroup per (batch row, chunk).  Every
+//   2. resolve: 512-thread workgroups, each owning some chunks of one batch
+//      row (one chunk each at small batches, several at large ones).  Every
 //      workgroup of a row first takes the row's accept/reject decisions from
 //      the chunk statistics (the same computation in each, so all agree on the
-//      first rejected position a), then works on its own chunk of the rejected
+//      first rejected position a), then works on its own chunks of the rejected
 //      target and draft rows in fp64: the exact sums of ep = exp((x_p - max)/T)
 //      and eq = exp((x_q - max)/T), and per 64-token sub-chunk the sums of ep
 //      and eq over the tokens where p > q under the statistics pass's
@@ -151,27 +152,25 @@ __global__ __launch_bounds__(256) void stats_kernel(VerifyArgs a, int nch, int p
   }
 }
 
-// Launch 2 (T > 0): one 512-thread workgroup per (batch row b, chunk c);
-// thread t owns tokens c*4096 + 8t .. +7, and each 8 consecutive threads one
-// 64-token sub-chunk.
+// Launch 2 (T > 0): 512-thread workgroups, nblk per batch row b, workgroup k
+// owning chunks k, k + nblk, ...; in chunk c thread t owns tokens c*4096 + 8t ..
+// +7, and each 8 consecutive threads one 64-token sub-chunk.
 constexpr int kResThreads = 512;
 constexpr int kResPer = kChunk / kResThreads;        // 8 tokens per thread
 constexpr int kSubThreads = kSubTok / kResPer;       // threads per sub-chunk
 
-__global__ __launch_bounds__(512) void resolve_kernel(VerifyArgs a, int nch, bool vec) {
+__global__ __launch_bounds__(512) void resolve_kernel(VerifyArgs a, int nch, int nblk, bool vec) {
   __shared__ double4 red4[kResThreads / 64];
   __shared__ int acc_sh[64];
   __shared__ double info_sh[64][4];
   __shared__ int first_sh;
-  const int b = blockIdx.x / nch, c = blockIdx.x % nch, tid = threadIdx.x;
+  const int b = blockIdx.x / nblk, c0 = blockIdx.x % nblk, tid = threadIdx.x;
   const int G = a.G, V = a.V;
   const double invT = 1.0 / a.temperature;
   const int kb = verify_len(a, b);
-  // the chunk at the first position, loaded while the decisions are taken: the
-  // usual rejected position when the draft and target disagree
-  const int e0 = c * kChunk + tid * kResPer;
   float vp[kResPer], vq[kResPer];
-  auto load_chunk = [&](int pos) {
+  auto load_chunk = [&](int pos, int c) {
+    const int e0 = c * kChunk + tid * kResPer;
     const float* pr = a.p + ((size_t)b * (G + 1) + pos) * V;
     const float* qr = a.q + ((size_t)b * G + pos) * V;
     if (vec && e0 + kResPer <= V) {
@@ -189,10 +188,12 @@ __global__ __launch_bounds__(512) void resolve_kernel(VerifyArgs a, int nch, boo
       }
     }
   };
-  if (kb > 0) load_chunk(0);
+  // the first chunk at the first position, loaded while the decisions are
+  // taken: the usual rejected position when the draft and target disagree
+  if (kb > 0) load_chunk(0, c0);
   const int ae = decide_block(a, b, kb, nch, acc_sh, info_sh, &first_sh);
   const bool rejected = ae < kb;
-  if (c == 0) {   // the accepted prefix and the padding; out[ae] is the draw's
+  if (c0 == 0) {   // the accepted prefix and the padding; out[ae] is the draw's
     int32_t* out = a.out_tokens + (size_t)b * (G + 1);
     for (int j = tid; j <= G; j += kResThreads)
       if (j != ae) out[j] = j < ae ? a.drafts[(size_t)b * G + j] : -1;
@@ -207,49 +208,54 @@ __global__ __launch_bounds__(512) void resolve_kernel(VerifyArgs a, int nch, boo
   if (!rejected) return;                               // uniform: the draw reads the statistics only
   const double Mp = info_sh[ae][0], a0 = 1.0 / info_sh[ae][1];
   const double Mq = info_sh[ae][2], b0 = 1.0 / info_sh[ae][3];
-  if (ae != 0) load_chunk(ae);
-  double sp = 0.0, sq = 0.0, P = 0.0, Q = 0.0;
+  if (ae != 0) load_chunk(ae, c0);
+  // this workgroup's chunks c0, c0 + nblk, ... of the rejected rows
+  for (int c = c0; c < nch; c += nblk) {
+    double sp = 0.0, sq = 0.0, P = 0.0, Q = 0.0;
 #pragma unroll
-  for (int e = 0; e < kResPer; ++e) {
-    const double ep = vp[e] == -INFINITY ? 0.0 : exp(((double)vp[e] - Mp) * invT);
-    const double eq = vq[e] == -INFINITY ? 0.0 : exp(((double)vq[e] - Mq) * invT);
-    sp += ep;
-    sq += eq;
-    if (a0 * ep > b0 * eq) {
-      P += ep;
-      Q += eq;
+    for (int e = 0; e < kResPer; ++e) {
+      const double ep = vp[e] == -INFINITY ? 0.0 : exp(((double)vp[e] - Mp) * invT);
+      const double eq = vq[e] == -INFINITY ? 0.0 : exp(((double)vq[e] - Mq) * invT);
+      sp += ep;
+      sq += eq;
+      if (a0 * ep > b0 * eq) {
+        P += ep;
+        Q += eq;
+      }
     }
-  }
-  // sub-chunk sums over the threads of the sub-chunk (fixed order)
+    if (c + nblk < nch) load_chunk(ae, c + nblk);      // the next chunk's loads, during this one's sums
+    // sub-chunk sums over the threads of the sub-chunk (fixed order)
 #pragma unroll
-  for (int o = kSubThreads / 2; o > 0; o >>= 1) {
-    P += __shfl_xor(P, o, 64);
-    Q += __shfl_xor(Q, o, 64);
-  }
-  double2* sub = a.sub + ((size_t)b * nch + c) * kSubPerChunk;
-  if ((tid & (kSubThreads - 1)) == 0) sub[tid / kSubThreads] = make_double2(P, Q);
-  if ((tid & (kSubThreads - 1)) != 0) P = Q = 0.0;    // each sub-chunk counted once below
-  // the four chunk sums in one workgroup reduction (the shuffles of the four
-  // run side by side)
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    sp += __shfl_xor(sp, o, 64);
-    sq += __shfl_xor(sq, o, 64);
-    P += __shfl_xor(P, o, 64);
-    Q += __shfl_xor(Q, o, 64);
-  }
-  if ((tid & 63) == 0) red4[tid >> 6] = make_double4(sp, sq, P, Q);
-  __syncthreads();
-  if (tid == 0) {
-    double4 t = red4[0];
-#pragma unroll
-    for (int w = 1; w < kResThreads / 64; ++w) {
-      t.x += red4[w].x;
-      t.y += red4[w].y;
-      t.z += red4[w].z;
-      t.w += red4[w].w;
+    for (int o = kSubThreads / 2; o > 0; o >>= 1) {
+      P += __shfl_xor(P, o, 64);
+      Q += __shfl_xor(Q, o, 64);
     }
-    *(double4*)(a.res + ((size_t)b * nch + c) * 4) = t;
+    double2* sub = a.sub + ((size_t)b * nch + c) * kSubPerChunk;
+    if ((tid & (kSubThreads - 1)) == 0) sub[tid / kSubThreads] = make_double2(P, Q);
+    if ((tid & (kSubThreads - 1)) != 0) P = Q = 0.0;  // each sub-chunk counted once below
+    // the four chunk sums in one workgroup reduction (the shuffles of the four
+    // run side by side)
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      sp += __shfl_xor(sp, o, 64);
+      sq += __shfl_xor(sq, o, 64);
+      P += __shfl_xor(P, o, 64);
+      Q += __shfl_xor(Q, o, 64);
+    }
+    __syncthreads();                                   // red4 free (previous chunk read)
+    if ((tid & 63) == 0) red4[tid >> 6] = make_double4(sp, sq, P, Q);
+    __syncthreads();
+    if (tid == 0) {
+      double4 t = red4[0];
+#pragma unroll
+      for (int w = 1; w < kResThreads / 64; ++w) {
+        t.x += red4[w].x;
+        t.y += red4[w].y;
+        t.z += red4[w].z;
+        t.w += red4[w].w;
+      }
+      *(double4*)(a.res + ((size_t)b * nch + c) * 4) = t;
+    }
   }
 }
 
@@ -390,7 +396,10 @@ hipError_t launch_verify(const VerifyArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(greedy_kernel, dim3(a.B), dim3(64 * kDecideWaves), 0, s, a, nch);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL(resolve_kernel, dim3((unsigned)((size_t)a.B * nch)), dim3(kResThreads), 0, s, a, nch,
+  // about two resident workgroups per CU: rows with many chunks per workgroup
+  // at large batches (each workgroup repeats its row's decisions once)
+  const int nblk = min(nch, max(1, ceil_div(512, a.B)));
+  hipLaunchKernelGGL(resolve_kernel, dim3((unsigned)((size_t)a.B * nblk)), dim3(kResThreads), 0, s, a, nch, nblk,
                      vec_p && vec_q);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(draw_kernel, dim3(a.B), dim3(64), 0, s, a, nch, vec_p && vec_q);
