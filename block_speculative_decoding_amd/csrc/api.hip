@@ -494,13 +494,16 @@ static hipError_t sample_position(int batch, int n_draft, int vocab, int i, cons
 }
 
 // statistics of every sampled row: per chunk (max, sum) and per 64-token sub-chunk sums
-static size_t sample_carve(int B, int G, int V, void* base, double2** stats, double** sub) {
+static size_t sample_carve(int B, int G, int V, void* base, double2** stats, double** sub,
+                           double2** head_sub = nullptr) {
   Carver cv(base);
   const size_t nch = (size_t)ceil_div(V, kChunk);
   double2* st = cv.take<double2>((size_t)B * G * nch);
   double* sb = cv.take<double>((size_t)B * G * nch * 64);
+  double2* hs = cv.take<double2>((size_t)B * ceil_div(V, 64));   // one position's head statistics
   if (stats) *stats = st;
   if (sub) *sub = sb;
+  if (head_sub) *head_sub = hs;
   return cv.off + 256;
 }
 
@@ -527,7 +530,8 @@ int markov_bias_sample(int32_t batch, int32_t n_draft, int32_t vocab, int32_t ra
   hipStream_t s = (hipStream_t)stream;
   double2* stats;
   double* sub;
-  sample_carve(batch, n_draft, vocab, workspace, &stats, &sub);
+  double2* head_sub;
+  sample_carve(batch, n_draft, vocab, workspace, &stats, &sub, &head_sub);
   const long rowV = (long)n_draft * vocab;
   if (rank == 0) {
     ProfScope ps("sample", s);
@@ -551,6 +555,10 @@ int markov_bias_sample(int32_t batch, int32_t n_draft, int32_t vocab, int32_t ra
   }
   ProfScope ps("markov", s);
   const GemmPlan plan = gemm_plan(batch, vocab, rank, uw_dtype, 1);
+  // rank 256, up to 32 rows, bf16: the product writes the per-64-token statistics
+  // the draw needs (2 launches per position instead of 3)
+  const bool fused = uw_dtype == DFS_BF16 && rank == 256 && batch <= 32 && vocab % 4 == 0 &&
+                     ceil_div(vocab, 64) <= kPickSubMax && ((uintptr_t)logits & 15) == 0;
   for (int i = 0; i < n_draft; ++i) {
     // final_i = base_i + U[prev] . W   (rows gathered by the previous token)
     GemmArgs ga;
@@ -569,6 +577,23 @@ int markov_bias_sample(int32_t batch, int32_t n_draft, int32_t vocab, int32_t ra
     ga.y_split_stride = 0;
     ga.accumulate = 1;
     ga.packed = uw_packed;
+    if (fused) {   // product + per-64-token statistics in one launch, then the draw
+      DFS_TRY(launch_head_gemm_stats(ga, temperature, head_sub, s));
+      PickArgs pa;
+      pa.x = logits + (size_t)i * vocab;
+      pa.row_stride = rowV;
+      pa.rows = batch;
+      pa.V = vocab;
+      pa.temperature = temperature;
+      pa.u = u_draft + i;
+      pa.u_stride = n_draft;
+      pa.tokens = draft_tokens + i;
+      pa.tok_stride = n_draft;
+      pa.row_stats = row_stats ? row_stats + 2 * i : nullptr;
+      pa.rs_stride = 2 * (long)n_draft;
+      DFS_TRY(launch_pick_sub(pa, head_sub, ceil_div(vocab, 64), s));
+      continue;
+    }
     DFS_TRY(launch_gemm(ga, plan, uw_dtype, s));
     DFS_TRY(sample_position(batch, n_draft, vocab, i, logits, u_draft, temperature, draft_tokens, row_stats, stats,
                             sub, s));

@@ -18,6 +18,7 @@ namespace {
 
 constexpr int BK = 64;
 constexpr int LDK = BK + 8;   // padded LDS row (bf16 elements): 144 bytes
+constexpr float kLog2eF = 1.4426950408889634f;
 
 // columns of W: K, or wk when the K columns of X hold K / wk terms that all
 // multiply the same W (GEMM column k uses W column k % wk)
@@ -578,6 +579,112 @@ __global__ __launch_bounds__(256) void gemm_short_bf16(GemmArgs a) {
   }
 }
 
+// The Markov head's per-position product with its sampling statistics in the
+// epilogue (K = 256, M <= 32, one term): final = base + X . W^T written over
+// the base logits, and for every row and 64-column sub-chunk of the output the
+// sub-chunk's max and sum exp2((x - max) * k) (k = log2(e) / T, fp32
+// exponentials summed in fp64), or for T == 0 (max, first column of the max).
+// One workgroup per sub-chunk, one wave per 16-column W row group: each wave
+// issues its whole group (8 KB of W, the base rows) before the X rows are staged
+// in LDS, so a wave makes one memory round trip and the grid (about 60 VGPRs a
+// wave) is resident at once.  The four waves combine the sub-chunk's max, then
+// its sum, through LDS.  The logits are read once and written once; no separate
+// statistics pass re-reads them.  sub[m * nsub + j] = (max, sum | first column).
+template <bool PACKED>
+__global__ __launch_bounds__(256) void head_gemm_stats_bf16(GemmArgs a, float T, double2* sub, int nsub) {
+  constexpr int K = 4 * BK, LDX = K + 8, MT = 2, R = 16 * MT;
+  __shared__ __attribute__((aligned(16))) bf16_t Xs[R * LDX];
+  __shared__ float smax[4][R];
+  __shared__ double ssum[4][R];
+  __shared__ int sfirst[4][R];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, c = lane & 15, g4 = lane >> 4;
+  const int u = blockIdx.x, ng = ceil_div(a.N, 16);
+  const int gw = 4 * u + wave;                           // this wave's W row group
+  const bool live = gw < ng;                             // uniform over the wave
+  const int g = min(gw, ng - 1);                         // past the end: the last group, nothing stored
+  bf16x8 wf[8];
+  {
+    const bf16_t* w = PACKED ? (const bf16_t*)a.seg[0].w + (size_t)g * 4 * kTileElems + lane * 8
+                             : (const bf16_t*)a.seg[0].w + (size_t)min(g * 16 + c, a.N - 1) * K + g4 * 8;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        wf[2 * kt + h] = ldg_bf16x8(w + (PACKED ? (size_t)kt * kTileElems + h * 512 : (size_t)kt * BK + h * 32));
+  }
+  f32x4 acc[MT];
+  const int n = g * 16 + 4 * g4;                         // this lane's 4 columns (N % 4 == 0)
+#pragma unroll
+  for (int i = 0; i < MT; ++i) acc[i] = *(const f32x4*)(a.Y + (size_t)min(i * 16 + c, a.M - 1) * a.ldy + min(n, a.N - 4));
+  // X rows 0 .. R-1 (rows past M repeat row M-1; their results are not stored)
+  for (int ch = tid; ch < R * (K / 8); ch += 256) {
+    const int row = ch / (K / 8), col = (ch % (K / 8)) * 8;
+    const int m = min(row, a.M - 1);
+    *(uint4*)&Xs[row * LDX + col] = ldg16((const bf16_t*)a.X + (size_t)x_row(a, m) * a.ldx + col);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+        acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            wf[2 * kt + h], *(const bf16x8*)&Xs[(i * 16 + c) * LDX + kt * BK + h * 32 + g4 * 8], acc[i], 0, 0, 0);
+  const bool cols = live && n < a.N;                     // lane (c, g4) holds row 16 i + c, columns n .. n+3
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+    if (cols && i * 16 + c < a.M) *(f32x4*)(a.Y + (size_t)(i * 16 + c) * a.ldy + n) = acc[i];
+  // the sub-chunk's max: over the 4 lanes g4 of a row, then over the 4 waves
+#pragma unroll
+  for (int i = 0; i < MT; ++i) {
+    float mx = -INFINITY;
+    if (cols)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) mx = fmaxf(mx, acc[i][e]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    if (g4 == 0) smax[wave][i * 16 + c] = mx;
+  }
+  __syncthreads();
+  const float kk = T > 0.f ? kLog2eF / T : 0.f;
+#pragma unroll
+  for (int i = 0; i < MT; ++i) {
+    const int row = i * 16 + c;
+    const float mx = fmaxf(fmaxf(smax[0][row], smax[1][row]), fmaxf(smax[2][row], smax[3][row]));
+    if (T > 0.f) {
+      double sl = 0.0;
+      if (cols && mx != -INFINITY)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sl += (double)exp2f((acc[i][e] - mx) * kk);
+      sl += __shfl_xor(sl, 16, 64);                      // g4 pairs (0,1), (2,3), then the two pairs
+      sl += __shfl_xor(sl, 32, 64);
+      if (g4 == 0) ssum[wave][row] = sl;
+    } else {
+      int first = 0x7fffffff;
+      if (cols)
+#pragma unroll
+        for (int e = 3; e >= 0; --e)
+          if (acc[i][e] == mx) first = n + e;
+      first = min(first, __shfl_xor(first, 16, 64));
+      first = min(first, __shfl_xor(first, 32, 64));
+      if (g4 == 0) sfirst[wave][row] = first;
+    }
+  }
+  __syncthreads();
+  if (tid < R && tid < a.M) {                            // wave 0 writes one row's entry per lane
+    const float mx = fmaxf(fmaxf(smax[0][tid], smax[1][tid]), fmaxf(smax[2][tid], smax[3][tid]));
+    double r;
+    if (T > 0.f) {
+      r = (ssum[0][tid] + ssum[1][tid]) + (ssum[2][tid] + ssum[3][tid]);
+    } else {
+      const int f = min(min(sfirst[0][tid], sfirst[1][tid]), min(sfirst[2][tid], sfirst[3][tid]));
+      r = f == 0x7fffffff ? -1.0 : (double)f;
+    }
+    sub[(size_t)tid * nsub + u] = make_double2((double)mx, r);
+  }
+}
+
 // Small-M GEMM (M <= 16 rows, K <= 512; the Markov head's per-position
 // U[prev] . W product): every wave is independent — it owns 16 W rows, loads
 // all their K at once (8 KB contiguous in the packed layout at K = 256), the
@@ -1076,6 +1183,19 @@ hipError_t launch_gemm(const GemmArgs& a, const GemmPlan& p, int dtype, hipStrea
     return hipErrorInvalidValue;
   }
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_head_gemm_stats(const GemmArgs& a, float temperature, double2* sub, hipStream_t s) {
+  ProfScope ps("gemm", s);
+  const bool ok = !a.gated && a.nseg == 1 && a.K == 4 * BK && a.M >= 1 && a.M <= 32 && a.N % 4 == 0 &&
+                  (a.ldy & 3) == 0 && ((uintptr_t)a.Y & 15) == 0 && !a.x_packed && (a.wk == 0 || a.wk == a.K) &&
+                  a.accumulate;
+  if (!ok) return hipErrorInvalidValue;
+  const int nsub = ceil_div(a.N, 64);
+  const dim3 grid(nsub);
+  if (a.packed) hipLaunchKernelGGL(head_gemm_stats_bf16<true>, grid, dim3(256), 0, s, a, temperature, sub, nsub);
+  else hipLaunchKernelGGL(head_gemm_stats_bf16<false>, grid, dim3(256), 0, s, a, temperature, sub, nsub);
+  return hipGetLastError();
 }
 
 size_t packed_matrix_elems(int N, int K) { return (size_t)ceil_div(N, 16) * 16 * K; }

@@ -171,6 +171,15 @@ struct PickArgs {
   long rs_stride;
 };
 hipError_t launch_pick(const PickArgs& a, hipStream_t s);
+// The Markov head's product Y += X . W^T (K = 256, M <= 32, accumulate) with, per
+// row and 64-column sub-chunk, (max, sum exp((x - max)/T)) or for T == 0 (max,
+// first column of the max) in sub [M][ceil(N/64)].
+hipError_t launch_head_gemm_stats(const GemmArgs& a, float temperature, double2* sub, hipStream_t s);
+// One workgroup per row: inverse-CDF draw / argmax from those sub-chunk
+// statistics (subst [rows][nsub], row r at subst + r * nsub, nsub <=
+// kPickSubMax); PickArgs.stats/.sub unused.
+constexpr int kPickSubMax = 4096;                    // V <= 262144 on the fused head path
+hipError_t launch_pick_sub(const PickArgs& a, const double2* subst, int nsub, hipStream_t s);
 
 struct VerifyArgs {
   const float* q;          // draft logits [B][G][V]

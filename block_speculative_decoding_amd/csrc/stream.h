@@ -34,6 +34,8 @@ __device__ __forceinline__ void load_run(const float* row, int V, int e0, bool v
 // j (j = 0..63, relative to the chunk max), the same per-token terms.
 constexpr int kSubTok = 64;                          // tokens per sub-chunk
 constexpr int kSubPerChunk = kChunk / kSubTok;       // 64
+constexpr int kPickSubThreads = 512;                 // one row pick from sub-chunk statistics
+constexpr int kPickSubPer = kPickSubMax / kPickSubThreads;   // sub-chunks per thread
 __device__ __forceinline__ double2 chunk_stat_block(const float* row, int V, int c, bool vec, float T,
                                                     float* redf /*4*/, double* redd /*4*/, double* sub = nullptr) {
   const int tid = threadIdx.x;
@@ -170,8 +172,9 @@ __device__ __forceinline__ int wave_draw(const float* row, int V, const double2*
   return tl < 0 ? -1 : cstar * kChunk + js * kSubTok + tl;
 }
 
-// exclusive prefix sum over the 256 threads of a block (fp64)
-__device__ __forceinline__ double block_exclusive_scan(double v, double* smem /*4*/, double* total) {
+// exclusive prefix sum over the NT threads of a block (fp64)
+template <int NT = 256>
+__device__ __forceinline__ double block_exclusive_scan(double v, double* smem /*NT/64*/, double* total) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   double inc = v;
 #pragma unroll
@@ -182,98 +185,14 @@ __device__ __forceinline__ double block_exclusive_scan(double v, double* smem /*
   __syncthreads();
   if (lane == 63) smem[w] = inc;
   __syncthreads();
-  double off = 0.0;
-  for (int i = 0; i < w; ++i) off += smem[i];
-  *total = smem[0] + smem[1] + smem[2] + smem[3];
+  double off = 0.0, tot = 0.0;
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) {
+    if (i < w) off += smem[i];
+    tot += smem[i];
+  }
+  *total = tot;
   return off + inc - v;
-}
-
-// Inverse-CDF over chunks, by the whole block: chunk c (c < nch) has mass
-// weight(c) >= 0; finds the first chunk whose running mass (chunks in order)
-// exceeds t, else the last chunk with positive mass (rounding), else chunk 0.
-// Returns the chunk and, in *before, the mass of the chunks ahead of it.  One
-// thread per chunk (a thread takes consecutive chunks when nch > 256) and an
-// fp64 block scan, instead of one thread walking every chunk.
-template <typename ChunkWeight>
-__device__ __forceinline__ int select_chunk(int nch, double t, ChunkWeight weight, double* before, double* smem,
-                                            int* smemi) {
-  const int tid = threadIdx.x;
-  const int per = (nch + 255) / 256, c0 = tid * per;
-  double w[4];                                   // per <= 4: nch <= 1024 chunks (V <= 4M)
-  double loc = 0.0;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    w[k] = (k < per && c0 + k < nch) ? weight(c0 + k) : 0.0;
-    loc += w[k];
-  }
-  double total;
-  double run = block_exclusive_scan(loc, smem, &total);
-  int found = 0x7fffffff, last = -1;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    if (found == 0x7fffffff && w[k] > 0.0 && run + w[k] > t) found = c0 + k;
-    if (w[k] > 0.0) last = c0 + k;
-    run += w[k];
-  }
-  __syncthreads();
-  if (tid == 0) {
-    smemi[0] = 0x7fffffff;
-    smemi[1] = -1;
-  }
-  __syncthreads();
-  if (found != 0x7fffffff) atomicMin(&smemi[0], found);
-  if (last >= 0) atomicMax(&smemi[1], last);
-  __syncthreads();
-  const int pick = smemi[0] != 0x7fffffff ? smemi[0] : (smemi[1] >= 0 ? smemi[1] : 0);
-  // the owner of the picked chunk publishes its prefix mass
-  __syncthreads();
-  if (pick >= c0 && pick < c0 + per) {
-    double r = 0.0;
-    for (int k = 0; k < 4; ++k)
-      if (k < per && c0 + k < pick) r += w[k];
-    smem[0] = run - loc + r;   // exclusive prefix of this thread + its chunks before `pick`
-  }
-  __syncthreads();
-  *before = smem[0];
-  __syncthreads();
-  return pick;
-}
-
-// Locate the token of an inverse-CDF draw inside one chunk (pick and verify).
-// weights16(e0, w) fills the unnormalised weights (>= 0, 0 past V) of the 16
-// consecutive elements e0 .. e0+15 a thread owns; `before` is the mass of all
-// earlier chunks and `t` the threshold.  Returns the first element whose running
-// sum exceeds t, else the last element of the chunk with positive weight
-// (rounding), else -1.
-template <typename Weights16>
-__device__ __forceinline__ int chunk_search(int c, int V, double before, double t, Weights16 weights16, double* smem,
-                                            int* smemi) {
-  const int tid = threadIdx.x;
-  const int e0 = c * kChunk + tid * kPer;
-  double w[kPer];
-  weights16(e0, w);
-  double loc = 0.0;
-#pragma unroll
-  for (int e = 0; e < kPer; ++e) loc += w[e];
-  double total;
-  double run = before + block_exclusive_scan(loc, smem, &total);
-  int found = 0x7fffffff, last_pos = -1;
-#pragma unroll
-  for (int e = 0; e < kPer; ++e) {
-    run += w[e];
-    if (found == 0x7fffffff && run > t) found = e0 + e;
-    if (w[e] > 0.0) last_pos = e0 + e;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    smemi[0] = 0x7fffffff;
-    smemi[1] = -1;
-  }
-  __syncthreads();
-  if (found != 0x7fffffff) atomicMin(&smemi[0], found);
-  if (last_pos >= 0) atomicMax(&smemi[1], last_pos);
-  __syncthreads();
-  return smemi[0] != 0x7fffffff ? smemi[0] : smemi[1];
 }
 
 }  // namespace dfs

@@ -245,11 +245,16 @@ def test_parallel_sampling_matches_oracle(D, V, T):
 
 # ---------------------------------------------------------------- Markov head
 
-@pytest.mark.parametrize("dtype,B,G,V,r", [("f32", 2, 3, 1000, 16), ("bf16", 4, 15, 5000, 64),
-                                           ("bf16", 33, 7, 9000, 256)])
-def test_markov_head_matches_oracle(D, dtype, B, G, V, r):
+# rank 256 with up to 32 rows runs the fused product + per-64-token statistics kernel
+# and the draw from those statistics (20 rows, V = 9000: a partial last sub-chunk;
+# T = 0.7 and greedy); 33 rows the separate statistics pass
+@pytest.mark.parametrize("dtype,B,G,V,r,T", [("f32", 2, 3, 1000, 16, 1.0), ("bf16", 4, 15, 5000, 64, 1.0),
+                                             ("bf16", 33, 7, 9000, 256, 1.0), ("bf16", 20, 5, 9000, 256, 1.0),
+                                             ("bf16", 20, 5, 9000, 256, 0.7), ("bf16", 20, 5, 9000, 256, 0.0),
+                                             ("bf16", 3, 4, 9004, 256, 1.0)])
+def test_markov_head_matches_oracle(D, dtype, B, G, V, r, T):
     import torch
-    say(f"markov {dtype} B={B} G={G} V={V} r={r}")
+    say(f"markov {dtype} B={B} G={G} V={V} r={r} T={T}")
     base = rng.normal(5, f"mb{V}", (B, G, V), 1.5)
     U = rng.normal(5, f"mU{V}", (V, r), r ** -0.25, dtype=dtype)
     Wt = rng.normal(5, f"mW{V}", (V, r), r ** -0.25, dtype=dtype)
@@ -259,17 +264,22 @@ def test_markov_head_matches_oracle(D, dtype, B, G, V, r):
     tok = torch.empty((B, G), dtype=torch.int32, device=DEV)
     rs = torch.empty((B, G, 2), dtype=torch.float64, device=DEV)
     ws = workspace(D.markov_bias_sample_workspace_size(B, G, V))
-    D.markov_bias_sample(lt, up(U, dtype), up(Wt, dtype), up(last, "i32"), up(u, "f32"), 1.0, tok, rs, ws)
-    final, otok, margins = oracle.markov_sample(base, U, Wt, dtype, last, u, 1.0)
+    D.markov_bias_sample(lt, up(U, dtype), up(Wt, dtype), up(last, "i32"), up(u, "f32"), T, tok, rs, ws)
+    final, otok, margins = oracle.markov_sample(base, U, Wt, dtype, last, u, T)
     got_tok = down(tok)
     got_final = down(lt)
+    got_rs = down(rs)
     n_cmp, n_flag = compare_sequential_draws(got_tok, otok, margins, "markov tokens")
-    # final logits where both sides used the same previous token
+    # final logits and row statistics where both sides used the same previous token
     for b in range(B):
         for i in range(G):
             if i > 0 and got_tok[b, i - 1] != otok[b, i - 1]:
                 break
             np.testing.assert_allclose(got_final[b, i], final[b, i], atol=1e-4, rtol=0)
+            x = final[b, i].astype(np.float64)
+            np.testing.assert_allclose(got_rs[b, i, 0], x.max(), atol=1e-4)
+            if T > 0:
+                np.testing.assert_allclose(got_rs[b, i, 1], np.exp((x - x.max()) / T).sum(), rtol=1e-4)
     assert n_flag <= flag_budget(V, B * G)
     say(f"  compared {n_cmp} draws, {n_flag} flagged")
 
