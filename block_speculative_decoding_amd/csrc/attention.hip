@@ -21,6 +21,11 @@ namespace dfs {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kNoMax = -1e30f;             // running max before the first key
+
+// 2^x by the hardware exponential (results below 2^-126 flush to zero, which
+// no softmax weight here can notice next to the running max's weight 1)
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 constexpr int kAttnTargetUnits = 256;        // context units per launch: one per CU
 
 __device__ __forceinline__ bf16x8 load8(const bf16_t* p) {
@@ -122,6 +127,14 @@ __global__ __launch_bounds__(256) void attn_bf16_d128(AttnArgs a) {
   };
   auto stage = [&](int st, const uint4* kr, const uint4* vr, int buf) {
     const int k0 = k_begin + st * KS;
+    if (k0 + KS <= k_end) {                              // uniform: every value slot is real
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        *(uint4*)&Ks[buf][kq_slot[i] * kKLd + kq_col[i]] = kr[i];
+        *(uint4*)&Vs[buf][vq_row[i] * kVLd + vq_col[i]] = vr[i];
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       *(uint4*)&Ks[buf][kq_slot[i] * kKLd + kq_col[i]] = kr[i];
@@ -148,7 +161,9 @@ __global__ __launch_bounds__(256) void attn_bf16_d128(AttnArgs a) {
   f32x4 o[8];
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
+  // m_run starts finite (far below any score) so that exp2(score - m_run) needs no
+  // guard for masked (-inf) scores; a unit that saw no key reports -inf below
+  float m_run = kNoMax, l_run = 0.f;
   const float sc = kLog2e * rsqrtf((float)D);
 
   auto compute = [&](int st, int buf) {
@@ -193,7 +208,7 @@ __global__ __launch_bounds__(256) void attn_bf16_d128(AttnArgs a) {
     // by more than 2^8 (weights stay <= 256, exact in the fp32/bf16 range), so
     // the O rescale below is skipped by the whole wave on most steps.
     const bool grow = mx > m_run + 8.f;
-    const float alpha = grow ? exp2f(m_run - mx) : 1.f;   // m_run = -inf -> 0
+    const float alpha = grow ? fast_exp2(m_run - mx) : 1.f;   // first key: 2^(kNoMax - mx) = 0
     if (grow) m_run = mx;
     // P enters the P.V product as two bf16 parts, hi = bf16(p) and lo = bf16(p - hi):
     // a single bf16 P (8 significant bits) costs ~1 bf16 ulp on every output element
@@ -201,7 +216,7 @@ __global__ __launch_bounds__(256) void attn_bf16_d128(AttnArgs a) {
     bf16x8 pf[2], pl[2];
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      const float p = v[j] > -INFINITY ? exp2f(v[j] - m_run) : 0.f;
+      const float p = fast_exp2(v[j] - m_run);           // masked: 2^-inf = 0
       const __bf16 hi = (__bf16)p;
       pf[j >> 3][j & 7] = hi;
       pl[j >> 3][j & 7] = (__bf16)(p - (float)hi);
@@ -281,7 +296,7 @@ __global__ __launch_bounds__(256) void attn_bf16_d128(AttnArgs a) {
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) *(f32x4*)(po + dt * 16 + 4 * g4) = o[dt];
   if (g4 == 0) {
-    a.part_ml[(ubase + row) * 2 + 0] = m_run;
+    a.part_ml[(ubase + row) * 2 + 0] = l_run > 0.f ? m_run : -INFINITY;
     a.part_ml[(ubase + row) * 2 + 1] = l_run;
   }
 }
