@@ -209,10 +209,12 @@ def profile_group(step, group, K, launches_per_step):
     return n, tot, ms
 
 
-def cpu_baseline(w, step, budget_s=20.0):
-    """The oracle, as it stands, on batch row 0 of the same workload: one drafter
-    call (its append + block), that row's sampling and its verification.  Scaled
-    to a whole step by the batch size."""
+def cpu_baseline(w, step, max_rows=8):
+    """The oracle, as it stands, on one step of the same workload: one drafter call
+    (the append and the block of every sampled batch row in one call), their
+    sampling and their verification, timed once.  Up to `max_rows` batch rows
+    (all 8 at the metric's configuration, so the whole step); for larger batches
+    the first `max_rows` rows, scaled to the batch."""
     import oracle
     from oracle import drafter as od
     try:
@@ -221,36 +223,34 @@ def cpu_baseline(w, step, budget_s=20.0):
     except Exception:
         blas_threads = None
     cores = len(os.sched_getaffinity(0))
+    n = min(w.batch, max_rows)
+    rows = slice(0, n)
     kc, vc = step.np_cache
     st = step.np_step
-    times = []
-    t_end = time.time() + budget_s
-    while not times or (time.time() < t_end and len(times) < 3):
-        ko = kc[:, :1].copy()
-        vo = vc[:, :1].copy()
-        t0 = time.perf_counter()
-        base, _ = od.draft_step(od.DrafterShape.of(w.with_(batch=1)), step.np_weights, st["hidden_new"][:1],
-                                st["n_new"][:1], ko, vo, st["ctx_len"][:1], st["last_token"][:1])
-        ud, ua, uf = (x[:1] for x in inputs.uniforms(w, 0))
-        if w.markov_rank > 0 and step.head == "rnn":
-            U, Wt = inputs.markov_factors(w, 0)
-            final, tok, _, _ = oracle.rnn_sample(base, U, Wt, inputs.rnn_recurrence(w, 0), w.dtype,
-                                                 st["last_token"][:1], ud, w.temperature)
-        elif w.markov_rank > 0:
-            U, Wt = inputs.markov_factors(w, 0)
-            final, tok, _ = oracle.markov_sample(base, U, Wt, w.dtype, st["last_token"][:1], ud, w.temperature)
-        else:
-            final, tok, _ = oracle.markov_sample(base, None, None, w.dtype, st["last_token"][:1], ud,
-                                                 w.temperature)
-        tgt = step.target[:1].cpu().numpy()
-        oracle.verify(final, tgt, tok, ua, uf, w.temperature)
-        times.append(time.perf_counter() - t0)
-    per_row = float(np.median(times))
-    return {"value": 1.0 / (per_row * w.batch), "unit": "steps/s", "cores": blas_threads or cores,
-            "kind": "oracle",
-            "sample": f"batch row 0 of {w.batch} (drafter call incl. its {w.block}-row append, sampling, "
-                      f"verify), median of {len(times)} run(s) of {per_row:.2f} s, scaled x{w.batch}; "
-                      f"{cores} host cores visible"}
+    ko = kc[:, rows].copy()
+    vo = vc[:, rows].copy()
+    ud, ua, uf = (x[rows] for x in inputs.uniforms(w, 0))
+    tgt = step.target[rows].cpu().numpy()
+    if w.markov_rank > 0:
+        U, Wt = inputs.markov_factors(w, 0)
+    t0 = time.perf_counter()
+    base, _ = od.draft_step(od.DrafterShape.of(w.with_(batch=n)), step.np_weights, st["hidden_new"][rows],
+                            st["n_new"][rows], ko, vo, st["ctx_len"][rows], st["last_token"][rows])
+    if w.markov_rank > 0 and step.head == "rnn":
+        final, tok, _, _ = oracle.rnn_sample(base, U, Wt, inputs.rnn_recurrence(w, 0), w.dtype, st["last_token"][rows],
+                                             ud, w.temperature)
+    elif w.markov_rank > 0:
+        final, tok, _ = oracle.markov_sample(base, U, Wt, w.dtype, st["last_token"][rows], ud, w.temperature)
+    else:
+        final, tok, _ = oracle.markov_sample(base, None, None, w.dtype, st["last_token"][rows], ud, w.temperature)
+    oracle.verify(final, tgt, tok, ua, uf, w.temperature)
+    secs = time.perf_counter() - t0
+    whole = n == w.batch
+    return {"value": (n / w.batch) / secs, "unit": "steps/s", "cores": blas_threads or 1, "kind": "oracle",
+            "host_cores_visible": cores, "blas_threads": blas_threads,
+            "sample": (f"one whole step (all {n} batch rows in one oracle call: drafter incl. its {w.block}-row "
+                       f"append, sampling, verify), {secs:.1f} s" if whole else
+                       f"batch rows 0..{n - 1} of {w.batch} in one oracle call ({secs:.1f} s), scaled x{w.batch / n:g}")}
 
 
 # ---------------------------------------------------------------- rocprofv3 summaries
@@ -308,6 +308,93 @@ def summarize_rocprof(d, steps):
         print(f"{'kernel':60s} {'counter':12s} {'dispatches':>10s} {'avg KiB/dispatch':>17s}")
         for (k, c), (n, v) in sorted(agg.items(), key=lambda x: -x[1][1]):
             print(f"{k:60s} {c:12s} {n:10d} {v / n:17.1f}")
+
+
+def _pmc_agg(d):
+    """Per-kernel (dispatches, sum) of each counter in a rocprofv3 --pmc run."""
+    import csv
+    import glob
+    agg = {}
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            k = (_short(r["Kernel_Name"]), r["Counter_Name"])
+            a = agg.setdefault(k, [0, 0.0])
+            a[0] += 1
+            a[1] += float(r["Counter_Value"])
+    return agg
+
+
+def _pmc_avg(d):
+    """Per-kernel average of each counter (per dispatch) in a rocprofv3 --pmc run."""
+    return {k: v / n for k, (n, v) in _pmc_agg(d).items()}
+
+
+def _copy_scales(cal_fetch_dir, cal_write_dir):
+    """Bytes per KiB of FETCH_SIZE and of WRITE_SIZE, from what a plain 1 GiB device
+    copy (bench.py --calibrate-copy) reads on those counters."""
+    copy_bytes = float(1 << 30)
+    f_cal = [v for (k, c), v in _pmc_avg(cal_fetch_dir).items() if "copy" in k.lower() and c == "FETCH_SIZE"]
+    w_cal = [v for (k, c), v in _pmc_avg(cal_write_dir).items() if "copy" in k.lower() and c == "WRITE_SIZE"]
+    return copy_bytes / (max(f_cal) * 1024.0), copy_bytes / (max(w_cal) * 1024.0), max(f_cal), max(w_cal)
+
+
+def record_gemm_traffic(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, workload, commands):
+    """Write the HBM bytes per drafter GEMM launch (all dfs::gemm_* dispatches of a
+    --pmc run, copy-calibrated) with the hash of the GEMM sources, the figure the
+    benchmark reports as roofline.traffic while the sources are unchanged."""
+    f_scale, w_scale, f_cal, w_cal = _copy_scales(cal_fetch_dir, cal_write_dir)
+    fa, wa = _pmc_agg(fetch_dir), _pmc_agg(write_dir)
+    rows, n_all, bytes_all = [], 0, 0.0
+    for (k, c), (n, v) in sorted(fa.items()):
+        if c != "FETCH_SIZE" or not k.startswith("dfs::gemm_"):
+            continue
+        wn, wv = wa.get((k, "WRITE_SIZE"), (n, 0.0))
+        per = (v / n) * 1024.0 * f_scale + (wv / wn) * 1024.0 * w_scale
+        rows.append((k, n, v / n, wv / wn, per))
+        n_all += n
+        bytes_all += n * per
+    w = WORKLOADS[workload]
+    alg = algorithmic_bytes(w)["gemm"] / (4 * w.n_layers + 2)
+    out = [f"HBM traffic of the drafter GEMM launches, {workload} workload ({w.name}), one MI355X.", "",
+           "Commands (run from the repository root on the GPU machine):"] + [f"  {c}" for c in commands] + [
+        "", f"Calibration: a plain 1 GiB device copy reads FETCH_SIZE = {f_cal:.1f} KiB and WRITE_SIZE = {w_cal:.1f} KiB",
+        f"per dispatch, so bytes fetched = {f_scale:.3f} x FETCH_SIZE KiB x 1024 and written = {w_scale:.3f} x WRITE_SIZE.",
+        "", f"  {'kernel':56s} {'dispatches':>10s} {'FETCH KiB':>10s} {'WRITE KiB':>10s} {'bytes/dispatch':>15s}"]
+    out += [f"  {k[:56]:56s} {n:10d} {f:10.1f} {wr:10.1f} {per:15.0f}" for k, n, f, wr, per in rows]
+    out += ["", f"Average HBM bytes per GEMM launch = {bytes_all / n_all:.0f}",
+            f"Algorithmic bytes per launch (weights once + activations in/out) = {alg:.0f}",
+            f"Ratio traffic / algorithmic = {bytes_all / n_all / alg:.3f}", "",
+            f"traffic_bytes_per_launch: {bytes_all / n_all:.0f}", f"source_sha256: {gemm_source_hash()}", "",
+            "(bench.py reports this traffic only while the GEMM sources hash to source_sha256.)"]
+    open(TRAFFIC_FILE, "w").write("\n".join(out) + "\n")
+    print("\n".join(out))
+
+
+def summarize_traffic(stats_dir, fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, steps):
+    """Per-kernel HBM traffic of a workload step: FETCH_SIZE and WRITE_SIZE (KiB per
+    dispatch, from two --pmc runs) scaled by what the same counters read for a plain
+    1 GiB device copy (bench.py --calibrate-copy), against each kernel's average
+    duration from a --kernel-trace --stats run: bytes per dispatch / duration.
+    steps: the steps (timed + warm-up) of the --kernel-trace --stats run, for calls
+    per step."""
+    import csv
+    import glob
+    f_scale, w_scale, f_cal, w_cal = _copy_scales(cal_fetch_dir, cal_write_dir)
+    print(f"calibration: a 1 GiB device copy reads FETCH_SIZE {f_cal:.1f} KiB and WRITE_SIZE {w_cal:.1f} KiB "
+          f"per dispatch -> bytes read = {f_scale:.3f} x FETCH_SIZE KiB x 1024, written = {w_scale:.3f} x WRITE_SIZE")
+    fetch, write = _pmc_avg(fetch_dir), _pmc_avg(write_dir)
+    rows = list(csv.DictReader(open(glob.glob(os.path.join(stats_dir, "**", "*kernel_stats.csv"), recursive=True)[0])))
+    print(f"{'kernel':58s} {'calls/step':>10s} {'avg us':>8s} {'read MB':>9s} {'write MB':>9s} {'GB/s':>8s} {'of 8 TB/s':>9s}")
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        name = _short(r["Name"])
+        n, avg_us = int(r["Calls"]), float(r["AverageNs"]) / 1e3
+        fk, wk = fetch.get((name, "FETCH_SIZE")), write.get((name, "WRITE_SIZE"))
+        if fk is None or wk is None or n / steps < 0.99 or not name.startswith("dfs::"):
+            continue
+        rb, wb = fk * 1024.0 * f_scale, wk * 1024.0 * w_scale
+        gbps = (rb + wb) / (avg_us * 1e-6) / 1e9
+        print(f"{name[:58]:58s} {n / steps:10.2f} {avg_us:8.2f} {rb / 1e6:9.2f} {wb / 1e6:9.2f} {gbps:8.0f} "
+              f"{gbps / HBM_PEAK_GBPS:9.3f}")
 
 
 def sweeps(steps, warmup):
@@ -509,9 +596,28 @@ def main():
                     help="sequential head of workloads that have one (rnn: the optional RNN head)")
     ap.add_argument("--summarize-rocprof", metavar="DIR",
                     help="print the kernel table / counter averages of a rocprofv3 output directory and exit")
+    ap.add_argument("--record-gemm-traffic", nargs=4, metavar=("FETCH", "WRITE", "CAL_FETCH", "CAL_WRITE"),
+                    help="write the GEMM launches' HBM bytes per launch (copy-calibrated FETCH/WRITE_SIZE runs of "
+                         "--workload) with the GEMM sources' hash to the profiles record, and exit")
+    ap.add_argument("--summarize-traffic", nargs=5, metavar=("STATS", "FETCH", "WRITE", "CAL_FETCH", "CAL_WRITE"),
+                    help="per-kernel HBM traffic (copy-calibrated FETCH/WRITE_SIZE) against kernel durations, and exit")
     args = ap.parse_args()
     if args.summarize_rocprof:
         summarize_rocprof(args.summarize_rocprof, args.steps + args.warmup)
+        return
+    if args.summarize_traffic:
+        summarize_traffic(*args.summarize_traffic, args.steps + args.warmup)
+        return
+    if args.record_gemm_traffic:
+        fd, wd, cf, cw = args.record_gemm_traffic
+        run = f"--workload {args.workload} --steps {args.steps} --warmup {args.warmup} --no-cpu-baseline --no-roofline"
+        record_gemm_traffic(fd, wd, cf, cw, args.workload, [
+            f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {fd} -o p -- python bench.py {run}",
+            f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {wd} -o p -- python bench.py {run}",
+            f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {cf} -o p -- python bench.py --calibrate-copy",
+            f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {cw} -o p -- python bench.py --calibrate-copy",
+            f"python bench.py --record-gemm-traffic {fd} {wd} {cf} {cw} --workload {args.workload} "
+            f"--steps {args.steps} --warmup {args.warmup}"])
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark measures one GPU only; --gpus must be 1"}))
@@ -553,18 +659,20 @@ def main():
     }
     if not args.no_roofline:
         L = w.n_layers
-        # GEMM launches of one step: fc, 4 per layer, LM head, and with a Markov head
-        # one per drafted position (its GEMMs run through the same launcher)
+        # GEMM launches of one step: fc, 4 per layer, LM head; a sequential head whose
+        # product runs through the plain GEMM launcher adds one per drafted position
+        # (the fused rank-256 Markov product is timed with the head instead)
         per_step = 4 * L + 2 + (w.gamma if w.markov_rank > 0 else 0)
         n, tot, ms_p = profile_group(step, "gemm", args.steps, per_step)
         per_launch_ms = tot / max(n, 1)
         launches_per_step = n / args.steps
-        step_bytes_g = ab["gemm"] + ab["markov_gemm"]
-        step_flops_g = ab["gemm_flops"] + ab["markov_flops"]
+        head_in_group = launches_per_step > 4 * L + 2 + 0.5
+        step_bytes_g = ab["gemm"] + (ab["markov_gemm"] if head_in_group else 0)
+        step_flops_g = ab["gemm_flops"] + (ab["markov_flops"] if head_in_group else 0)
         bytes_per_launch = step_bytes_g / launches_per_step
         flops_per_launch = step_flops_g / launches_per_step
         kernel = "drafter GEMM launches (gemm_stream_bf16" + (", gemm_tile_bf16" if w.batch * w.block > 256 else "") \
-            + (", Markov-head GEMMs" if w.markov_rank > 0 else "") + ")"
+            + (", Markov-head GEMMs" if head_in_group else "") + ")"
         ach = achievable_peaks(step.torch)
         if w.batch * w.block > 256 and w.dtype == "bf16":
             # M > 256: the drafter GEMMs are bound by the matrix cores

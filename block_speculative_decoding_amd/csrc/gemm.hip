@@ -1186,7 +1186,6 @@ hipError_t launch_gemm(const GemmArgs& a, const GemmPlan& p, int dtype, hipStrea
 }
 
 hipError_t launch_head_gemm_stats(const GemmArgs& a, float temperature, double2* sub, hipStream_t s) {
-  ProfScope ps("gemm", s);
   const bool ok = !a.gated && a.nseg == 1 && a.K == 4 * BK && a.M >= 1 && a.M <= 32 && a.N % 4 == 0 &&
                   (a.ldy & 3) == 0 && ((uintptr_t)a.Y & 15) == 0 && !a.x_packed && (a.wk == 0 || a.wk == a.K) &&
                   a.accumulate;
