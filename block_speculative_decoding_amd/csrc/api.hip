@@ -555,9 +555,9 @@ int markov_bias_sample(int32_t batch, int32_t n_draft, int32_t vocab, int32_t ra
   }
   ProfScope ps("markov", s);
   const GemmPlan plan = gemm_plan(batch, vocab, rank, uw_dtype, 1);
-  // rank 256, up to 32 rows, bf16: the product writes the per-64-token statistics
+  // rank 256, up to 128 rows, bf16: the product writes the per-64-token statistics
   // the draw needs (2 launches per position instead of 3)
-  const bool fused = uw_dtype == DFS_BF16 && rank == 256 && batch <= 32 && vocab % 4 == 0 &&
+  const bool fused = uw_dtype == DFS_BF16 && rank == 256 && batch <= 128 && vocab % 4 == 0 &&
                      ceil_div(vocab, 64) <= kPickSubMax && ((uintptr_t)logits & 15) == 0;
   for (int i = 0; i < n_draft; ++i) {
     // final_i = base_i + U[prev] . W   (rows gathered by the previous token)

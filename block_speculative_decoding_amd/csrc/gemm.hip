@@ -580,25 +580,30 @@ __global__ __launch_bounds__(256) void gemm_short_bf16(GemmArgs a) {
 }
 
 // The Markov head's per-position product with its sampling statistics in the
-// epilogue (K = 256, M <= 32, one term): final = base + X . W^T written over
+// epilogue (K = 256, M <= 128, one term): final = base + X . W^T written over
 // the base logits, and for every row and 64-column sub-chunk of the output the
 // sub-chunk's max and sum exp2((x - max) * k) (k = log2(e) / T, fp32
 // exponentials summed in fp64), or for T == 0 (max, first column of the max).
-// One workgroup per sub-chunk, one wave per 16-column W row group: each wave
-// issues its whole group (8 KB of W, the base rows) before the X rows are staged
-// in LDS, so a wave makes one memory round trip and the grid (about 60 VGPRs a
-// wave) is resident at once.  The four waves combine the sub-chunk's max, then
-// its sum, through LDS.  The logits are read once and written once; no separate
-// statistics pass re-reads them.  sub[m * nsub + j] = (max, sum | first column).
+// One workgroup per (sub-chunk, chunk of 32 rows), one wave per 16-column W row
+// group: each wave issues its whole group (8 KB of W, the base rows) before the
+// X rows are staged in LDS, so a wave makes one memory round trip (about 60
+// VGPRs a wave: at 32 rows the whole grid is resident at once).  The four waves
+// combine the sub-chunk's max, then its sum, through LDS.  The logits are read
+// once and written once; no separate statistics pass re-reads them.
+// sub[m * nsub + j] = (max, sum | first column).  The row chunks of a sub-chunk
+// take consecutive logical ids, which the XCD remap puts on one XCD, so its W
+// slab comes from HBM once and from that L2 after.
 template <bool PACKED>
-__global__ __launch_bounds__(256) void head_gemm_stats_bf16(GemmArgs a, float T, double2* sub, int nsub) {
+__global__ __launch_bounds__(256) void head_gemm_stats_bf16(GemmArgs a, float T, double2* sub, int nsub, int nrc) {
   constexpr int K = 4 * BK, LDX = K + 8, MT = 2, R = 16 * MT;
   __shared__ __attribute__((aligned(16))) bf16_t Xs[R * LDX];
   __shared__ float smax[4][R];
   __shared__ double ssum[4][R];
   __shared__ int sfirst[4][R];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, c = lane & 15, g4 = lane >> 4;
-  const int u = blockIdx.x, ng = ceil_div(a.N, 16);
+  const int lid = xcd_logical_id(blockIdx.x, gridDim.x);
+  const int u = lid / nrc, m0 = (lid % nrc) * R, ng = ceil_div(a.N, 16);
+  const int mr = a.M - m0;                               // rows of this chunk: min(mr, R)
   const int gw = 4 * u + wave;                           // this wave's W row group
   const bool live = gw < ng;                             // uniform over the wave
   const int g = min(gw, ng - 1);                         // past the end: the last group, nothing stored
@@ -615,11 +620,12 @@ __global__ __launch_bounds__(256) void head_gemm_stats_bf16(GemmArgs a, float T,
   f32x4 acc[MT];
   const int n = g * 16 + 4 * g4;                         // this lane's 4 columns (N % 4 == 0)
 #pragma unroll
-  for (int i = 0; i < MT; ++i) acc[i] = *(const f32x4*)(a.Y + (size_t)min(i * 16 + c, a.M - 1) * a.ldy + min(n, a.N - 4));
-  // X rows 0 .. R-1 (rows past M repeat row M-1; their results are not stored)
+  for (int i = 0; i < MT; ++i)
+    acc[i] = *(const f32x4*)(a.Y + (size_t)(m0 + min(i * 16 + c, mr - 1)) * a.ldy + min(n, a.N - 4));
+  // X rows m0 .. m0+R-1 (rows past M repeat row M-1; their results are not stored)
   for (int ch = tid; ch < R * (K / 8); ch += 256) {
     const int row = ch / (K / 8), col = (ch % (K / 8)) * 8;
-    const int m = min(row, a.M - 1);
+    const int m = m0 + min(row, mr - 1);
     *(uint4*)&Xs[row * LDX + col] = ldg16((const bf16_t*)a.X + (size_t)x_row(a, m) * a.ldx + col);
   }
   __syncthreads();
@@ -634,7 +640,7 @@ __global__ __launch_bounds__(256) void head_gemm_stats_bf16(GemmArgs a, float T,
   const bool cols = live && n < a.N;                     // lane (c, g4) holds row 16 i + c, columns n .. n+3
 #pragma unroll
   for (int i = 0; i < MT; ++i)
-    if (cols && i * 16 + c < a.M) *(f32x4*)(a.Y + (size_t)(i * 16 + c) * a.ldy + n) = acc[i];
+    if (cols && i * 16 + c < mr) *(f32x4*)(a.Y + (size_t)(m0 + i * 16 + c) * a.ldy + n) = acc[i];
   // the sub-chunk's max: over the 4 lanes g4 of a row, then over the 4 waves
 #pragma unroll
   for (int i = 0; i < MT; ++i) {
@@ -672,7 +678,7 @@ __global__ __launch_bounds__(256) void head_gemm_stats_bf16(GemmArgs a, float T,
     }
   }
   __syncthreads();
-  if (tid < R && tid < a.M) {                            // wave 0 writes one row's entry per lane
+  if (tid < R && tid < mr) {                             // wave 0 writes one row's entry per lane
     const float mx = fmaxf(fmaxf(smax[0][tid], smax[1][tid]), fmaxf(smax[2][tid], smax[3][tid]));
     double r;
     if (T > 0.f) {
@@ -681,7 +687,7 @@ __global__ __launch_bounds__(256) void head_gemm_stats_bf16(GemmArgs a, float T,
       const int f = min(min(sfirst[0][tid], sfirst[1][tid]), min(sfirst[2][tid], sfirst[3][tid]));
       r = f == 0x7fffffff ? -1.0 : (double)f;
     }
-    sub[(size_t)tid * nsub + u] = make_double2((double)mx, r);
+    sub[(size_t)(m0 + tid) * nsub + u] = make_double2((double)mx, r);
   }
 }
 
@@ -1186,14 +1192,14 @@ hipError_t launch_gemm(const GemmArgs& a, const GemmPlan& p, int dtype, hipStrea
 }
 
 hipError_t launch_head_gemm_stats(const GemmArgs& a, float temperature, double2* sub, hipStream_t s) {
-  const bool ok = !a.gated && a.nseg == 1 && a.K == 4 * BK && a.M >= 1 && a.M <= 32 && a.N % 4 == 0 &&
+  const bool ok = !a.gated && a.nseg == 1 && a.K == 4 * BK && a.M >= 1 && a.M <= 128 && a.N % 4 == 0 &&
                   (a.ldy & 3) == 0 && ((uintptr_t)a.Y & 15) == 0 && !a.x_packed && (a.wk == 0 || a.wk == a.K) &&
                   a.accumulate;
   if (!ok) return hipErrorInvalidValue;
-  const int nsub = ceil_div(a.N, 64);
-  const dim3 grid(nsub);
-  if (a.packed) hipLaunchKernelGGL(head_gemm_stats_bf16<true>, grid, dim3(256), 0, s, a, temperature, sub, nsub);
-  else hipLaunchKernelGGL(head_gemm_stats_bf16<false>, grid, dim3(256), 0, s, a, temperature, sub, nsub);
+  const int nsub = ceil_div(a.N, 64), nrc = ceil_div(a.M, 32);
+  const dim3 grid(nsub * nrc);
+  if (a.packed) hipLaunchKernelGGL(head_gemm_stats_bf16<true>, grid, dim3(256), 0, s, a, temperature, sub, nsub, nrc);
+  else hipLaunchKernelGGL(head_gemm_stats_bf16<false>, grid, dim3(256), 0, s, a, temperature, sub, nsub, nrc);
   return hipGetLastError();
 }
 

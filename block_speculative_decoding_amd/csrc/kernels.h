@@ -171,7 +171,7 @@ struct PickArgs {
   long rs_stride;
 };
 hipError_t launch_pick(const PickArgs& a, hipStream_t s);
-// The Markov head's product Y += X . W^T (K = 256, M <= 32, accumulate) with, per
+// The Markov head's product Y += X . W^T (K = 256, M <= 128, accumulate) with, per
 // row and 64-column sub-chunk, (max, sum exp((x - max)/T)) or for T == 0 (max,
 // first column of the max) in sub [M][ceil(N/64)].
 hipError_t launch_head_gemm_stats(const GemmArgs& a, float temperature, double2* sub, hipStream_t s);
