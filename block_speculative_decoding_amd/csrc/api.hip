@@ -306,9 +306,6 @@ int dflash_draft_step(const dfs_drafter_cfg* cfg, const dfs_drafter_weights* wt,
   ma.d = d.d;
   ma.ctx_bound = ctx_bound;
   ma.theta = cfg->rope_theta;
-  DFS_TRY(launch_prep(ma, s));
-  DFS_TRY(launch_embed(dt, wt->embed, last_token, cfg->mask_token_id, d.V, d.H, d.B, d.S, w.resid, w.meta, ctx_len,
-                       s));
 
   int sp;
   size_t pst;
@@ -319,35 +316,41 @@ int dflash_draft_step(const dfs_drafter_cfg* cfg, const dfs_drafter_weights* wt,
   const int xp_mlp = dt == DFS_BF16 && gated.kind == 3;
   const int xp_down = gated.kind > 0 && pack_x(d.Mb, d.H, d.F, dt);
   const int xp_lm = pack_x(d.B * d.G, d.V, d.H, dt, 1);
-  // 1. context features f = RMSNorm(concat(h) . fc^T) -> xs rows [0, Mc)
+  // 1. context features f = RMSNorm(concat(h) . fc^T) -> xs rows [0, Mc); in the
+  //    same launch the block embedding [last, MASK x gamma] with layer 0's
+  //    attention pre-norm, and the positions / rotary table / bookkeeping
+  NormArgs nf;
   if (d.Mc > 0) {
     DFS_TRY(run_gemm(hidden_new, d.nT * d.H, d.Mc, d.H, d.nT * d.H, wt->fc, nullptr, 0, nullptr, 0, w.part, dt, pk, s,
                      &sp, &pst));
-    NormArgs na;
-    na.part = w.part;
-    na.sp = sp;
-    na.part_stride = pst;
-    na.gain = wt->fc_norm;
-    na.out = w.xs;
-    na.out_packed = xp_qkv;
-    na.rows = d.Mc;
-    na.H = d.H;
-    na.eps = cfg->rms_eps;
-    DFS_TRY(launch_norm(na, dt, s));
+    nf.part = w.part;
+    nf.sp = sp;
+    nf.part_stride = pst;
+    nf.gain = wt->fc_norm;
+    nf.out = w.xs;
+    nf.out_packed = xp_qkv;
+    nf.rows = d.Mc;
+    nf.H = d.H;
+    nf.eps = cfg->rms_eps;
   }
   // block rows of xs: rows Mc.. (packed: same buffer, row offset Mc)
   char* xs_blk = xp_qkv ? w.xs : w.xs + (size_t)d.Mc * d.H * es;
-  {  // layer 0 attention pre-norm of the block rows
-    NormArgs na;
-    na.resid = w.resid;
-    na.gain = wt->attn_norm[0];
-    na.out = xs_blk;
-    na.out_packed = xp_qkv;
-    na.out_row0 = xp_qkv ? d.Mc : 0;
-    na.rows = d.Mb;
-    na.H = d.H;
-    na.eps = cfg->rms_eps;
-    DFS_TRY(launch_norm(na, dt, s));
+  {
+    NormArgs nb;
+    nb.resid = w.resid;
+    nb.embed = wt->embed;
+    nb.last_token = last_token;
+    nb.mask_id = cfg->mask_token_id;
+    nb.V = d.V;
+    nb.S = d.S;
+    nb.gain = wt->attn_norm[0];
+    nb.out = xs_blk;
+    nb.out_packed = xp_qkv;
+    nb.out_row0 = xp_qkv ? d.Mc : 0;
+    nb.rows = d.Mb;
+    nb.H = d.H;
+    nb.eps = cfg->rms_eps;
+    DFS_TRY(launch_front(nf, nb, ma, dt, s));
   }
   const int rgs = dt == DFS_BF16 ? ceil_div(d.R, 64) : 1;   // 64-row groups of the R query rows
   const AttnPlan ap = attn_plan(d.B, d.nkv, ctx_bound, dt, rgs, cfg->window);
@@ -376,6 +379,7 @@ int dflash_draft_step(const dfs_drafter_cfg* cfg, const dfs_drafter_weights* wt,
     qa.d = d.d;
     qa.max_ctx = d.max_ctx;
     qa.Rpad = d.Rpad;
+    qa.ctx_len_out = l == 0 ? ctx_len : nullptr;   // every read of the caller's lengths is behind us
     DFS_TRY(launch_qkv_epilogue(qa, dt, s));
     // 3. block attention over [context keys ; block keys]
     AttnArgs aa;

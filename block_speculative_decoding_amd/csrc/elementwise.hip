@@ -15,14 +15,14 @@ namespace {
 //   block row (b, s), s < S            -> position C_b + s,  C_b = ctx_len[b] + n_new[b]
 // Angles pos * theta^(-2i/d) are formed and evaluated in fp64 (positions reach
 // 32K, where an fp32 angle would already be off by ~1e-3 rad), then stored fp32.
-// Block 0 also publishes per-row bookkeeping (clamped) of every batch row, its
-// threads striding over the rows: base, appended rows, C_b.
-__global__ void prep_kernel(MetaArgs a) {
+// Work block 0 also publishes per-row bookkeeping (clamped) of every batch row,
+// its threads striding over the rows: base, appended rows, C_b.
+__device__ __forceinline__ void prep_work(const MetaArgs& a, int blk, int nthr) {
   const int half = a.d / 2;
   const int Mc = a.B * a.n_new_max, Mx = Mc + a.B * a.S;
-  const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (blockIdx.x == 0) {
-    for (int b = threadIdx.x; b < a.B; b += blockDim.x) {
+  const long idx = (long)blk * nthr + threadIdx.x;
+  if (blk == 0) {
+    for (int b = threadIdx.x; b < a.B; b += nthr) {
       const int base = min(max(a.ctx_len[b], 0), a.ctx_bound);
       const int nn = min(max(a.n_new[b], 0), a.n_new_max);
       const int cb = min(base + nn, a.ctx_bound);
@@ -50,49 +50,27 @@ __global__ void prep_kernel(MetaArgs a) {
   a.rope[idx] = make_float2((float)cs, (float)sn);
 }
 
-template <typename T>
-__global__ __launch_bounds__(256) void embed_kernel(const T* E, const int32_t* last_token, int mask_id,
-                                                    int V, int H, int S, float* resid, const int32_t* meta,
-                                                    int32_t* ctx_len, int B) {
-  const int r = blockIdx.x, b = r / S, s = r % S;
-  if (r == 0)
-    for (int i = threadIdx.x; i < B; i += 256) ctx_len[i] = meta[2 * B + i];
-  int tok = s == 0 ? last_token[b] : mask_id;
-  tok = tok < 0 ? 0 : (tok >= V ? V - 1 : tok);
-  const T* e = E + (size_t)tok * H;
-  float* x = resid + (size_t)r * H;
-  if (sizeof(T) == 2 && H % 8 == 0) {
-    for (int h = threadIdx.x * 8; h < H; h += 256 * 8) {
-      const uint4 v = ldg16(e + h);
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-      float f[8];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        f[2 * k] = __uint_as_float(w[k] << 16);
-        f[2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
-      }
-      *(float4*)(x + h) = make_float4(f[0], f[1], f[2], f[3]);
-      *(float4*)(x + h + 4) = make_float4(f[4], f[5], f[6], f[7]);
-    }
-  } else {
-    for (int h = threadIdx.x; h < H; h += 256) x[h] = Elem<T>::load(e, h);
-  }
-}
-
 // RMSNorm of one row per workgroup (1024 threads), fused with the reduction of
 // split-K GEMM partials and the fp32 residual update:
 //   x = (resid or 0) + sum_z part[z]   (partials summed in z order after resid)
 //   resid = x (when update_resid), out = T(x * rsqrt(mean(x^2)+eps) * g)
+// or, for embedding rows, x = E[token] (stored to resid as well).
 // Each thread holds up to two 4-element groups (H <= 8192); vector accesses
 // when H is a multiple of 4.
 constexpr int kNormThreads = 1024;
 template <typename T>
-__global__ __launch_bounds__(1024) void norm_kernel(NormArgs a) {
-  __shared__ float red[kNormThreads / 64];
-  const int r = blockIdx.x, tid = threadIdx.x;
+__device__ __forceinline__ void norm_row(const NormArgs& a, int r, float* red) {
+  const int tid = threadIdx.x;
   const bool vec = (a.H & 3) == 0;
   const size_t row0 = (size_t)r * a.H;
   const bool use_resid = a.resid && (a.update_resid || !a.part);
+  const T* erow = nullptr;
+  if (a.embed) {
+    const int b = r / a.S, s = r % a.S;
+    int tok = s == 0 ? a.last_token[b] : a.mask_id;
+    tok = tok < 0 ? 0 : (tok >= a.V ? a.V - 1 : tok);
+    erow = (const T*)a.embed + (size_t)tok * a.H;
+  }
   float v[2][4];
   float ss = 0.f;
 #pragma unroll
@@ -100,7 +78,26 @@ __global__ __launch_bounds__(1024) void norm_kernel(NormArgs a) {
     const int h = 4 * (tid + i * kNormThreads);
 #pragma unroll
     for (int e = 0; e < 4; ++e) v[i][e] = 0.f;
-    if (h < a.H) {
+    if (h < a.H && erow) {
+      if (vec) {
+        if constexpr (sizeof(T) == 2) {   // 4 bf16: element h in the low half of the first word
+          const uint2 w = *(const uint2*)(erow + h);
+          v[i][0] = __uint_as_float(w.x << 16), v[i][1] = __uint_as_float(w.x & 0xFFFF0000u);
+          v[i][2] = __uint_as_float(w.y << 16), v[i][3] = __uint_as_float(w.y & 0xFFFF0000u);
+        } else {
+          const float4 t = *(const float4*)(erow + h);
+          v[i][0] = t.x, v[i][1] = t.y, v[i][2] = t.z, v[i][3] = t.w;
+        }
+        *(float4*)(a.resid + row0 + h) = make_float4(v[i][0], v[i][1], v[i][2], v[i][3]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (h + e < a.H) {
+            v[i][e] = Elem<T>::load(erow, h + e);
+            a.resid[row0 + h + e] = v[i][e];
+          }
+      }
+    } else if (h < a.H) {
       if (vec) {
         if (use_resid) {
           const float4 t = *(const float4*)(a.resid + row0 + h);
@@ -159,6 +156,25 @@ __global__ __launch_bounds__(1024) void norm_kernel(NormArgs a) {
   }
 }
 
+template <typename T>
+__global__ __launch_bounds__(1024) void norm_kernel(NormArgs a) {
+  __shared__ float red[kNormThreads / 64];
+  norm_row<T>(a, blockIdx.x, red);
+}
+
+// The start of a drafter call: workgroups [0, f.rows) normalise the context
+// features, the next b.rows embed and normalise the block rows, the rest build
+// the positions and rotary table (work block 0: the bookkeeping).  Independent
+// rows, so one launch instead of three.
+template <typename T>
+__global__ __launch_bounds__(1024) void front_kernel(NormArgs f, NormArgs b, MetaArgs m) {
+  __shared__ float red[kNormThreads / 64];
+  const int r = blockIdx.x;
+  if (r < f.rows) norm_row<T>(f, r, red);
+  else if (r < f.rows + b.rows) norm_row<T>(b, r - f.rows, red);
+  else prep_work(m, r - f.rows - b.rows, kNormThreads);
+}
+
 // Q/K/V epilogue: one workgroup per (row, head).  Sums the GEMM's split-K
 // partials, applies the rotary embedding to queries and keys, and scatters:
 //   context row -> K cache slot base+j (KV injection, layout [b][g][slot][d]),
@@ -168,6 +184,8 @@ __global__ __launch_bounds__(1024) void norm_kernel(NormArgs a) {
 template <typename T>
 __global__ __launch_bounds__(64) void qkv_kernel(QkvArgs a) {
   const int row = blockIdx.x, hd = blockIdx.y;
+  if (a.ctx_len_out && row == 0 && hd == 0)
+    for (int b = threadIdx.x; b < a.B; b += 64) a.ctx_len_out[b] = a.meta[2 * a.B + b];
   const int d = a.d, half = d / 2;
   const int Mc = a.B * a.n_new_max;
   const int Nqkv = (a.nq + 2 * a.nkv) * d;
@@ -230,6 +248,8 @@ __global__ __launch_bounds__(256) void qkv_tile_kernel(QkvArgs a) {
   constexpr int D = 128, HALF = 64, TR = 16;
   __shared__ bf16_t vt[D][TR + 2];
   const int tid = threadIdx.x, hd = blockIdx.y;
+  if (a.ctx_len_out && blockIdx.x == 0 && hd == 0)
+    for (int b = tid; b < a.B; b += 256) a.ctx_len_out[b] = a.meta[2 * a.B + b];
   const int ctx_tiles = (a.n_new_max + TR - 1) / TR, blk_tiles = (a.S + TR - 1) / TR;
   const int per_b = ctx_tiles + blk_tiles;
   const int b = blockIdx.x / per_b, tile = blockIdx.x % per_b;
@@ -362,31 +382,24 @@ hipError_t launch_reduce(const float* part, int sp, size_t ps, size_t n, float* 
   return hipGetLastError();
 }
 
-hipError_t launch_prep(const MetaArgs& a, hipStream_t s) {
-  ProfScope ps("elementwise", s);
-  const long n = (long)(a.B * a.n_new_max + a.B * a.S) * (a.d / 2);
-  const int grid = n > 0 ? (int)((n + 255) / 256) : 1;
-  hipLaunchKernelGGL(prep_kernel, dim3(grid), dim3(256), 0, s, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_embed(int dtype, const void* embed, const int32_t* last_token, int mask_id, int V,
-                        int H, int B, int S, float* resid, const int32_t* meta, int32_t* ctx_len, hipStream_t s) {
-  ProfScope ps("elementwise", s);
-  if (dtype == 1)
-    hipLaunchKernelGGL(embed_kernel<bf16_t>, dim3(B * S), dim3(256), 0, s, (const bf16_t*)embed, last_token,
-                       mask_id, V, H, S, resid, meta, ctx_len, B);
-  else
-    hipLaunchKernelGGL(embed_kernel<float>, dim3(B * S), dim3(256), 0, s, (const float*)embed, last_token,
-                       mask_id, V, H, S, resid, meta, ctx_len, B);
-  return hipGetLastError();
-}
-
 hipError_t launch_norm(const NormArgs& a, int dtype, hipStream_t s) {
   if (a.out_packed && (dtype != 1 || a.H % 64)) return hipErrorInvalidValue;
   ProfScope ps("elementwise", s);
   if (dtype == 1) hipLaunchKernelGGL(norm_kernel<bf16_t>, dim3(a.rows), dim3(kNormThreads), 0, s, a);
   else hipLaunchKernelGGL(norm_kernel<float>, dim3(a.rows), dim3(kNormThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_front(const NormArgs& f, const NormArgs& b, const MetaArgs& m, int dtype, hipStream_t s) {
+  if ((f.out_packed && (dtype != 1 || f.H % 64)) || (b.out_packed && (dtype != 1 || b.H % 64)) || !b.embed ||
+      !b.resid || b.part || b.out_mode != 0)
+    return hipErrorInvalidValue;
+  ProfScope ps("elementwise", s);
+  const long n = (long)(m.B * m.n_new_max + m.B * m.S) * (m.d / 2);
+  const int prep = m.rope && n > 0 ? (int)((n + kNormThreads - 1) / kNormThreads) : 1;
+  const dim3 grid(f.rows + b.rows + prep);
+  if (dtype == 1) hipLaunchKernelGGL(front_kernel<bf16_t>, grid, dim3(kNormThreads), 0, s, f, b, m);
+  else hipLaunchKernelGGL(front_kernel<float>, grid, dim3(kNormThreads), 0, s, f, b, m);
   return hipGetLastError();
 }
 

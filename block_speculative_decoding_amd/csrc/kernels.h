@@ -101,12 +101,6 @@ struct MetaArgs {
   int B, S, n_new_max, d, ctx_bound;
   float theta;
 };
-hipError_t launch_prep(const MetaArgs& a, hipStream_t s);
-// also advances ctx_len to meta's C_b
-hipError_t launch_embed(int dtype, const void* embed, const int32_t* last_token, int mask_id,
-                        int V, int H, int B, int S, float* resid, const int32_t* meta, int32_t* ctx_len,
-                        hipStream_t s);
-
 // out[row_map(r)] = T( RMSNorm( in[r] (+= sum_z part[z][r]) ; gain ) )
 struct NormArgs {
   float* resid = nullptr;         // [rows][H] fp32 residual (updated when part != null and update_resid)
@@ -122,8 +116,17 @@ struct NormArgs {
   int S = 1;
   int out_packed = 0;             // bf16: out tile-packed (xpk_index), output row + out_row0 in it
   int out_row0 = 0;
+  // embedding rows (embed != null): row r = b*S + s is E[token], token = last_token[b]
+  // at s == 0 else mask_id (clamped to [0, V)), written to resid, then normalised
+  const void* embed = nullptr;    // [V][H] dtype
+  const int32_t* last_token = nullptr;
+  int mask_id = 0, V = 0;
 };
 hipError_t launch_norm(const NormArgs& a, int dtype, hipStream_t s);
+// The start of a drafter call in one launch: the context features' RMSNorm
+// (feat, rows may be 0), the block rows' embedding and first pre-norm (blk), and
+// the positions, rotary table and per-row bookkeeping (m; meta[2B + b] = C_b).
+hipError_t launch_front(const NormArgs& feat, const NormArgs& blk, const MetaArgs& m, int dtype, hipStream_t s);
 
 struct QkvArgs {
   const float* part;     // [sp][Mx][Nqkv]
@@ -138,6 +141,7 @@ struct QkvArgs {
   void* k_blk;           // [B][nkv][64][d]
   void* v_blk;           // [B][nkv][d][64]
   int B, S, n_new_max, nq, nkv, d, max_ctx, Rpad;
+  int32_t* ctx_len_out = nullptr;   // when set: ctx_len_out[b] = meta C_b (the caller's context lengths advanced)
 };
 hipError_t launch_qkv_epilogue(const QkvArgs& a, int dtype, hipStream_t s);
 
