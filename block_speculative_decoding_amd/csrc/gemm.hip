@@ -594,14 +594,15 @@ __global__ __launch_bounds__(256) void gemm_short_bf16(GemmArgs a) {
 // take consecutive logical ids, which the XCD remap puts on one XCD, so its W
 // slab comes from HBM once and from that L2 after.
 template <bool PACKED>
-__global__ __launch_bounds__(256) void head_gemm_stats_bf16(GemmArgs a, float T, double2* sub, int nsub, int nrc) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8)))
+void head_gemm_stats_bf16(GemmArgs a, float T, double2* sub, int nsub, int nrc) {
   constexpr int K = 4 * BK, LDX = K + 8, MT = 2, R = 16 * MT;
   __shared__ __attribute__((aligned(16))) bf16_t Xs[R * LDX];
   __shared__ float smax[4][R];
   __shared__ double ssum[4][R];
   __shared__ int sfirst[4][R];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, c = lane & 15, g4 = lane >> 4;
-  const int lid = xcd_logical_id(blockIdx.x, gridDim.x);
+  const int lid = nrc > 1 ? xcd_logical_id(blockIdx.x, gridDim.x) : blockIdx.x;
   const int u = lid / nrc, m0 = (lid % nrc) * R, ng = ceil_div(a.N, 16);
   const int mr = a.M - m0;                               // rows of this chunk: min(mr, R)
   const int gw = 4 * u + wave;                           // this wave's W row group
