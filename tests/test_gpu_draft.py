@@ -45,6 +45,13 @@ CASES = {
     # (base, appended count, new length) must still be published
     "tiny_b300_ragged": (TINY.with_(batch=300), 12, [(37 * b) % 125 for b in range(300)],
                          [b % 5 for b in range(300)], 4),
+    # no context rows appended at all (n_new_max = 0: no feature projection; the call
+    # still embeds, normalises and advances nothing)
+    "tiny_no_append": (TINY.with_(batch=2), 13, [50, 20], [0, 0], 0),
+    "medium_no_append": (MEDIUM.with_(batch=2), 14, [300, 9], [0, 0], 0),
+    # a hidden size that is not a multiple of 4: the scalar paths of the embedding
+    # and the RMSNorm rows
+    "tiny_h250": (TINY.with_(batch=2, hidden=250), 15, None, None, None),
 }
 
 
@@ -67,9 +74,10 @@ def run_case(D, w, seed, ctx_len, n_new, nmax, packed=False, gain_std=0.1):
     ctx_dev = up(step["ctx_len"], "i32")
     logits = torch.full((B, G, w.vocab), float("nan"), dtype=torch.float32, device=DEV)
     ctx_bound = int((step["ctx_len"] + step["n_new"]).max())
-    ws = workspace(D.dflash_draft_workspace_size(cfg, B, step["n_new_max"]))
-    D.dflash_draft_step(cfg, wdev, up(step["hidden_new"], w.dtype), up(step["n_new"], "i32"),
-                        step["n_new_max"], ctx_bound, kdev, vdev, ctx_dev, up(step["last_token"], "i32"),
+    lib_nmax = 0 if nmax == 0 else step["n_new_max"]   # the generators keep one (unused) row
+    ws = workspace(D.dflash_draft_workspace_size(cfg, B, lib_nmax))
+    D.dflash_draft_step(cfg, wdev, up(step["hidden_new"], w.dtype) if lib_nmax else None, up(step["n_new"], "i32"),
+                        lib_nmax, ctx_bound, kdev, vdev, ctx_dev, up(step["last_token"], "i32"),
                         logits, ws)
     torch.cuda.synchronize()
     k_log, v_log = D.cache_to_logical(kdev, vdev)

@@ -252,7 +252,8 @@ def test_parallel_sampling_matches_oracle(D, V, T):
 @pytest.mark.parametrize("dtype,B,G,V,r,T", [("f32", 2, 3, 1000, 16, 1.0), ("bf16", 4, 15, 5000, 64, 1.0),
                                              ("bf16", 33, 7, 9000, 256, 1.0), ("bf16", 20, 5, 9000, 256, 1.0),
                                              ("bf16", 20, 5, 9000, 256, 0.7), ("bf16", 20, 5, 9000, 256, 0.0),
-                                             ("bf16", 3, 4, 9004, 256, 1.0), ("bf16", 100, 3, 9000, 256, 0.7),
+                                             ("bf16", 3, 4, 9004, 256, 1.0), ("bf16", 1, 4, 9000, 256, 1.0),
+                                             ("bf16", 100, 3, 9000, 256, 0.7),
                                              ("bf16", 129, 2, 5000, 256, 1.0)])
 def test_markov_head_matches_oracle(D, dtype, B, G, V, r, T):
     import torch
