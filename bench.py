@@ -305,7 +305,7 @@ def summarize_rocprof(d, steps):
             a = agg.setdefault(k, [0, 0.0])
             a[0] += 1
             a[1] += float(r["Counter_Value"])
-        print(f"{'kernel':60s} {'counter':12s} {'dispatches':>10s} {'avg KiB/dispatch':>17s}")
+        print(f"{'kernel':60s} {'counter':12s} {'dispatches':>10s} {'avg/dispatch':>17s}")
         for (k, c), (n, v) in sorted(agg.items(), key=lambda x: -x[1][1]):
             print(f"{k:60s} {c:12s} {n:10d} {v / n:17.1f}")
 
