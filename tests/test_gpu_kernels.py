@@ -247,13 +247,15 @@ def test_parallel_sampling_matches_oracle(D, V, T):
 
 # rank 256 with up to 128 rows runs the fused product + per-64-token statistics kernel
 # (32-row chunks) and the draw from those statistics (20 rows, V = 9000: a partial last
-# sub-chunk; T = 0.7 and greedy; 33 and 100 rows: a ragged last row chunk); 129 rows
-# the product, then the separate statistics pass
+# sub-chunk; T = 0.7 and greedy; 33 and 100 rows: a ragged last row chunk; V = 68 and 4:
+# two sub-chunks, the second of 4 tokens, and a single partial one); 129 rows the
+# product, then the separate statistics pass
 @pytest.mark.parametrize("dtype,B,G,V,r,T", [("f32", 2, 3, 1000, 16, 1.0), ("bf16", 4, 15, 5000, 64, 1.0),
                                              ("bf16", 33, 7, 9000, 256, 1.0), ("bf16", 20, 5, 9000, 256, 1.0),
                                              ("bf16", 20, 5, 9000, 256, 0.7), ("bf16", 20, 5, 9000, 256, 0.0),
                                              ("bf16", 3, 4, 9004, 256, 1.0), ("bf16", 1, 4, 9000, 256, 1.0),
-                                             ("bf16", 100, 3, 9000, 256, 0.7),
+                                             ("bf16", 100, 3, 9000, 256, 0.7), ("bf16", 5, 3, 68, 256, 1.0),
+                                             ("bf16", 2, 2, 4, 256, 0.0),
                                              ("bf16", 129, 2, 5000, 256, 1.0)])
 def test_markov_head_matches_oracle(D, dtype, B, G, V, r, T):
     import torch
