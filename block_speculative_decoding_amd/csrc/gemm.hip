@@ -825,6 +825,7 @@ static const Cand kCands[] = {
     {1, 128, 128, 8, 2}, {1, 128, 64, 8, 1}, {1, 64, 128, 4, 2}, {1, 64, 64, 4, 1},
     {1, 32, 128, 2, 2},  {1, 32, 64, 2, 1},  {1, 256, 64, 16, 1}, {3, 256, 256, 0, 0},
     {1, 128, 96, 8, 2},  {1, 64, 96, 4, 2},   // 3 consumer waves: 96 columns per workgroup
+    {1, 160, 128, 10, 2}, {1, 160, 96, 10, 2},  // 160-row tiles: M in (128, 160] in one M tile
 };
 
 // Cost model, two regimes.
@@ -890,7 +891,7 @@ static void plan_take(GemmPlan& p, const Cand& c, int sp, int kps_blocks) {
   p.splits = sp;
   p.k_per_split = kps_blocks * BK;
   // X prefetched as deep as W where that streaming variant is built (measured a little faster)
-  p.xd = ((c.mt == 8 && c.nw == 2) || (c.mt == 16 && c.nw == 1)) ? 4 : 2;
+  p.xd = ((c.mt >= 8 && c.nw == 2) || (c.mt == 16 && c.nw == 1)) ? 4 : 2;
 }
 
 GemmPlan gemm_plan(int M, int N, int K, int dtype, int force_splits) {
@@ -990,7 +991,7 @@ GemmPlan gemm_plan_gated(int M, int N, int K, int dtype) {
   // with 16 gate + 16 up rows), priced by the same model on the 2N weight rows:
   // 48 features make 256 workgroups of the drafter's 12288 features
   double best = 1e300;
-  for (int mt : {2, 4, 8}) {
+  for (int mt : {2, 4, 8, 10}) {
     if (M > 256 && mt != 8) continue;
     for (int fpt : {48, 64}) {
       const Cand c = {1, 16 * mt, 2 * fpt, mt, 2};
@@ -1000,7 +1001,7 @@ GemmPlan gemm_plan_gated(int M, int N, int K, int dtype) {
         p.mt = mt;
         p.bm = 16 * mt;
         p.bn = fpt;
-        p.xd = mt == 8 ? 4 : 2;
+        p.xd = mt >= 8 ? 4 : 2;
       }
     }
   }
@@ -1101,16 +1102,19 @@ hipError_t launch_gemm(const GemmArgs& a, const GemmPlan& p, int dtype, hipStrea
     DFS_STREAM(4, 1, 4, 2)
     DFS_STREAM(8, 1, 4, 2)
     DFS_STREAM(8, 2, 4, 4)
+    DFS_STREAM(10, 2, 4, 4)
     DFS_STREAM(16, 1, 4, 4)
     // 96 columns per workgroup (3 consumer waves)
     if (!a.gated && p.bn == 96) {
       if (p.mt == 8 && p.nw == 2 && p.pd == 4 && p.xd == 4) return launch_stream<8, 2, 4, 4, 3>(a, g1, kps, mtl, ntl, s);
+      if (p.mt == 10 && p.nw == 2 && p.pd == 4 && p.xd == 4) return launch_stream<10, 2, 4, 4, 3>(a, g1, kps, mtl, ntl, s);
       if (p.mt == 4 && p.nw == 2 && p.pd == 4 && p.xd == 2) return launch_stream<4, 2, 4, 2, 3>(a, g1, kps, mtl, ntl, s);
       return hipErrorInvalidValue;
     }
     // gated tiles of 48 features (3 consumer waves)
     if (a.gated && p.bn == 48) {
       if (p.mt == 8 && p.nw == 2 && p.pd == 4 && p.xd == 4) return launch_stream<8, 2, 4, 4, 3>(a, g1, kps, mtl, ntl, s);
+      if (p.mt == 10 && p.nw == 2 && p.pd == 4 && p.xd == 4) return launch_stream<10, 2, 4, 4, 3>(a, g1, kps, mtl, ntl, s);
       if (p.mt == 4 && p.nw == 2 && p.pd == 4 && p.xd == 2) return launch_stream<4, 2, 4, 2, 3>(a, g1, kps, mtl, ntl, s);
       if (p.mt == 2 && p.nw == 2 && p.pd == 4 && p.xd == 2) return launch_stream<2, 2, 4, 2, 3>(a, g1, kps, mtl, ntl, s);
       return hipErrorInvalidValue;

@@ -29,11 +29,14 @@ def D():
 # ((5, 3001, 512), (1, 64, 64)) runs the independent-wave small-M kernel, ragged N; K = 256 with
 # M <= 128 ((16, 1000, 256), (32, 1000, 256), (120, 300, 256)) the persistent short-K kernel.
 # (100, 6000, 1024 / 2048) get 96-column streaming tiles (3 consumer waves, 64 and 128 rows).
+# M in (128, 160] runs one 160-row M tile: (150, 4096, 4096) with 128 columns and 8 splits
+# (ragged M), forced to 3 splits with 96 columns, and (160, 6000, 2048) with 96 columns.
 @pytest.mark.parametrize("M,N,K,splits", [(1, 64, 64, 0), (120, 300, 256, 0), (120, 300, 256, 3),
                                           (256, 1000, 512, 7), (64, 128, 4096, 0), (130, 4096, 1024, 0),
                                           (640, 8200, 1024, 0), (640, 8200, 1024, 3), (600, 16400, 512, 0),
                                           (32, 1000, 256, 0), (5, 3001, 512, 0), (16, 1000, 256, 0), (17, 129, 192, 0),
-                                          (100, 6000, 1024, 0), (100, 6000, 2048, 0)])
+                                          (100, 6000, 1024, 0), (100, 6000, 2048, 0),
+                                          (150, 4096, 4096, 0), (150, 4096, 4096, 3), (160, 6000, 2048, 0)])
 def test_gemm_bf16_matches_fp64_product(D, M, N, K, splits):
     say(f"gemm bf16 M={M} N={N} K={K} splits={splits}")
     X = rng.normal(1, "gx", (M, K), 1.0, dtype="bf16")
@@ -72,7 +75,8 @@ def test_pack_matrix_layout(D, N, K):
 
 @pytest.mark.parametrize("M,N,K,splits", [(1, 64, 64, 0), (120, 300, 256, 3), (128, 1000, 512, 0),
                                           (256, 1000, 512, 7), (300, 200, 256, 0), (130, 4096, 1024, 0),
-                                          (640, 8200, 1024, 0), (16, 1000, 256, 0), (3, 100, 64, 0), (100, 6000, 2048, 0)])
+                                          (640, 8200, 1024, 0), (16, 1000, 256, 0), (3, 100, 64, 0), (100, 6000, 2048, 0),
+                                          (150, 4096, 4096, 0), (160, 6000, 2048, 0)])
 def test_gemm_packed_weights_bit_identical(D, M, N, K, splits):
     # same operands in the same order: the packed and row-major kernels agree bit for bit
     import torch
@@ -91,9 +95,11 @@ def test_gemm_packed_weights_bit_identical(D, M, N, K, splits):
 
 
 # (48, 1000, 256) and (320, 1536, 512) run the weight-streaming kernel with paired
-# gate/up tiles; (700, 8200, 1024) is planned onto the LDS-ring tile kernel
+# gate/up tiles; (150, 6144, 1024) and (150, 16384, 1024) its 160-row tiles of 48 and
+# 64 features (ragged M); (700, 8200, 1024) is planned onto the LDS-ring tile kernel
 # (ragged M, and F not a multiple of 16).
-@pytest.mark.parametrize("M,F,K", [(48, 1000, 256), (320, 1536, 512), (700, 8200, 1024)])
+@pytest.mark.parametrize("M,F,K", [(48, 1000, 256), (320, 1536, 512), (150, 6144, 1024), (150, 16384, 1024),
+                                   (700, 8200, 1024)])
 def test_gemm_swiglu_matches_fp64(D, M, F, K):
     import torch
     say(f"gemm swiglu M={M} F={F} K={K}")
