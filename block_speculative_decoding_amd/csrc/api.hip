@@ -137,14 +137,14 @@ DraftWs carve_draft(void* base, const DraftDims& d, int dtype) {
   w.k_blk = cv.take<char>((size_t)d.B * d.nkv * 64 * d.d * d.es);
   w.v_blk = cv.take<char>((size_t)d.B * d.nkv * d.d * 64 * d.es);
   size_t part = 0;
-  auto upd = [&](int M, int N, int K) {
+  auto upd = [&](int M, int N, int K, int skip_m = 0, int skip_n = 0) {
     if (M <= 0) return;
-    const GemmPlan p = gemm_plan(M, N, K, dtype);
+    const GemmPlan p = gemm_plan(M, N, K, dtype, 0, skip_m, skip_n);
     const size_t e = gemm_partial_elems(p, M, N);
     if (e > part) part = e;
   };
   upd(d.Mc, d.H, d.nT * d.H);
-  upd(d.Mx, d.Nqkv, d.H);
+  upd(d.Mx, d.Nqkv, d.H, d.Mc, d.nq * d.d);
   upd(d.Mb, d.H, d.nq * d.d);
   upd(d.Mb, 2 * d.F, d.H);
   upd(d.Mb, d.H, d.F);
@@ -159,14 +159,20 @@ DraftWs carve_draft(void* base, const DraftDims& d, int dtype) {
 // Whether the GEMM's X is produced in the tile-packed layout: the LDS-ring tile
 // kernel loads a packed half tile as one contiguous kilobyte per wave instead of
 // gathering 16 row pieces (bf16 activations this library writes itself).
-bool pack_x(int M, int N, int K, int dtype, int force_splits = 0) {
-  return dtype == DFS_BF16 && M > 0 && K % 64 == 0 && gemm_plan(M, N, K, dtype, force_splits).kind == 3;
+bool pack_x(int M, int N, int K, int dtype, int force_splits = 0, int skip_m = 0, int skip_n = 0) {
+  return dtype == DFS_BF16 && M > 0 && K % 64 == 0 &&
+         gemm_plan(M, N, K, dtype, force_splits, skip_m, skip_n).kind == 3;
 }
 
+// skip_m, skip_n: output tiles entirely inside rows [0, skip_m) x columns
+// [0, skip_n) are not computed (GemmArgs.skip_m)
 hipError_t run_gemm(const void* X, int ldx, int M, int N, int K, const void* w0, const void* w1, int n1,
                     const void* w2, int n2, float* Y, int dtype, int packed, hipStream_t s, int* splits_out,
-                    size_t* stride_out, int force_splits = 0, long ldy = 0, int nt_store = 0, int x_packed = 0) {
+                    size_t* stride_out, int force_splits = 0, long ldy = 0, int nt_store = 0, int x_packed = 0,
+                    int skip_m = 0, int skip_n = 0) {
   GemmArgs a;
+  a.skip_m = skip_m;
+  a.skip_n = skip_n;
   a.packed = packed;
   a.nt_store = nt_store;
   a.x_packed = x_packed;
@@ -189,7 +195,7 @@ hipError_t run_gemm(const void* X, int ldx, int M, int N, int K, const void* w0,
     a.seg[2].n0 = n2;
     a.nseg = 3;
   }
-  const GemmPlan p = gemm_plan(M, N, K, dtype, force_splits);
+  const GemmPlan p = gemm_plan(M, N, K, dtype, force_splits, skip_m, skip_n);
   a.Y = Y;
   a.ldy = ldy ? ldy : N;
   a.y_split_stride = (size_t)M * N;
@@ -311,7 +317,9 @@ int dflash_draft_step(const dfs_drafter_cfg* cfg, const dfs_drafter_weights* wt,
   size_t pst;
   // which GEMM inputs are written tile-packed (those read by the LDS-ring tile kernel)
   const GemmPlan gated = gemm_plan_gated(d.Mb, d.F, d.H, dt);
-  const int xp_qkv = pack_x(d.Mx, d.Nqkv, d.H, dt);
+  // no queries are needed for the context rows: the Q|K|V product skips those tiles
+  const int qkv_skip_m = d.Mc, qkv_skip_n = d.nq * d.d;
+  const int xp_qkv = pack_x(d.Mx, d.Nqkv, d.H, dt, 0, qkv_skip_m, qkv_skip_n);
   const int xp_o = pack_x(d.Mb, d.H, d.nq * d.d, dt);
   const int xp_mlp = dt == DFS_BF16 && gated.kind == 3;
   const int xp_down = gated.kind > 0 && pack_x(d.Mb, d.H, d.F, dt);
@@ -358,7 +366,7 @@ int dflash_draft_step(const dfs_drafter_cfg* cfg, const dfs_drafter_weights* wt,
   for (int l = 0; l < d.L; ++l) {
     // 2. Q|K|V of [features ; block rows] in one pass over wq|wk|wv
     DFS_TRY(run_gemm(w.xs, d.H, d.Mx, d.Nqkv, d.H, wt->wq[l], wt->wk[l], d.nq * d.d, wt->wv[l],
-                     (d.nq + d.nkv) * d.d, w.part, dt, pk, s, &sp, &pst, 0, 0, 0, xp_qkv));
+                     (d.nq + d.nkv) * d.d, w.part, dt, pk, s, &sp, &pst, 0, 0, 0, xp_qkv, qkv_skip_m, qkv_skip_n));
     QkvArgs qa;
     qa.part = w.part;
     qa.sp = sp;

@@ -72,6 +72,30 @@ __device__ __forceinline__ int xcd_logical_id(int id, int total) {
   return (id & 7) * (full >> 3) + (id >> 3);
 }
 
+// Tile of a logical workgroup id: M tiles fastest, then N tiles, then K splits,
+// over the computed tiles only.  The corner of the m_lo M tiles below skip_m
+// and the n_lo N tiles left of skip_n is left out: the first n_lo N tiles have
+// M tiles m_lo .. mtiles-1, the rest all mtiles (m_lo = 0 or n_lo = 0: every tile).
+struct TileIdx {
+  int m, n, z;
+};
+__device__ __forceinline__ TileIdx tile_of(int lid, int mtiles, int ntiles, int m_lo, int n_lo) {
+  const int mq = mtiles - m_lo, corner = n_lo * mq;
+  const int per = corner + (ntiles - n_lo) * mtiles;
+  TileIdx t;
+  t.z = lid / per;
+  int r = lid - t.z * per;
+  if (r < corner) {
+    t.n = r / mq;
+    t.m = m_lo + r % mq;
+  } else {
+    r -= corner;
+    t.n = n_lo + r / mtiles;
+    t.m = r % mtiles;
+  }
+  return t;
+}
+
 // GATED (NW = 2): the workgroup covers 64 output features; wave w streams the
 // rows of features n0+16w .. +15 from W_gate (j = 0) and W_up (j = 1), so its
 // epilogue holds gate and up of the same outputs and writes the SwiGLU product.
@@ -95,8 +119,9 @@ void gemm_stream_bf16(GemmArgs a, int k_per_split, int mtiles, int ntiles) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const bool producer = wave >= CW;
   const int lid = xcd_logical_id(blockIdx.x, gridDim.x);
-  const int mtile = lid % mtiles, rest = lid / mtiles;
-  const int n0 = (rest % ntiles) * BN, m0 = mtile * BM, z = rest / ntiles;
+  const TileIdx tix = tile_of(lid, mtiles, ntiles, GATED ? 0 : min(a.skip_m / BM, mtiles),
+                              GATED ? 0 : min(a.skip_n / BN, ntiles));
+  const int n0 = tix.n * BN, m0 = tix.m * BM, z = tix.z;
   const int kbeg = z * k_per_split;
   const int kend = min(a.K, kbeg + k_per_split);
   const int nk = kend > kbeg ? (kend - kbeg) / BK : 0;
@@ -336,9 +361,10 @@ void gemm_tile_bf16(GemmArgs a, int k_per_split, int mtiles, int ntiles) {
   const int wm = wave >> 2, wn = wave & 3;
   const int c = lane & 15, g4 = lane >> 4;
   const int lid = xcd_logical_id(blockIdx.x, gridDim.x);
-  const int mtile = lid % mtiles, rest = lid / mtiles;
-  const int ntile = rest % ntiles, z = rest / ntiles;
-  const int m0 = mtile * BM;
+  const TileIdx tix = tile_of(lid, mtiles, ntiles, GATED ? 0 : min(a.skip_m / BM, mtiles),
+                              GATED ? 0 : min(a.skip_n / BN, ntiles));
+  const int ntile = tix.n, z = tix.z;
+  const int m0 = tix.m * BM;
   const int kbeg = z * k_per_split;
   const int kend = min(a.K, kbeg + k_per_split);
   const int nh = kend > kbeg ? (kend - kbeg) / 32 : 0;  // half steps
@@ -848,25 +874,35 @@ static const Cand kCands[] = {
 // splits fp32 on top.  Fitted to measurements of the drafter shapes at M = 320
 // .. 2048, the cost of a split including its consumer's extra reads (the picks
 // sum to within 1.2 % of the fastest configurations').
-static double plan_cost(const Cand& c, int sp, int M, int N, int K) {
+// With a skipped corner (no queries for the drafter's context rows) the n_lo
+// N tiles left of skip_n hold only the M tiles from m_lo on: fewer tiles, and
+// those weight rows are read by fewer M tiles.
+static double plan_cost(const Cand& c, int sp, int M, int N, int K, int skip_m, int skip_n) {
   const bool big = M > 256;
   const int mt = ceil_div(M, c.bm), nt = ceil_div(N, c.bn);
-  const double wgs = (double)mt * nt * sp;
+  const int m_lo = min(skip_m / c.bm, mt), n_lo = min(skip_n / c.bn, nt);
+  const int mq = mt - m_lo;
+  const double tiles = (double)n_lo * mq + (double)(nt - n_lo) * mt;
+  const double wgs = tiles * sp;
+  // weight rows times the M tiles that read them (the first from HBM, the rest
+  // mostly from L2 at half weight)
+  const double nc = fmin((double)N, (double)n_lo * c.bn);
+  const double wrows = nc * (mq > 0 ? 1.0 + 0.5 * (mq - 1) : 0.0) + (N - nc) * (1.0 + 0.5 * (mt - 1));
   // fp32 output: one slice, or sp slices written and read back by the consumer
   const double part = sp > 1 ? 1.5 * 4.0 * M * N * sp : 4.0 * M * N;
   if (!big) {
     const int kps = ceil_div(K / BK, sp);
     const double pad = (double)(kps % 8 == 0 ? kps : ceil_div(kps, 4) * 4) / kps;
-    const double w = 2.0 * N * K * (1.0 + 0.5 * (mt - 1)) * pad;
-    const double x = 2.0 * (double)mt * c.bm * K * nt * pad;
-    const double flops = 2.0 * (double)mt * c.bm * nt * c.bn * K;
+    const double w = 2.0 * wrows * K * pad;
+    const double x = 2.0 * tiles * c.bm * K * pad;
+    const double flops = 2.0 * tiles * c.bm * c.bn * K;
     const double rounds = ceil(wgs / 256.0);
     const double fill = wgs < 256.0 ? pow(wgs / 256.0, 0.55) : wgs / (rounds * 256.0);
     return fmax((w + 0.5 * x + part) / 8.0e12, flops / 1.2e15) / fill + rounds * 1.5e-6;
   }
-  const double w = 2.0 * N * K * (1.0 + 0.5 * (mt - 1));
-  const double x = 2.0 * (double)mt * c.bm * K * nt;
-  const double flops = 2.0 * (double)mt * c.bm * nt * c.bn * K;
+  const double w = 2.0 * wrows * K;
+  const double x = 2.0 * tiles * c.bm * K;
+  const double flops = 2.0 * tiles * c.bm * c.bn * K;
   const double fill = wgs >= 192.0 ? 1.0 : wgs / 192.0;
   const double mem = (w + 0.5 * x + part) / 8.0e12;
   const double waves = ceil(wgs / 256.0);
@@ -894,7 +930,14 @@ static void plan_take(GemmPlan& p, const Cand& c, int sp, int kps_blocks) {
   p.xd = ((c.mt >= 8 && c.nw == 2) || (c.mt == 16 && c.nw == 1)) ? 4 : 2;
 }
 
-GemmPlan gemm_plan(int M, int N, int K, int dtype, int force_splits) {
+int gemm_tiles(const GemmPlan& p, int M, int N, int skip_m, int skip_n) {
+  const int mt = ceil_div(M, p.bm), nt = ceil_div(N, p.bn);
+  if (p.kind != 1 && p.kind != 3) return mt * nt;
+  const int m_lo = min(skip_m / p.bm, mt), n_lo = min(skip_n / p.bn, nt);
+  return n_lo * (mt - m_lo) + (nt - n_lo) * mt;
+}
+
+GemmPlan gemm_plan(int M, int N, int K, int dtype, int force_splits, int skip_m, int skip_n) {
   GemmPlan best;
   if (dtype != 1) {   // fp32 VALU kernel
     best.kind = 2;
@@ -935,7 +978,7 @@ GemmPlan gemm_plan(int M, int N, int K, int dtype, int force_splits) {
       const int real_sp = ceil_div(kb, kps_blocks);
       if (real_sp != sp) continue;
       if (sp > 1 && kps_blocks < 4 && !force_splits) continue;
-      const double cost = plan_cost(c, sp, M, N, K);
+      const double cost = plan_cost(c, sp, M, N, K, skip_m, skip_n);
       if (cost < best_cost * 0.999) {
         best_cost = cost;
         plan_take(best, c, sp, kps_blocks);
@@ -995,7 +1038,7 @@ GemmPlan gemm_plan_gated(int M, int N, int K, int dtype) {
     if (M > 256 && mt != 8) continue;
     for (int fpt : {48, 64}) {
       const Cand c = {1, 16 * mt, 2 * fpt, mt, 2};
-      const double cost = plan_cost(c, 1, M, 2 * N, K);
+      const double cost = plan_cost(c, 1, M, 2 * N, K, 0, 0);
       if (cost < best * 0.999) {
         best = cost;
         p.mt = mt;
@@ -1008,7 +1051,7 @@ GemmPlan gemm_plan_gated(int M, int N, int K, int dtype) {
   if (M > 256) {
     // both read 2N weight rows; the LDS tile covers 128 features
     const Cand tile = {3, 256, 256, 0, 0};
-    if (plan_cost(tile, 1, M, 2 * N, K) < best) {
+    if (plan_cost(tile, 1, M, 2 * N, K, 0, 0) < best) {
       p.kind = 3;
       p.bm = 256;
       p.bn = 256;
@@ -1092,7 +1135,7 @@ hipError_t launch_gemm(const GemmArgs& a, const GemmPlan& p, int dtype, hipStrea
   const int kps = p.k_per_split;
   if (p.kind == 1) {
     const int mtl = ceil_div(a.M, p.bm), ntl = ceil_div(a.N, p.bn);
-    const dim3 g1(mtl * ntl * p.splits);
+    const dim3 g1(gemm_tiles(p, a.M, a.N, a.gated ? 0 : a.skip_m, a.gated ? 0 : a.skip_n) * p.splits);
 #define DFS_STREAM(MT_, NW_, PD_, XD_)                                                                   \
   if (p.mt == MT_ && p.nw == NW_ && p.pd == PD_ && p.xd == XD_ && p.bn != 48 && p.bn != 96)              \
     return launch_stream<MT_, NW_, PD_, XD_>(a, g1, kps, mtl, ntl, s);
@@ -1189,7 +1232,7 @@ hipError_t launch_gemm(const GemmArgs& a, const GemmPlan& p, int dtype, hipStrea
       return launch_gemm(a, q, dtype, s);
     }
     const int mtl = ceil_div(a.M, p.bm), ntl = ceil_div(a.N, a.gated ? p.bn / 2 : p.bn);
-    const dim3 g1(mtl * ntl * p.splits);
+    const dim3 g1((a.gated ? mtl * ntl : gemm_tiles(p, a.M, a.N, a.skip_m, a.skip_n)) * p.splits);
     if (p.bm == 256 && p.bn == 256) return launch_tile<256, 256>(a, g1, kps, mtl, ntl, s);
     return hipErrorInvalidValue;
   }

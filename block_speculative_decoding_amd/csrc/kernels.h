@@ -38,6 +38,11 @@ struct GemmArgs {
   int wk = 0;
   int x_packed = 0;                   // 1: X in the tile-packed layout (xpk_index; tile kernel only)
   int h_packed = 0;                   // 1: gated output hout written tile-packed (K = N features)
+  // output tiles whose rows all lie below skip_m and whose columns all lie below
+  // skip_n are not computed and their Y is left untouched (the drafter's Q|K|V
+  // product: no queries for the context rows); the weight-streaming and LDS-ring
+  // kernels honour it, the others compute those tiles too
+  int skip_m = 0, skip_n = 0;
 };
 
 struct GemmPlan {
@@ -47,7 +52,9 @@ struct GemmPlan {
   int pd = 4, xd = 2;      // weight-streaming kernel: k steps of W / X in flight per wave
 };
 
-GemmPlan gemm_plan(int M, int N, int K, int dtype, int force_splits = 0);
+GemmPlan gemm_plan(int M, int N, int K, int dtype, int force_splits = 0, int skip_m = 0, int skip_n = 0);
+// output tiles of a plan's grid per K split, the skipped corner (GemmArgs.skip_m/n) left out
+int gemm_tiles(const GemmPlan& p, int M, int N, int skip_m, int skip_n);
 // plan of a single-split GEMM whose X holds K / wk terms against W's wk columns
 GemmPlan gemm_plan_wrapped(int M, int N, int K, int wk, int dtype);
 // plan of a gated gate|up GEMM (N = features), or kind < 0 when no gated kernel fits
