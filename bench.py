@@ -51,7 +51,7 @@ def algorithmic_bytes(w):
     gated = w.dtype == "bf16"
     gateup_out = Mb * F * es if gated else Mb * 2 * F * 4
     gemm_act = (Mc * nT * H * es + Mc * H * 4
-                + L * ((Mc + Mb) * H * es + (Mc + Mb) * (nq + 2 * nkv) * d * 4
+                + L * ((Mc + Mb) * H * es + (Mc * 2 * nkv + Mb * (nq + 2 * nkv)) * d * 4
                        + Mb * nq * d * es + Mb * H * 4 + Mb * H * es + gateup_out
                        + Mb * F * es + Mb * H * 4)
                 + B * G * H * es + B * G * V * 4)
@@ -60,9 +60,11 @@ def algorithmic_bytes(w):
     sample = B * G * V * 4                               # read final logits once
     markov = (V * r * es + B * G * V * 4 * 2) if r > 0 else 0
     verify = B * (G + 1) * V * 4 + 2 * B * V * 4        # target rows + the two rows at the rejection
-    # dense products of the drafter GEMMs (the QKV GEMM runs over context and block rows)
+    # dense products of the drafter GEMMs (the QKV GEMM runs over context and block rows;
+    # the context rows need keys and values only)
     gemm_flops = 2.0 * (Mc * H * nT * H + B * G * V * H
-                        + L * ((Mc + Mb) * (nq + 2 * nkv) * d * H + Mb * H * nq * d + Mb * 2 * F * H + Mb * H * F))
+                        + L * ((Mc * 2 * nkv + Mb * (nq + 2 * nkv)) * d * H + Mb * H * nq * d + Mb * 2 * F * H
+                               + Mb * H * F))
     # the Markov head's per-position GEMM: W once, gathered U rows, logits rows read and written
     markov_gemm = (V * r * es + B * G * r * es + 2 * B * G * V * 4) if r > 0 else 0
     markov_flops = 2.0 * B * G * V * r
