@@ -57,6 +57,55 @@ __device__ __forceinline__ void prep_work(const MetaArgs& a, int blk, int nthr) 
 // or, for embedding rows, x = E[token] (stored to resid as well).
 // Each thread holds up to two 4-element groups (H <= 8192); vector accesses
 // when H is a multiple of 4.
+// v += sum over z of the float4 at p + z * stride, z = 0 .. sp-1 in that order.  The
+// loads go out in batches of 8 (then 4, then 1) before the adds, so a split-K sum
+// costs one memory round trip per batch instead of one per partial.
+__device__ __forceinline__ void add_partials4(const float* p, int sp, size_t stride, float* v) {
+  int z = 0;
+  for (; z + 8 <= sp; z += 8) {
+    float4 t[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) t[j] = *(const float4*)(p + (z + j) * stride);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[0] += t[j].x, v[1] += t[j].y, v[2] += t[j].z, v[3] += t[j].w;
+  }
+  for (; z + 4 <= sp; z += 4) {
+    float4 t[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) t[j] = *(const float4*)(p + (z + j) * stride);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[0] += t[j].x, v[1] += t[j].y, v[2] += t[j].z, v[3] += t[j].w;
+  }
+  for (; z < sp; ++z) {
+    const float4 t = *(const float4*)(p + z * stride);
+    v[0] += t.x, v[1] += t.y, v[2] += t.z, v[3] += t.w;
+  }
+}
+
+// The same for two float4 runs (p into v, q into w) with their loads batched together.
+__device__ __forceinline__ void add_partials4x2(const float* p, const float* q, int sp, size_t stride, float* v,
+                                                float* w) {
+  int z = 0;
+  for (; z + 4 <= sp; z += 4) {
+    float4 t[4], u[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      t[j] = *(const float4*)(p + (z + j) * stride);
+      u[j] = *(const float4*)(q + (z + j) * stride);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[0] += t[j].x, v[1] += t[j].y, v[2] += t[j].z, v[3] += t[j].w;
+      w[0] += u[j].x, w[1] += u[j].y, w[2] += u[j].z, w[3] += u[j].w;
+    }
+  }
+  for (; z < sp; ++z) {
+    const float4 t = *(const float4*)(p + z * stride), u = *(const float4*)(q + z * stride);
+    v[0] += t.x, v[1] += t.y, v[2] += t.z, v[3] += t.w;
+    w[0] += u.x, w[1] += u.y, w[2] += u.z, w[3] += u.w;
+  }
+}
+
 constexpr int kNormThreads = 1024;
 template <typename T>
 __device__ __forceinline__ void norm_row(const NormArgs& a, int r, float* red) {
@@ -103,10 +152,7 @@ __device__ __forceinline__ void norm_row(const NormArgs& a, int r, float* red) {
           const float4 t = *(const float4*)(a.resid + row0 + h);
           v[i][0] = t.x, v[i][1] = t.y, v[i][2] = t.z, v[i][3] = t.w;
         }
-        for (int z = 0; z < (a.part ? a.sp : 0); ++z) {
-          const float4 t = *(const float4*)(a.part + z * a.part_stride + row0 + h);
-          v[i][0] += t.x, v[i][1] += t.y, v[i][2] += t.z, v[i][3] += t.w;
-        }
+        add_partials4(a.part ? a.part + row0 + h : nullptr, a.part ? a.sp : 0, a.part_stride, v[i]);
         if (a.part && a.update_resid) *(float4*)(a.resid + row0 + h) = make_float4(v[i][0], v[i][1], v[i][2], v[i][3]);
       } else {
 #pragma unroll
@@ -271,12 +317,7 @@ __global__ __launch_bounds__(256) void qkv_tile_kernel(QkvArgs a) {
   float x1[4] = {0.f, 0.f, 0.f, 0.f}, x2[4] = {0.f, 0.f, 0.f, 0.f};
   if (valid) {
     const size_t off = (size_t)row * Nqkv + hd * D + i0;
-    for (int z = 0; z < a.sp; ++z) {
-      const float4 u = *(const float4*)(a.part + z * a.part_stride + off);
-      const float4 w = *(const float4*)(a.part + z * a.part_stride + off + HALF);
-      x1[0] += u.x; x1[1] += u.y; x1[2] += u.z; x1[3] += u.w;
-      x2[0] += w.x; x2[1] += w.y; x2[2] += w.z; x2[3] += w.w;
-    }
+    add_partials4x2(a.part + off, a.part + off + HALF, a.sp, a.part_stride, x1, x2);
     if ((is_q || is_k) && a.use_rope) {
       const float4 c01 = *(const float4*)(a.rope + (size_t)row * HALF + i0);
       const float4 c23 = *(const float4*)(a.rope + (size_t)row * HALF + i0 + 2);
