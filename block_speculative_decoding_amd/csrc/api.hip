@@ -903,18 +903,26 @@ size_t dfs_gemm_workspace_size(int32_t M, int32_t N, int32_t K, int32_t dtype, i
 
 int dfs_gemm(int32_t M, int32_t N, int32_t K, int32_t dtype, const void* X, const void* W, float* Y,
              int32_t splits, int32_t w_packed, void* workspace, size_t workspace_bytes, void* stream) {
+  return dfs_gemm_skip(M, N, K, dtype, X, W, Y, splits, w_packed, 0, 0, workspace, workspace_bytes, stream);
+}
+
+int dfs_gemm_skip(int32_t M, int32_t N, int32_t K, int32_t dtype, const void* X, const void* W, float* Y,
+                  int32_t splits, int32_t w_packed, int32_t skip_m, int32_t skip_n, void* workspace,
+                  size_t workspace_bytes, void* stream) {
   if (M < 1 || N < 1 || K < 1 || !X || !W || !Y || splits < 0 || (dtype != DFS_F32 && dtype != DFS_BF16) ||
-      (w_packed != 0 && w_packed != 1))
+      (w_packed != 0 && w_packed != 1) || skip_m < 0 || skip_m > M || skip_n < 0 || skip_n > N)
     return DFS_EINVAL;
+  if ((skip_m > 0 || skip_n > 0) && splits < 1) return DFS_EINVAL;   // the workspace size needs the split count
   if (dtype == DFS_BF16 && K % 64) return DFS_EUNSUPPORTED;
   if (w_packed && dtype != DFS_BF16) return DFS_EUNSUPPORTED;
   if (workspace_bytes < dfs_gemm_workspace_size(M, N, K, dtype, splits) || !workspace) return DFS_EWORKSPACE;
   hipStream_t s = (hipStream_t)stream;
-  const GemmPlan p = gemm_plan(M, N, K, dtype, splits);
+  const GemmPlan p = gemm_plan(M, N, K, dtype, splits, skip_m, skip_n);
   float* target = p.splits > 1 ? (float*)workspace : Y;
   int sp;
   size_t pst;
-  DFS_TRY(run_gemm(X, K, M, N, K, W, nullptr, 0, nullptr, 0, target, dtype, w_packed, s, &sp, &pst, splits));
+  DFS_TRY(run_gemm(X, K, M, N, K, W, nullptr, 0, nullptr, 0, target, dtype, w_packed, s, &sp, &pst, splits, 0, 0, 0,
+                   skip_m, skip_n));
   if (sp > 1) DFS_TRY(launch_reduce(target, sp, pst, (size_t)M * N, Y, s));
   return DFS_OK;
 }

@@ -26,7 +26,7 @@ EXPORTS = [
     "dfs_block_attention_workspace_size", "dfs_block_attention",
     "dfs_gemm_workspace_size", "dfs_gemm", "dfs_profile_begin", "dfs_profile_end",
     "dfs_packed_matrix_bytes", "dfs_pack_matrix", "dfs_gemm_swiglu", "spec_cycle_advance", "spec_schedule_verify",
-    "dfs_draft_trace_layout", "spec_verify_static",
+    "dfs_draft_trace_layout", "spec_verify_static", "dfs_gemm_skip",
 ]
 
 
@@ -77,6 +77,7 @@ def _load():
                                                vp, vp, vp, vp, sz, vp]),
         "dfs_gemm_workspace_size": (sz, [i32, i32, i32, i32, i32]),
         "dfs_gemm": (ctypes.c_int, [i32, i32, i32, i32, vp, vp, vp, i32, i32, vp, sz, vp]),
+        "dfs_gemm_skip": (ctypes.c_int, [i32, i32, i32, i32, vp, vp, vp, i32, i32, i32, i32, vp, sz, vp]),
         "dfs_gemm_swiglu": (ctypes.c_int, [i32, i32, i32, vp, vp, vp, vp, i32, vp]),
         "spec_cycle_advance": (ctypes.c_int, [i32, i32, vp, vp, vp, vp, vp, vp]),
         "spec_schedule_verify": (ctypes.c_int, [i32, i32, vp, i32, ctypes.POINTER(f32), ctypes.POINTER(f32), vp,
@@ -378,6 +379,19 @@ def dfs_gemm(X, W, Y, splits: int, workspace, stream=None, w_packed: bool = Fals
                       _ptr(Y, torch.float32, M * N, "Y"), splits, int(w_packed),
                       _ptr(workspace, torch.uint8, None, "workspace"), workspace.numel(), _stream(stream))
     _check(st, "dfs_gemm")
+
+
+def dfs_gemm_skip(X, W, Y, splits: int, skip_m: int, skip_n: int, workspace, stream=None, w_packed: bool = False):
+    """dfs_gemm whose output tiles inside rows [0, skip_m) x columns [0, skip_n) may be
+    left uncomputed (Y there unspecified); splits >= 1 when a corner is skipped."""
+    M, K = X.shape
+    N = Y.shape[1] if w_packed else W.shape[0]
+    dtype = DFS_BF16 if X.dtype == torch.bfloat16 else DFS_F32
+    wn = packed_matrix_bytes(N, K) // 2 if w_packed else N * K
+    st = LIB.dfs_gemm_skip(M, N, K, dtype, _ptr(X, X.dtype, name="X"), _ptr(W, X.dtype, wn, "W"),
+                           _ptr(Y, torch.float32, M * N, "Y"), splits, int(w_packed), skip_m, skip_n,
+                           _ptr(workspace, torch.uint8, None, "workspace"), workspace.numel(), _stream(stream))
+    _check(st, "dfs_gemm_skip")
 
 
 def dfs_gemm_swiglu(X, Wg, Wu, H, stream=None, w_packed: bool = False):

@@ -390,6 +390,18 @@ int dfs_gemm(int32_t M, int32_t N, int32_t K, int32_t dtype, const void* X, cons
              float* Y, int32_t splits, int32_t w_packed, void* workspace, size_t workspace_bytes,
              void* stream);
 
+/* dfs_gemm with a skipped corner, the form dflash_draft_step's Q|K|V product takes
+ * (the new context rows need keys and values only, no queries): output tiles lying
+ * entirely inside rows [0, skip_m) x columns [0, skip_n) may be left uncomputed.
+ * Y outside that corner is X . W^T as for dfs_gemm; inside it Y is unspecified (untouched by the
+ * tiles the kernels skip, overwritten by a split-K reduction or by kernels that
+ * compute every tile).  0 <= skip_m <= M, 0 <= skip_n <= N; with a skipped corner
+ * `splits` must be >= 1 (the split count dfs_gemm_workspace_size was asked for).
+ * DFS_EINVAL otherwise; the other errors as for dfs_gemm. */
+int dfs_gemm_skip(int32_t M, int32_t N, int32_t K, int32_t dtype, const void* X, const void* W,
+                  float* Y, int32_t splits, int32_t w_packed, int32_t skip_m, int32_t skip_n,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
 /* H[M, F] bf16 = silu(X . Wg^T) * (X . Wu^T), the gated gate|up product of the
  * drafter's SwiGLU MLP (the layer form read for the DFlash drafter: pre-norm
  * attention then a SwiGLU MLP), computed in the epilogue of the drafter's

@@ -119,6 +119,16 @@ def test_invalid_arguments_rejected_on_host(lib):
     assert lib.markov_bias_sample(4, 3, 4194305, 0, fake, None, None, 1, fake, fake, 1.0, fake, None,
                                   fake, 1 << 30, None) == -2
     assert lib.markov_bias_sample_workspace_size(2, 2, 4194304) > 0
+    # GEMM with a skipped corner: corner inside the matrix, a split count when a corner is skipped
+    lib.dfs_gemm_skip.argtypes = [ctypes.c_int32] * 4 + [ctypes.c_void_p] * 3 + [ctypes.c_int32] * 4 + \
+        [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    gs = lambda sp, sm, sn, wsb=1 << 30: lib.dfs_gemm_skip(300, 1000, 512, 1, fake, fake, fake, sp, 0, sm, sn,
+                                                            fake, wsb, None)
+    assert gs(1, 301, 0) == -1                                 # skip_m > M
+    assert gs(1, 0, 1001) == -1                                # skip_n > N
+    assert gs(1, -1, 0) == -1
+    assert gs(0, 150, 512) == -1                               # automatic split count with a corner
+    assert gs(2, 150, 512, wsb=16) == -4
     lib.dfs_status_string.restype = ctypes.c_char_p
     assert lib.dfs_status_string(-4) == b"workspace too small"
 
