@@ -1136,6 +1136,7 @@ hipError_t launch_gemm(const GemmArgs& a, const GemmPlan& p, int dtype, hipStrea
   if (p.kind == 1) {
     const int mtl = ceil_div(a.M, p.bm), ntl = ceil_div(a.N, p.bn);
     const dim3 g1(gemm_tiles(p, a.M, a.N, a.gated ? 0 : a.skip_m, a.gated ? 0 : a.skip_n) * p.splits);
+    if (g1.x == 0) return hipSuccess;   // the skipped corner is the whole output
 #define DFS_STREAM(MT_, NW_, PD_, XD_)                                                                   \
   if (p.mt == MT_ && p.nw == NW_ && p.pd == PD_ && p.xd == XD_ && p.bn != 48 && p.bn != 96)              \
     return launch_stream<MT_, NW_, PD_, XD_>(a, g1, kps, mtl, ntl, s);
@@ -1233,6 +1234,7 @@ hipError_t launch_gemm(const GemmArgs& a, const GemmPlan& p, int dtype, hipStrea
     }
     const int mtl = ceil_div(a.M, p.bm), ntl = ceil_div(a.N, a.gated ? p.bn / 2 : p.bn);
     const dim3 g1((a.gated ? mtl * ntl : gemm_tiles(p, a.M, a.N, a.skip_m, a.skip_n)) * p.splits);
+    if (g1.x == 0) return hipSuccess;   // the skipped corner is the whole output
     if (p.bm == 256 && p.bn == 256) return launch_tile<256, 256>(a, g1, kps, mtl, ntl, s);
     return hipErrorInvalidValue;
   }
