@@ -610,26 +610,29 @@ __global__ __launch_bounds__(256) void gemm_short_bf16(GemmArgs a) {
 // the base logits, and for every row and 64-column sub-chunk of the output the
 // sub-chunk's max and sum exp2((x - max) * k) (k = log2(e) / T, fp32
 // exponentials summed in fp64), or for T == 0 (max, first column of the max).
-// One workgroup per (sub-chunk, chunk of 32 rows), one wave per 16-column W row
-// group: each wave issues its whole group (8 KB of W, the base rows) before the
-// X rows are staged in LDS, so a wave makes one memory round trip (about 60
+// One workgroup per (pair of sub-chunks, chunk of 32 rows), one wave per
+// 16-column W row group (waves 0-3 the first sub-chunk, 4-7 the second): each
+// wave issues its whole group (8 KB of W, the base rows) before the X rows are
+// staged in LDS — once for both sub-chunks, half the gathered-row traffic of one
+// workgroup per sub-chunk — so a wave makes one memory round trip (about 60
 // VGPRs a wave: at 32 rows the whole grid is resident at once).  The four waves
-// combine the sub-chunk's max, then its sum, through LDS.  The logits are read
+// of a sub-chunk combine its max, then its sum, through LDS.  The logits are read
 // once and written once; no separate statistics pass re-reads them.
 // sub[m * nsub + j] = (max, sum | first column).  The row chunks of a sub-chunk
-// take consecutive logical ids, which the XCD remap puts on one XCD, so its W
-// slab comes from HBM once and from that L2 after.
+// pair take consecutive logical ids, which the XCD remap puts on one XCD, so its
+// W slab comes from HBM once and from that L2 after.
 template <bool PACKED>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8)))
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(8, 8)))
 void head_gemm_stats_bf16(GemmArgs a, float T, double2* sub, int nsub, int nrc) {
   constexpr int K = 4 * BK, LDX = K + 8, MT = 2, R = 16 * MT;
   __shared__ __attribute__((aligned(16))) bf16_t Xs[R * LDX];
-  __shared__ float smax[4][R];
-  __shared__ double ssum[4][R];
-  __shared__ int sfirst[4][R];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, c = lane & 15, g4 = lane >> 4;
+  __shared__ float smax[8][R];
+  __shared__ double ssum[8][R];
+  __shared__ int sfirst[8][R];
+  const int tid = threadIdx.x, lane = tid & 63, wave8 = tid >> 6, c = lane & 15, g4 = lane >> 4;
   const int lid = nrc > 1 ? xcd_logical_id(blockIdx.x, gridDim.x) : blockIdx.x;
-  const int u = lid / nrc, m0 = (lid % nrc) * R, ng = ceil_div(a.N, 16);
+  const int hs = wave8 >> 2, wave = wave8 & 3;           // sub-chunk of the pair, wave in it
+  const int u = 2 * (lid / nrc) + hs, m0 = (lid % nrc) * R, ng = ceil_div(a.N, 16);
   const int mr = a.M - m0;                               // rows of this chunk: min(mr, R)
   const int gw = 4 * u + wave;                           // this wave's W row group
   const bool live = gw < ng;                             // uniform over the wave
@@ -650,7 +653,7 @@ void head_gemm_stats_bf16(GemmArgs a, float T, double2* sub, int nsub, int nrc) 
   for (int i = 0; i < MT; ++i)
     acc[i] = *(const f32x4*)(a.Y + (size_t)(m0 + min(i * 16 + c, mr - 1)) * a.ldy + min(n, a.N - 4));
   // X rows m0 .. m0+R-1 (rows past M repeat row M-1; their results are not stored)
-  for (int ch = tid; ch < R * (K / 8); ch += 256) {
+  for (int ch = tid; ch < R * (K / 8); ch += 512) {
     const int row = ch / (K / 8), col = (ch % (K / 8)) * 8;
     const int m = m0 + min(row, mr - 1);
     *(uint4*)&Xs[row * LDX + col] = ldg16((const bf16_t*)a.X + (size_t)x_row(a, m) * a.ldx + col);
@@ -677,14 +680,14 @@ void head_gemm_stats_bf16(GemmArgs a, float T, double2* sub, int nsub, int nrc) 
       for (int e = 0; e < 4; ++e) mx = fmaxf(mx, acc[i][e]);
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    if (g4 == 0) smax[wave][i * 16 + c] = mx;
+    if (g4 == 0) smax[wave8][i * 16 + c] = mx;
   }
   __syncthreads();
   const float kk = T > 0.f ? kLog2eF / T : 0.f;
 #pragma unroll
   for (int i = 0; i < MT; ++i) {
     const int row = i * 16 + c;
-    const float mx = fmaxf(fmaxf(smax[0][row], smax[1][row]), fmaxf(smax[2][row], smax[3][row]));
+    const float mx = fmaxf(fmaxf(smax[4 * hs][row], smax[4 * hs + 1][row]), fmaxf(smax[4 * hs + 2][row], smax[4 * hs + 3][row]));
     if (T > 0.f) {
       double sl = 0.0;
       if (cols && mx != -INFINITY)
@@ -692,7 +695,7 @@ void head_gemm_stats_bf16(GemmArgs a, float T, double2* sub, int nsub, int nrc) 
         for (int e = 0; e < 4; ++e) sl += (double)exp2f((acc[i][e] - mx) * kk);
       sl += __shfl_xor(sl, 16, 64);                      // g4 pairs (0,1), (2,3), then the two pairs
       sl += __shfl_xor(sl, 32, 64);
-      if (g4 == 0) ssum[wave][row] = sl;
+      if (g4 == 0) ssum[wave8][row] = sl;
     } else {
       int first = 0x7fffffff;
       if (cols)
@@ -701,20 +704,21 @@ void head_gemm_stats_bf16(GemmArgs a, float T, double2* sub, int nsub, int nrc) 
           if (acc[i][e] == mx) first = n + e;
       first = min(first, __shfl_xor(first, 16, 64));
       first = min(first, __shfl_xor(first, 32, 64));
-      if (g4 == 0) sfirst[wave][row] = first;
+      if (g4 == 0) sfirst[wave8][row] = first;
     }
   }
   __syncthreads();
-  if (tid < R && tid < mr) {                             // wave 0 writes one row's entry per lane
-    const float mx = fmaxf(fmaxf(smax[0][tid], smax[1][tid]), fmaxf(smax[2][tid], smax[3][tid]));
+  const int th = tid & 63, o = 4 * hs;                   // lanes of wave 0 (sub-chunk 0) and wave 4 (sub-chunk 1)
+  if (wave == 0 && th < R && th < mr && u < nsub) {
+    const float mx = fmaxf(fmaxf(smax[o][th], smax[o + 1][th]), fmaxf(smax[o + 2][th], smax[o + 3][th]));
     double r;
     if (T > 0.f) {
-      r = (ssum[0][tid] + ssum[1][tid]) + (ssum[2][tid] + ssum[3][tid]);
+      r = (ssum[o][th] + ssum[o + 1][th]) + (ssum[o + 2][th] + ssum[o + 3][th]);
     } else {
-      const int f = min(min(sfirst[0][tid], sfirst[1][tid]), min(sfirst[2][tid], sfirst[3][tid]));
+      const int f = min(min(sfirst[o][th], sfirst[o + 1][th]), min(sfirst[o + 2][th], sfirst[o + 3][th]));
       r = f == 0x7fffffff ? -1.0 : (double)f;
     }
-    sub[(size_t)(m0 + tid) * nsub + u] = make_double2((double)mx, r);
+    sub[(size_t)(m0 + th) * nsub + u] = make_double2((double)mx, r);
   }
 }
 
@@ -1247,9 +1251,9 @@ hipError_t launch_head_gemm_stats(const GemmArgs& a, float temperature, double2*
                   a.accumulate;
   if (!ok) return hipErrorInvalidValue;
   const int nsub = ceil_div(a.N, 64), nrc = ceil_div(a.M, 32);
-  const dim3 grid(nsub * nrc);
-  if (a.packed) hipLaunchKernelGGL(head_gemm_stats_bf16<true>, grid, dim3(256), 0, s, a, temperature, sub, nsub, nrc);
-  else hipLaunchKernelGGL(head_gemm_stats_bf16<false>, grid, dim3(256), 0, s, a, temperature, sub, nsub, nrc);
+  const dim3 grid(ceil_div(nsub, 2) * nrc);
+  if (a.packed) hipLaunchKernelGGL(head_gemm_stats_bf16<true>, grid, dim3(512), 0, s, a, temperature, sub, nsub, nrc);
+  else hipLaunchKernelGGL(head_gemm_stats_bf16<false>, grid, dim3(512), 0, s, a, temperature, sub, nsub, nrc);
   return hipGetLastError();
 }
 
